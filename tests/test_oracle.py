@@ -1,0 +1,373 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test compares the oracle with something other than itself: values the
+pages print (tests/golden), hand-worked values, library routines (numpy's
+binary16, torch's bfloat16, numpy float64 matmul and lexsort), closed forms
+and special cases.
+"""
+import math
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import accept
+from tests.conftest import read_golden
+
+F32, BF16, Q8_0 = oracle.F32, oracle.BF16, oracle.Q8_0
+DT = {"f32": F32, "bf16": BF16, "q8_0": Q8_0}
+
+
+# ---------------------------------------------------------------- sizes (pages)
+def test_row_and_table_sizes_match_pages():
+    for name, dt, V, d, qty, expected, unit, src in read_golden("sizes.txt"):
+        rb = oracle.row_bytes(DT[dt], int(d))
+        n = rb * int(V)
+        if unit == "B":
+            got = n
+            assert got == int(expected), (name, got, expected, src)
+            continue
+        div, nd = {"KiB1": (1024, 1), "kB1": (1000, 1), "MiB2": (1024 ** 2, 2), "GB2": (1e9, 2)}[unit]
+        assert round(n / div, nd) == float(expected), (name, n / div, expected, src)
+
+
+def test_row_bytes_rejects_bad_shapes():
+    assert oracle.row_bytes(Q8_0, 48) == -1      # not a whole number of 32-value blocks
+    assert oracle.row_bytes(BF16, 0) == -1
+    assert oracle.row_bytes(7, 64) == -1
+    assert oracle.row_bytes(Q8_0, 768) == 816
+
+
+# ---------------------------------------------------------------- decoders
+def test_f16_decoder_matches_numpy_for_every_pattern():
+    bits = np.arange(65536, dtype=np.uint16)
+    got = oracle.f16_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signs of zeros too
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_decoder_matches_torch_for_every_pattern():
+    bits = np.arange(65536, dtype=np.uint16)
+    got = oracle.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def _q8_row(blocks):
+    """blocks: list of (scale_bits, [32 ints]) -> bytes of one Q8_0 row."""
+    raw = b""
+    for sbits, qs in blocks:
+        raw += struct.pack("<H", sbits) + struct.pack("<32b", *qs)
+    return np.frombuffer(raw, np.uint8)
+
+
+def test_q8_0_hand_built_blocks():
+    rows = read_golden("q8_0_blocks.txt")
+    for sbits_s, q_s, expected, note in rows:
+        sbits, q = int(sbits_s, 16), int(q_s)
+        qs = [0] * 32
+        qs[5] = q
+        qs[31] = q
+        row = _q8_row([(0x3C00, list(range(-16, 16))), (sbits, qs)])
+        x = oracle.dequant_row(row, Q8_0, 64)
+        want = float(Fraction(expected))
+        assert x[32 + 5] == want and x[32 + 31] == want, (note, x[37], want)
+        # the first block (scale 1.0) decodes to its integers
+        assert np.array_equal(x[:32], np.arange(-16, 16, dtype=np.float64))
+        # values are exact in float32
+        assert float(np.float32(x[37])) == x[37]
+
+
+def test_q8_0_block_order_and_signed_bytes():
+    # value c of the row lives in block c // 32 at byte 2 + c % 32; bytes are signed
+    qs0 = [(-128 + 7 * j) for j in range(32)]
+    qs1 = [(127 - 3 * j) for j in range(32)]
+    row = _q8_row([(0x4000, qs0), (0x3800, qs1)])      # scales 2.0 and 0.5
+    x = oracle.dequant_row(row, Q8_0, 64)
+    assert np.array_equal(x[:32], 2.0 * np.array(qs0, np.float64))
+    assert np.array_equal(x[32:], 0.5 * np.array(qs1, np.float64))
+
+
+# ---------------------------------------------------------------- embedding scale
+def test_sqrt_d_is_nearest_f32_to_sqrt_768():
+    (hidden, hexbits, dec), = read_golden("embed_scale.txt")
+    got = oracle.sqrt_d(int(hidden))
+    bits = struct.unpack("<I", struct.pack("<f", float(got)))[0]
+    assert bits == int(hexbits, 16)
+    assert float(got) == float(dec)
+    # independent check with exact rationals: no other f32 lies closer to sqrt(768)
+    f = Fraction(float(got))
+    up = Fraction(float(np.nextafter(np.float32(got), np.float32(np.inf))))
+    dn = Fraction(float(np.nextafter(np.float32(got), np.float32(-np.inf))))
+    # compare squared distances |f - s| with s^2 = 768 via midpoints: s lies between the midpoints
+    assert ((f + dn) / 2) ** 2 < 768 < ((f + up) / 2) ** 2
+
+
+@pytest.mark.parametrize("d", [1, 2, 3, 256, 768, 896, 5120, 5376, 12345])
+def test_sqrt_d_matches_midpoint_bracket(d):
+    got = np.float32(oracle.sqrt_d(d))
+    f = Fraction(float(got))
+    up = Fraction(float(np.nextafter(got, np.float32(np.inf))))
+    dn = Fraction(float(np.nextafter(got, np.float32(-np.inf))))
+    assert ((f + dn) / 2) ** 2 <= d <= ((f + up) / 2) ** 2
+
+
+# ---------------------------------------------------------------- gather
+def _table(dtype, V, d, seed=0):
+    g = np.random.default_rng(seed)
+    if dtype == F32:
+        return (g.standard_normal((V, d)) * 0.02).astype(np.float32)
+    if dtype == BF16:
+        x = torch.from_numpy((g.standard_normal((V, d)) * 0.02).astype(np.float32))
+        return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nb = d // 32
+    out = np.empty((V, nb, 34), np.uint8)
+    sc = np.abs(g.standard_normal((V, nb)) * 0.01).astype(np.float16)
+    out[:, :, :2] = sc.view(np.uint8).reshape(V, nb, 2)
+    out[:, :, 2:] = g.integers(-128, 128, (V, nb, 32)).astype(np.int8).view(np.uint8)
+    return out.reshape(V, nb * 34)
+
+
+def _library_dequant(table, dtype, V, d):
+    """Dequantize with library routines only (numpy binary16, torch bfloat16)."""
+    if dtype == F32:
+        return table.astype(np.float64)
+    if dtype == BF16:
+        return torch.from_numpy(table.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    blk = table.reshape(V, d // 32, 34)
+    s = blk[:, :, :2].copy().view("<f2").astype(np.float64)          # [V, nb, 1]
+    q = blk[:, :, 2:].view(np.int8).astype(np.float64)                # [V, nb, 32]
+    return (q * s).reshape(V, d)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16, Q8_0])
+def test_gather_equals_library_dequant_rows(dtype):
+    V, d = 300, 96
+    t = _table(dtype, V, d, seed=dtype)
+    ids = np.array([0, 299, 5, 5, 17, 299, 0], np.int32)
+    out, bad = oracle.embed_gather(t, dtype, V, d, ids)
+    ref = _library_dequant(t, dtype, V, d)[ids].astype(np.float32)
+    assert bad == 0
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16, Q8_0])
+def test_gather_scale_is_one_f32_rounding(dtype):
+    V, d = 64, 768
+    t = _table(dtype, V, d, seed=10 + dtype)
+    ids = np.arange(V, dtype=np.int32)[::-1].copy()
+    s = np.float32(math.sqrt(d))
+    out, _ = oracle.embed_gather(t, dtype, V, d, ids, scale=s)
+    x = _library_dequant(t, dtype, V, d)[ids].astype(np.float32)
+    ref = x * s                      # numpy float32 multiply: one IEEE round-to-nearest-even
+    assert ref.dtype == np.float32
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    # and it is not the same as multiplying by the scale in a different order for Q8_0
+    if dtype == Q8_0:
+        blk = t.reshape(V, d // 32, 34)
+        sc = blk[:, :, :2].copy().view("<f2").astype(np.float32)
+        q = blk[:, :, 2:].view(np.int8).astype(np.float32)
+        other = (q * (sc * s)).reshape(V, d)[ids]
+        assert not np.array_equal(other.view(np.uint32), out.view(np.uint32))
+
+
+def test_gather_address_pin_rows_encode_their_id():
+    V, d = 4097, 8
+    t = np.zeros((V, d), np.float32)
+    t[:, :] = np.arange(V, dtype=np.float32)[:, None] * 16 + np.arange(d, dtype=np.float32)
+    ids = np.array([4096, 0, 1, 4095, 2048, 1], np.int32)
+    out, bad = oracle.embed_gather(t, F32, V, d, ids)
+    assert bad == 0
+    assert np.array_equal(out, ids[:, None].astype(np.float32) * 16 + np.arange(d, dtype=np.float32))
+
+
+def test_gather_64bit_offsets_past_2_and_4_gib():
+    # 31B-shaped rows (hidden 5376, bf16 -> 10,752 B): id 199,729 starts past 2^31 bytes
+    # and id 399,458 past 2^32 bytes.
+    d = 5376
+    V = 399_460
+    rb = 2 * d
+    assert 199_729 * rb > 2 ** 31 > 199_728 * rb
+    assert 399_458 * rb > 2 ** 32 > 399_457 * rb
+    t = np.zeros((V, d), np.uint16)          # calloc'd: only touched rows are backed
+    rows = (0, 1, 199_728, 199_729, 199_730, 399_457, 399_458, 399_459)
+    for i in rows:
+        t[i, :] = 0x3F80 + (i % 64)          # bf16 1 + (i % 64) / 128
+    ids = np.array([199_729, 0, 399_458, 199_730, 399_459, 199_728, 1, 399_457], np.int32)
+    out, bad = oracle.embed_gather(t, BF16, V, d, ids)
+    assert bad == 0
+    want = 1.0 + (ids % 64) / 128.0
+    assert np.array_equal(out, np.repeat(want[:, None], d, axis=1).astype(np.float32))
+
+
+def test_gather_bad_ids_zero_rows_and_count():
+    V, d = 100, 32
+    t = _table(BF16, V, d)
+    ids = np.array([3, -1, 100, 2 ** 31 - 1, 99, -(2 ** 31)], np.int32)
+    out, bad = oracle.embed_gather(t, BF16, V, d, ids, scale=np.float32(2.0))
+    assert bad == 4
+    for j in (1, 2, 3, 5):
+        assert np.array_equal(out[j].view(np.uint32), np.zeros(d, np.uint32))
+    ref = _library_dequant(t, BF16, V, d)
+    assert np.array_equal(out[0], (ref[3] * 2).astype(np.float32))
+    assert np.array_equal(out[4], (ref[99] * 2).astype(np.float32))
+
+
+def test_gather_empty():
+    t = _table(F32, 10, 8)
+    out, bad = oracle.embed_gather(t, F32, 10, 8, np.zeros(0, np.int32))
+    assert out.shape == (0, 8) and bad == 0
+
+
+# ---------------------------------------------------------------- logits
+@pytest.mark.parametrize("dtype", [F32, BF16, Q8_0])
+def test_logits_match_numpy_float64(dtype):
+    V, d, B = 517, 256, 3
+    t = _table(dtype, V, d, seed=20 + dtype)
+    R = np.random.default_rng(5).standard_normal((B, d)).astype(np.float32)
+    L, A = oracle.logits(t, dtype, V, d, R)
+    E = _library_dequant(t, dtype, V, d)
+    Lref = R.astype(np.float64) @ E.T
+    Aref = np.abs(R.astype(np.float64)) @ np.abs(E).T
+    assert np.all(np.abs(L - Lref) <= 1e-12 * Aref)
+    assert np.allclose(A, Aref, rtol=1e-13, atol=0)
+
+
+def test_logits_one_hot_residual_selects_a_column_exactly():
+    V, d = 300, 64
+    t = _table(BF16, V, d, seed=3)
+    E = _library_dequant(t, BF16, V, d)
+    for j in (0, 17, 63):
+        r = np.zeros((1, d), np.float32)
+        r[0, j] = 1.0
+        L, _ = oracle.logits(t, BF16, V, d, r)
+        assert np.array_equal(L[0], E[:, j])
+
+
+def test_logits_are_not_transposed_or_shifted():
+    # a table whose row v is v * e_0 and residual e_0: logits are exactly 0, 1, 2, ...
+    V, d = 50, 32
+    t = np.zeros((V, d), np.float32)
+    t[:, 0] = np.arange(V)
+    t[:, 1] = 1000.0            # ignored by the residual below
+    r = np.zeros((2, d), np.float32)
+    r[0, 0] = 1.0
+    r[1, 0] = -2.0
+    L, A = oracle.logits(t, F32, V, d, r)
+    assert np.array_equal(L[0], np.arange(V, dtype=np.float64))
+    assert np.array_equal(L[1], -2.0 * np.arange(V))
+    assert np.array_equal(A[1], 2.0 * np.arange(V))
+
+
+def test_logits_at_matches_full_logits():
+    V, d, B = 200, 96, 4
+    t = _table(Q8_0, V, d, seed=7)
+    R = np.random.default_rng(9).standard_normal((B, d)).astype(np.float32)
+    L, A = oracle.logits(t, Q8_0, V, d, R)
+    bs = np.array([0, 3, 3, 1])
+    vs = np.array([199, 0, 57, 57], np.int32)
+    l2, a2 = oracle.logits_at(t, Q8_0, V, d, R, bs, vs)
+    assert np.array_equal(l2, L[bs, vs]) and np.array_equal(a2, A[bs, vs])
+
+
+# ---------------------------------------------------------------- top-k
+def test_topk_matches_lexsort_on_random_logits():
+    g = np.random.default_rng(11)
+    L = g.standard_normal((6, 1000))
+    L[2, 10:20] = L[2, 5]                    # ties resolved by the smaller id
+    for k in (1, 5, 64):
+        ids, sc = oracle.topk(L, k)
+        for b in range(L.shape[0]):
+            order = np.lexsort((np.arange(L.shape[1]), -L[b]))
+            assert np.array_equal(ids[b], order[:k])
+            assert np.array_equal(sc[b], L[b, order[:k]].astype(np.float32))
+
+
+def test_topk_k1_is_argmax():
+    g = np.random.default_rng(12)
+    L = np.round(g.standard_normal((5, 300)), 1)       # many exact ties
+    ids, _ = oracle.topk(L, 1)
+    assert np.array_equal(ids[:, 0], np.argmax(L, axis=1))
+
+
+def test_zero_residual_gives_first_k_ids():
+    V, d = 40, 32
+    t = _table(BF16, V, d, seed=1)
+    L, _ = oracle.logits(t, BF16, V, d, np.zeros((1, d), np.float32))
+    ids, sc = oracle.topk(L, 7)
+    assert np.array_equal(ids[0], np.arange(7))
+    assert np.all(sc == 0)
+
+
+def test_negative_zero_ties_with_positive_zero():
+    L = np.array([[-0.0, 0.0, -1.0, -0.0, 0.0]])
+    ids, _ = oracle.topk(L, 4)
+    assert np.array_equal(ids[0], [0, 1, 3, 4])
+
+
+def test_duplicate_rows_rank_by_id():
+    V, d = 64, 32
+    t = _table(F32, V, d, seed=4) * 0.01
+    r = np.random.default_rng(6).standard_normal((1, d)).astype(np.float32)
+    best = (r[0] / np.linalg.norm(r[0])).astype(np.float32)
+    for v in (41, 3, 17):
+        t[v] = best
+    L, _ = oracle.logits(t, F32, V, d, r)
+    ids, _ = oracle.topk(L, 3)
+    assert np.array_equal(ids[0], [3, 17, 41])
+
+
+def test_planted_winners_come_out_in_order():
+    V, d = 2000, 128
+    t = _table(F32, V, d, seed=8)
+    r = np.random.default_rng(13).standard_normal((1, d)).astype(np.float32)
+    u = r[0] / np.linalg.norm(r[0])
+    planted = [1234, 7, 1999, 512]
+    for j, v in enumerate(planted):
+        t[v] = (u * (10.0 - j)).astype(np.float32)
+    L, _ = oracle.logits(t, F32, V, d, r)
+    ids, _ = oracle.topk(L, 4)
+    assert list(ids[0]) == planted
+
+
+def test_permuting_rows_permutes_ids():
+    V, d = 500, 64
+    t = _table(BF16, V, d, seed=14)
+    R = np.random.default_rng(15).standard_normal((2, d)).astype(np.float32)
+    perm = np.random.default_rng(16).permutation(V)
+    L1, _ = oracle.logits(t, BF16, V, d, R)
+    L2, _ = oracle.logits(t[perm], BF16, V, d, R)
+    assert np.array_equal(L2, L1[:, perm])
+    i1, _ = oracle.topk(L1, 10)
+    i2, _ = oracle.topk(L2, 10)
+    inv = np.argsort(perm)
+    assert np.array_equal(inv[i1], i2)
+
+
+# ---------------------------------------------------------------- acceptance rule
+def test_acceptance_rule_accepts_exact_and_rejects_wrong():
+    V, d = 300, 64
+    t = _table(BF16, V, d, seed=17)
+    R = np.random.default_rng(18).standard_normal((2, d)).astype(np.float32)
+    L, A = oracle.logits(t, BF16, V, d, R)
+    ids, sc = oracle.topk(L, 5)
+    assert accept.check_full(ids, sc, L, A, ids, 2e-3) == []
+    bad = ids.copy()
+    bad[0, 0] = np.argmin(L[0])                        # a clearly wrong id
+    assert accept.check_full(bad, sc, L, A, ids, 2e-3)
+    dup = ids.copy()
+    dup[1, 1] = dup[1, 0]
+    assert accept.check_full(dup, sc, L, A, ids, 2e-3)
+    inc = sc.copy()
+    inc[0] = inc[0][::-1]
+    assert accept.check_full(ids, inc, L, A, ids, 2e-3)
