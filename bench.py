@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the static embedding / tied lm_head service on one MI355X.
+
+A step is one decode step of the service on the 31B-shaped tied table
+(bf16, V = 262,144, hidden = 5,376, 2.82 GB): embed_gather of one token id
+(ADR-0008 "POST /v1/embed") and logits_topk of one residual with k = 10
+(ADR-0008 "POST /v1/logits"), which streams the whole table once.  Inputs are
+seeded synthetic arrays (synth/), resident in HBM before the timed region.
+
+value = algorithmic bytes of the step / time per step, in GB/s.  The roofline
+object times the table-streaming kernel alone with HIP events recorded on the
+stream it runs on.  The other workloads of the page set (batches of 8 and 64,
+the 1,024-row contraction, the EmbeddingGemma-shaped Q8_0 gather) are measured
+after the timed steps and reported under "also".  The CPU oracle is timed on a
+bounded sample of the same workload under "cpu_baseline".
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "embedding_table_gather_amd", "csrc", "logits.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the kernel source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel)
+    if not ent or ent.get("source_sha256_16") != _source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def _timed(torch, fn, iters: int, events: bool = False):
+    """Average ms per call of fn(); with events=True fn takes (ev_before, ev_after)
+    and the mean kernel ms between them is returned too."""
+    E = torch.cuda.Event
+    evs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(iters)] if events else None
+    s, e = E(enable_timing=True), E(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for i in range(iters):
+        fn(evs[i]) if events else fn()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / iters
+    kms = sum(a.elapsed_time(b) for a, b in evs) / iters if events else None
+    return ms, kms
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="only the timed decode steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the vocab-sharded multi-GPU design is not built", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import embedding_table_gather_amd as etg
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.CONFIGS["lm31b"]
+    B, k = 1, 10
+    log(f"generating the {cfg.name} table ({cfg.table_bytes / 1e9:.2f} GB)")
+    t0 = time.time()
+    host = cfg.table()
+    log(f"generated in {time.time() - t0:.1f} s; uploading")
+    rows = torch.from_numpy(host.view(np.int16)).to(dev)
+    table = etg.Table(rows, cfg.dtype, cfg.V, cfg.d)
+    ids = torch.from_numpy(synth.zipf_ids(B, cfg.V, cfg.ids_seed)).to(dev)
+    R = torch.from_numpy(cfg.residuals(B)).to(dev)
+    x = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
+    ws = table.workspace(B, k)
+    oid = torch.empty((B, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((B, k), dtype=torch.float32, device=dev)
+
+    def step(evs=None):
+        table.embed_gather(ids, out=x, check=False)
+        table.logits_topk(R, k, workspace=ws, out_ids=oid, out_scores=osc, events=evs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ms, kms = _timed(torch, step, args.steps, events=True)
+
+    gather_bytes = B * cfg.row_bytes + B * cfg.d * 4 + B * 4
+    logits_bytes = cfg.table_bytes + B * cfg.d * 4 + B * k * 8
+    step_bytes = gather_bytes + logits_bytes
+    value = step_bytes / (ms * 1e-3) / 1e9
+    kernel_name = "stream_logits_kernel<1>"
+    achieved = cfg.table_bytes / (kms * 1e-3) / 1e9
+    traffic = _traffic(kernel_name)
+    out = {
+        "metric": "lm_head logits+top-k GB/s (% HBM peak) at V=262144; gather rows/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 table, N(0,1) residual)",
+        "config": {
+            "workload": "31B-shaped tied lm_head decode step: embed_gather(1 id) + logits_topk(1 residual, k=10)",
+            "table_dtype": "bf16", "vocab": cfg.V, "hidden": cfg.d, "batch": B, "k": k,
+            "table_bytes": cfg.table_bytes,
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 1),
+        "roofline": {
+            "kernel": kernel_name,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel_us": round(kms * 1e3, 2),
+            "bytes_per_launch": cfg.table_bytes,
+        },
+    }
+    log(f"step {ms * 1e3:.1f} us, table kernel {kms * 1e3:.1f} us -> {achieved:.0f} GB/s")
+
+    also = {}
+    if not args.no_extras:
+        for b in (8, 64):
+            Rb = torch.from_numpy(cfg.residuals(b)).to(dev)
+            wsb = table.workspace(b, k)
+            f = lambda evs=None: table.logits_topk(Rb, k, workspace=wsb, events=evs)
+            f()
+            mb, kb = _timed(torch, f, 20, events=True)
+            also[f"lm31b_logits_top10_B{b}"] = {
+                "us_per_call": round(mb * 1e3, 1), "kernel_us": round(kb * 1e3, 1),
+                "GBps": round(cfg.table_bytes / (mb * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * cfg.table_bytes / (mb * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
+            log(f"B={b}: {mb * 1e3:.1f} us")
+    del table, rows
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        g = synth.CONFIGS["gemma_embed"]
+        gh = g.table()
+        gt = etg.Table(torch.from_numpy(gh).to(dev), g.dtype, g.V, g.d)
+        gids_host = g.ids()
+        gids = torch.from_numpy(gids_host).to(dev)
+        gx = torch.empty((gids.numel(), g.d), dtype=torch.float32, device=dev)
+        f = lambda: gt.embed_gather(gids, scale="sqrt_d", out=gx, check=False)
+        f()
+        mg, _ = _timed(torch, f, 100)
+        U = int(np.unique(gids_host).size)
+        alg = U * g.row_bytes + gids.numel() * g.d * 4 + gids.numel() * 4
+        also["gemma_embed_gather_q8_0_x_sqrt_d"] = {
+            "rows": int(gids.numel()), "distinct_rows": U, "us_per_call": round(mg * 1e3, 2),
+            "rows_per_s": round(gids.numel() / (mg * 1e-3)), "alg_GBps": round(alg / (mg * 1e-3) / 1e9, 1)}
+        out["gather_rows_per_s"] = also["gemma_embed_gather_q8_0_x_sqrt_d"]["rows_per_s"]
+        log(f"gather: {mg * 1e3:.1f} us")
+        del gt
+        torch.cuda.empty_cache()
+
+        p = synth.CONFIGS["prefill"]
+        ph = p.table()
+        pt = etg.Table(torch.from_numpy(ph.view(np.int16)).to(dev), p.dtype, p.V, p.d)
+        del ph
+        Bp = p.batches[0]
+        Rp = torch.from_numpy(p.residuals(Bp)).to(dev)
+        wsp = pt.workspace(Bp, p.k)
+        f = lambda evs=None: pt.logits_topk(Rp, p.k, workspace=wsp, events=evs)
+        f()
+        mp, kp = _timed(torch, f, 5, events=True)
+        flops = 2.0 * Bp * p.V * p.d
+        also["prefill_logits_top40_B1024"] = {
+            "ms_per_call": round(mp, 3), "kernel_ms": round(kp, 3),
+            "TFLOPs": round(flops / (mp * 1e-3) / 1e12, 1),
+            "pct_bf16_mfma_peak": round(100 * flops / (mp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1)}
+        log(f"prefill B=1024: {mp:.2f} ms")
+        del pt
+        torch.cuda.empty_cache()
+    if also:
+        out["also"] = also
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = 1 << 30
+
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the CPU oracle on the same decode workload")
+        Rh = cfg.residuals(B)
+        reps, t_cpu = 0, 0.0
+        while reps < 5 and t_cpu < 10.0:
+            t1 = time.perf_counter()
+            L, _ = oracle.logits(host, cfg.dtype, cfg.V, cfg.d, Rh)
+            oracle.topk(L, k)
+            t_cpu += time.perf_counter() - t1
+            reps += 1
+        out["cpu_baseline"] = {
+            "value": round(cfg.table_bytes * reps / t_cpu / 1e9, 3),
+            "unit": "GB/s",
+            "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full pass(es) of logits+top-10 for 1 residual over the "
+                      f"262,144 x 5,376 bf16 table (f64 accumulation), {t_cpu:.1f} s",
+        }
+        log(f"oracle: {reps} passes in {t_cpu:.1f} s")
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,215 @@
+"""Python binding of libetg: the static embedding / tied lm_head service on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+``libetg.so`` (built in-tree by ``embedding_table_gather_amd/build.py``);
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: if the library is missing, every call raises.
+
+    t = Table(rows, BF16, vocab, hidden)          # rows: device tensor, borrowed
+    x = t.embed_gather(ids)                       # ADR-0008 "POST /v1/embed"
+    ids, scores = t.logits_topk(residual, k=10)   # ADR-0008 "POST /v1/logits"
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+F32, BF16, Q8_0 = 0, 1, 2
+PATH_AUTO, PATH_VALU, PATH_STREAM, PATH_GEMM = 0, 1, 2, 3
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libetg.so")
+
+_STATUS = {
+    0: "ETG_OK", -1: "ETG_EINVAL", -2: "ETG_EDTYPE", -3: "ETG_ESHAPE", -4: "ETG_EALIGN",
+    -5: "ETG_ERANGE", -6: "ETG_EWORKSPACE", -8: "ETG_EHIP",
+}
+
+# Functions declared in include/etg.h, with their ctypes signatures.
+_I32, _I64, _VP, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+SIGNATURES = {
+    "etg_version": (_I32, []),
+    "etg_row_bytes": (_I64, [_I32, _I64]),
+    "etg_sqrt_d": (_F, [_I64]),
+    "etg_table_create": (_I32, [_VP, _I32, _I64, _I64, ctypes.POINTER(_VP)]),
+    "etg_table_destroy": (_I32, [_VP]),
+    "etg_embed_gather": (_I32, [_VP, _VP, _I64, _F, _VP, _VP, _VP]),
+    "etg_logits_topk_workspace": (_I64, [_VP, _I64, _I32]),
+    "etg_logits_topk_workspace_ex": (_I64, [_VP, _I64, _I32, _I32]),
+    "etg_logits_topk": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    "etg_logits_topk_ex": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP]),
+    "etg_logits_topk_profiled": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP, _VP,
+                                        _VP]),
+    "etg_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class EtgError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libetg.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with embedding_table_gather_amd/build.py "
+                               "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise EtgError(status, lib().etg_last_error().decode())
+
+
+def row_bytes(dtype: int, hidden: int) -> int:
+    return int(lib().etg_row_bytes(int(dtype), int(hidden)))
+
+
+def sqrt_d(hidden: int) -> float:
+    return float(lib().etg_sqrt_d(int(hidden)))
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _event_handle(ev: torch.cuda.Event, device: torch.device) -> int:
+    """The hipEvent_t behind a torch event (created on first record)."""
+    if ev.cuda_event == 0:
+        ev.record(torch.cuda.current_stream(device))
+    return ev.cuda_event
+
+
+class Table:
+    """A V x hidden table already in device memory (f32, bf16 or Q8_0 rows).
+
+    ``rows`` is any contiguous CUDA tensor holding exactly vocab * row_bytes bytes
+    (e.g. uint16 [V, d] bf16 bits, float32 [V, d], uint8 [V, 34 d / 32]).  It is
+    borrowed: the handle keeps a reference but never copies it.
+    """
+
+    def __init__(self, rows: torch.Tensor, dtype: int, vocab: int, hidden: int):
+        if not rows.is_cuda:
+            raise ValueError("table rows must be a device tensor")
+        if not rows.is_contiguous():
+            raise ValueError("table rows must be contiguous")
+        rb = row_bytes(dtype, hidden)
+        if rb < 0:
+            raise ValueError(f"hidden {hidden} cannot be stored as dtype {dtype}")
+        nbytes = rows.numel() * rows.element_size()
+        if nbytes != vocab * rb:
+            raise ValueError(f"rows hold {nbytes} bytes, expected {vocab} * {rb}")
+        self.rows, self.dtype, self.vocab, self.hidden, self.row_bytes = rows, int(dtype), int(vocab), int(hidden), rb
+        self.device = rows.device
+        h = ctypes.c_void_p()
+        _check(lib().etg_table_create(_ptr(rows), self.dtype, self.vocab, self.hidden, ctypes.byref(h)))
+        self._h = h
+        self._ws = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.etg_table_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    # ------------------------------------------------------------------ gather
+    def embed_gather(self, ids: torch.Tensor, scale=None, out: torch.Tensor | None = None,
+                     bad_count: torch.Tensor | None = None, check: bool = True) -> torch.Tensor:
+        """f32 [n, hidden] rows for int32 ids (ADR-0008 "POST /v1/embed").
+
+        scale: None (no scale), "sqrt_d" (the f32 nearest sqrt(hidden)), or a number.
+        check: count bad ids on the device, synchronize, and raise ValueError if
+        any; with check=False nothing waits (bad rows are still zero-filled, and
+        counted into ``bad_count`` if one is given).
+        """
+        if ids.dtype != torch.int32 or ids.device != self.device:
+            raise ValueError("ids must be an int32 tensor on the table's device")
+        ids = ids.contiguous().view(-1)
+        n = ids.numel()
+        sc = 1.0 if scale is None else (sqrt_d(self.hidden) if scale == "sqrt_d" else float(scale))
+        if out is None:
+            out = torch.empty((n, self.hidden), dtype=torch.float32, device=self.device)
+        elif out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != n * self.hidden:
+            raise ValueError("out must be a contiguous float32 tensor of n * hidden values")
+        if check and bad_count is None:
+            bad_count = torch.zeros(1, dtype=torch.int32, device=self.device)
+        bad_ptr = _ptr(bad_count) if bad_count is not None else None
+        with torch.cuda.device(self.device):
+            _check(lib().etg_embed_gather(self._h, _ptr(ids), n, sc, _ptr(out), bad_ptr,
+                                          _stream_ptr(self.device)))
+            if check:
+                nbad = int(bad_count.item())
+                if nbad:
+                    raise ValueError(f"bad token id: {nbad} of {n} ids are not in [0, {self.vocab})")
+        return out
+
+    # ------------------------------------------------------------------ logits
+    def workspace_bytes(self, batch: int, k: int, path: int = PATH_AUTO) -> int:
+        n = int(lib().etg_logits_topk_workspace_ex(self._h, int(batch), int(k), int(path)))
+        if n < 0:
+            _check(n)
+        return n
+
+    def workspace(self, batch: int, k: int, path: int = PATH_AUTO) -> torch.Tensor:
+        key = (int(batch), int(k), int(path))
+        ws = self._ws.get(key)
+        if ws is None:
+            ws = torch.empty(max(self.workspace_bytes(batch, k, path), 256), dtype=torch.uint8, device=self.device)
+            self._ws[key] = ws
+        return ws
+
+    def logits_topk(self, residual: torch.Tensor, k: int, path: int = PATH_AUTO,
+                    workspace: torch.Tensor | None = None, out_ids: torch.Tensor | None = None,
+                    out_scores: torch.Tensor | None = None, events=None):
+        """Top-k (ids int32 [B, k], logits f32 [B, k]) of residual @ table.T per row.
+
+        events: optional (before, after) torch.cuda.Event pair, recorded around the
+        kernel that streams the table (for timing that kernel alone).
+        """
+        if residual.dtype != torch.float32 or residual.device != self.device:
+            raise ValueError("residual must be a float32 tensor on the table's device")
+        R = residual.contiguous().view(-1, self.hidden)
+        B = R.shape[0]
+        if workspace is None:
+            workspace = self.workspace(B, k, path)
+        if out_ids is None:
+            out_ids = torch.empty((B, k), dtype=torch.int32, device=self.device)
+        if out_scores is None:
+            out_scores = torch.empty((B, k), dtype=torch.float32, device=self.device)
+        ev0 = ev1 = None
+        if events is not None:
+            ev0, ev1 = (ctypes.c_void_p(_event_handle(e, self.device)) for e in events)
+        with torch.cuda.device(self.device):
+            _check(lib().etg_logits_topk_profiled(self._h, _ptr(R), B, int(k), _ptr(out_ids), _ptr(out_scores),
+                                                  _ptr(workspace), workspace.numel(), int(path), ev0, ev1,
+                                                  _stream_ptr(self.device)))
+        return out_ids, out_scores
+
+
+def embed_gather(table: Table, ids: torch.Tensor, scale=None, **kw) -> torch.Tensor:
+    return table.embed_gather(ids, scale=scale, **kw)
+
+
+def logits_topk(table: Table, residual: torch.Tensor, k: int, **kw):
+    return table.logits_topk(residual, k, **kw)

@@ -1,0 +1,57 @@
+// Host-side declarations shared by the C-ABI layer and the kernel launchers of libetg.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace etg {
+
+struct TableDesc {
+  const uint8_t* rows;  // device pointer, 16-byte aligned
+  int32_t dtype;        // 0 f32, 1 bf16, 2 Q8_0
+  int64_t V;            // rows
+  int64_t hidden;       // values per row
+  int64_t row_bytes;
+};
+
+// Launch geometry and workspace layout of one etg_logits_topk call.  A pure
+// function of (table shape, batch, k, path): the workspace size can be queried
+// without a device.
+struct LogitsPlan {
+  int32_t path;          // 1 valu, 2 stream, 3 gemm
+  int32_t k;
+  int64_t batch;
+  // stream path
+  int32_t nimg;          // residual operand images: 1 (hi+lo packed, 4 rows per pass), 2 (8 rows)
+  int32_t nbc;           // residual rows per pass
+  int32_t steps;         // 64-value K steps = ceil(hidden / 64)
+  int32_t chunk;         // K steps of the residual image staged in LDS at a time
+  int64_t ngroups;       // 8-row table groups = ceil(V / 8)
+  int32_t max_groups;    // most 8-row groups one wave handles
+  // valu path
+  int32_t rb;            // residual rows per pass (1, 2, 4 or 8)
+  int64_t rows_per_blk;  // most table rows one block handles
+  // common
+  int32_t npass;         // batch passes (grid.y)
+  int32_t nblk;          // blocks per pass; each emits k candidates per residual row
+  size_t lds_bytes;      // dynamic LDS of the main kernel
+  size_t img_offset, img_bytes;    // bf16 residual image (stream path)
+  size_t cand_offset, cand_bytes;  // u64 keys [batch][nblk][k]
+  size_t ws_bytes;
+};
+
+// Returns 0 or a negative etg_status; fills *plan.  `why` receives a short reason.
+int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, LogitsPlan* plan,
+                    const char** why);
+
+hipError_t launch_gather(const TableDesc& t, const int32_t* ids, int64_t n, float scale,
+                         float* out, int32_t* bad, hipStream_t stream);
+
+// ev_before / ev_after (nullable) are recorded around the table-streaming kernel.
+hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const float* R,
+                              int32_t* ids, float* scores, void* ws, hipStream_t stream,
+                              hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr);
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+}  // namespace etg

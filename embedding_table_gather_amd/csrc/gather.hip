@@ -1,0 +1,136 @@
+// Token-id row gather with per-row dequant and an optional x sqrt(d) scale.
+//
+// ADR-0008 "POST /v1/embed" returns one f32 row of `hidden` values per token id,
+// found by one pointer offset per id; a prefill of N ids is N independent
+// lookups ("Open Questions" item 2).  Rows are addressed as row i at byte
+// offset i * row_bytes (HELIX Columnar Embedding proposal, section 3).  The
+// embeddinggemma.c port specification ("Forward graph") scales the gathered
+// Q8_0 rows by sqrt(768).
+//
+// One wavefront per output row.  f32 / bf16 rows are read with 16-byte loads
+// straight into registers; Q8_0 rows (34-byte blocks, so only 2-byte aligned)
+// are staged through the wave's slice of LDS with aligned dword loads and then
+// unpacked.  Stores are 16-byte f32x4, contiguous across the wave.
+//
+// Bit-exactness: dequant is exact in f32 (copy; bf16 widening; int8 * f16 has at
+// most 19 significant bits) and the scale is one f32 multiply, so there is one
+// rounding at most.  FP contraction is off in this file.
+#include "etg_device.hpp"
+#include "etg_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace etg {
+
+static constexpr int kGatherWaves = 4;
+
+template <int DT, bool SCALE>
+__global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ table, uint32_t V,
+                                                     int hidden, int64_t row_bytes,
+                                                     const int32_t* __restrict__ ids, int64_t n,
+                                                     float scale, float* __restrict__ out,
+                                                     int32_t* __restrict__ bad, int lds_words) {
+  extern __shared__ uint32_t lds_words_buf[];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kGatherWaves + wv;
+  if (row >= n) return;  // whole wave; the kernel has no block-level barrier
+  const uint32_t id = (uint32_t)ids[row];
+  f32x4* o = (f32x4*)(out + row * (int64_t)hidden);
+  const int n4 = hidden >> 2;
+  if (id >= V) {
+    for (int c4 = lane; c4 < n4; c4 += 64) o[c4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (lane == 0 && bad != nullptr) atomicAdd(bad, 1);
+    return;
+  }
+  const uint8_t* src = table + (uint64_t)id * (uint64_t)row_bytes;
+
+  if constexpr (DT == DT_F32) {
+    const f32x4* s4 = (const f32x4*)src;
+    for (int c4 = lane; c4 < n4; c4 += 64) {
+      f32x4 v = s4[c4];
+      if (SCALE) v = v * scale;
+      o[c4] = v;
+    }
+  } else if constexpr (DT == DT_BF16) {
+    const u32x4* s8 = (const u32x4*)src;
+    const int n8 = hidden >> 3;
+    for (int c8 = lane; c8 < n8; c8 += 64) {
+      u32x4 w = s8[c8];
+      f32x4 a = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+      f32x4 b = {bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+      if (SCALE) {
+        a = a * scale;
+        b = b * scale;
+      }
+      o[2 * c8] = a;
+      o[2 * c8 + 1] = b;
+    }
+  } else {
+    // Q8_0: stage [src & ~3, src + row_bytes) as aligned dwords.  row_bytes is even
+    // and the table base is 16-byte aligned, so src % 4 is 0 or 2: the first dword
+    // may start 2 bytes before the row (inside the previous row, never before the
+    // table), and a last dword that would run 2 bytes past the row is read as u16.
+    uint32_t* w = lds_words_buf + wv * lds_words;
+    const uintptr_t a = (uintptr_t)src;
+    const uintptr_t a0 = a & ~(uintptr_t)3;
+    const int head = (int)(a - a0);
+    const int nbytes = head + (int)row_bytes;
+    const int ndw = (nbytes + 3) >> 2;
+    const uint32_t* s = (const uint32_t*)a0;
+    for (int i = lane; i < ndw; i += 64) {
+      uint32_t v;
+      if (i == ndw - 1 && (nbytes & 3)) v = *(const uint16_t*)(s + i);
+      else v = s[i];
+      w[i] = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint8_t* wb = (const uint8_t*)w;
+    for (int c4 = lane; c4 < n4; c4 += 64) {
+      const int c = 4 * c4;
+      const int off = head + 34 * (c >> 5);  // even
+      const float sc = f16_bits_to_f32(*(const uint16_t*)(wb + off));
+      const int qo = off + 2 + (c & 31);     // even
+      const uint32_t q01 = *(const uint16_t*)(wb + qo);
+      const uint32_t q23 = *(const uint16_t*)(wb + qo + 2);
+      f32x4 v = {(float)(int8_t)(q01 & 0xffu) * sc, (float)(int8_t)(q01 >> 8) * sc,
+                 (float)(int8_t)(q23 & 0xffu) * sc, (float)(int8_t)(q23 >> 8) * sc};
+      if (SCALE) v = v * scale;
+      o[c4] = v;
+    }
+  }
+}
+
+template <int DT>
+static hipError_t launch_dt(const TableDesc& t, const int32_t* ids, int64_t n, float scale, float* out,
+                            int32_t* bad, hipStream_t stream) {
+  const bool sc = !(scale == 1.0f);
+  const dim3 grid((unsigned)((n + kGatherWaves - 1) / kGatherWaves));
+  const dim3 block(64 * kGatherWaves);
+  int lds_words = 0;
+  size_t lds = 0;
+  if (DT == DT_Q8_0) {
+    lds_words = (int)((t.row_bytes + 8 + 3) / 4);
+    lds = (size_t)kGatherWaves * lds_words * 4;
+  }
+  if (sc)
+    hipLaunchKernelGGL((gather_kernel<DT, true>), grid, block, lds, stream, t.rows, (uint32_t)t.V,
+                       (int)t.hidden, t.row_bytes, ids, n, scale, out, bad, lds_words);
+  else
+    hipLaunchKernelGGL((gather_kernel<DT, false>), grid, block, lds, stream, t.rows, (uint32_t)t.V,
+                       (int)t.hidden, t.row_bytes, ids, n, scale, out, bad, lds_words);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const TableDesc& t, const int32_t* ids, int64_t n, float scale, float* out,
+                         int32_t* bad, hipStream_t stream) {
+  switch (t.dtype) {
+    case DT_F32: return launch_dt<DT_F32>(t, ids, n, scale, out, bad, stream);
+    case DT_BF16: return launch_dt<DT_BF16>(t, ids, n, scale, out, bad, stream);
+    default: return launch_dt<DT_Q8_0>(t, ids, n, scale, out, bad, stream);
+  }
+}
+
+}  // namespace etg

@@ -1,0 +1,457 @@
+// Tied lm_head projection fused with per-row top-k.
+//
+// ADR-0008 "POST /v1/logits": logits = residual @ lm_head.T over every vocabulary
+// row (every row is needed for the argmax, HELIX Columnar Embedding proposal
+// section 5), answered as the top_k tokens in descending order.  The V-wide
+// logits never reach HBM: each block keeps the logits of its slice of the
+// vocabulary in LDS, emits its k best per residual row as 64-bit order keys,
+// and topk_merge_kernel reduces those lists to the final answer.
+//
+// Paths (chosen by the host, see plan_logits):
+//  * stream: bf16 tables, memory-bound batches.  One pass over the table per 8
+//    residual rows (per 4 when packed), the residual entering as a hi+lo pair of
+//    bf16 values.  bf16 MFMA (v_mfma_f32_16x16x32_bf16) is only the dot engine;
+//    the table is read once, straight into VGPRs.
+//  * valu:   any dtype (f32, bf16, Q8_0); f32 FMAs per lane, one table pass per
+//    up to 8 residual rows.
+#include <algorithm>
+
+#include "etg_device.hpp"
+#include "etg_internal.hpp"
+
+namespace etg {
+
+// ---------------------------------------------------------------------------
+// Stream path layout.
+//
+// The table is cut into 8-row groups.  One MFMA step covers 8 rows x 64 values
+// (128 contiguous bytes per row) of the table.  Lane l loads row (l % 8), bytes
+// [128 s + 16 (l / 8), +16): one load instruction reads 8 full 128-byte lines.
+//
+// In the 16x16x32 MFMA, lane l supplies A row m = l % 16 with K-group g = l / 16.
+// So A row m is table row m % 8, and its K slice is the half h = m / 8 of the
+// lane's 32-value window: value index 64 s + 16 g + 8 h + e (e = 0..7).  A dot
+// product does not depend on the order of its terms, so any bijection of value
+// indices works as long as the residual operand uses the same one.
+//
+// B column n (lane l supplies column n = l % 16, group g = l / 16) carries a
+// residual row at the same value indices for half h = n / 8.  Rows with h = 0
+// meet columns with h = 0 and likewise for h = 1; the cross terms D[r][8 + ...]
+// and D[r + 8][...] are unused.
+//
+// The residual is carried as a pair of bf16 values, hi = bf16(x) and
+// lo = bf16(x - hi), so the operand error is at most 2^-16 |x| (one bf16
+// rounding alone can be 2^-8 |x|).  Two layouts:
+//   packed (batch <= 4): one operand image, column n % 8 = b + 4 * part
+//                        (part 0 = hi, 1 = lo); one MFMA per step;
+//   dual   (batch <= 8): image 0 holds hi, image 1 holds lo, column n % 8 = b;
+//                        two MFMAs per step into the same accumulator.
+// Then logit[row r][b] = sum over h (and part) of D[r + 8h][8h + ...].
+// D layout: lane L holds D[4 (L / 16) + i][L % 16], i = 0..3.  For L < 32 with
+// b = L % 16 < nbc, the terms sit in lanes L, L + 40 (+ 4, + 44 when packed).
+//
+// Global image: [pass][step][image][64 lanes] x 16 bytes.  A block stages up to
+// `chunk` steps of it in LDS at a time (all of it when it fits).
+// ---------------------------------------------------------------------------
+
+static constexpr int kStreamWaves = 16;
+static constexpr int kStreamUnroll = 8;
+static constexpr int kStreamMaxPairs = 4;  // a wave handles at most 8 groups (64 rows)
+
+// fp32 residual [B][hidden] -> bf16 hi/lo operand image.
+template <int NIMG>
+__global__ void __launch_bounds__(256) stream_prep_kernel(const float* __restrict__ R, int64_t B,
+                                                          int hidden, int steps, int npass,
+                                                          u32x4* __restrict__ img) {
+  constexpr int NBC = NIMG == 1 ? 4 : 8;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)npass * steps * NIMG * 64) return;
+  const int lane = (int)(t & 63);
+  const int64_t q = t >> 6;
+  const int im = (int)(q % NIMG);
+  const int s = (int)((q / NIMG) % steps);
+  const int pass = (int)(q / ((int64_t)NIMG * steps));
+  const int n = lane & 15, g = lane >> 4;
+  const int h = n >> 3, j8 = n & 7;
+  const int part = NIMG == 1 ? j8 / NBC : im;
+  const int bl = j8 % NBC;
+  const int64_t b = (int64_t)pass * NBC + bl;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const int c = 64 * s + 16 * g + 8 * h + e;
+    const float x = (b < B && c < hidden) ? R[b * hidden + c] : 0.0f;
+    const uint32_t hi = bf16_rne(x);
+    // part 1 carries the remainder x - hi (exact in f32), rounded to bf16
+    v[e] = part == 1 ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;
+  }
+  img[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+}
+
+template <int NBC>
+__device__ __forceinline__ void stream_store_group(f32x4 acc, float* dst, int lane) {
+  f32x4 y;
+#pragma unroll
+  for (int i = 0; i < 4; i++) y[i] = acc[i] + __shfl(acc[i], (lane + 40) & 63, 64);
+  if (NBC == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) y[i] = y[i] + __shfl(y[i], (lane + 4) & 63, 64);
+  }
+  if (lane < 32 && (lane & 15) < NBC) {
+    const int b = lane & 15, r0 = 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) dst[(r0 + i) * NBC + b] = y[i];
+  }
+}
+
+// Select the k best (logit, row) of this block for residual column b.  Values
+// live in slog as [wave][group * 8 + r][NBC]; rows >= V are skipped.  Round t
+// takes the largest key below the key of round t - 1 (keys are unique).
+template <int NBC>
+__device__ void stream_block_topk(const float* slog, int b, int lane, int64_t blk_gw0, int64_t ngroups,
+                                  int64_t nw, int max_groups, int64_t V, int k, uint64_t* out) {
+  const int per_wave = max_groups * 8;
+  const int total = kStreamWaves * per_wave;
+  uint64_t prev = ~0ull;
+  for (int t = 0; t < k; t++) {
+    uint64_t best = 0;
+    for (int i = lane; i < total; i += 64) {
+      const int w = i / per_wave, li = i - w * per_wave;
+      const int64_t gw = blk_gw0 + w;
+      const int64_t g0 = gw * ngroups / nw, g1 = (gw + 1) * ngroups / nw;
+      const int64_t row = g0 * 8 + li;
+      if (li < (int)(g1 - g0) * 8 && row < V) {
+        const uint64_t key = make_key(slog[i * NBC + b], (uint32_t)row);
+        if (key < prev && key > best) best = key;
+      }
+    }
+    best = wave_max_u64(best);
+    if (lane == 0) out[t] = best;
+    prev = best;
+  }
+}
+
+template <int NIMG>
+__global__ void __launch_bounds__(1024) stream_logits_kernel(
+    const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden,
+    const u32x4* __restrict__ img, int steps, int chunk, int64_t B, int k, uint64_t* __restrict__ cand,
+    int64_t ngroups, int max_groups) {
+  constexpr int NBC = NIMG == 1 ? 4 : 8;
+  constexpr int U = kStreamUnroll;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  u32x4* simg = (u32x4*)smem;
+  float* slog = (float*)(smem + (size_t)chunk * NIMG * 1024);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int pass = blockIdx.y;
+  const u32x4* pimg = img + (size_t)pass * steps * NIMG * 64;
+
+  const int64_t nw = (int64_t)gridDim.x * kStreamWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kStreamWaves + wv;
+  const int64_t g_begin = gw * ngroups / nw;
+  const int ng = (int)((gw + 1) * ngroups / nw - g_begin);
+  const int npairs = (ng + 1) >> 1;
+  const int r = lane & 7, ck = lane >> 3;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  f32x4 acc0[kStreamMaxPairs], acc1[kStreamMaxPairs];
+#pragma unroll
+  for (int p = 0; p < kStreamMaxPairs; p++) acc0[p] = acc1[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < steps; c0 += chunk) {
+    const int c1 = min(steps, c0 + chunk);
+    if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
+    for (int i = tid; i < (c1 - c0) * NIMG * 64; i += blockDim.x) simg[i] = pimg[(size_t)c0 * NIMG * 64 + i];
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kStreamMaxPairs; p++) {
+      if (p < npairs) {
+        const int64_t row0 = (g_begin + 2 * p) * 8 + r;
+        const int64_t row1 = row0 + 8;
+        const bool ok0 = row0 < V;
+        const bool ok1 = (2 * p + 1 < ng) && (row1 < V);
+        const u32x4* p0 = (const u32x4*)(table + (uint64_t)(ok0 ? row0 : 0) * (uint64_t)row_bytes) + ck;
+        const u32x4* p1 = (const u32x4*)(table + (uint64_t)(ok1 ? row1 : 0) * (uint64_t)row_bytes) + ck;
+        for (int s0 = c0; s0 < c1; s0 += U) {
+          u32x4 a0[U], a1[U];
+#pragma unroll
+          for (int j = 0; j < U; j++) {
+            const int s = s0 + j;
+            const bool kv = (s < c1) && (64 * s + 8 * ck < hidden);
+            a0[j] = (ok0 && kv) ? p0[8 * s] : zero;
+            a1[j] = (ok1 && kv) ? p1[8 * s] : zero;
+          }
+#pragma unroll
+          for (int j = 0; j < U; j++) {
+            const int s = s0 + j;
+            if (s < c1) {
+              const u32x4* bl = simg + (size_t)(s - c0) * NIMG * 64 + lane;
+#pragma unroll
+              for (int im = 0; im < NIMG; im++) {
+                const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[im * 64]);
+                acc0[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0[j]), bop, acc0[p],
+                                                                  0, 0, 0);
+                acc1[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1[j]), bop, acc1[p],
+                                                                  0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  float* mylog = slog + (size_t)wv * max_groups * 8 * NBC;
+#pragma unroll
+  for (int p = 0; p < kStreamMaxPairs; p++) {
+    if (2 * p < ng) stream_store_group<NBC>(acc0[p], mylog + (size_t)(2 * p) * 8 * NBC, lane);
+    if (2 * p + 1 < ng) stream_store_group<NBC>(acc1[p], mylog + (size_t)(2 * p + 1) * 8 * NBC, lane);
+  }
+  __syncthreads();
+
+  const int64_t b0 = (int64_t)pass * NBC;
+  if (wv < NBC && b0 + wv < B) {
+    uint64_t* out = cand + ((b0 + wv) * gridDim.x + blockIdx.x) * (int64_t)k;
+    stream_block_topk<NBC>(slog, wv, lane, (int64_t)blockIdx.x * kStreamWaves, ngroups, nw, max_groups, V,
+                           k, out);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// VALU path: any dtype.  Block = 4 waves over a contiguous slice of rows; a wave
+// takes one row at a time, each lane accumulates RB residual rows over values
+// lane, lane + 64, ... with f32 FMAs, then a butterfly sum per residual row.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float deq_value(const uint8_t* row, int c) {
+  if constexpr (DT == DT_F32) {
+    return ((const float*)row)[c];
+  } else if constexpr (DT == DT_BF16) {
+    return __uint_as_float((uint32_t)((const uint16_t*)row)[c] << 16);
+  } else {
+    const uint8_t* blk = row + 34 * (c >> 5);
+    const float s = f16_bits_to_f32(*(const uint16_t*)blk);
+    return (float)(int8_t)blk[2 + (c & 31)] * s;
+  }
+}
+
+template <int DT, int RB>
+__global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restrict__ table, int64_t V,
+                                                          int64_t row_bytes, int hidden,
+                                                          const float* __restrict__ R, int64_t B, int k,
+                                                          uint64_t* __restrict__ cand) {
+  extern __shared__ float vlog[];  // [rows of this block][RB]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t nblk = gridDim.x;
+  const int64_t r_begin = (int64_t)blockIdx.x * V / nblk;
+  const int nrows = (int)(((int64_t)blockIdx.x + 1) * V / nblk - r_begin);
+  const int64_t b0 = (int64_t)blockIdx.y * RB;
+  const int nb = (int)((B - b0) < RB ? (B - b0) : RB);
+  for (int lr = wv; lr < nrows; lr += 4) {
+    const uint8_t* row = table + (uint64_t)(r_begin + lr) * (uint64_t)row_bytes;
+    float acc[RB];
+#pragma unroll
+    for (int b = 0; b < RB; b++) acc[b] = 0.f;
+    for (int c = lane; c < hidden; c += 64) {
+      const float x = deq_value<DT>(row, c);
+#pragma unroll
+      for (int b = 0; b < RB; b++)
+        if (b < nb) acc[b] = __builtin_fmaf(x, R[(b0 + b) * hidden + c], acc[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < RB; b++) {
+      const float s = wave_sum(acc[b]);
+      if (lane == 0) vlog[lr * RB + b] = s;
+    }
+  }
+  __syncthreads();
+  for (int b = wv; b < nb; b += 4) {
+    uint64_t* out = cand + ((b0 + b) * nblk + blockIdx.x) * (int64_t)k;
+    uint64_t prev = ~0ull;
+    for (int t = 0; t < k; t++) {
+      uint64_t best = 0;
+      for (int i = lane; i < nrows; i += 64) {
+        const uint64_t key = make_key(vlog[i * RB + b], (uint32_t)(r_begin + i));
+        if (key < prev && key > best) best = key;
+      }
+      best = wave_max_u64(best);
+      if (lane == 0) out[t] = best;
+      prev = best;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-block merge: per residual row, the k largest of nblk * k keys.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) topk_merge_kernel(const uint64_t* __restrict__ cand, int nblk, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ scores) {
+  __shared__ uint64_t red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t b = blockIdx.x;
+  const uint64_t* c = cand + b * (int64_t)nblk * k;
+  const int n = nblk * k;
+  uint64_t prev = ~0ull;
+  for (int t = 0; t < k; t++) {
+    uint64_t best = 0;
+    for (int i = tid; i < n; i += 256) {
+      const uint64_t key = c[i];
+      if (key < prev && key > best) best = key;
+    }
+    best = wave_max_u64(best);
+    if (lane == 0) red[wv] = best;
+    __syncthreads();
+    uint64_t m = red[0];
+#pragma unroll
+    for (int w = 1; w < 4; w++) m = red[w] > m ? red[w] : m;
+    __syncthreads();
+    if (tid == 0) {
+      ids[b * k + t] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
+      scores[b * k + t] = ord_score((uint32_t)(m >> 32));
+    }
+    prev = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+static hipError_t set_lds(const void* fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  return e;
+}
+
+static hipError_t record(hipEvent_t ev, hipStream_t stream) {
+  return ev ? hipEventRecord(ev, stream) : hipSuccess;
+}
+
+template <int DT>
+static hipError_t launch_valu(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
+                              hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const dim3 grid((unsigned)p.nblk, (unsigned)p.npass), block(256);
+  hipError_t e = set_lds((const void*)valu_logits_kernel<DT, 1>, p.lds_bytes);
+  if (e == hipSuccess) e = set_lds((const void*)valu_logits_kernel<DT, 2>, p.lds_bytes);
+  if (e == hipSuccess) e = set_lds((const void*)valu_logits_kernel<DT, 4>, p.lds_bytes);
+  if (e == hipSuccess) e = set_lds((const void*)valu_logits_kernel<DT, 8>, p.lds_bytes);
+  if (e != hipSuccess) return e;
+  if ((e = record(ev0, stream)) != hipSuccess) return e;
+  switch (p.rb) {
+#define ETG_VALU_CASE(RBV)                                                                          \
+  case RBV:                                                                                         \
+    hipLaunchKernelGGL((valu_logits_kernel<DT, RBV>), grid, block, p.lds_bytes, stream, t.rows, t.V, \
+                       t.row_bytes, (int)t.hidden, R, p.batch, p.k, cand);                          \
+    break;
+    ETG_VALU_CASE(1)
+    ETG_VALU_CASE(2)
+    ETG_VALU_CASE(4)
+    ETG_VALU_CASE(8)
+#undef ETG_VALU_CASE
+    default: return hipErrorInvalidValue;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return record(ev1, stream);
+}
+
+template <int NIMG>
+static hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const float* R, u32x4* img,
+                                uint64_t* cand, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const int64_t nprep = (int64_t)p.npass * p.steps * NIMG * 64;
+  hipLaunchKernelGGL((stream_prep_kernel<NIMG>), dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream,
+                     R, p.batch, (int)t.hidden, p.steps, p.npass, img);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = set_lds((const void*)stream_logits_kernel<NIMG>, p.lds_bytes);
+  if (e != hipSuccess) return e;
+  if ((e = record(ev0, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((stream_logits_kernel<NIMG>), dim3((unsigned)p.nblk, (unsigned)p.npass),
+                     dim3(64 * kStreamWaves), p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (int)t.hidden, img,
+                     p.steps, p.chunk, p.batch, p.k, cand, p.ngroups, p.max_groups);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return record(ev1, stream);
+}
+
+hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const float* R, int32_t* ids,
+                              float* scores, void* ws, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  uint8_t* base = (uint8_t*)ws;
+  uint64_t* cand = (uint64_t*)(base + p.cand_offset);
+  hipError_t e;
+  if (p.path == 2) {
+    u32x4* img = (u32x4*)(base + p.img_offset);
+    e = p.nimg == 1 ? launch_stream<1>(t, p, R, img, cand, stream, ev0, ev1)
+                    : launch_stream<2>(t, p, R, img, cand, stream, ev0, ev1);
+  } else {
+    switch (t.dtype) {
+      case DT_F32: e = launch_valu<DT_F32>(t, p, R, cand, stream, ev0, ev1); break;
+      case DT_BF16: e = launch_valu<DT_BF16>(t, p, R, cand, stream, ev0, ev1); break;
+      default: e = launch_valu<DT_Q8_0>(t, p, R, cand, stream, ev0, ev1); break;
+    }
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)p.batch), dim3(256), 0, stream, cand, p.nblk, p.k, ids,
+                     scores);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Planning (host only, no device calls).
+// ---------------------------------------------------------------------------
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, LogitsPlan* p,
+                    const char** why) {
+  *p = LogitsPlan{};
+  p->k = k;
+  p->batch = batch;
+  const int kTargetBlocks = 256;  // one block per MI355X compute unit
+  if (path == 0) path = (t.dtype == DT_BF16) ? 2 : 1;
+  if (path == 3) path = 2;  // the large-batch contraction shares the stream kernel for now
+  if (path == 2 && t.dtype != DT_BF16) {
+    *why = "the stream path needs a bf16 table";
+    return -5;
+  }
+  if (path != 1 && path != 2) {
+    *why = "unknown path";
+    return -5;
+  }
+  p->path = path;
+  if (path == 2) {
+    p->nimg = batch <= 4 ? 1 : 2;
+    p->nbc = p->nimg == 1 ? 4 : 8;
+    p->steps = (int32_t)cdiv(t.hidden, 64);
+    p->ngroups = cdiv(t.V, 8);
+    p->npass = (int32_t)cdiv(batch, p->nbc);
+    // one block per CU, unless a wave would then own more than 8 groups
+    const int64_t per_blk = (int64_t)kStreamWaves * 2 * kStreamMaxPairs;
+    p->nblk = (int32_t)std::max<int64_t>(cdiv(p->ngroups, per_blk),
+                                         std::min<int64_t>(kTargetBlocks, cdiv(p->ngroups, kStreamWaves)));
+    p->max_groups = (int32_t)cdiv(p->ngroups, (int64_t)p->nblk * kStreamWaves);
+    const size_t log_bytes = (size_t)kStreamWaves * p->max_groups * 8 * p->nbc * 4;
+    const size_t img_room = kMaxLds - log_bytes;
+    const int64_t max_chunk = (int64_t)(img_room / ((size_t)p->nimg * 1024));
+    // equal chunks, as few as fit
+    const int64_t nchunks = cdiv(p->steps, max_chunk);
+    p->chunk = (int32_t)cdiv(p->steps, nchunks);
+    p->lds_bytes = (size_t)p->chunk * p->nimg * 1024 + log_bytes;
+    p->img_bytes = (size_t)p->npass * p->steps * p->nimg * 1024;
+  } else {
+    p->rb = batch >= 8 ? 8 : batch >= 4 ? 4 : batch >= 2 ? 2 : 1;
+    p->npass = (int32_t)cdiv(batch, p->rb);
+    // at most 4096 rows per block (16 KiB of logits per residual row in the pass)
+    int64_t nblk = std::max<int64_t>(cdiv(t.V, 64), 1);
+    nblk = std::min<int64_t>(nblk, 4 * kTargetBlocks);
+    nblk = std::max<int64_t>(nblk, cdiv(t.V * p->rb, 16384));
+    p->nblk = (int32_t)nblk;
+    p->rows_per_blk = cdiv(t.V, nblk);
+    p->lds_bytes = (size_t)p->rows_per_blk * p->rb * 4;
+    p->img_bytes = 0;
+  }
+  p->img_offset = 0;
+  p->cand_offset = align_up(p->img_bytes, 256);
+  p->cand_bytes = (size_t)batch * p->nblk * k * 8;
+  p->ws_bytes = align_up(p->cand_offset + p->cand_bytes, 256);
+  return 0;
+}
+
+}  // namespace etg

@@ -1,0 +1,175 @@
+/*
+ * etg.h -- static embedding / tied lm_head service on AMD Instinct MI355X (gfx950).
+ *
+ * Two operations, after the embed server of "ADR-0008 -- Remote Embeddings and
+ * lm_head Service":
+ *
+ *   etg_embed_gather   token ids -> f32 residual_0 rows        ("POST /v1/embed")
+ *   etg_logits_topk    residuals -> top-k (id, logit) per row  ("POST /v1/logits")
+ *
+ * The table is row-major and row-addressed: row i occupies bytes
+ * [i * row_bytes, (i + 1) * row_bytes) of the table (HELIX Columnar Embedding
+ * proposal, section 3, "Wire format" and "Index").  The lm_head is tied: the
+ * same table serves both operations (ADR-0008, "Open Questions" item 1; HELIX
+ * proposal section 5(a)); an untied lm_head is simply a second table handle.
+ *
+ * Conventions for every function below:
+ *  - Pointers named d_* are DEVICE pointers (HBM of the current HIP device); the
+ *    caller owns all of them.  The library keeps no device allocations and no
+ *    hidden state: a table handle is immutable host metadata and may be shared
+ *    by threads.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work
+ *    is enqueued on it and the call returns without waiting.
+ *  - Every function returns an etg_status; 0 is success.  A negative status
+ *    means nothing was enqueued; etg_last_error() then holds a message for the
+ *    calling thread (the analog of the pages' {"error": "message"} envelope,
+ *    ADR-0008 "Error contract").  No function aborts or throws.
+ */
+#ifndef ETG_H
+#define ETG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtype of the table rows. */
+typedef enum {
+  ETG_F32 = 0,  /* little-endian IEEE binary32; row_bytes = 4 * hidden             */
+  ETG_BF16 = 1, /* bfloat16 (upper half of a binary32); row_bytes = 2 * hidden       */
+  ETG_Q8_0 = 2  /* blocks of 32 values: little-endian binary16 scale, then 32 int8;
+                   value = int8 * scale; row_bytes = 34 * hidden / 32.  (The
+                   embeddinggemma.c port specification, "Tensor inventory": the Q8_0
+                   token_embd is used by row-gather + dequant only.) */
+} etg_dtype;
+
+typedef enum {
+  ETG_OK = 0,
+  ETG_EINVAL = -1,     /* null pointer or handle                                       */
+  ETG_EDTYPE = -2,     /* unknown dtype                                                */
+  ETG_ESHAPE = -3,     /* hidden not a multiple of 4 (f32) / 8 (bf16) / 32 (Q8_0), or
+                          outside [1, 65536]; vocab outside [1, 2^31 - 1]; seq_len or
+                          batch outside the supported range                            */
+  ETG_EALIGN = -4,     /* a device pointer lacks the alignment its argument states     */
+  ETG_ERANGE = -5,     /* k outside [1, min(vocab, 64)], or an unknown path            */
+  ETG_EWORKSPACE = -6, /* workspace smaller than etg_logits_topk_workspace() bytes     */
+  ETG_EHIP = -8        /* a HIP runtime call failed (the message names it)             */
+} etg_status;
+
+typedef struct etg_table etg_table;
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t etg_version(void);
+
+/* Bytes of one stored row (HELIX proposal, section 3: row_bytes = hidden * itemsize;
+ * Q8_0: 34 bytes per 32 values).  Returns -1 for an unknown dtype or a hidden size
+ * the dtype cannot store. */
+int64_t etg_row_bytes(int32_t dtype, int64_t hidden);
+
+/* The float32 nearest to sqrt(hidden), computed on the host: the embedding scale of
+ * the embeddinggemma.c port specification, "Forward graph" (x = token_embd[ids] *
+ * sqrt(768)).  Returns 0 for hidden < 1. */
+float etg_sqrt_d(int64_t hidden);
+
+/* Describe a table that already lives in device memory.
+ *   d_rows  device pointer to vocab * etg_row_bytes(dtype, hidden) bytes, 16-byte
+ *           aligned; BORROWED: the caller keeps it alive and unchanged while the
+ *           handle is used.
+ *   out     receives a new handle (host memory only; no device allocation).
+ * Errors: EINVAL (null), EDTYPE, ESHAPE, EALIGN. */
+int32_t etg_table_create(const void* d_rows, int32_t dtype, int64_t vocab, int64_t hidden,
+                         etg_table** out);
+
+/* Free a handle (not the rows).  NULL is accepted. */
+int32_t etg_table_destroy(etg_table* table);
+
+/*
+ * Row gather (ADR-0008 "POST /v1/embed": one residual row of hidden f32 values per
+ * token id; "Open Questions" item 2: a prefill of N ids is N independent lookups).
+ *
+ *   out[n][c] = deq(row ids[n])[c]                  when scale == 1.0f
+ *   out[n][c] = round_f32(deq(row ids[n])[c] * scale) otherwise
+ *
+ * deq is exact: f32 rows are copied, bf16 rows widened, Q8_0 values are int8 * the
+ * block's binary16 scale (exact in f32).  The optional scale is applied after the
+ * dequant with one round-to-nearest-even f32 multiply; pass etg_sqrt_d(hidden) for
+ * the x * sqrt(d) of the embeddinggemma.c "Forward graph".
+ *
+ *   d_ids        int32 [seq_len], 4-byte aligned; read as uint32 (ADR-0008 "GET
+ *                /v1/embed/{token_id}": a 32-bit key).  An id >= vocab (as uint32;
+ *                so every negative int32) is a bad token id.
+ *   seq_len      0 <= seq_len <= 2^31 - 1; 0 enqueues nothing and returns ETG_OK.
+ *   d_out        f32 [seq_len][hidden] row-major, 16-byte aligned, caller-owned.
+ *   d_bad_count  NULLABLE int32 on the device.  For each bad id the kernel writes an
+ *                all-zero row and atomically adds 1 here; the caller zeroes it before
+ *                the call and reads it after the stream is synchronized.
+ * Results are bit-identical to the definition above.
+ */
+int32_t etg_embed_gather(const etg_table* table, const int32_t* d_ids, int64_t seq_len,
+                         float scale, float* d_out, int32_t* d_bad_count, void* stream);
+
+/* Kernel path for etg_logits_topk_ex (ETG_PATH_AUTO is what etg_logits_topk uses). */
+typedef enum {
+  ETG_PATH_AUTO = 0,   /* pick by dtype and batch                                        */
+  ETG_PATH_VALU = 1,   /* any dtype: f32 vector FMAs, one table pass per 8 residuals     */
+  ETG_PATH_STREAM = 2, /* bf16 tables: one HBM pass per 8 residuals, bf16 MFMA dot engine;
+                          batches of <= 4 use a hi+lo bf16 split of the residual          */
+  ETG_PATH_GEMM = 3    /* bf16 tables: tiled bf16 MFMA contraction for large batches     */
+} etg_path;
+
+/* Device workspace bytes etg_logits_topk(_ex) needs for this table, batch and k
+ * (and path; ETG_PATH_AUTO for etg_logits_topk).  Depends only on these arguments.
+ * Returns a negative etg_status for invalid arguments. */
+int64_t etg_logits_topk_workspace(const etg_table* lm_head, int64_t batch, int32_t k);
+int64_t etg_logits_topk_workspace_ex(const etg_table* lm_head, int64_t batch, int32_t k,
+                                     int32_t path);
+
+/*
+ * Tied lm_head projection fused with top-k (ADR-0008 "POST /v1/logits":
+ * logits = residual @ lm_head.T over every vocabulary row, then the top_k tokens in
+ * descending order).  The V-wide logits are never written to memory.
+ *
+ *   L[b][v] = sum_i residual[b][i] * deq(row v)[i]   (f32 accumulation)
+ *
+ *   d_residual     f32 [batch][hidden] row-major, contiguous, 4-byte aligned.
+ *   batch          1 <= batch <= 65536.
+ *   k              1 <= k <= min(vocab, 64).
+ *   d_topk_ids     int32 [batch][k]: ids ordered by logit descending; equal logits
+ *                  (including -0 and +0) are ordered by ascending id.
+ *   d_topk_scores  f32 [batch][k]: the logits of those ids.
+ *   d_workspace    at least etg_logits_topk_workspace() bytes, 256-byte aligned.
+ * Accuracy: |score - exact logit| <= 2e-3 * sum_i |r_i e_i| for bf16 and Q8_0
+ * tables and <= 1e-5 * sum_i |r_i e_i| for f32 tables; ids can differ from the
+ * exact order only among logits that tie within that bound.  Results are
+ * deterministic (bitwise repeatable) for a given path.
+ */
+int32_t etg_logits_topk(const etg_table* lm_head, const float* d_residual, int64_t batch,
+                        int32_t k, int32_t* d_topk_ids, float* d_topk_scores,
+                        void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* As etg_logits_topk, with an explicit kernel path (ETG_ERANGE if the path does
+ * not support the table's dtype). */
+int32_t etg_logits_topk_ex(const etg_table* lm_head, const float* d_residual, int64_t batch,
+                           int32_t k, int32_t* d_topk_ids, float* d_topk_scores,
+                           void* d_workspace, size_t workspace_bytes, int32_t path,
+                           void* stream);
+
+/* As etg_logits_topk_ex, and records two caller-created hipEvent_t (passed as void*,
+ * either may be NULL) on `stream` immediately before and after the kernel that
+ * streams the table, so a caller can time that kernel alone with
+ * hipEventElapsedTime.  For measurement; results are identical to etg_logits_topk_ex. */
+int32_t etg_logits_topk_profiled(const etg_table* lm_head, const float* d_residual, int64_t batch,
+                                 int32_t k, int32_t* d_topk_ids, float* d_topk_scores,
+                                 void* d_workspace, size_t workspace_bytes, int32_t path,
+                                 void* event_before, void* event_after, void* stream);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* etg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ETG_H */

@@ -1,0 +1,158 @@
+"""The C-ABI library without a GPU: it loads, exports what include/etg.h declares,
+and every host-detectable error returns its status and message without a launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import embedding_table_gather_amd as etg
+from tests.conftest import ROOT, read_golden
+
+H = os.path.join(ROOT, "include", "etg.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return etg.lib()
+
+
+def _declared():
+    src = open(H).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(etg_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported_and_bound(L):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in etg.SIGNATURES, f"{n} has no ctypes signature in the binding"
+    assert set(etg.SIGNATURES) == set(names)
+
+
+def test_version(L):
+    assert L.etg_version() >= 100
+
+
+def test_row_bytes_matches_page_sizes(L):
+    dts = {"f32": etg.F32, "bf16": etg.BF16, "q8_0": etg.Q8_0}
+    for name, dt, V, d, qty, expected, unit, src in read_golden("sizes.txt"):
+        if unit == "B" and int(V) == 1:
+            assert L.etg_row_bytes(dts[dt], int(d)) == int(expected), (name, src)
+    assert L.etg_row_bytes(etg.BF16, 5376) == 10752
+    assert L.etg_row_bytes(etg.Q8_0, 768) == 816
+    for dt, d in [(etg.F32, 6), (etg.BF16, 12), (etg.Q8_0, 48), (etg.BF16, 0), (etg.F32, 65540), (9, 64)]:
+        assert L.etg_row_bytes(dt, d) == -1, (dt, d)
+
+
+def test_sqrt_d_matches_fixture(L):
+    (hidden, hexbits, dec), = read_golden("embed_scale.txt")
+    v = L.etg_sqrt_d(int(hidden))
+    import struct
+    assert struct.unpack("<I", struct.pack("<f", v))[0] == int(hexbits, 16)
+    assert L.etg_sqrt_d(0) == 0.0
+
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced on these paths
+
+
+def _create(L, ptr, dt, V, d):
+    h = ctypes.c_void_p()
+    st = L.etg_table_create(ctypes.c_void_p(ptr), dt, V, d, ctypes.byref(h))
+    return st, h
+
+
+def _err(L):
+    return L.etg_last_error().decode()
+
+
+def test_table_create_errors(L):
+    assert _create(L, 0, etg.BF16, 10, 64)[0] == -1 and "NULL" in _err(L)
+    assert _create(L, FAKE, 7, 10, 64)[0] == -2 and "dtype" in _err(L)
+    assert _create(L, FAKE, etg.BF16, 0, 64)[0] == -3 and "vocab" in _err(L)
+    assert _create(L, FAKE, etg.BF16, 2 ** 31, 64)[0] == -3
+    assert _create(L, FAKE, etg.BF16, 10, 60)[0] == -3 and "hidden" in _err(L)
+    assert _create(L, FAKE, etg.Q8_0, 10, 48)[0] == -3
+    assert _create(L, FAKE + 8, etg.BF16, 10, 64)[0] == -4 and "aligned" in _err(L)
+    assert L.etg_table_create(ctypes.c_void_p(FAKE), 1, 10, 64, None) == -1
+    st, h = _create(L, FAKE, etg.Q8_0, 262144, 768)
+    assert st == 0 and h.value
+    assert L.etg_table_destroy(h) == 0
+    assert L.etg_table_destroy(None) == 0
+
+
+@pytest.fixture
+def table(L):
+    st, h = _create(L, FAKE, etg.BF16, 262144, 5376)
+    assert st == 0
+    yield h
+    L.etg_table_destroy(h)
+
+
+def test_gather_errors_without_launch(L, table):
+    ids, out = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE)
+    assert L.etg_embed_gather(None, ids, 4, 1.0, out, None, None) == -1
+    assert L.etg_embed_gather(table, ids, -1, 1.0, out, None, None) == -3
+    assert L.etg_embed_gather(table, ids, 2 ** 31, 1.0, out, None, None) == -3
+    assert L.etg_embed_gather(table, None, 4, 1.0, out, None, None) == -1
+    assert L.etg_embed_gather(table, ids, 4, 1.0, None, None, None) == -1
+    assert L.etg_embed_gather(table, ctypes.c_void_p(FAKE + 2), 4, 1.0, out, None, None) == -4
+    assert L.etg_embed_gather(table, ids, 4, 1.0, ctypes.c_void_p(FAKE + 4), None, None) == -4
+    assert L.etg_embed_gather(table, ids, 4, 1.0, out, ctypes.c_void_p(FAKE + 1), None) == -4
+    assert L.etg_embed_gather(table, ids, 4, float("inf"), out, None, None) == -5
+    # seq_len 0 enqueues nothing and succeeds, even with null buffers
+    assert L.etg_embed_gather(table, None, 0, 1.0, None, None, None) == 0
+
+
+def test_workspace_is_host_computable(L, table):
+    n1 = L.etg_logits_topk_workspace(table, 1, 10)
+    n64 = L.etg_logits_topk_workspace(table, 64, 10)
+    assert 0 < n1 < n64
+    assert n1 % 256 == 0
+    assert L.etg_logits_topk_workspace_ex(table, 8, 10, etg.PATH_VALU) > 0
+    assert L.etg_logits_topk_workspace(table, 0, 10) == -3
+    assert L.etg_logits_topk_workspace(table, 1, 0) == -5
+    assert L.etg_logits_topk_workspace(table, 1, 65) == -5
+    assert L.etg_logits_topk_workspace_ex(table, 1, 10, 9) == -5
+    assert L.etg_logits_topk_workspace(None, 1, 10) == -1
+
+
+def test_workspace_rejects_stream_path_for_q8_0(L):
+    st, h = _create(L, FAKE, etg.Q8_0, 1000, 64)
+    assert st == 0
+    assert L.etg_logits_topk_workspace_ex(h, 1, 5, etg.PATH_STREAM) == -5
+    assert "bf16" in _err(L)
+    assert L.etg_logits_topk_workspace_ex(h, 1, 5, etg.PATH_VALU) > 0
+    L.etg_table_destroy(h)
+
+
+def test_k_is_capped_by_vocab(L):
+    st, h = _create(L, FAKE, etg.F32, 7, 64)
+    assert L.etg_logits_topk_workspace(h, 1, 7) > 0
+    assert L.etg_logits_topk_workspace(h, 1, 8) == -5
+    L.etg_table_destroy(h)
+
+
+def test_logits_errors_without_launch(L, table):
+    p = ctypes.c_void_p(FAKE)
+    ws_n = L.etg_logits_topk_workspace(table, 2, 10)
+    f = L.etg_logits_topk
+    assert f(None, p, 2, 10, p, p, p, ws_n, None) == -1
+    assert f(table, None, 2, 10, p, p, p, ws_n, None) == -1
+    assert f(table, p, 2, 10, None, p, p, ws_n, None) == -1
+    assert f(table, p, 2, 10, p, p, None, ws_n, None) == -1
+    assert f(table, p, 0, 10, p, p, p, ws_n, None) == -3
+    assert f(table, p, 2, 0, p, p, p, ws_n, None) == -5
+    assert f(table, ctypes.c_void_p(FAKE + 2), 2, 10, p, p, p, ws_n, None) == -4
+    assert f(table, p, 2, 10, ctypes.c_void_p(FAKE + 1), p, p, ws_n, None) == -4
+    assert f(table, p, 2, 10, p, p, ctypes.c_void_p(FAKE + 16), ws_n, None) == -4
+    assert f(table, p, 2, 10, p, p, p, ws_n - 1, None) == -6 and "workspace" in _err(L)
+    assert L.etg_logits_topk_ex(table, p, 2, 10, p, p, p, ws_n, 9, None) == -5
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        etg.Table(torch.zeros(16, dtype=torch.int16), etg.BF16, 1, 16)

@@ -1,0 +1,84 @@
+"""Full-size workloads on the GPU, in the launch configuration the bench times.
+
+The oracle computes full logits only for a few sampled residual rows per call
+(each is one f64 pass over the table); every other row is checked through
+properties that hold at any size: k distinct ids, scores equal to the oracle's
+logits at those ids within tolerance, non-increasing order, and no id whose
+logit falls below the oracle's k-th best by more than the tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import accept
+from tests.gpu_util import note, table, to_dev
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def _table(name):
+    if name not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        cfg = synth.CONFIGS[name]
+        note(f"generate {name} table ({cfg.table_bytes / 1e9:.2f} GB)")
+        host = cfg.table()
+        _cache[name] = (cfg, host, table(host, cfg.dtype, cfg.V, cfg.d))
+    return _cache[name]
+
+
+def _check(name, B, k, sample_rows):
+    cfg, host, t = _table(name)
+    R = synth.residuals(B, cfg.d, cfg.residual_seed(B))
+    note(f"logits_topk {name} B={B} k={k}")
+    gids, gsc = t.logits_topk(to_dev(R), k)
+    torch.cuda.synchronize()
+    gids, gsc = gids.cpu().numpy(), gsc.cpu().numpy()
+    c = accept.tol_coeff(cfg.dtype)
+    # every row: properties with the oracle's logits at the returned ids
+    bs = np.repeat(np.arange(B), k)
+    Lg, Ag = oracle.logits_at(host, cfg.dtype, cfg.V, cfg.d, R, bs, gids.reshape(-1))
+    Lg, Ag = Lg.reshape(B, k), Ag.reshape(B, k)
+    fails = []
+    for b in range(B):
+        fails += [f"row {b}: {s}" for s in accept.check_row(gids[b], gsc[b], cfg.V, c, Lg[b], Ag[b])]
+    # sampled rows: the oracle's own top-k from a full pass
+    for b in sample_rows:
+        L, A = oracle.logits(host, cfg.dtype, cfg.V, cfg.d, R[b:b + 1])
+        oids, _ = oracle.topk(L, k)
+        fails += [f"row {b}: {s}" for s in accept.check_full(gids[b:b + 1], gsc[b:b + 1], L, A, oids, c)]
+        # every returned logit is at least the oracle's k-th best minus the tolerance
+        kth = L[0, oids[0, -1]]
+        assert np.all(Lg[b] >= kth - c * (Ag[b] + A[0, oids[0, -1]]))
+    assert not fails, fails[:5]
+
+
+def test_qwen05b_logits_b1():
+    _check("qwen05b", 1, 10, [0])
+
+
+@pytest.mark.parametrize("B,sample", [(1, [0]), (8, [0, 7]), (64, [5, 63])])
+def test_lm31b_logits(B, sample):
+    _check("lm31b", B, 10, sample)
+
+
+def test_prefill_logits_b1024():
+    _check("prefill", 1024, 40, [0, 1023])
+
+
+def test_lm31b_tied_gather_then_logits():
+    # tied lm_head: gather rows from the same table, then project them back
+    cfg, host, t = _table("lm31b")
+    ids = np.array([0, 262143, 199729, 123456], np.int32)
+    note("lm31b tied gather")
+    x = t.embed_gather(torch.from_numpy(ids).cuda(), check=False)
+    ref, _ = oracle.embed_gather(host, cfg.dtype, cfg.V, cfg.d, ids)
+    assert torch.equal(x.cpu(), torch.from_numpy(ref))
+    gids, gsc = t.logits_topk(x, 1)
+    torch.cuda.synchronize()
+    # a row's dot product with itself is its squared norm, by far the largest logit here
+    assert gids.cpu().numpy()[:, 0].tolist() == ids.tolist()

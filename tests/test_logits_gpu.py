@@ -1,0 +1,180 @@
+"""logits_topk on the GPU against the CPU oracle.
+
+Small and ragged shapes compare every row with the oracle's full logits under
+the acceptance rule (oracle/accept.py); the special cases (zero and one-hot
+residuals, duplicate rows, planted winners) pin exact ids and scores.  Every
+path (valu, stream) is forced on the same inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import embedding_table_gather_amd as etg
+import oracle
+import synth
+from oracle import accept
+from tests.gpu_util import note, table, to_dev
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16, Q8_0 = etg.F32, etg.BF16, etg.Q8_0
+VALU, STREAM = etg.PATH_VALU, etg.PATH_STREAM
+
+
+def run(t, R, k, path):
+    note(f"logits dtype={t.dtype} V={t.vocab} d={t.hidden} B={R.shape[0]} k={k} path={path}")
+    ids, sc = t.logits_topk(to_dev(R), k, path=path)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), sc.cpu().numpy()
+
+
+def full_check(host, dtype, V, d, R, k, path, t=None):
+    t = t or table(host, dtype, V, d)
+    gids, gsc = run(t, R, k, path)
+    L, A = oracle.logits(host, dtype, V, d, R)
+    oids, osc = oracle.topk(L, k)
+    fails = accept.check_full(gids, gsc, L, A, oids, accept.tol_coeff(dtype))
+    assert not fails, fails[:5]
+    return gids, gsc, oids, osc
+
+
+def test_tiny_config_f32():
+    cfg = synth.CONFIGS["tiny"]
+    host = cfg.table()
+    R = cfg.residuals(4)
+    full_check(host, cfg.dtype, cfg.V, cfg.d, R, cfg.k, etg.PATH_AUTO)
+
+
+@pytest.mark.parametrize("dtype,V,d", [(F32, 2049, 100), (BF16, 5003, 200), (BF16, 4099, 896),
+                                       (Q8_0, 3001, 96), (Q8_0, 2000, 768)])
+@pytest.mark.parametrize("B", [1, 3, 9])
+def test_valu_path_ragged(dtype, V, d, B):
+    host = synth.make_table(dtype, V, d, seed=100 + V)
+    R = synth.residuals(B, d, seed=200 + B)
+    full_check(host, dtype, V, d, R, 10, VALU)
+
+
+@pytest.mark.parametrize("V,d", [(5003, 200), (4099, 896), (1001, 64), (20000, 5376), (37, 8)])
+@pytest.mark.parametrize("B", [1, 2, 4, 5, 8, 9, 17])
+def test_stream_path_ragged(V, d, B):
+    host = synth.make_table(BF16, V, d, seed=300 + V)
+    R = synth.residuals(B, d, seed=400 + B)
+    k = min(10, V)
+    full_check(host, BF16, V, d, R, k, STREAM)
+
+
+@pytest.mark.parametrize("k", [1, 2, 40, 64])
+@pytest.mark.parametrize("path", [VALU, STREAM])
+def test_k_range(k, path):
+    V, d = 7001, 256
+    host = synth.make_table(BF16, V, d, seed=17)
+    R = synth.residuals(3, d, seed=18)
+    full_check(host, BF16, V, d, R, k, path)
+
+
+@pytest.mark.parametrize("path", [VALU, STREAM])
+def test_zero_residual_gives_ids_in_order(path):
+    V, d = 3000, 128
+    host = synth.make_table(BF16, V, d, seed=5)
+    ids, sc = run(table(host, BF16, V, d), np.zeros((2, d), np.float32), 64, path)
+    assert np.array_equal(ids, np.tile(np.arange(64), (2, 1)))
+    assert np.all(sc == 0)
+
+
+@pytest.mark.parametrize("path", [VALU, STREAM])
+@pytest.mark.parametrize("B", [1, 6])
+def test_one_hot_residual_selects_column_exactly(path, B):
+    V, d = 4000, 192
+    host = synth.make_table(BF16, V, d, seed=6)
+    R = np.zeros((B, d), np.float32)
+    cols = [0, 191, 64, 65, 127, 3][:B]
+    for b, j in enumerate(cols):
+        R[b, j] = 1.0
+    gids, gsc = run(table(host, BF16, V, d), R, 20, path)
+    L, _ = oracle.logits(host, BF16, V, d, R)
+    oids, osc = oracle.topk(L, 20)
+    assert np.array_equal(gids, oids)
+    assert np.array_equal(gsc.view(np.uint32), osc.view(np.uint32))
+
+
+@pytest.mark.parametrize("path", [VALU, STREAM])
+def test_duplicate_rows_rank_by_id(path):
+    V, d = 5000, 256
+    host = synth.make_table(BF16, V, d, seed=9)
+    R = synth.residuals(1, d, seed=10)
+    best = synth.f32_to_bf16_bits((R[0] / np.linalg.norm(R[0]) * 0.5).astype(np.float32))
+    for v in (4999, 17, 2048, 8):
+        host[v] = best
+    gids, _, oids, _ = full_check(host, BF16, V, d, R, 6, path)
+    assert list(gids[0][:4]) == [8, 17, 2048, 4999]
+    assert np.array_equal(gids, oids)
+
+
+@pytest.mark.parametrize("path", [VALU, STREAM])
+def test_planted_winners_exact_order(path):
+    V, d = 30000, 512
+    host = synth.make_table(BF16, V, d, seed=11)
+    R = synth.residuals(2, d, seed=12)
+    planted = [[29999, 5, 12345, 777], [0, 15000, 29998, 1]]
+    for b in range(2):
+        u = R[b] / np.linalg.norm(R[b])
+        for j, v in enumerate(planted[b]):
+            host[v] = synth.f32_to_bf16_bits((u * (0.6 - 0.1 * j)).astype(np.float32))
+    gids, _, oids, _ = full_check(host, BF16, V, d, R, 4, path)
+    assert gids.tolist() == planted
+    assert np.array_equal(gids, oids)
+
+
+@pytest.mark.parametrize("path", [VALU, STREAM])
+def test_repeatable_bitwise(path):
+    V, d = 50000, 896
+    host = synth.make_table(BF16, V, d, seed=13)
+    R = to_dev(synth.residuals(5, d, seed=14))
+    t = table(host, BF16, V, d)
+    note(f"logits repeat x20 path={path}")
+    i0, s0 = t.logits_topk(R, 10, path=path)
+    i0, s0 = i0.clone(), s0.clone()
+    for _ in range(20):
+        i1, s1 = t.logits_topk(R, 10, path=path)
+        assert torch.equal(i0, i1) and torch.equal(s0.view(torch.int32), s1.view(torch.int32))
+
+
+def test_paths_agree_on_bf16():
+    V, d = 20011, 1024
+    host = synth.make_table(BF16, V, d, seed=15)
+    R = synth.residuals(6, d, seed=16)
+    t = table(host, BF16, V, d)
+    a = run(t, R, 10, VALU)
+    b = run(t, R, 10, STREAM)
+    L, A = oracle.logits(host, BF16, V, d, R)
+    oids, _ = oracle.topk(L, 10)
+    for g in (a, b):
+        assert not accept.check_full(g[0], g[1], L, A, oids, accept.tol_coeff(BF16))
+
+
+def test_vocab_smaller_than_k_slots():
+    # fewer rows than one block's share: blocks with no rows must not leak empty keys
+    V, d = 9, 64
+    host = synth.make_table(BF16, V, d, seed=19)
+    R = synth.residuals(2, d, seed=20)
+    for path in (VALU, STREAM):
+        full_check(host, BF16, V, d, R, 9, path)
+
+
+@pytest.mark.parametrize("path", [VALU, STREAM])
+@pytest.mark.parametrize("B,d", [(1, 64), (3, 896), (6, 5376), (8, 200)])
+def test_residual_at_bf16_midpoints_stays_within_tolerance(path, B, d):
+    # r_i = (1 + 2^-8) * sign(e_i) sits halfway between two bf16 values; rounding it
+    # once would lose 2^-8 / (1 + 2^-8) = 3.9e-3 of sum|r e|, twice the 2e-3 bound.
+    V = 777
+    host = synth.make_table(BF16, V, d, seed=21)
+    E = oracle.bf16_to_f64(host)
+    R = np.empty((B, d), np.float32)
+    for b in range(B):
+        R[b] = np.where(E[(37 * b) % V] >= 0, 1.0, -1.0) * np.float32(1 + 2 ** -8)
+        # one bf16 rounding of this residual misses the bound on the row it is aligned with
+        row = E[(37 * b) % V]
+        single = oracle.bf16_to_f64(synth.f32_to_bf16_bits(R[b])) @ row
+        exact = R[b].astype(np.float64) @ row
+        assert abs(single - exact) > 2e-3 * (np.abs(R[b]).astype(np.float64) @ np.abs(row))
+    full_check(host, BF16, V, d, R, 5, path)
