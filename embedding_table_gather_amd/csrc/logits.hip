@@ -50,42 +50,42 @@ namespace etg {
 // D layout: lane L holds D[4 (L / 16) + i][L % 16], i = 0..3.  For L < 32 with
 // b = L % 16 < nbc, the terms sit in lanes L, L + 40 (+ 4, + 44 when packed).
 //
-// Global image: [pass][step][image][64 lanes] x 16 bytes.  A block stages up to
-// `chunk` steps of it in LDS at a time (all of it when it fits).
+// Each block builds the operand image [step][image][64 lanes] x 16 bytes in LDS
+// from the fp32 residual, `chunk` steps at a time (all of it when it fits).
 // ---------------------------------------------------------------------------
 
 static constexpr int kStreamWaves = 16;
-static constexpr int kStreamUnroll = 8;
+static constexpr int kStreamUnroll = 6;  // K steps per load group (half of it with two images)
 static constexpr int kStreamMaxPairs = 4;  // a wave handles at most 8 groups (64 rows)
 
-// fp32 residual [B][hidden] -> bf16 hi/lo operand image.
+// Fill LDS with steps [c0, c0 + n) of the bf16 hi/lo operand image, converted from
+// the fp32 residual rows of this pass.  Image slot (s, im, lane) holds the 8
+// values of B column n = lane % 16, K-group g = lane / 16 (layout above).
 template <int NIMG>
-__global__ void __launch_bounds__(256) stream_prep_kernel(const float* __restrict__ R, int64_t B,
-                                                          int hidden, int steps, int npass,
-                                                          u32x4* __restrict__ img) {
+__device__ __forceinline__ void stream_stage_image(u32x4* simg, const float* __restrict__ R, int64_t B,
+                                                   int hidden, int64_t b0, int c0, int n) {
   constexpr int NBC = NIMG == 1 ? 4 : 8;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)npass * steps * NIMG * 64) return;
-  const int lane = (int)(t & 63);
-  const int64_t q = t >> 6;
-  const int im = (int)(q % NIMG);
-  const int s = (int)((q / NIMG) % steps);
-  const int pass = (int)(q / ((int64_t)NIMG * steps));
-  const int n = lane & 15, g = lane >> 4;
-  const int h = n >> 3, j8 = n & 7;
-  const int part = NIMG == 1 ? j8 / NBC : im;
-  const int bl = j8 % NBC;
-  const int64_t b = (int64_t)pass * NBC + bl;
-  uint32_t v[8];
+  for (int i = threadIdx.x; i < n * NIMG * 64; i += blockDim.x) {
+    const int lane = i & 63;
+    const int q = i >> 6;
+    const int im = q % NIMG;
+    const int s = c0 + q / NIMG;
+    const int nn = lane & 15, g = lane >> 4;
+    const int h = nn >> 3, j8 = nn & 7;
+    const int part = NIMG == 1 ? j8 / NBC : im;
+    const int64_t b = b0 + j8 % NBC;
+    const int cbase = 64 * s + 16 * g + 8 * h;
+    uint32_t v[8];
 #pragma unroll
-  for (int e = 0; e < 8; e++) {
-    const int c = 64 * s + 16 * g + 8 * h + e;
-    const float x = (b < B && c < hidden) ? R[b * hidden + c] : 0.0f;
-    const uint32_t hi = bf16_rne(x);
-    // part 1 carries the remainder x - hi (exact in f32), rounded to bf16
-    v[e] = part == 1 ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;
+    for (int e = 0; e < 8; e++) {
+      const int c = cbase + e;
+      const float x = (b < B && c < hidden) ? R[b * hidden + c] : 0.0f;
+      const uint32_t hi = bf16_rne(x);
+      // part 1 carries the remainder x - hi (exact in f32), rounded to bf16
+      v[e] = part == 1 ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;
+    }
+    simg[i] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
   }
-  img[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
 }
 
 template <int NBC>
@@ -104,54 +104,70 @@ __device__ __forceinline__ void stream_store_group(f32x4 acc, float* dst, int la
   }
 }
 
-// Select the k best (logit, row) of this block for residual column b.  Values
-// live in slog as [wave][group * 8 + r][NBC]; rows >= V are skipped.  Round t
-// takes the largest key below the key of round t - 1 (keys are unique).
+// The k best (logit, row) of this block for residual column b, as descending keys.
+// slog is [wave][group * 8 + r][NBC]; wave w owns groups [sg0[w], sg0[w] + sng[w]).
+// Each lane holds one row per wave in registers; round t takes the largest key
+// below the key of round t - 1 (keys are unique).
 template <int NBC>
-__device__ void stream_block_topk(const float* slog, int b, int lane, int64_t blk_gw0, int64_t ngroups,
-                                  int64_t nw, int max_groups, int64_t V, int k, uint64_t* out) {
-  const int per_wave = max_groups * 8;
-  const int total = kStreamWaves * per_wave;
+__device__ void stream_block_topk(const float* slog, const int64_t* sg0, const int* sng, int b, int lane,
+                                  int max_groups, int64_t V, int k, uint64_t* out) {
+  const int per_wave = max_groups * 8;  // <= 64
+  uint64_t key[kStreamWaves];
+#pragma unroll
+  for (int w = 0; w < kStreamWaves; w++) {
+    const int64_t row = sg0[w] * 8 + lane;
+    key[w] = (lane < sng[w] * 8 && row < V) ? make_key(slog[(w * per_wave + lane) * NBC + b], (uint32_t)row) : 0;
+  }
   uint64_t prev = ~0ull;
   for (int t = 0; t < k; t++) {
     uint64_t best = 0;
-    for (int i = lane; i < total; i += 64) {
-      const int w = i / per_wave, li = i - w * per_wave;
-      const int64_t gw = blk_gw0 + w;
-      const int64_t g0 = gw * ngroups / nw, g1 = (gw + 1) * ngroups / nw;
-      const int64_t row = g0 * 8 + li;
-      if (li < (int)(g1 - g0) * 8 && row < V) {
-        const uint64_t key = make_key(slog[i * NBC + b], (uint32_t)row);
-        if (key < prev && key > best) best = key;
-      }
-    }
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; w++) best = (key[w] < prev && key[w] > best) ? key[w] : best;
     best = wave_max_u64(best);
     if (lane == 0) out[t] = best;
     prev = best;
   }
 }
 
+// One pass over the table for NBC residual rows (pass = blockIdx.y).
+//  table      bf16 [V][hidden], row_bytes = 2 * hidden
+//  R          fp32 [B][hidden]
+//  steps      64-value K steps, ceil(hidden / 64)
+//  chunk      K steps staged in LDS at a time (a multiple of the unroll)
+// Out-of-range rows and K positions are read from clamped in-range addresses and
+// meet zero residual values or are never ranked, so no load is predicated (table
+// entries are assumed finite).
 template <int NIMG>
 __global__ void __launch_bounds__(1024) stream_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden,
-    const u32x4* __restrict__ img, int steps, int chunk, int64_t B, int k, uint64_t* __restrict__ cand,
+    const float* __restrict__ R, int64_t B, int steps, int chunk, int k, uint64_t* __restrict__ cand,
     int64_t ngroups, int max_groups) {
   constexpr int NBC = NIMG == 1 ? 4 : 8;
-  constexpr int U = kStreamUnroll;
+  constexpr int U = NIMG == 1 ? kStreamUnroll : kStreamUnroll / 2;
+  const int steps_full = hidden / 64;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   u32x4* simg = (u32x4*)smem;
   float* slog = (float*)(smem + (size_t)chunk * NIMG * 1024);
+  __shared__ int64_t sg0[kStreamWaves];
+  __shared__ int sng[kStreamWaves];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int pass = blockIdx.y;
-  const u32x4* pimg = img + (size_t)pass * steps * NIMG * 64;
+  const int64_t b0 = (int64_t)blockIdx.y * NBC;
 
+  // Waves own contiguous runs of group pairs (16 rows); only the last pair of the
+  // table can be half empty.
   const int64_t nw = (int64_t)gridDim.x * kStreamWaves;
   const int64_t gw = (int64_t)blockIdx.x * kStreamWaves + wv;
-  const int64_t g_begin = gw * ngroups / nw;
-  const int ng = (int)((gw + 1) * ngroups / nw - g_begin);
-  const int npairs = (ng + 1) >> 1;
+  const int64_t npairs_all = (ngroups + 1) >> 1;
+  const int64_t pb = gw * npairs_all / nw;
+  const int npairs = (int)((gw + 1) * npairs_all / nw - pb);
+  const int64_t g_begin = 2 * pb;
+  const int ng = (int)min((int64_t)(2 * npairs), ngroups - g_begin);
+  if (lane == 0) {
+    sg0[wv] = g_begin;
+    sng[wv] = ng;
+  }
   const int r = lane & 7, ck = lane >> 3;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int64_t last_off = row_bytes - 16;
 
   f32x4 acc0[kStreamMaxPairs], acc1[kStreamMaxPairs];
 #pragma unroll
@@ -160,40 +176,54 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
   for (int c0 = 0; c0 < steps; c0 += chunk) {
     const int c1 = min(steps, c0 + chunk);
     if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
-    for (int i = tid; i < (c1 - c0) * NIMG * 64; i += blockDim.x) simg[i] = pimg[(size_t)c0 * NIMG * 64 + i];
+    stream_stage_image<NIMG>(simg, R, B, hidden, b0, c0, c1 - c0);
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kStreamMaxPairs; p++) {
       if (p < npairs) {
-        const int64_t row0 = (g_begin + 2 * p) * 8 + r;
-        const int64_t row1 = row0 + 8;
-        const bool ok0 = row0 < V;
-        const bool ok1 = (2 * p + 1 < ng) && (row1 < V);
-        const u32x4* p0 = (const u32x4*)(table + (uint64_t)(ok0 ? row0 : 0) * (uint64_t)row_bytes) + ck;
-        const u32x4* p1 = (const u32x4*)(table + (uint64_t)(ok1 ? row1 : 0) * (uint64_t)row_bytes) + ck;
-        for (int s0 = c0; s0 < c1; s0 += U) {
+        const int64_t row0 = min((g_begin + 2 * p) * 8 + r, V - 1);
+        const int64_t row1 = min((g_begin + 2 * p) * 8 + 8 + r, V - 1);
+        const uint8_t* p0 = table + (uint64_t)row0 * (uint64_t)row_bytes;
+        const uint8_t* p1 = table + (uint64_t)row1 * (uint64_t)row_bytes;
+        const u32x4* q0 = (const u32x4*)(p0 + 16 * ck);
+        const u32x4* q1 = (const u32x4*)(p1 + 16 * ck);
+        // complete steps, U at a time: all loads of the group are issued before the
+        // MFMAs that consume them
+        const int cf = min(c1, steps_full);
+        int s0 = c0;
+        for (; s0 + U <= cf; s0 += U) {
           u32x4 a0[U], a1[U];
 #pragma unroll
           for (int j = 0; j < U; j++) {
-            const int s = s0 + j;
-            const bool kv = (s < c1) && (64 * s + 8 * ck < hidden);
-            a0[j] = (ok0 && kv) ? p0[8 * s] : zero;
-            a1[j] = (ok1 && kv) ? p1[8 * s] : zero;
+            a0[j] = __builtin_nontemporal_load(q0 + 8 * (s0 + j));
+            a1[j] = __builtin_nontemporal_load(q1 + 8 * (s0 + j));
           }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < U; j++) {
-            const int s = s0 + j;
-            if (s < c1) {
-              const u32x4* bl = simg + (size_t)(s - c0) * NIMG * 64 + lane;
+            const u32x4* bl = simg + (size_t)(s0 + j - c0) * NIMG * 64 + lane;
 #pragma unroll
-              for (int im = 0; im < NIMG; im++) {
-                const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[im * 64]);
-                acc0[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0[j]), bop, acc0[p],
-                                                                  0, 0, 0);
-                acc1[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1[j]), bop, acc1[p],
-                                                                  0, 0, 0);
-              }
+            for (int im = 0; im < NIMG; im++) {
+              const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[im * 64]);
+              acc0[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0[j]), bop, acc0[p], 0,
+                                                                0, 0);
+              acc1[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1[j]), bop, acc1[p], 0,
+                                                                0, 0);
             }
+          }
+        }
+        // remaining steps of the chunk, one at a time; a K position at or past
+        // `hidden` reads the row's last 16 bytes and meets a zero residual value
+        for (; s0 < min(c1, steps); s0++) {
+          const int64_t off = min((int64_t)(128 * s0 + 16 * ck), last_off);
+          const u32x4 a0 = __builtin_nontemporal_load((const u32x4*)(p0 + off));
+          const u32x4 a1 = __builtin_nontemporal_load((const u32x4*)(p1 + off));
+          const u32x4* bl = simg + (size_t)(s0 - c0) * NIMG * 64 + lane;
+#pragma unroll
+          for (int im = 0; im < NIMG; im++) {
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[im * 64]);
+            acc0[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bop, acc0[p], 0, 0, 0);
+            acc1[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bop, acc1[p], 0, 0, 0);
           }
         }
       }
@@ -208,11 +238,9 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
   }
   __syncthreads();
 
-  const int64_t b0 = (int64_t)pass * NBC;
   if (wv < NBC && b0 + wv < B) {
     uint64_t* out = cand + ((b0 + wv) * gridDim.x + blockIdx.x) * (int64_t)k;
-    stream_block_topk<NBC>(slog, wv, lane, (int64_t)blockIdx.x * kStreamWaves, ngroups, nw, max_groups, V,
-                           k, out);
+    stream_block_topk<NBC>(slog, sg0, sng, wv, lane, max_groups, V, k, out);
   }
 }
 
@@ -281,35 +309,84 @@ __global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Cross-block merge: per residual row, the k largest of nblk * k keys.
+// Cross-block merge: per residual row (blockIdx.x), the k largest of n keys.
+// Each thread keeps up to KPT keys in registers; round t takes the largest key
+// below the key of round t - 1 with a wave max and a 16-way exchange in LDS
+// (double-buffered by round parity, so one barrier per round).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) topk_merge_kernel(const uint64_t* __restrict__ cand, int nblk, int k,
-                                                         int32_t* __restrict__ ids, float* __restrict__ scores) {
-  __shared__ uint64_t red[4];
+static constexpr int kMergeThreads = 1024;
+
+template <int KPT>
+__global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __restrict__ cand, int n, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ scores) {
+  __shared__ uint64_t red[2][kMergeThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t b = blockIdx.x;
-  const uint64_t* c = cand + b * (int64_t)nblk * k;
-  const int n = nblk * k;
+  const uint64_t* c = cand + b * (int64_t)n;
+  uint64_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; j++) {
+    const int i = tid + j * kMergeThreads;
+    key[j] = i < n ? c[i] : 0;
+  }
   uint64_t prev = ~0ull;
   for (int t = 0; t < k; t++) {
     uint64_t best = 0;
-    for (int i = tid; i < n; i += 256) {
-      const uint64_t key = c[i];
-      if (key < prev && key > best) best = key;
-    }
-    best = wave_max_u64(best);
-    if (lane == 0) red[wv] = best;
-    __syncthreads();
-    uint64_t m = red[0];
 #pragma unroll
-    for (int w = 1; w < 4; w++) m = red[w] > m ? red[w] : m;
+    for (int j = 0; j < KPT; j++) best = (key[j] < prev && key[j] > best) ? key[j] : best;
+    best = wave_max_u64(best);
+    if (lane == 0) red[t & 1][wv] = best;
     __syncthreads();
+    uint64_t m = red[t & 1][0];
+#pragma unroll
+    for (int w = 1; w < kMergeThreads / 64; w++) m = red[t & 1][w] > m ? red[t & 1][w] : m;
     if (tid == 0) {
       ids[b * k + t] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
       scores[b * k + t] = ord_score((uint32_t)(m >> 32));
     }
     prev = m;
   }
+}
+
+// Same, for more keys than fit in registers: every round rescans global memory.
+__global__ void __launch_bounds__(1024) topk_merge_wide_kernel(const uint64_t* __restrict__ cand, int n, int k,
+                                                               int32_t* __restrict__ ids, float* __restrict__ scores) {
+  __shared__ uint64_t red[2][kMergeThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t b = blockIdx.x;
+  const uint64_t* c = cand + b * (int64_t)n;
+  uint64_t prev = ~0ull;
+  for (int t = 0; t < k; t++) {
+    uint64_t best = 0;
+    for (int i = tid; i < n; i += kMergeThreads) {
+      const uint64_t key = c[i];
+      best = (key < prev && key > best) ? key : best;
+    }
+    best = wave_max_u64(best);
+    if (lane == 0) red[t & 1][wv] = best;
+    __syncthreads();
+    uint64_t m = red[t & 1][0];
+    for (int w = 1; w < kMergeThreads / 64; w++) m = red[t & 1][w] > m ? red[t & 1][w] : m;
+    if (tid == 0) {
+      ids[b * k + t] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
+      scores[b * k + t] = ord_score((uint32_t)(m >> 32));
+    }
+    prev = m;
+  }
+}
+
+static hipError_t launch_merge(const uint64_t* cand, int64_t batch, int n, int k, int32_t* ids, float* scores,
+                               hipStream_t stream) {
+  const dim3 grid((unsigned)batch), block(kMergeThreads);
+  const int kpt = (n + kMergeThreads - 1) / kMergeThreads;
+#define ETG_MERGE_CASE(KV) \
+  if (kpt <= KV) { hipLaunchKernelGGL((topk_merge_kernel<KV>), grid, block, 0, stream, cand, n, k, ids, scores); }
+  ETG_MERGE_CASE(1)
+  else ETG_MERGE_CASE(2) else ETG_MERGE_CASE(4) else ETG_MERGE_CASE(8) else ETG_MERGE_CASE(16)
+  else ETG_MERGE_CASE(32) else hipLaunchKernelGGL(topk_merge_wide_kernel, grid, block, 0, stream, cand, n, k, ids,
+                                                   scores);
+#undef ETG_MERGE_CASE
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -353,19 +430,14 @@ static hipError_t launch_valu(const TableDesc& t, const LogitsPlan& p, const flo
 }
 
 template <int NIMG>
-static hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const float* R, u32x4* img,
-                                uint64_t* cand, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  const int64_t nprep = (int64_t)p.npass * p.steps * NIMG * 64;
-  hipLaunchKernelGGL((stream_prep_kernel<NIMG>), dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream,
-                     R, p.batch, (int)t.hidden, p.steps, p.npass, img);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = set_lds((const void*)stream_logits_kernel<NIMG>, p.lds_bytes);
+static hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
+                                hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  hipError_t e = set_lds((const void*)stream_logits_kernel<NIMG>, p.lds_bytes);
   if (e != hipSuccess) return e;
   if ((e = record(ev0, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((stream_logits_kernel<NIMG>), dim3((unsigned)p.nblk, (unsigned)p.npass),
-                     dim3(64 * kStreamWaves), p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (int)t.hidden, img,
-                     p.steps, p.chunk, p.batch, p.k, cand, p.ngroups, p.max_groups);
+                     dim3(64 * kStreamWaves), p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (int)t.hidden, R,
+                     p.batch, p.steps, p.chunk, p.k, cand, p.ngroups, p.max_groups);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record(ev1, stream);
 }
@@ -376,9 +448,8 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const flo
   uint64_t* cand = (uint64_t*)(base + p.cand_offset);
   hipError_t e;
   if (p.path == 2) {
-    u32x4* img = (u32x4*)(base + p.img_offset);
-    e = p.nimg == 1 ? launch_stream<1>(t, p, R, img, cand, stream, ev0, ev1)
-                    : launch_stream<2>(t, p, R, img, cand, stream, ev0, ev1);
+    e = p.nimg == 1 ? launch_stream<1>(t, p, R, cand, stream, ev0, ev1)
+                    : launch_stream<2>(t, p, R, cand, stream, ev0, ev1);
   } else {
     switch (t.dtype) {
       case DT_F32: e = launch_valu<DT_F32>(t, p, R, cand, stream, ev0, ev1); break;
@@ -387,9 +458,7 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const flo
     }
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)p.batch), dim3(256), 0, stream, cand, p.nblk, p.k, ids,
-                     scores);
-  return hipGetLastError();
+  return launch_merge(cand, p.batch, p.nblk * p.k, p.k, ids, scores, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -422,19 +491,19 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     p->steps = (int32_t)cdiv(t.hidden, 64);
     p->ngroups = cdiv(t.V, 8);
     p->npass = (int32_t)cdiv(batch, p->nbc);
-    // one block per CU, unless a wave would then own more than 8 groups
-    const int64_t per_blk = (int64_t)kStreamWaves * 2 * kStreamMaxPairs;
-    p->nblk = (int32_t)std::max<int64_t>(cdiv(p->ngroups, per_blk),
-                                         std::min<int64_t>(kTargetBlocks, cdiv(p->ngroups, kStreamWaves)));
-    p->max_groups = (int32_t)cdiv(p->ngroups, (int64_t)p->nblk * kStreamWaves);
+    // one block per CU, unless a wave would then own more than kStreamMaxPairs pairs
+    const int64_t npairs_all = cdiv(p->ngroups, 2);
+    p->nblk = (int32_t)std::max<int64_t>(cdiv(npairs_all, (int64_t)kStreamWaves * kStreamMaxPairs),
+                                         std::min<int64_t>(kTargetBlocks, cdiv(npairs_all, kStreamWaves)));
+    p->max_groups = (int32_t)(2 * cdiv(npairs_all, (int64_t)p->nblk * kStreamWaves));
     const size_t log_bytes = (size_t)kStreamWaves * p->max_groups * 8 * p->nbc * 4;
-    const size_t img_room = kMaxLds - log_bytes;
-    const int64_t max_chunk = (int64_t)(img_room / ((size_t)p->nimg * 1024));
-    // equal chunks, as few as fit
+    const size_t img_room = kMaxLds - 1024 - log_bytes;
+    const int64_t max_chunk = (int64_t)(img_room / ((size_t)p->nimg * 1024)) / kStreamUnroll * kStreamUnroll;
+    // equal chunks (multiples of the unroll), as few as fit
     const int64_t nchunks = cdiv(p->steps, max_chunk);
-    p->chunk = (int32_t)cdiv(p->steps, nchunks);
+    p->chunk = (int32_t)std::min<int64_t>(max_chunk, cdiv(cdiv(p->steps, nchunks), kStreamUnroll) * kStreamUnroll);
     p->lds_bytes = (size_t)p->chunk * p->nimg * 1024 + log_bytes;
-    p->img_bytes = (size_t)p->npass * p->steps * p->nimg * 1024;
+    p->img_bytes = 0;
   } else {
     p->rb = batch >= 8 ? 8 : batch >= 4 ? 4 : batch >= 2 ? 2 : 1;
     p->npass = (int32_t)cdiv(batch, p->rb);
