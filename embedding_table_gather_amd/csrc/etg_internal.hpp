@@ -28,14 +28,20 @@ struct LogitsPlan {
   int32_t chunk;         // K steps of the residual image staged in LDS at a time
   int64_t ngroups;       // 8-row table groups = ceil(V / 8)
   int32_t max_groups;    // most 8-row groups one wave handles
+  // gemm path
+  int32_t kpad;          // hidden rounded up to the K stage
+  int32_t nct;           // column tiles of 64 residual rows
+  int32_t nvr;           // vocabulary ranges
+  int32_t tiles_per_range;
   // valu path
   int32_t rb;            // residual rows per pass (1, 2, 4 or 8)
   int64_t rows_per_blk;  // most table rows one block handles
   // common
   int32_t npass;         // batch passes (grid.y)
-  int32_t nblk;          // blocks per pass; each emits k candidates per residual row
+  int32_t nblk;          // blocks per pass
+  int32_t ncand;         // candidate keys per residual row
   size_t lds_bytes;      // dynamic LDS of the main kernel
-  size_t img_offset, img_bytes;    // bf16 residual image (stream path)
+  size_t img_offset, img_bytes;    // split bf16 residual rows (gemm path)
   size_t cand_offset, cand_bytes;  // u64 keys [batch][nblk][k]
   size_t ws_bytes;
 };

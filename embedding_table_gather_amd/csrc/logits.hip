@@ -245,6 +245,201 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// GEMM path: bf16 tables, larger batches.
+//
+// C[v][j] = sum_i E[v][i] * Rs[j][i] with Rs the residual rows as hi and lo bf16
+// rows, so logit[v][b] = C[v][hi(b)] + C[v][lo(b)].  A workgroup (4 waves, 2 x 2)
+// owns a tile of 128 split columns (64 residual rows) and walks a range of
+// 256-row vocabulary tiles; per tile it runs the K loop in stages of 64 values
+// through double-buffered LDS and v_mfma_f32_32x32x16_bf16.  Wave (mw, nw)
+// computes rows [128 mw, +128) x split columns [64 nw, +64): N-tile 0 holds the
+// hi rows of residual rows [32 nw, +32) of the tile, N-tile 1 their lo rows, so
+// the hi + lo sum is a register add.
+//
+// LDS rows are 128 bytes (64 values); 16-byte piece p of row r is stored at
+// piece p ^ ((r >> 1) & 7), which keeps both the stage stores (8 rows x 128 B
+// per wave instruction) and the MFMA fragment reads (one piece of 16
+// consecutive rows per 16 lanes) free of bank conflicts.
+//
+// Top-k: every (wave, residual row) keeps a descending list of k keys in LDS.
+// After a vocabulary tile, each lane compares its 64 logits with the list's
+// last key and inserts the few that beat it (lanes 0-31 first, then 32-63,
+// which share the lists).  At the end the lists are written out as candidates:
+// [batch][vocab range][2 row halves][k].
+//
+// Workgroup ids are mapped so the column tiles of one vocabulary range sit on
+// the same XCD (ids go round-robin over the 8 XCDs): a table tile is fetched
+// from HBM once and served to the other column tiles from that XCD's L2.
+// ---------------------------------------------------------------------------
+static constexpr int kGemmTM = 256;    // vocabulary rows per tile
+static constexpr int kGemmTN = 128;    // split residual columns per tile
+static constexpr int kGemmTK = 64;     // K values per stage
+static constexpr int kGemmStage = (kGemmTM + kGemmTN) * kGemmTK * 2;  // bytes
+static constexpr int kXcds = 8;
+
+__device__ __forceinline__ int gemm_swz(int r, int piece) { return r * 128 + 16 * (piece ^ ((r >> 1) & 7)); }
+
+// fp32 residual [B][hidden] -> split bf16 rows [nct][128][kpad]; row j of tile ct
+// is residual row 64 ct + 32 (j / 64) + j % 32, part (j / 32) % 2 (0 hi, 1 lo).
+__global__ void __launch_bounds__(256) gemm_prep_kernel(const float* __restrict__ R, int64_t B, int hidden, int kpad,
+                                                        int64_t nrows, u32x4* __restrict__ Rs) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int kc = kpad / 8;
+  if (t >= nrows * kc) return;
+  const int64_t row = t / kc;
+  const int c0 = (int)(t % kc) * 8;
+  const int64_t ct = row / kGemmTN;
+  const int j = (int)(row % kGemmTN);
+  const int64_t b = 64 * ct + 32 * (j / 64) + j % 32;
+  const int part = (j / 32) % 2;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const int c = c0 + e;
+    const float x = (b < B && c < hidden) ? R[b * hidden + c] : 0.0f;
+    const uint32_t hi = bf16_rne(x);
+    v[e] = part == 1 ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;
+  }
+  Rs[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void list_insert(uint64_t* list, int k, uint64_t key) {
+  int j = k - 1;
+  while (j > 0) {
+    const uint64_t up = list[j - 1];
+    if (up > key) break;
+    list[j] = up;
+    j--;
+  }
+  list[j] = key;
+}
+
+__global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
+    const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden,
+    const uint8_t* __restrict__ Rs, int kpad, int64_t B, int k, uint64_t* __restrict__ cand,
+    int nct, int nvr, int tiles_per_range) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* stage_buf = smem;                                   // 2 x kGemmStage
+  uint64_t* lists = (uint64_t*)(smem + 2 * kGemmStage);              // [4 waves][32][k]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int mw = wv >> 1, nw = wv & 1;
+
+  // XCD-aware placement: ids {x, x + 8, ...} run on XCD x.
+  const int id = blockIdx.x;
+  const int xcd = id % kXcds, local = id / kXcds;
+  const int ct = local % nct;
+  const int vr = xcd + kXcds * (local / nct);
+  if (vr >= nvr) return;  // whole workgroup; no barrier has been reached
+
+  for (int i = tid; i < 4 * 32 * k; i += 256) lists[i] = 0;
+
+  const int nstage = kpad / kGemmTK;
+  const uint8_t* rs_tile = Rs + (size_t)ct * kGemmTN * kpad * 2;
+  const int64_t last_off = row_bytes - 16;
+  // loader mapping: chunk c = tid + 256 j -> row c / 8, piece c % 8
+  const int lrow = tid >> 3, lpiece = tid & 7;
+
+  for (int vt = 0; vt < tiles_per_range; vt++) {
+    const int64_t v0 = ((int64_t)vr * tiles_per_range + vt) * kGemmTM;
+    if (v0 >= V) break;
+    const uint8_t* arow[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) arow[j] = table + (uint64_t)min(v0 + lrow + 32 * j, V - 1) * (uint64_t)row_bytes;
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; a++) acc[a][0] = acc[a][1] = f32x16{};
+
+    u32x4 pa[8], pb[4];
+    auto load_stage = [&](int st) {
+      const int64_t kb = (int64_t)st * 128 + 16 * lpiece;
+      const int64_t koff = min(kb, last_off);
+#pragma unroll
+      for (int j = 0; j < 8; j++) pa[j] = __builtin_nontemporal_load((const u32x4*)(arow[j] + koff));
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        pb[j] = *(const u32x4*)(rs_tile + (size_t)(lrow + 32 * j) * kpad * 2 + kb);
+    };
+    auto store_stage = [&](int buf) {
+      unsigned char* base = stage_buf + buf * kGemmStage;
+#pragma unroll
+      for (int j = 0; j < 8; j++) *(u32x4*)(base + gemm_swz(lrow + 32 * j, lpiece)) = pa[j];
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        *(u32x4*)(base + kGemmTM * 128 + gemm_swz(lrow + 32 * j, lpiece)) = pb[j];
+    };
+
+    load_stage(0);
+    __syncthreads();  // previous tile's readers of both buffers are done
+    store_stage(0);
+    if (nstage > 1) load_stage(1);
+    __syncthreads();
+    for (int st = 0; st < nstage; st++) {
+      const unsigned char* A = stage_buf + (st & 1) * kGemmStage;
+      const unsigned char* Bt = A + kGemmTM * 128;
+#pragma unroll
+      for (int ks = 0; ks < 4; ks++) {
+        const int piece = 2 * ks + (lane >> 5);
+        bf16x8 af[4], bfr[2];
+#pragma unroll
+        for (int a = 0; a < 4; a++)
+          af[a] = __builtin_bit_cast(bf16x8, *(const u32x4*)(A + gemm_swz(128 * mw + 32 * a + (lane & 31), piece)));
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+          bfr[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bt + gemm_swz(64 * nw + 32 * t + (lane & 31), piece)));
+#pragma unroll
+        for (int a = 0; a < 4; a++)
+#pragma unroll
+          for (int t = 0; t < 2; t++) acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[t], acc[a][t], 0, 0, 0);
+      }
+      if (st + 1 < nstage) {
+        store_stage((st + 1) & 1);
+        if (st + 2 < nstage) load_stage(st + 2);
+      }
+      __syncthreads();
+    }
+
+    // epilogue: logits of rows v0 + 128 mw + 32 a + 8 (i / 4) + 4 (lane / 32) + i % 4,
+    // residual row 64 ct + 32 nw + lane % 32
+    const int64_t b = 64 * (int64_t)ct + 32 * nw + (lane & 31);
+    uint64_t* list = lists + ((size_t)wv * 32 + (lane & 31)) * k;
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+      if ((lane >> 5) == half && b < B) {
+        uint64_t thr = list[k - 1];
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            const int64_t row = v0 + 128 * mw + 32 * a + 8 * (i >> 2) + 4 * half + (i & 3);
+            const float logit = acc[a][0][i] + acc[a][1][i];
+            const uint64_t key = row < V ? make_key(logit, (uint32_t)row) : 0;
+            if (key > thr) {
+              list_insert(list, k, key);
+              thr = list[k - 1];
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  }
+  __syncthreads();
+  // lists -> candidates [B][nvr][2][k]
+  {
+    const int64_t b = 64 * (int64_t)ct + 32 * nw + (lane & 31);
+    if (lane < 32 && b < B) {
+      const uint64_t* list = lists + ((size_t)wv * 32 + lane) * k;
+      uint64_t* out = cand + ((b * nvr + vr) * 2 + mw) * (int64_t)k;
+      for (int j = 0; j < k; j++) out[j] = list[j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // VALU path: any dtype.  Block = 4 waves over a contiguous slice of rows; a wave
 // takes one row at a time, each lane accumulates RB residual rows over values
 // lane, lane + 64, ... with f32 FMAs, then a butterfly sum per residual row.
@@ -442,6 +637,23 @@ static hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const f
   return record(ev1, stream);
 }
 
+static hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs,
+                              uint64_t* cand, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const int64_t nrows = (int64_t)p.nct * kGemmTN;
+  const int64_t nprep = nrows * (p.kpad / 8);
+  hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream, R, p.batch,
+                     (int)t.hidden, p.kpad, nrows, (u32x4*)rs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = set_lds((const void*)gemm_logits_kernel, p.lds_bytes)) != hipSuccess) return e;
+  if ((e = record(ev0, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL(gemm_logits_kernel, dim3((unsigned)p.nblk), dim3(256), p.lds_bytes, stream, t.rows, t.V,
+                     t.row_bytes, (int)t.hidden, (const uint8_t*)rs, p.kpad, p.batch, p.k, cand, p.nct, p.nvr,
+                     p.tiles_per_range);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return record(ev1, stream);
+}
+
 hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const float* R, int32_t* ids,
                               float* scores, void* ws, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   uint8_t* base = (uint8_t*)ws;
@@ -450,6 +662,8 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const flo
   if (p.path == 2) {
     e = p.nimg == 1 ? launch_stream<1>(t, p, R, cand, stream, ev0, ev1)
                     : launch_stream<2>(t, p, R, cand, stream, ev0, ev1);
+  } else if (p.path == 3) {
+    e = launch_gemm(t, p, R, base + p.img_offset, cand, stream, ev0, ev1);
   } else {
     switch (t.dtype) {
       case DT_F32: e = launch_valu<DT_F32>(t, p, R, cand, stream, ev0, ev1); break;
@@ -458,7 +672,7 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const flo
     }
   }
   if (e != hipSuccess) return e;
-  return launch_merge(cand, p.batch, p.nblk * p.k, p.k, ids, scores, stream);
+  return launch_merge(cand, p.batch, p.ncand, p.k, ids, scores, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -474,13 +688,12 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
   p->k = k;
   p->batch = batch;
   const int kTargetBlocks = 256;  // one block per MI355X compute unit
-  if (path == 0) path = (t.dtype == DT_BF16) ? 2 : 1;
-  if (path == 3) path = 2;  // the large-batch contraction shares the stream kernel for now
-  if (path == 2 && t.dtype != DT_BF16) {
-    *why = "the stream path needs a bf16 table";
+  if (path == 0) path = (t.dtype != DT_BF16) ? 1 : (batch <= 8 ? 2 : 3);
+  if ((path == 2 || path == 3) && t.dtype != DT_BF16) {
+    *why = "the stream and gemm paths need a bf16 table";
     return -5;
   }
-  if (path != 1 && path != 2) {
+  if (path != 1 && path != 2 && path != 3) {
     *why = "unknown path";
     return -5;
   }
@@ -504,6 +717,22 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     p->chunk = (int32_t)std::min<int64_t>(max_chunk, cdiv(cdiv(p->steps, nchunks), kStreamUnroll) * kStreamUnroll);
     p->lds_bytes = (size_t)p->chunk * p->nimg * 1024 + log_bytes;
     p->img_bytes = 0;
+    p->ncand = p->nblk * k;
+  } else if (path == 3) {
+    p->kpad = (int32_t)(cdiv(t.hidden, kGemmTK) * kGemmTK);
+    p->nct = (int32_t)cdiv(batch, kGemmTN / 2);
+    const int64_t vtiles = cdiv(t.V, kGemmTM);
+    // about one workgroup per CU; vocabulary ranges in multiples of the XCD count
+    int64_t nvr = std::max<int64_t>(1, kTargetBlocks / p->nct);
+    nvr = std::min<int64_t>(nvr, vtiles);
+    nvr = cdiv(nvr, kXcds) * kXcds;
+    p->tiles_per_range = (int32_t)cdiv(vtiles, nvr);
+    p->nvr = (int32_t)nvr;
+    p->nblk = (int32_t)(p->nct * nvr);
+    p->npass = 1;
+    p->lds_bytes = 2 * (size_t)kGemmStage + (size_t)4 * 32 * k * 8;
+    p->img_bytes = (size_t)p->nct * kGemmTN * p->kpad * 2;
+    p->ncand = (int32_t)(nvr * 2 * k);
   } else {
     p->rb = batch >= 8 ? 8 : batch >= 4 ? 4 : batch >= 2 ? 2 : 1;
     p->npass = (int32_t)cdiv(batch, p->rb);
@@ -515,10 +744,11 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     p->rows_per_blk = cdiv(t.V, nblk);
     p->lds_bytes = (size_t)p->rows_per_blk * p->rb * 4;
     p->img_bytes = 0;
+    p->ncand = p->nblk * k;
   }
   p->img_offset = 0;
   p->cand_offset = align_up(p->img_bytes, 256);
-  p->cand_bytes = (size_t)batch * p->nblk * k * 8;
+  p->cand_bytes = (size_t)batch * p->ncand * 8;
   p->ws_bytes = align_up(p->cand_offset + p->cand_bytes, 256);
   return 0;
 }

@@ -18,7 +18,8 @@ from tests.gpu_util import note, table, to_dev
 pytestmark = pytest.mark.gpu
 
 F32, BF16, Q8_0 = etg.F32, etg.BF16, etg.Q8_0
-VALU, STREAM = etg.PATH_VALU, etg.PATH_STREAM
+VALU, STREAM, GEMM = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM
+ALL = [VALU, STREAM, GEMM]
 
 
 def run(t, R, k, path):
@@ -63,8 +64,16 @@ def test_stream_path_ragged(V, d, B):
     full_check(host, BF16, V, d, R, k, STREAM)
 
 
+@pytest.mark.parametrize("V,d", [(5003, 200), (4099, 896), (1001, 64), (20000, 5376), (37, 8), (70000, 512)])
+@pytest.mark.parametrize("B", [1, 9, 33, 64, 65, 130])
+def test_gemm_path_ragged(V, d, B):
+    host = synth.make_table(BF16, V, d, seed=500 + V)
+    R = synth.residuals(B, d, seed=600 + B)
+    full_check(host, BF16, V, d, R, min(10, V), GEMM)
+
+
 @pytest.mark.parametrize("k", [1, 2, 40, 64])
-@pytest.mark.parametrize("path", [VALU, STREAM])
+@pytest.mark.parametrize("path", ALL)
 def test_k_range(k, path):
     V, d = 7001, 256
     host = synth.make_table(BF16, V, d, seed=17)
@@ -72,7 +81,7 @@ def test_k_range(k, path):
     full_check(host, BF16, V, d, R, k, path)
 
 
-@pytest.mark.parametrize("path", [VALU, STREAM])
+@pytest.mark.parametrize("path", ALL)
 def test_zero_residual_gives_ids_in_order(path):
     V, d = 3000, 128
     host = synth.make_table(BF16, V, d, seed=5)
@@ -81,7 +90,7 @@ def test_zero_residual_gives_ids_in_order(path):
     assert np.all(sc == 0)
 
 
-@pytest.mark.parametrize("path", [VALU, STREAM])
+@pytest.mark.parametrize("path", ALL)
 @pytest.mark.parametrize("B", [1, 6])
 def test_one_hot_residual_selects_column_exactly(path, B):
     V, d = 4000, 192
@@ -97,7 +106,7 @@ def test_one_hot_residual_selects_column_exactly(path, B):
     assert np.array_equal(gsc.view(np.uint32), osc.view(np.uint32))
 
 
-@pytest.mark.parametrize("path", [VALU, STREAM])
+@pytest.mark.parametrize("path", ALL)
 def test_duplicate_rows_rank_by_id(path):
     V, d = 5000, 256
     host = synth.make_table(BF16, V, d, seed=9)
@@ -110,7 +119,7 @@ def test_duplicate_rows_rank_by_id(path):
     assert np.array_equal(gids, oids)
 
 
-@pytest.mark.parametrize("path", [VALU, STREAM])
+@pytest.mark.parametrize("path", ALL)
 def test_planted_winners_exact_order(path):
     V, d = 30000, 512
     host = synth.make_table(BF16, V, d, seed=11)
@@ -125,7 +134,7 @@ def test_planted_winners_exact_order(path):
     assert np.array_equal(gids, oids)
 
 
-@pytest.mark.parametrize("path", [VALU, STREAM])
+@pytest.mark.parametrize("path", ALL)
 def test_repeatable_bitwise(path):
     V, d = 50000, 896
     host = synth.make_table(BF16, V, d, seed=13)
@@ -144,11 +153,10 @@ def test_paths_agree_on_bf16():
     host = synth.make_table(BF16, V, d, seed=15)
     R = synth.residuals(6, d, seed=16)
     t = table(host, BF16, V, d)
-    a = run(t, R, 10, VALU)
-    b = run(t, R, 10, STREAM)
+    outs = [run(t, R, 10, path) for path in ALL]
     L, A = oracle.logits(host, BF16, V, d, R)
     oids, _ = oracle.topk(L, 10)
-    for g in (a, b):
+    for g in outs:
         assert not accept.check_full(g[0], g[1], L, A, oids, accept.tol_coeff(BF16))
 
 
@@ -157,11 +165,11 @@ def test_vocab_smaller_than_k_slots():
     V, d = 9, 64
     host = synth.make_table(BF16, V, d, seed=19)
     R = synth.residuals(2, d, seed=20)
-    for path in (VALU, STREAM):
+    for path in ALL:
         full_check(host, BF16, V, d, R, 9, path)
 
 
-@pytest.mark.parametrize("path", [VALU, STREAM])
+@pytest.mark.parametrize("path", ALL)
 @pytest.mark.parametrize("B,d", [(1, 64), (3, 896), (6, 5376), (8, 200)])
 def test_residual_at_bf16_midpoints_stays_within_tolerance(path, B, d):
     # r_i = (1 + 2^-8) * sign(e_i) sits halfway between two bf16 values; rounding it
