@@ -29,8 +29,9 @@ struct LogitsPlan {
   int64_t ngroups;       // 8-row table groups = ceil(V / 8)
   int32_t max_groups;    // most 8-row groups one wave handles
   // gemm path
+  int32_t tn;            // split residual columns per column tile (128 or 256)
   int32_t kpad;          // hidden rounded up to the K stage
-  int32_t nct;           // column tiles of 64 residual rows
+  int32_t nct;           // column tiles of tn / 2 residual rows
   int32_t nvr;           // vocabulary ranges
   int32_t tiles_per_range;
   // valu path

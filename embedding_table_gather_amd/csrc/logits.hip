@@ -249,49 +249,55 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
 //
 // C[v][j] = sum_i E[v][i] * Rs[j][i] with Rs the residual rows as hi and lo bf16
 // rows, so logit[v][b] = C[v][hi(b)] + C[v][lo(b)].  A workgroup (4 waves, 2 x 2)
-// owns a tile of 128 split columns (64 residual rows) and walks a range of
-// 256-row vocabulary tiles; per tile it runs the K loop in stages of 64 values
+// owns a tile of TN split columns (TN / 2 residual rows) and walks a range of
+// 256-row vocabulary tiles; per tile it runs the K loop in stages of TK values
 // through double-buffered LDS and v_mfma_f32_32x32x16_bf16.  Wave (mw, nw)
-// computes rows [128 mw, +128) x split columns [64 nw, +64): N-tile 0 holds the
-// hi rows of residual rows [32 nw, +32) of the tile, N-tile 1 their lo rows, so
-// the hi + lo sum is a register add.
+// computes rows [128 mw, +128) x split columns [TN/2 nw, +TN/2) as 4 x NT
+// 32x32 tiles: N-tiles [0, NT/2) hold hi rows and [NT/2, NT) the matching lo
+// rows, so the hi + lo sum is a register add.
 //
-// LDS rows are 128 bytes (64 values); 16-byte piece p of row r is stored at
-// piece p ^ ((r >> 1) & 7), which keeps both the stage stores (8 rows x 128 B
-// per wave instruction) and the MFMA fragment reads (one piece of 16
-// consecutive rows per 16 lanes) free of bank conflicts.
+// An LDS row holds the TK values of one table or residual row (2 TK bytes, P =
+// TK / 8 pieces of 16 bytes); piece p of row r is stored at p ^ ((r / W) % P),
+// W = 128 / TK rows per 256-byte bank window.  That keeps the stage stores and
+// the MFMA fragment reads (one piece of 16 consecutive rows per 16 lanes) free
+// of bank conflicts.
 //
-// Top-k: every (wave, residual row) keeps a descending list of k keys in LDS.
-// After a vocabulary tile, each lane compares its 64 logits with the list's
-// last key and inserts the few that beat it (lanes 0-31 first, then 32-63,
-// which share the lists).  At the end the lists are written out as candidates:
-// [batch][vocab range][2 row halves][k].
+// Top-k: every (wave, residual row) keeps a min-heap of k keys in LDS, owned by
+// one lane.  After a vocabulary tile the logits pass through LDS and each lane
+// offers its row's logits to its heap; only those that beat the root (rare
+// after the first tiles) are inserted.  At the end the heaps are written out,
+// unordered, as candidates: [batch][vocab range][2 row halves][k].
 //
 // Workgroup ids are mapped so the column tiles of one vocabulary range sit on
 // the same XCD (ids go round-robin over the 8 XCDs): a table tile is fetched
 // from HBM once and served to the other column tiles from that XCD's L2.
 // ---------------------------------------------------------------------------
-static constexpr int kGemmTM = 256;    // vocabulary rows per tile
-static constexpr int kGemmTN = 128;    // split residual columns per tile
-static constexpr int kGemmTK = 64;     // K values per stage
-static constexpr int kGemmStage = (kGemmTM + kGemmTN) * kGemmTK * 2;  // bytes
+static constexpr int kGemmTM = 256;  // vocabulary rows per tile
 static constexpr int kXcds = 8;
 
-__device__ __forceinline__ int gemm_swz(int r, int piece) { return r * 128 + 16 * (piece ^ ((r >> 1) & 7)); }
+template <int TK>
+__device__ __forceinline__ int gemm_swz(int r, int piece) {
+  constexpr int P = TK / 8, W = 128 / TK;
+  return r * (2 * TK) + 16 * (piece ^ ((r / W) % P));
+}
 
-// fp32 residual [B][hidden] -> split bf16 rows [nct][128][kpad]; row j of tile ct
-// is residual row 64 ct + 32 (j / 64) + j % 32, part (j / 32) % 2 (0 hi, 1 lo).
+// fp32 residual [B][hidden] -> split bf16 rows [nct][TN][kpad].  Row j of tile ct
+// belongs to wave nw = j / (TN/2), N-tile t = (j % (TN/2)) / 32; it is the hi
+// (t < NT/2) or lo part of residual row ct TN/2 + nw TN/4 + (t % (NT/2)) 32 + j % 32.
+template <int TN>
 __global__ void __launch_bounds__(256) gemm_prep_kernel(const float* __restrict__ R, int64_t B, int hidden, int kpad,
                                                         int64_t nrows, u32x4* __restrict__ Rs) {
+  constexpr int NT = TN / 64;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int kc = kpad / 8;
   if (t >= nrows * kc) return;
   const int64_t row = t / kc;
   const int c0 = (int)(t % kc) * 8;
-  const int64_t ct = row / kGemmTN;
-  const int j = (int)(row % kGemmTN);
-  const int64_t b = 64 * ct + 32 * (j / 64) + j % 32;
-  const int part = (j / 32) % 2;
+  const int64_t ct = row / TN;
+  const int j = (int)(row % TN);
+  const int nw = j / (TN / 2), tt = (j % (TN / 2)) / 32;
+  const int part = tt >= NT / 2;
+  const int64_t b = ct * (TN / 2) + nw * (TN / 4) + (tt % (NT / 2)) * 32 + j % 32;
   uint32_t v[8];
 #pragma unroll
   for (int e = 0; e < 8; e++) {
@@ -305,24 +311,50 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(const float* __restrict_
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ void list_insert(uint64_t* list, int k, uint64_t key) {
-  int j = k - 1;
-  while (j > 0) {
-    const uint64_t up = list[j - 1];
-    if (up > key) break;
-    list[j] = up;
-    j--;
+// Min-heap of k keys in LDS (root = smallest kept key = admission threshold).
+// Replacing the root and sifting down costs at most log2(k) levels.
+__device__ __forceinline__ void heap_replace_root(uint64_t* h, int k, uint64_t key) {
+  int i = 0;
+  while (true) {
+    int c = 2 * i + 1;
+    if (c >= k) break;
+    uint64_t cv = h[c];
+    if (c + 1 < k) {
+      const uint64_t c2 = h[c + 1];
+      if (c2 < cv) {
+        cv = c2;
+        c = c + 1;
+      }
+    }
+    if (cv >= key) break;
+    h[i] = cv;
+    i = c;
   }
-  list[j] = key;
+  h[i] = key;
 }
 
+template <int TN, int TK>
+struct GemmCfg {
+  static constexpr int NT = TN / 64;                        // 32-column N-tiles per wave
+  static constexpr int KS = TK / 16;                        // MFMA K sub-steps per stage
+  static constexpr int P = TK / 8;                          // 16-byte pieces per LDS row
+  static constexpr int RPT = 256 / P;                       // rows a 256-thread pass covers
+  static constexpr int LA = kGemmTM / RPT;                  // table loads per thread per stage
+  static constexpr int LB = TN / RPT;                       // residual loads per thread per stage
+  static constexpr int STAGE = (kGemmTM + TN) * TK * 2;     // bytes
+  static constexpr int COLS = TN / 4;                       // residual rows per wave
+};
+
+template <int TN, int TK>
 __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden,
     const uint8_t* __restrict__ Rs, int kpad, int64_t B, int k, uint64_t* __restrict__ cand,
     int nct, int nvr, int tiles_per_range) {
+  using C = GemmCfg<TN, TK>;
+  constexpr int NT = C::NT, KS = C::KS, P = C::P, RPT = C::RPT, LA = C::LA, LB = C::LB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* stage_buf = smem;                                   // 2 x kGemmStage
-  uint64_t* lists = (uint64_t*)(smem + 2 * kGemmStage);              // [4 waves][32][k]
+  unsigned char* stage_buf = smem;                                   // 2 x STAGE
+  uint64_t* heaps = (uint64_t*)(smem + 2 * C::STAGE);                // [4 waves][COLS][k]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int mw = wv >> 1, nw = wv & 1;
 
@@ -333,92 +365,135 @@ __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
   const int vr = xcd + kXcds * (local / nct);
   if (vr >= nvr) return;  // whole workgroup; no barrier has been reached
 
-  for (int i = tid; i < 4 * 32 * k; i += 256) lists[i] = 0;
+  for (int i = tid; i < 4 * C::COLS * k; i += 256) heaps[i] = 0;
 
-  const int nstage = kpad / kGemmTK;
-  const uint8_t* rs_tile = Rs + (size_t)ct * kGemmTN * kpad * 2;
+  const int nstage = kpad / TK;
+  const uint8_t* rs_tile = Rs + (size_t)ct * TN * kpad * 2;
   const int64_t last_off = row_bytes - 16;
-  // loader mapping: chunk c = tid + 256 j -> row c / 8, piece c % 8
-  const int lrow = tid >> 3, lpiece = tid & 7;
+  // loader mapping: chunk c = tid + 256 j -> row c / P, piece c % P
+  const int lrow = tid / P, lpiece = tid % P;
 
   for (int vt = 0; vt < tiles_per_range; vt++) {
     const int64_t v0 = ((int64_t)vr * tiles_per_range + vt) * kGemmTM;
     if (v0 >= V) break;
-    const uint8_t* arow[8];
+    const uint8_t* arow[LA];
 #pragma unroll
-    for (int j = 0; j < 8; j++) arow[j] = table + (uint64_t)min(v0 + lrow + 32 * j, V - 1) * (uint64_t)row_bytes;
-    f32x16 acc[4][2];
+    for (int j = 0; j < LA; j++) arow[j] = table + (uint64_t)min(v0 + lrow + RPT * j, V - 1) * (uint64_t)row_bytes;
+    f32x16 acc[4][NT];
 #pragma unroll
-    for (int a = 0; a < 4; a++) acc[a][0] = acc[a][1] = f32x16{};
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+      for (int t = 0; t < NT; t++) acc[a][t] = f32x16{};
 
-    u32x4 pa[8], pb[4];
-    auto load_stage = [&](int st) {
-      const int64_t kb = (int64_t)st * 128 + 16 * lpiece;
+    // Two register stage buffers; stage s lives in buffer s % 2 from its load
+    // until its store.  Step st computes stage st from LDS, stores stage st + 1
+    // into the other LDS buffer and reuses that register buffer for the loads of
+    // stage st + 3, which have two compute stages to arrive.  Loads and stores
+    // are unconditional (stage indices past the end are clamped) so the wait
+    // counts do not depend on the path taken.
+    u32x4 pa0[LA], pb0[LB], pa1[LA], pb1[LB];
+    auto load_stage = [&](int st, u32x4* pa, u32x4* pb) {
+      const int64_t kb = (int64_t)min(st, nstage - 1) * (2 * TK) + 16 * lpiece;
       const int64_t koff = min(kb, last_off);
 #pragma unroll
-      for (int j = 0; j < 8; j++) pa[j] = __builtin_nontemporal_load((const u32x4*)(arow[j] + koff));
+      for (int j = 0; j < LA; j++) pa[j] = *(const u32x4*)(arow[j] + koff);
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        pb[j] = *(const u32x4*)(rs_tile + (size_t)(lrow + 32 * j) * kpad * 2 + kb);
+      for (int j = 0; j < LB; j++) pb[j] = *(const u32x4*)(rs_tile + (size_t)(lrow + RPT * j) * kpad * 2 + kb);
     };
-    auto store_stage = [&](int buf) {
-      unsigned char* base = stage_buf + buf * kGemmStage;
+    auto store_stage = [&](int buf, const u32x4* pa, const u32x4* pb) {
+      unsigned char* base = stage_buf + buf * C::STAGE;
 #pragma unroll
-      for (int j = 0; j < 8; j++) *(u32x4*)(base + gemm_swz(lrow + 32 * j, lpiece)) = pa[j];
+      for (int j = 0; j < LA; j++) *(u32x4*)(base + gemm_swz<TK>(lrow + RPT * j, lpiece)) = pa[j];
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        *(u32x4*)(base + kGemmTM * 128 + gemm_swz(lrow + 32 * j, lpiece)) = pb[j];
+      for (int j = 0; j < LB; j++)
+        *(u32x4*)(base + kGemmTM * 2 * TK + gemm_swz<TK>(lrow + RPT * j, lpiece)) = pb[j];
     };
-
-    load_stage(0);
-    __syncthreads();  // previous tile's readers of both buffers are done
-    store_stage(0);
-    if (nstage > 1) load_stage(1);
-    __syncthreads();
-    for (int st = 0; st < nstage; st++) {
-      const unsigned char* A = stage_buf + (st & 1) * kGemmStage;
-      const unsigned char* Bt = A + kGemmTM * 128;
-#pragma unroll
-      for (int ks = 0; ks < 4; ks++) {
+    // MFMA fragments for K sub-step ks are read while sub-step ks - 1 computes
+    // (narrow tile; the wide tile reads them just before use)
+    auto compute_stage = [&](int buf) {
+      const unsigned char* A = stage_buf + buf * C::STAGE;
+      const unsigned char* Bt = A + kGemmTM * 2 * TK;
+      constexpr int FS = NT > 2 ? 1 : 2;  // fragment sets (the wide tile has no registers for two)
+      bf16x8 af[FS][4], bfr[FS][NT];
+      auto read = [&](int ks, int set) {
         const int piece = 2 * ks + (lane >> 5);
-        bf16x8 af[4], bfr[2];
 #pragma unroll
         for (int a = 0; a < 4; a++)
-          af[a] = __builtin_bit_cast(bf16x8, *(const u32x4*)(A + gemm_swz(128 * mw + 32 * a + (lane & 31), piece)));
+          af[set][a] =
+              __builtin_bit_cast(bf16x8, *(const u32x4*)(A + gemm_swz<TK>(128 * mw + 32 * a + (lane & 31), piece)));
 #pragma unroll
-        for (int t = 0; t < 2; t++)
-          bfr[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bt + gemm_swz(64 * nw + 32 * t + (lane & 31), piece)));
+        for (int t = 0; t < NT; t++)
+          bfr[set][t] = __builtin_bit_cast(
+              bf16x8, *(const u32x4*)(Bt + gemm_swz<TK>((TN / 2) * nw + 32 * t + (lane & 31), piece)));
+      };
+      if (FS == 2) read(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const int cur = FS == 2 ? (ks & 1) : 0;
+        if (FS == 1) read(ks, 0);
+        else if (ks + 1 < KS) read(ks + 1, (ks + 1) & 1);
 #pragma unroll
         for (int a = 0; a < 4; a++)
 #pragma unroll
-          for (int t = 0; t < 2; t++) acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[t], acc[a][t], 0, 0, 0);
+          for (int t = 0; t < NT; t++)
+            acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][a], bfr[cur][t], acc[a][t], 0, 0, 0);
       }
-      if (st + 1 < nstage) {
-        store_stage((st + 1) & 1);
-        if (st + 2 < nstage) load_stage(st + 2);
-      }
+    };
+    auto step = [&](int st, u32x4* npa, u32x4* npb) {
+      compute_stage(st & 1);
+      store_stage((st + 1) & 1, npa, npb);
+      load_stage(st + 3, npa, npb);
       __syncthreads();
-    }
+    };
 
-    // epilogue: logits of rows v0 + 128 mw + 32 a + 8 (i / 4) + 4 (lane / 32) + i % 4,
-    // residual row 64 ct + 32 nw + lane % 32
-    const int64_t b = 64 * (int64_t)ct + 32 * nw + (lane & 31);
-    uint64_t* list = lists + ((size_t)wv * 32 + (lane & 31)) * k;
+    load_stage(0, pa0, pb0);
+    load_stage(1, pa1, pb1);
+    __syncthreads();  // previous tile's readers of both buffers are done
+    store_stage(0, pa0, pb0);
+    load_stage(2, pa0, pb0);
+    __syncthreads();
+    int st = 0;
+    for (; st + 1 < nstage; st += 2) {
+      step(st, pa1, pb1);
+      step(st + 1, pa0, pb0);
+    }
+    if (st < nstage) step(st, pa1, pb1);
+
+    // Epilogue, in two passes of 64 rows: the hi + lo sums go to this wave's
+    // 16 KB slice of the (now idle) stage buffers as [64 rows][64 columns]; then
+    // lane c walks column c (residual row ct TN/2 + nw TN/4 + c) and offers each
+    // logit that beats its heap root.  Row of register i of M-tile a:
+    // 128 mw + 32 a + 8 (i / 4) + 4 (lane / 32) + i % 4.
+    float* tl = (float*)(stage_buf + (size_t)wv * 64 * 64 * 4);
+    const int64_t bcol = (int64_t)ct * (TN / 2) + nw * (TN / 4) + lane;
+    const bool own = lane < C::COLS && bcol < B;
+    uint64_t* heap = heaps + ((size_t)wv * C::COLS + (own ? lane : 0)) * k;
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
-      if ((lane >> 5) == half && b < B) {
-        uint64_t thr = list[k - 1];
+    for (int pass = 0; pass < 2; pass++) {
 #pragma unroll
-        for (int a = 0; a < 4; a++) {
+      for (int aa = 0; aa < 2; aa++) {
+        const int a = 2 * pass + aa;
 #pragma unroll
-          for (int i = 0; i < 16; i++) {
-            const int64_t row = v0 + 128 * mw + 32 * a + 8 * (i >> 2) + 4 * half + (i & 3);
-            const float logit = acc[a][0][i] + acc[a][1][i];
-            const uint64_t key = row < V ? make_key(logit, (uint32_t)row) : 0;
-            if (key > thr) {
-              list_insert(list, k, key);
-              thr = list[k - 1];
-            }
+        for (int t = 0; t < NT / 2; t++) {
+          __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 tile in flight at a time
+#pragma unroll
+          for (int i = 0; i < 16; i++)
+            tl[(32 * aa + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * 64 + 32 * t + (lane & 31)] =
+                acc[a][t][i] + acc[a][t + NT / 2][i];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (own) {
+        uint64_t thr = heap[0];
+        const int64_t r0 = v0 + 128 * mw + 64 * pass;
+        for (int r = 0; r < 64; r++) {
+          const int64_t row = r0 + r;
+          const uint64_t key = row < V ? make_key(tl[r * 64 + lane], (uint32_t)row) : 0;
+          if (key > thr) {
+            heap_replace_root(heap, k, key);
+            thr = heap[0];
           }
         }
       }
@@ -428,13 +503,13 @@ __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
     }
   }
   __syncthreads();
-  // lists -> candidates [B][nvr][2][k]
+  // heaps -> candidates [B][nvr][2][k]
   {
-    const int64_t b = 64 * (int64_t)ct + 32 * nw + (lane & 31);
-    if (lane < 32 && b < B) {
-      const uint64_t* list = lists + ((size_t)wv * 32 + lane) * k;
+    const int64_t b = (int64_t)ct * (TN / 2) + nw * (TN / 4) + lane;
+    if (lane < C::COLS && b < B) {
+      const uint64_t* heap = heaps + ((size_t)wv * C::COLS + lane) * k;
       uint64_t* out = cand + ((b * nvr + vr) * 2 + mw) * (int64_t)k;
-      for (int j = 0; j < k; j++) out[j] = list[j];
+      for (int j = 0; j < k; j++) out[j] = heap[j];
     }
   }
 }
@@ -637,21 +712,28 @@ static hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const f
   return record(ev1, stream);
 }
 
-static hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs,
-                              uint64_t* cand, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  const int64_t nrows = (int64_t)p.nct * kGemmTN;
+template <int TN, int TK>
+static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs,
+                                  uint64_t* cand, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const int64_t nrows = (int64_t)p.nct * TN;
   const int64_t nprep = nrows * (p.kpad / 8);
-  hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream, R, p.batch,
+  hipLaunchKernelGGL((gemm_prep_kernel<TN>), dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream, R, p.batch,
                      (int)t.hidden, p.kpad, nrows, (u32x4*)rs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = set_lds((const void*)gemm_logits_kernel, p.lds_bytes)) != hipSuccess) return e;
+  if ((e = set_lds((const void*)gemm_logits_kernel<TN, TK>, p.lds_bytes)) != hipSuccess) return e;
   if ((e = record(ev0, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(gemm_logits_kernel, dim3((unsigned)p.nblk), dim3(256), p.lds_bytes, stream, t.rows, t.V,
-                     t.row_bytes, (int)t.hidden, (const uint8_t*)rs, p.kpad, p.batch, p.k, cand, p.nct, p.nvr,
+  hipLaunchKernelGGL((gemm_logits_kernel<TN, TK>), dim3((unsigned)p.nblk), dim3(256), p.lds_bytes, stream, t.rows,
+                     t.V, t.row_bytes, (int)t.hidden, (const uint8_t*)rs, p.kpad, p.batch, p.k, cand, p.nct, p.nvr,
                      p.tiles_per_range);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record(ev1, stream);
+}
+
+static hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs, uint64_t* cand,
+                              hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (p.tn == 256) return launch_gemm_cfg<256, 32>(t, p, R, rs, cand, stream, ev0, ev1);
+  return launch_gemm_cfg<128, 64>(t, p, R, rs, cand, stream, ev0, ev1);
 }
 
 hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const float* R, int32_t* ids,
@@ -719,8 +801,13 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     p->img_bytes = 0;
     p->ncand = p->nblk * k;
   } else if (path == 3) {
-    p->kpad = (int32_t)(cdiv(t.hidden, kGemmTK) * kGemmTK);
-    p->nct = (int32_t)cdiv(batch, kGemmTN / 2);
+    // wide column tiles (128 residual rows) when the batch fills them and the heaps fit
+    const bool wide = batch > 64 && (size_t)2 * GemmCfg<256, 32>::STAGE + (size_t)4 * 64 * k * 8 <= kMaxLds;
+    p->tn = wide ? 256 : 128;
+    const int tk = wide ? 32 : 64;
+    const size_t stage = wide ? GemmCfg<256, 32>::STAGE : GemmCfg<128, 64>::STAGE;
+    p->kpad = (int32_t)(cdiv(t.hidden, tk) * tk);
+    p->nct = (int32_t)cdiv(batch, p->tn / 2);
     const int64_t vtiles = cdiv(t.V, kGemmTM);
     // about one workgroup per CU; vocabulary ranges in multiples of the XCD count
     int64_t nvr = std::max<int64_t>(1, kTargetBlocks / p->nct);
@@ -730,8 +817,8 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     p->nvr = (int32_t)nvr;
     p->nblk = (int32_t)(p->nct * nvr);
     p->npass = 1;
-    p->lds_bytes = 2 * (size_t)kGemmStage + (size_t)4 * 32 * k * 8;
-    p->img_bytes = (size_t)p->nct * kGemmTN * p->kpad * 2;
+    p->lds_bytes = 2 * stage + (size_t)4 * (p->tn / 4) * k * 8;
+    p->img_bytes = (size_t)p->nct * p->tn * p->kpad * 2;
     p->ncand = (int32_t)(nvr * 2 * k);
   } else {
     p->rb = batch >= 8 ? 8 : batch >= 4 ? 4 : batch >= 2 ? 2 : 1;
