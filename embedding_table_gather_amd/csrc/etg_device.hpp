@@ -33,13 +33,29 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t id) {
   return ((uint64_t)score_ord(s) << 32) | (uint64_t)(~id);
 }
 
+// One DPP step of a 64-bit prefix max: lanes whose source lane is outside the
+// row (or whose row is masked off) see 0, which is below every key.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, ROWMASK, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, ROWMASK, 0xf, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Maximum over the wave, returned to every lane: shifts of 1, 2, 4 and 8 within
+// each 16-lane row leave the row maximum in lane 15 of the row; row_bcast:15 and
+// row_bcast:31 carry it across rows, so lane 63 holds the wave maximum.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_u64<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_u64<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_u64<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_u64<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_max_u64<0x142, 0xa>(v);  // row_bcast:15
+  v = dpp_max_u64<0x143, 0xc>(v);  // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Butterfly sum: every lane ends with the same (bitwise) value because each

@@ -30,6 +30,7 @@ struct LogitsPlan {
   int32_t max_groups;    // most 8-row groups one wave handles
   // gemm path
   int32_t tn;            // split residual columns per column tile (128 or 256)
+  int32_t gemm_mw;       // waves along the vocabulary (2: 4 waves, 4: 8 waves)
   int32_t kpad;          // hidden rounded up to the K stage
   int32_t nct;           // column tiles of tn / 2 residual rows
   int32_t nvr;           // vocabulary ranges

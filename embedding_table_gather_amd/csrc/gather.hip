@@ -23,6 +23,7 @@
 namespace etg {
 
 static constexpr int kGatherWaves = 4;
+static constexpr int kGatherUnroll = 4;
 
 template <int DT, bool SCALE>
 __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ table, uint32_t V,
@@ -45,26 +46,47 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
   }
   const uint8_t* src = table + (uint64_t)id * (uint64_t)row_bytes;
 
+  // f32 / bf16: groups of kGatherUnroll loads are issued before their stores, so a
+  // single long row costs a few memory round trips, not one per 1 KB.
   if constexpr (DT == DT_F32) {
     const f32x4* s4 = (const f32x4*)src;
-    for (int c4 = lane; c4 < n4; c4 += 64) {
-      f32x4 v = s4[c4];
-      if (SCALE) v = v * scale;
-      o[c4] = v;
+    for (int c0 = lane; c0 < n4; c0 += 64 * kGatherUnroll) {
+      f32x4 v[kGatherUnroll];
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; u++) {
+        const int c4 = c0 + 64 * u;
+        if (c4 < n4) v[u] = s4[c4];
+      }
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; u++) {
+        const int c4 = c0 + 64 * u;
+        if (c4 < n4) o[c4] = SCALE ? v[u] * scale : v[u];
+      }
     }
   } else if constexpr (DT == DT_BF16) {
     const u32x4* s8 = (const u32x4*)src;
     const int n8 = hidden >> 3;
-    for (int c8 = lane; c8 < n8; c8 += 64) {
-      u32x4 w = s8[c8];
-      f32x4 a = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
-      f32x4 b = {bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-      if (SCALE) {
-        a = a * scale;
-        b = b * scale;
+    for (int c0 = lane; c0 < n8; c0 += 64 * kGatherUnroll) {
+      u32x4 w[kGatherUnroll];
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; u++) {
+        const int c8 = c0 + 64 * u;
+        if (c8 < n8) w[u] = s8[c8];
       }
-      o[2 * c8] = a;
-      o[2 * c8 + 1] = b;
+#pragma unroll
+      for (int u = 0; u < kGatherUnroll; u++) {
+        const int c8 = c0 + 64 * u;
+        if (c8 < n8) {
+          f32x4 a = {bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y)};
+          f32x4 b = {bf16_lo(w[u].z), bf16_hi(w[u].z), bf16_lo(w[u].w), bf16_hi(w[u].w)};
+          if (SCALE) {
+            a = a * scale;
+            b = b * scale;
+          }
+          o[2 * c8] = a;
+          o[2 * c8 + 1] = b;
+        }
+      }
     }
   } else {
     // Q8_0: stage [src & ~3, src + row_bytes) as aligned dwords.  row_bytes is even

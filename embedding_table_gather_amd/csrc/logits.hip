@@ -266,7 +266,7 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
 // one lane.  After a vocabulary tile the logits pass through LDS and each lane
 // offers its row's logits to its heap; only those that beat the root (rare
 // after the first tiles) are inserted.  At the end the heaps are written out,
-// unordered, as candidates: [batch][vocab range][2 row halves][k].
+// unordered, as candidates: [batch][vocab range][MW row slices][k].
 //
 // Workgroup ids are mapped so the column tiles of one vocabulary range sit on
 // the same XCD (ids go round-robin over the 8 XCDs): a table tile is fetched
@@ -274,6 +274,7 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
 // ---------------------------------------------------------------------------
 static constexpr int kGemmTM = 256;  // vocabulary rows per tile
 static constexpr int kXcds = 8;
+static constexpr int kGemmWideMW = 2;    // 4 waves: 128-row wave tiles
 
 template <int TK>
 __device__ __forceinline__ int gemm_swz(int r, int piece) {
@@ -333,28 +334,36 @@ __device__ __forceinline__ void heap_replace_root(uint64_t* h, int k, uint64_t k
   h[i] = key;
 }
 
-template <int TN, int TK>
+template <int TN, int TK, int MW>
 struct GemmCfg {
+  static constexpr int NWAVES = 2 * MW;                     // MW along the vocabulary, 2 along the columns
+  static constexpr int THREADS = 64 * NWAVES;
+  static constexpr int WROWS = kGemmTM / MW;                // vocabulary rows per wave
+  static constexpr int MT = WROWS / 32;                     // 32-row M-tiles per wave
   static constexpr int NT = TN / 64;                        // 32-column N-tiles per wave
   static constexpr int KS = TK / 16;                        // MFMA K sub-steps per stage
   static constexpr int P = TK / 8;                          // 16-byte pieces per LDS row
-  static constexpr int RPT = 256 / P;                       // rows a 256-thread pass covers
+  static constexpr int RPT = THREADS / P;                   // rows one pass of the block covers
   static constexpr int LA = kGemmTM / RPT;                  // table loads per thread per stage
   static constexpr int LB = TN / RPT;                       // residual loads per thread per stage
   static constexpr int STAGE = (kGemmTM + TN) * TK * 2;     // bytes
   static constexpr int COLS = TN / 4;                       // residual rows per wave
+  static constexpr int EPI_ROWS = WROWS / 2;                // epilogue rows per pass
+  static_assert(kGemmTM % RPT == 0 && TN % RPT == 0, "stage must split evenly over the block");
+  static_assert(NWAVES * EPI_ROWS * 64 * 4 <= 2 * STAGE, "epilogue staging must fit the stage buffers");
 };
 
-template <int TN, int TK>
-__global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
+template <int TN, int TK, int MW>
+__global__ void __launch_bounds__(64 * 2 * MW) gemm_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden,
     const uint8_t* __restrict__ Rs, int kpad, int64_t B, int k, uint64_t* __restrict__ cand,
     int nct, int nvr, int tiles_per_range) {
-  using C = GemmCfg<TN, TK>;
-  constexpr int NT = C::NT, KS = C::KS, P = C::P, RPT = C::RPT, LA = C::LA, LB = C::LB;
+  using C = GemmCfg<TN, TK, MW>;
+  constexpr int NT = C::NT, MT = C::MT, KS = C::KS, P = C::P, RPT = C::RPT, LA = C::LA, LB = C::LB;
+  constexpr int WROWS = C::WROWS, THREADS = C::THREADS, ER = C::EPI_ROWS;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* stage_buf = smem;                                   // 2 x STAGE
-  uint64_t* heaps = (uint64_t*)(smem + 2 * C::STAGE);                // [4 waves][COLS][k]
+  uint64_t* heaps = (uint64_t*)(smem + 2 * C::STAGE);                // [waves][COLS][k]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int mw = wv >> 1, nw = wv & 1;
 
@@ -365,12 +374,12 @@ __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
   const int vr = xcd + kXcds * (local / nct);
   if (vr >= nvr) return;  // whole workgroup; no barrier has been reached
 
-  for (int i = tid; i < 4 * C::COLS * k; i += 256) heaps[i] = 0;
+  for (int i = tid; i < C::NWAVES * C::COLS * k; i += THREADS) heaps[i] = 0;
 
   const int nstage = kpad / TK;
   const uint8_t* rs_tile = Rs + (size_t)ct * TN * kpad * 2;
   const int64_t last_off = row_bytes - 16;
-  // loader mapping: chunk c = tid + 256 j -> row c / P, piece c % P
+  // loader mapping: chunk c = tid + THREADS j -> row c / P, piece c % P
   const int lrow = tid / P, lpiece = tid % P;
 
   for (int vt = 0; vt < tiles_per_range; vt++) {
@@ -379,9 +388,9 @@ __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
     const uint8_t* arow[LA];
 #pragma unroll
     for (int j = 0; j < LA; j++) arow[j] = table + (uint64_t)min(v0 + lrow + RPT * j, V - 1) * (uint64_t)row_bytes;
-    f32x16 acc[4][NT];
+    f32x16 acc[MT][NT];
 #pragma unroll
-    for (int a = 0; a < 4; a++)
+    for (int a = 0; a < MT; a++)
 #pragma unroll
       for (int t = 0; t < NT; t++) acc[a][t] = f32x16{};
 
@@ -413,14 +422,14 @@ __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
     auto compute_stage = [&](int buf) {
       const unsigned char* A = stage_buf + buf * C::STAGE;
       const unsigned char* Bt = A + kGemmTM * 2 * TK;
-      constexpr int FS = NT > 2 ? 1 : 2;  // fragment sets (the wide tile has no registers for two)
-      bf16x8 af[FS][4], bfr[FS][NT];
+      constexpr int FS = MT * NT > 8 ? 1 : 2;  // fragment sets (the largest wave tile has no registers for two)
+      bf16x8 af[FS][MT], bfr[FS][NT];
       auto read = [&](int ks, int set) {
         const int piece = 2 * ks + (lane >> 5);
 #pragma unroll
-        for (int a = 0; a < 4; a++)
+        for (int a = 0; a < MT; a++)
           af[set][a] =
-              __builtin_bit_cast(bf16x8, *(const u32x4*)(A + gemm_swz<TK>(128 * mw + 32 * a + (lane & 31), piece)));
+              __builtin_bit_cast(bf16x8, *(const u32x4*)(A + gemm_swz<TK>(WROWS * mw + 32 * a + (lane & 31), piece)));
 #pragma unroll
         for (int t = 0; t < NT; t++)
           bfr[set][t] = __builtin_bit_cast(
@@ -433,7 +442,7 @@ __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
         if (FS == 1) read(ks, 0);
         else if (ks + 1 < KS) read(ks + 1, (ks + 1) & 1);
 #pragma unroll
-        for (int a = 0; a < 4; a++)
+        for (int a = 0; a < MT; a++)
 #pragma unroll
           for (int t = 0; t < NT; t++)
             acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][a], bfr[cur][t], acc[a][t], 0, 0, 0);
@@ -459,20 +468,20 @@ __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
     }
     if (st < nstage) step(st, pa1, pb1);
 
-    // Epilogue, in two passes of 64 rows: the hi + lo sums go to this wave's
-    // 16 KB slice of the (now idle) stage buffers as [64 rows][64 columns]; then
+    // Epilogue, in two passes of WROWS / 2 rows: the hi + lo sums go to this
+    // wave's slice of the (now idle) stage buffers as [rows][64 columns]; then
     // lane c walks column c (residual row ct TN/2 + nw TN/4 + c) and offers each
     // logit that beats its heap root.  Row of register i of M-tile a:
-    // 128 mw + 32 a + 8 (i / 4) + 4 (lane / 32) + i % 4.
-    float* tl = (float*)(stage_buf + (size_t)wv * 64 * 64 * 4);
+    // WROWS mw + 32 a + 8 (i / 4) + 4 (lane / 32) + i % 4.
+    float* tl = (float*)(stage_buf + (size_t)wv * ER * 64 * 4);
     const int64_t bcol = (int64_t)ct * (TN / 2) + nw * (TN / 4) + lane;
     const bool own = lane < C::COLS && bcol < B;
     uint64_t* heap = heaps + ((size_t)wv * C::COLS + (own ? lane : 0)) * k;
 #pragma unroll
     for (int pass = 0; pass < 2; pass++) {
 #pragma unroll
-      for (int aa = 0; aa < 2; aa++) {
-        const int a = 2 * pass + aa;
+      for (int aa = 0; aa < MT / 2; aa++) {
+        const int a = (MT / 2) * pass + aa;
 #pragma unroll
         for (int t = 0; t < NT / 2; t++) {
           __builtin_amdgcn_sched_barrier(0);  // one 32 x 32 tile in flight at a time
@@ -487,8 +496,8 @@ __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       if (own) {
         uint64_t thr = heap[0];
-        const int64_t r0 = v0 + 128 * mw + 64 * pass;
-        for (int r = 0; r < 64; r++) {
+        const int64_t r0 = v0 + WROWS * mw + ER * pass;
+        for (int r = 0; r < ER; r++) {
           const int64_t row = r0 + r;
           const uint64_t key = row < V ? make_key(tl[r * 64 + lane], (uint32_t)row) : 0;
           if (key > thr) {
@@ -503,12 +512,12 @@ __global__ void __launch_bounds__(256, 1) gemm_logits_kernel(
     }
   }
   __syncthreads();
-  // heaps -> candidates [B][nvr][2][k]
+  // heaps -> candidates [B][nvr][MW][k]
   {
     const int64_t b = (int64_t)ct * (TN / 2) + nw * (TN / 4) + lane;
     if (lane < C::COLS && b < B) {
       const uint64_t* heap = heaps + ((size_t)wv * C::COLS + lane) * k;
-      uint64_t* out = cand + ((b * nvr + vr) * 2 + mw) * (int64_t)k;
+      uint64_t* out = cand + ((b * nvr + vr) * MW + mw) * (int64_t)k;
       for (int j = 0; j < k; j++) out[j] = heap[j];
     }
   }
@@ -580,16 +589,18 @@ __global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restr
 
 // ---------------------------------------------------------------------------
 // Cross-block merge: per residual row (blockIdx.x), the k largest of n keys.
-// Each thread keeps up to KPT keys in registers; round t takes the largest key
-// below the key of round t - 1 with a wave max and a 16-way exchange in LDS
-// (double-buffered by round parity, so one barrier per round).
+// Each thread keeps up to KPT keys in registers.  Every wave first takes the k
+// best of its own keys (round t: the largest key below round t - 1's, by a wave
+// max); wave 0 then does the same over the 16 per-wave lists.  The k best of
+// the union of the waves' k best are the k best overall.
 // ---------------------------------------------------------------------------
 static constexpr int kMergeThreads = 1024;
+static constexpr int kMergeWaves = kMergeThreads / 64;
 
 template <int KPT>
 __global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __restrict__ cand, int n, int k,
                                                           int32_t* __restrict__ ids, float* __restrict__ scores) {
-  __shared__ uint64_t red[2][kMergeThreads / 64];
+  __shared__ uint64_t part[kMergeWaves * 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t b = blockIdx.x;
   const uint64_t* c = cand + b * (int64_t)n;
@@ -605,23 +616,37 @@ __global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __rest
 #pragma unroll
     for (int j = 0; j < KPT; j++) best = (key[j] < prev && key[j] > best) ? key[j] : best;
     best = wave_max_u64(best);
-    if (lane == 0) red[t & 1][wv] = best;
-    __syncthreads();
-    uint64_t m = red[t & 1][0];
+    if (lane == 0) part[wv * k + t] = best;
+    prev = best;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    // kMergeWaves * k <= 1024 keys: 16 per lane
+    uint64_t key2[kMergeWaves];
 #pragma unroll
-    for (int w = 1; w < kMergeThreads / 64; w++) m = red[t & 1][w] > m ? red[t & 1][w] : m;
-    if (tid == 0) {
-      ids[b * k + t] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
-      scores[b * k + t] = ord_score((uint32_t)(m >> 32));
+    for (int j = 0; j < kMergeWaves; j++) {
+      const int i = lane + 64 * j;
+      key2[j] = i < kMergeWaves * k ? part[i] : 0;
     }
-    prev = m;
+    prev = ~0ull;
+    for (int t = 0; t < k; t++) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int j = 0; j < kMergeWaves; j++) best = (key2[j] < prev && key2[j] > best) ? key2[j] : best;
+      best = wave_max_u64(best);
+      if (lane == 0) {
+        ids[b * k + t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
+        scores[b * k + t] = ord_score((uint32_t)(best >> 32));
+      }
+      prev = best;
+    }
   }
 }
 
 // Same, for more keys than fit in registers: every round rescans global memory.
 __global__ void __launch_bounds__(1024) topk_merge_wide_kernel(const uint64_t* __restrict__ cand, int n, int k,
                                                                int32_t* __restrict__ ids, float* __restrict__ scores) {
-  __shared__ uint64_t red[2][kMergeThreads / 64];
+  __shared__ uint64_t red[2][kMergeWaves];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t b = blockIdx.x;
   const uint64_t* c = cand + b * (int64_t)n;
@@ -636,7 +661,7 @@ __global__ void __launch_bounds__(1024) topk_merge_wide_kernel(const uint64_t* _
     if (lane == 0) red[t & 1][wv] = best;
     __syncthreads();
     uint64_t m = red[t & 1][0];
-    for (int w = 1; w < kMergeThreads / 64; w++) m = red[t & 1][w] > m ? red[t & 1][w] : m;
+    for (int w = 1; w < kMergeWaves; w++) m = red[t & 1][w] > m ? red[t & 1][w] : m;
     if (tid == 0) {
       ids[b * k + t] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
       scores[b * k + t] = ord_score((uint32_t)(m >> 32));
@@ -712,7 +737,7 @@ static hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const f
   return record(ev1, stream);
 }
 
-template <int TN, int TK>
+template <int TN, int TK, int MW>
 static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs,
                                   uint64_t* cand, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t nrows = (int64_t)p.nct * TN;
@@ -721,19 +746,20 @@ static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const
                      (int)t.hidden, p.kpad, nrows, (u32x4*)rs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = set_lds((const void*)gemm_logits_kernel<TN, TK>, p.lds_bytes)) != hipSuccess) return e;
+  if ((e = set_lds((const void*)gemm_logits_kernel<TN, TK, MW>, p.lds_bytes)) != hipSuccess) return e;
   if ((e = record(ev0, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_logits_kernel<TN, TK>), dim3((unsigned)p.nblk), dim3(256), p.lds_bytes, stream, t.rows,
-                     t.V, t.row_bytes, (int)t.hidden, (const uint8_t*)rs, p.kpad, p.batch, p.k, cand, p.nct, p.nvr,
-                     p.tiles_per_range);
+  hipLaunchKernelGGL((gemm_logits_kernel<TN, TK, MW>), dim3((unsigned)p.nblk), dim3(GemmCfg<TN, TK, MW>::THREADS),
+                     p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (int)t.hidden, (const uint8_t*)rs, p.kpad, p.batch,
+                     p.k, cand, p.nct, p.nvr, p.tiles_per_range);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record(ev1, stream);
 }
 
 static hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs, uint64_t* cand,
                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  if (p.tn == 256) return launch_gemm_cfg<256, 32>(t, p, R, rs, cand, stream, ev0, ev1);
-  return launch_gemm_cfg<128, 64>(t, p, R, rs, cand, stream, ev0, ev1);
+  if (p.tn == 256) return launch_gemm_cfg<256, 32, kGemmWideMW>(t, p, R, rs, cand, stream, ev0, ev1);
+  if (p.gemm_mw == 4) return launch_gemm_cfg<128, 64, 4>(t, p, R, rs, cand, stream, ev0, ev1);
+  return launch_gemm_cfg<128, 64, 2>(t, p, R, rs, cand, stream, ev0, ev1);
 }
 
 hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const float* R, int32_t* ids,
@@ -801,11 +827,23 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     p->img_bytes = 0;
     p->ncand = p->nblk * k;
   } else if (path == 3) {
-    // wide column tiles (128 residual rows) when the batch fills them and the heaps fit
-    const bool wide = batch > 64 && (size_t)2 * GemmCfg<256, 32>::STAGE + (size_t)4 * 64 * k * 8 <= kMaxLds;
-    p->tn = wide ? 256 : 128;
-    const int tk = wide ? 32 : 64;
-    const size_t stage = wide ? GemmCfg<256, 32>::STAGE : GemmCfg<128, 64>::STAGE;
+    // Wide column tiles (128 residual rows) when the batch fills them; otherwise
+    // 64-row tiles with 8 waves, or 4 waves when the per-wave heaps of a large k
+    // would not fit beside the stage buffers.
+    using Wide = GemmCfg<256, 32, kGemmWideMW>;
+    using N8 = GemmCfg<128, 64, 4>;
+    using N4 = GemmCfg<128, 64, 2>;
+    auto lds_of = [&](size_t stage, int nwaves, int cols) { return 2 * stage + (size_t)nwaves * cols * k * 8; };
+    int tk, nwaves, mw;
+    size_t stage;
+    if (batch > 64 && lds_of(Wide::STAGE, Wide::NWAVES, Wide::COLS) <= kMaxLds) {
+      p->tn = 256, tk = 32, stage = Wide::STAGE, nwaves = Wide::NWAVES, mw = kGemmWideMW;
+    } else if (lds_of(N8::STAGE, N8::NWAVES, N8::COLS) <= kMaxLds) {
+      p->tn = 128, tk = 64, stage = N8::STAGE, nwaves = N8::NWAVES, mw = 4;
+    } else {
+      p->tn = 128, tk = 64, stage = N4::STAGE, nwaves = N4::NWAVES, mw = 2;
+    }
+    p->gemm_mw = mw;
     p->kpad = (int32_t)(cdiv(t.hidden, tk) * tk);
     p->nct = (int32_t)cdiv(batch, p->tn / 2);
     const int64_t vtiles = cdiv(t.V, kGemmTM);
@@ -817,9 +855,13 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     p->nvr = (int32_t)nvr;
     p->nblk = (int32_t)(p->nct * nvr);
     p->npass = 1;
-    p->lds_bytes = 2 * stage + (size_t)4 * (p->tn / 4) * k * 8;
+    p->lds_bytes = 2 * stage + (size_t)nwaves * (p->tn / 4) * k * 8;
+    if (p->lds_bytes > kMaxLds) {
+      *why = "k too large for the gemm path's LDS heaps";
+      return -5;
+    }
     p->img_bytes = (size_t)p->nct * p->tn * p->kpad * 2;
-    p->ncand = (int32_t)(nvr * 2 * k);
+    p->ncand = (int32_t)(nvr * mw * k);
   } else {
     p->rb = batch >= 8 ? 8 : batch >= 4 ? 4 : batch >= 2 ? 2 : 1;
     p->npass = (int32_t)cdiv(batch, p->rb);
