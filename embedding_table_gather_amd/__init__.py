@@ -17,7 +17,7 @@ import os
 import torch
 
 F32, BF16, Q8_0 = 0, 1, 2
-PATH_AUTO, PATH_VALU, PATH_STREAM, PATH_GEMM = 0, 1, 2, 3
+PATH_AUTO, PATH_VALU, PATH_STREAM, PATH_GEMM, PATH_WIDE = 0, 1, 2, 3, 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libetg.so")
 

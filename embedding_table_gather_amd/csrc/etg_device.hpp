@@ -58,6 +58,42 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// 32-bit maximum / minimum over the wave, returned to every lane (same DPP
+// pattern as wave_max_u64; lanes outside the source row see the identity).
+template <bool MAX>
+__device__ __forceinline__ uint32_t dpp_minmax_u32(uint32_t v, uint32_t o) { return MAX ? max(v, o) : min(v, o); }
+
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+  constexpr uint32_t id = MAX ? 0u : 0xffffffffu;
+  v = dpp_minmax_u32<MAX>(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = dpp_minmax_u32<MAX>(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = dpp_minmax_u32<MAX>(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = dpp_minmax_u32<MAX>(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = dpp_minmax_u32<MAX>(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = dpp_minmax_u32<MAX>(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// wave_minmax_u32 on N independent values at once, stage by stage, so that each
+// DPP move reads a register written N instructions earlier (no hazard stalls).
+template <bool MAX, int N>
+__device__ __forceinline__ void wave_minmax_u32_multi(uint32_t (&v)[N]) {
+  constexpr uint32_t id = MAX ? 0u : 0xffffffffu;
+#define ETG_DPP_STAGE(CTRL, RM)                                                                     \
+  _Pragma("unroll") for (int i = 0; i < N; i++)                                                     \
+      v[i] = dpp_minmax_u32<MAX>(v[i], __builtin_amdgcn_update_dpp(id, v[i], CTRL, RM, 0xf, false));
+  ETG_DPP_STAGE(0x111, 0xf)
+  ETG_DPP_STAGE(0x112, 0xf)
+  ETG_DPP_STAGE(0x114, 0xf)
+  ETG_DPP_STAGE(0x118, 0xf)
+  ETG_DPP_STAGE(0x142, 0xa)
+  ETG_DPP_STAGE(0x143, 0xc)
+#undef ETG_DPP_STAGE
+#pragma unroll
+  for (int i = 0; i < N; i++) v[i] = __builtin_amdgcn_readlane(v[i], 63);
+}
+
 // Butterfly sum: every lane ends with the same (bitwise) value because each
 // pairwise add is commutative.
 __device__ __forceinline__ float wave_sum(float v) {

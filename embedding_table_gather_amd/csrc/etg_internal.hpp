@@ -18,13 +18,13 @@ struct TableDesc {
 // function of (table shape, batch, k, path): the workspace size can be queried
 // without a device.
 struct LogitsPlan {
-  int32_t path;          // 1 valu, 2 stream, 3 gemm
+  int32_t path;          // 1 valu, 2 stream, 3 gemm, 4 wide
   int32_t k;
   int64_t batch;
   // stream path
   int32_t nimg;          // residual operand images: 1 (hi+lo packed, 4 rows per pass), 2 (8 rows)
   int32_t nbc;           // residual rows per pass
-  int32_t steps;         // 64-value K steps = ceil(hidden / 64)
+  int32_t steps;         // 64-value K steps = ceil(hidden / 64) (wide: padded to the chunk)
   int32_t chunk;         // K steps of the residual image staged in LDS at a time
   int64_t ngroups;       // 8-row table groups = ceil(V / 8)
   int32_t max_groups;    // most 8-row groups one wave handles
@@ -35,6 +35,8 @@ struct LogitsPlan {
   int32_t nct;           // column tiles of tn / 2 residual rows
   int32_t nvr;           // vocabulary ranges
   int32_t tiles_per_range;
+  // wide path
+  int32_t ntile;         // 16-column N-tiles per pass (residual rows per pass / 16)
   // valu path
   int32_t rb;            // residual rows per pass (1, 2, 4 or 8)
   int64_t rows_per_blk;  // most table rows one block handles
@@ -43,8 +45,9 @@ struct LogitsPlan {
   int32_t nblk;          // blocks per pass
   int32_t ncand;         // candidate keys per residual row
   size_t lds_bytes;      // dynamic LDS of the main kernel
-  size_t img_offset, img_bytes;    // split bf16 residual rows (gemm path)
+  size_t img_offset, img_bytes;    // bf16 residual operand (gemm and wide paths)
   size_t cand_offset, cand_bytes;  // u64 keys [batch][nblk][k]
+  size_t aux_offset, aux_bytes;    // wide path: u64 top-k lower bound per residual row
   size_t ws_bytes;
 };
 

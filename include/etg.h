@@ -112,11 +112,14 @@ int32_t etg_embed_gather(const etg_table* table, const int32_t* d_ids, int64_t s
 
 /* Kernel path for etg_logits_topk_ex (ETG_PATH_AUTO is what etg_logits_topk uses). */
 typedef enum {
-  ETG_PATH_AUTO = 0,   /* pick by dtype and batch                                        */
+  ETG_PATH_AUTO = 0,   /* f32 and Q8_0 tables: VALU; bf16 tables: STREAM up to 8 rows,
+                          WIDE up to 64, GEMM beyond                                      */
   ETG_PATH_VALU = 1,   /* any dtype: f32 vector FMAs, one table pass per 8 residuals     */
   ETG_PATH_STREAM = 2, /* bf16 tables: one HBM pass per 8 residuals, bf16 MFMA dot engine;
                           batches of <= 4 use a hi+lo bf16 split of the residual          */
-  ETG_PATH_GEMM = 3    /* bf16 tables: tiled bf16 MFMA contraction for large batches     */
+  ETG_PATH_GEMM = 3,   /* bf16 tables: tiled bf16 MFMA contraction for large batches     */
+  ETG_PATH_WIDE = 4    /* bf16 tables: one HBM pass per 64 residuals, bf16 MFMA dot engine,
+                          hi+lo bf16 split of the residual                                */
 } etg_path;
 
 /* Device workspace bytes etg_logits_topk(_ex) needs for this table, batch and k

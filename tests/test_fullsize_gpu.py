@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import embedding_table_gather_amd as etg
 import oracle
 import synth
 from oracle import accept
@@ -31,11 +32,11 @@ def _table(name):
     return _cache[name]
 
 
-def _check(name, B, k, sample_rows):
+def _check(name, B, k, sample_rows, path=0):
     cfg, host, t = _table(name)
     R = synth.residuals(B, cfg.d, cfg.residual_seed(B))
-    note(f"logits_topk {name} B={B} k={k}")
-    gids, gsc = t.logits_topk(to_dev(R), k)
+    note(f"logits_topk {name} B={B} k={k} path={path}")
+    gids, gsc = t.logits_topk(to_dev(R), k, path=path)
     torch.cuda.synchronize()
     gids, gsc = gids.cpu().numpy(), gsc.cpu().numpy()
     c = accept.tol_coeff(cfg.dtype)
@@ -64,6 +65,11 @@ def test_qwen05b_logits_b1():
 @pytest.mark.parametrize("B,sample", [(1, [0]), (8, [0, 7]), (64, [5, 63])])
 def test_lm31b_logits(B, sample):
     _check("lm31b", B, 10, sample)
+
+
+@pytest.mark.parametrize("path", [etg.PATH_GEMM, etg.PATH_WIDE])
+def test_lm31b_logits_b64_mfma_paths(path):
+    _check("lm31b", 64, 10, [31], path)
 
 
 def test_prefill_logits_b1024():

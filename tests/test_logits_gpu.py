@@ -18,8 +18,8 @@ from tests.gpu_util import note, table, to_dev
 pytestmark = pytest.mark.gpu
 
 F32, BF16, Q8_0 = etg.F32, etg.BF16, etg.Q8_0
-VALU, STREAM, GEMM = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM
-ALL = [VALU, STREAM, GEMM]
+VALU, STREAM, GEMM, WIDE = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE
+ALL = [VALU, STREAM, GEMM, WIDE]
 
 
 def run(t, R, k, path):
@@ -70,6 +70,17 @@ def test_gemm_path_ragged(V, d, B):
     host = synth.make_table(BF16, V, d, seed=500 + V)
     R = synth.residuals(B, d, seed=600 + B)
     full_check(host, BF16, V, d, R, min(10, V), GEMM)
+
+
+# the wide path: 512-row blocks (ragged last block), 4-step K chunks (ragged last
+# chunk and 64-value step), 1 to 4 N-tiles per pass and several passes
+@pytest.mark.parametrize("V,d", [(5003, 200), (4099, 896), (1001, 64), (20000, 5376), (37, 8), (70000, 512),
+                                 (1536, 1032)])
+@pytest.mark.parametrize("B", [1, 9, 16, 17, 33, 48, 64, 65, 130, 200])
+def test_wide_path_ragged(V, d, B):
+    host = synth.make_table(BF16, V, d, seed=700 + V)
+    R = synth.residuals(B, d, seed=800 + B)
+    full_check(host, BF16, V, d, R, min(10, V), WIDE)
 
 
 @pytest.mark.parametrize("k", [1, 2, 40, 64])
