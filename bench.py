@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "embedding_table_gather_amd", "csrc", "logits.hip")
+# sources of the roofline kernel: the traffic record is void once either changes
+KERNEL_SOURCES = [os.path.join(ROOT, "embedding_table_gather_amd", "csrc", f)
+                  for f in ("stream.hip", "etg_device.hpp")]
 
 
 def log(msg: str) -> None:
@@ -39,8 +41,11 @@ def log(msg: str) -> None:
 
 
 def _source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(kernel: str):
@@ -55,6 +60,56 @@ def _traffic(kernel: str):
     if not ent or ent.get("source_sha256_16") != _source_hash():
         return None
     return ent.get("bytes_per_launch")
+
+
+def _counter_means(csv_path: str, counter: str):
+    """Per-dispatch values of one rocprofv3 counter, grouped by kernel name."""
+    import csv
+    out = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def write_traffic(fetch_csv: str, write_csv: str, kernel: str = "stream_logits_kernel<1>") -> dict:
+    """Turn a FETCH_SIZE run and a WRITE_SIZE run of `bench.py --no-extras --calib-copy`
+    (rocprofv3 --pmc ..., csv output) into profiles/traffic.json.
+
+    Both counters are in KiB per dispatch.  Each is scaled by what it reads for the
+    plain 1 GiB device copy of the same run (the largest copy dispatches), so that
+    bytes_per_launch is in the copy's units: a copy of N bytes counts as N read
+    and N written.
+    """
+    fetch, write = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+
+    def copy_factor(d):
+        vals = [v for name, vs in d.items() if "copyBuffer" in name for v in vs]
+        big = [v for v in vals if v > 0.25 * gib_kib]
+        if not big:
+            raise SystemExit("no 1 GiB copy dispatch in the counter file (run bench.py with --calib-copy)")
+        return gib_kib / (sum(big) / len(big))
+
+    def kernel_mean(d):
+        vs = [v for name, vals in d.items() if kernel in name for v in vals]
+        if not vs:
+            raise SystemExit(f"{kernel} not found in the counter file")
+        return sum(vs) / len(vs)
+
+    ff, fw = copy_factor(fetch), copy_factor(write)
+    fk, wk = kernel_mean(fetch), kernel_mean(write)
+    rec = {kernel: {
+        "source_sha256_16": _source_hash(),
+        "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+        "copy_fetch_factor": round(ff, 5), "copy_write_factor": round(fw, 5),
+        "bytes_per_launch": round((fk * ff + wk * fw) * 1024),
+    }}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
 
 
 def _timed(torch, fn, iters: int, events: bool = False):
@@ -83,7 +138,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter files and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(write_traffic(*args.traffic_from)))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -64,5 +64,32 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const flo
                               hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr);
 
 constexpr size_t kMaxLds = 160 * 1024;
+constexpr int kTargetBlocks = 256;  // one workgroup per MI355X compute unit
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Opt a kernel in to more than 64 KiB of dynamic LDS.
+inline hipError_t set_dynamic_lds(const void* fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+inline hipError_t record_event(hipEvent_t ev, hipStream_t stream) {
+  return ev ? hipEventRecord(ev, stream) : hipSuccess;
+}
+
+// Per-path geometry (fill the path's fields and nblk, npass, lds_bytes,
+// img_bytes, aux_bytes, ncand) and launchers of the table-streaming kernel
+// (recording ev0 / ev1 around it).  stream.hip, wide.hip, gemm.hip.
+int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
+int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
+int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
+hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
+                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* img, uint64_t* cand,
+                       uint64_t* thr, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs, uint64_t* cand,
+                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace etg

@@ -1,0 +1,278 @@
+// Stream path of the tied lm_head projection (bf16 tables, up to 8 residual rows
+// per table pass): ADR-0008 "POST /v1/logits", logits = residual @ lm_head.T over
+// every vocabulary row, fused with a per-block top-k.
+#include <algorithm>
+
+#include "etg_device.hpp"
+#include "etg_internal.hpp"
+
+namespace etg {
+
+// ---------------------------------------------------------------------------
+// Stream path layout.
+//
+// The table is cut into 8-row groups.  One MFMA step covers 8 rows x 64 values
+// (128 contiguous bytes per row) of the table.  Lane l loads row (l % 8), bytes
+// [128 s + 16 (l / 8), +16): one load instruction reads 8 full 128-byte lines.
+//
+// In the 16x16x32 MFMA, lane l supplies A row m = l % 16 with K-group g = l / 16.
+// So A row m is table row m % 8, and its K slice is the half h = m / 8 of the
+// lane's 32-value window: value index 64 s + 16 g + 8 h + e (e = 0..7).  A dot
+// product does not depend on the order of its terms, so any bijection of value
+// indices works as long as the residual operand uses the same one.
+//
+// B column n (lane l supplies column n = l % 16, group g = l / 16) carries a
+// residual row at the same value indices for half h = n / 8.  Rows with h = 0
+// meet columns with h = 0 and likewise for h = 1; the cross terms D[r][8 + ...]
+// and D[r + 8][...] are unused.
+//
+// The residual is carried as a pair of bf16 values, hi = bf16(x) and
+// lo = bf16(x - hi), so the operand error is at most 2^-16 |x| (one bf16
+// rounding alone can be 2^-8 |x|).  Two layouts:
+//   packed (batch <= 4): one operand image, column n % 8 = b + 4 * part
+//                        (part 0 = hi, 1 = lo); one MFMA per step;
+//   dual   (batch <= 8): image 0 holds hi, image 1 holds lo, column n % 8 = b;
+//                        two MFMAs per step into the same accumulator.
+// Then logit[row r][b] = sum over h (and part) of D[r + 8h][8h + ...].
+// D layout: lane L holds D[4 (L / 16) + i][L % 16], i = 0..3.  For L < 32 with
+// b = L % 16 < nbc, the terms sit in lanes L, L + 40 (+ 4, + 44 when packed).
+//
+// Each block builds the operand image [step][image][64 lanes] x 16 bytes in LDS
+// from the fp32 residual, `chunk` steps at a time (all of it when it fits).
+// ---------------------------------------------------------------------------
+
+static constexpr int kStreamWaves = 16;
+static constexpr int kStreamUnroll = 6;  // K steps per load group (half of it with two images)
+static constexpr int kStreamMaxPairs = 4;  // a wave handles at most 8 groups (64 rows)
+
+// Fill LDS with steps [c0, c0 + n) of the bf16 hi/lo operand image, converted from
+// the fp32 residual rows of this pass.  Image slot (s, im, lane) holds the 8
+// values of B column n = lane % 16, K-group g = lane / 16 (layout above).
+template <int NIMG>
+__device__ __forceinline__ void stream_stage_image(u32x4* simg, const float* __restrict__ R, int64_t B,
+                                                   int hidden, int64_t b0, int c0, int n) {
+  constexpr int NBC = NIMG == 1 ? 4 : 8;
+  for (int i = threadIdx.x; i < n * NIMG * 64; i += blockDim.x) {
+    const int lane = i & 63;
+    const int q = i >> 6;
+    const int im = q % NIMG;
+    const int s = c0 + q / NIMG;
+    const int nn = lane & 15, g = lane >> 4;
+    const int h = nn >> 3, j8 = nn & 7;
+    const int part = NIMG == 1 ? j8 / NBC : im;
+    const int64_t b = b0 + j8 % NBC;
+    const int cbase = 64 * s + 16 * g + 8 * h;
+    uint32_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const int c = cbase + e;
+      const float x = (b < B && c < hidden) ? R[b * hidden + c] : 0.0f;
+      const uint32_t hi = bf16_rne(x);
+      // part 1 carries the remainder x - hi (exact in f32), rounded to bf16
+      v[e] = part == 1 ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;
+    }
+    simg[i] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+  }
+}
+
+template <int NBC>
+__device__ __forceinline__ void stream_store_group(f32x4 acc, float* dst, int lane) {
+  f32x4 y;
+#pragma unroll
+  for (int i = 0; i < 4; i++) y[i] = acc[i] + __shfl(acc[i], (lane + 40) & 63, 64);
+  if (NBC == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) y[i] = y[i] + __shfl(y[i], (lane + 4) & 63, 64);
+  }
+  if (lane < 32 && (lane & 15) < NBC) {
+    const int b = lane & 15, r0 = 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) dst[(r0 + i) * NBC + b] = y[i];
+  }
+}
+
+// The k best (logit, row) of this block for residual column b, as descending keys.
+// slog is [wave][group * 8 + r][NBC]; wave w owns groups [sg0[w], sg0[w] + sng[w]).
+// Each lane holds one row per wave in registers; round t takes the largest key
+// below the key of round t - 1 (keys are unique).
+template <int NBC>
+__device__ void stream_block_topk(const float* slog, const int64_t* sg0, const int* sng, int b, int lane,
+                                  int max_groups, int64_t V, int k, uint64_t* out) {
+  const int per_wave = max_groups * 8;  // <= 64
+  uint64_t key[kStreamWaves];
+#pragma unroll
+  for (int w = 0; w < kStreamWaves; w++) {
+    const int64_t row = sg0[w] * 8 + lane;
+    key[w] = (lane < sng[w] * 8 && row < V) ? make_key(slog[(w * per_wave + lane) * NBC + b], (uint32_t)row) : 0;
+  }
+  uint64_t prev = ~0ull;
+  for (int t = 0; t < k; t++) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; w++) best = (key[w] < prev && key[w] > best) ? key[w] : best;
+    best = wave_max_u64(best);
+    if (lane == 0) out[t] = best;
+    prev = best;
+  }
+}
+
+// One pass over the table for NBC residual rows (pass = blockIdx.y).
+//  table      bf16 [V][hidden], row_bytes = 2 * hidden
+//  R          fp32 [B][hidden]
+//  steps      64-value K steps, ceil(hidden / 64)
+//  chunk      K steps staged in LDS at a time (a multiple of the unroll)
+// Out-of-range rows and K positions are read from clamped in-range addresses and
+// meet zero residual values or are never ranked, so no load is predicated (table
+// entries are assumed finite).
+template <int NIMG>
+__global__ void __launch_bounds__(1024) stream_logits_kernel(
+    const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden,
+    const float* __restrict__ R, int64_t B, int steps, int chunk, int k, uint64_t* __restrict__ cand,
+    int64_t ngroups, int max_groups) {
+  constexpr int NBC = NIMG == 1 ? 4 : 8;
+  constexpr int U = NIMG == 1 ? kStreamUnroll : kStreamUnroll / 2;
+  const int steps_full = hidden / 64;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  u32x4* simg = (u32x4*)smem;
+  float* slog = (float*)(smem + (size_t)chunk * NIMG * 1024);
+  __shared__ int64_t sg0[kStreamWaves];
+  __shared__ int sng[kStreamWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t b0 = (int64_t)blockIdx.y * NBC;
+
+  // Waves own contiguous runs of group pairs (16 rows); only the last pair of the
+  // table can be half empty.
+  const int64_t nw = (int64_t)gridDim.x * kStreamWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kStreamWaves + wv;
+  const int64_t npairs_all = (ngroups + 1) >> 1;
+  const int64_t pb = gw * npairs_all / nw;
+  const int npairs = (int)((gw + 1) * npairs_all / nw - pb);
+  const int64_t g_begin = 2 * pb;
+  const int ng = (int)min((int64_t)(2 * npairs), ngroups - g_begin);
+  if (lane == 0) {
+    sg0[wv] = g_begin;
+    sng[wv] = ng;
+  }
+  const int r = lane & 7, ck = lane >> 3;
+  const int64_t last_off = row_bytes - 16;
+
+  f32x4 acc0[kStreamMaxPairs], acc1[kStreamMaxPairs];
+#pragma unroll
+  for (int p = 0; p < kStreamMaxPairs; p++) acc0[p] = acc1[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < steps; c0 += chunk) {
+    const int c1 = min(steps, c0 + chunk);
+    if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
+    stream_stage_image<NIMG>(simg, R, B, hidden, b0, c0, c1 - c0);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kStreamMaxPairs; p++) {
+      if (p < npairs) {
+        const int64_t row0 = min((g_begin + 2 * p) * 8 + r, V - 1);
+        const int64_t row1 = min((g_begin + 2 * p) * 8 + 8 + r, V - 1);
+        const uint8_t* p0 = table + (uint64_t)row0 * (uint64_t)row_bytes;
+        const uint8_t* p1 = table + (uint64_t)row1 * (uint64_t)row_bytes;
+        const u32x4* q0 = (const u32x4*)(p0 + 16 * ck);
+        const u32x4* q1 = (const u32x4*)(p1 + 16 * ck);
+        // complete steps, U at a time: all loads of the group are issued before the
+        // MFMAs that consume them
+        const int cf = min(c1, steps_full);
+        int s0 = c0;
+        for (; s0 + U <= cf; s0 += U) {
+          u32x4 a0[U], a1[U];
+#pragma unroll
+          for (int j = 0; j < U; j++) {
+            a0[j] = __builtin_nontemporal_load(q0 + 8 * (s0 + j));
+            a1[j] = __builtin_nontemporal_load(q1 + 8 * (s0 + j));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < U; j++) {
+            const u32x4* bl = simg + (size_t)(s0 + j - c0) * NIMG * 64 + lane;
+#pragma unroll
+            for (int im = 0; im < NIMG; im++) {
+              const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[im * 64]);
+              acc0[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0[j]), bop, acc0[p], 0,
+                                                                0, 0);
+              acc1[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1[j]), bop, acc1[p], 0,
+                                                                0, 0);
+            }
+          }
+        }
+        // remaining steps of the chunk, one at a time; a K position at or past
+        // `hidden` reads the row's last 16 bytes and meets a zero residual value
+        for (; s0 < min(c1, steps); s0++) {
+          const int64_t off = min((int64_t)(128 * s0 + 16 * ck), last_off);
+          const u32x4 a0 = __builtin_nontemporal_load((const u32x4*)(p0 + off));
+          const u32x4 a1 = __builtin_nontemporal_load((const u32x4*)(p1 + off));
+          const u32x4* bl = simg + (size_t)(s0 - c0) * NIMG * 64 + lane;
+#pragma unroll
+          for (int im = 0; im < NIMG; im++) {
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[im * 64]);
+            acc0[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bop, acc0[p], 0, 0, 0);
+            acc1[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bop, acc1[p], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  float* mylog = slog + (size_t)wv * max_groups * 8 * NBC;
+#pragma unroll
+  for (int p = 0; p < kStreamMaxPairs; p++) {
+    if (2 * p < ng) stream_store_group<NBC>(acc0[p], mylog + (size_t)(2 * p) * 8 * NBC, lane);
+    if (2 * p + 1 < ng) stream_store_group<NBC>(acc1[p], mylog + (size_t)(2 * p + 1) * 8 * NBC, lane);
+  }
+  __syncthreads();
+
+  if (wv < NBC && b0 + wv < B) {
+    uint64_t* out = cand + ((b0 + wv) * gridDim.x + blockIdx.x) * (int64_t)k;
+    stream_block_topk<NBC>(slog, sg0, sng, wv, lane, max_groups, V, k, out);
+  }
+}
+
+
+template <int NIMG>
+static hipError_t launch_stream_nimg(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
+                                hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  hipError_t e = set_dynamic_lds((const void*)stream_logits_kernel<NIMG>, p.lds_bytes);
+  if (e != hipSuccess) return e;
+  if ((e = record_event(ev0, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((stream_logits_kernel<NIMG>), dim3((unsigned)p.nblk, (unsigned)p.npass),
+                     dim3(64 * kStreamWaves), p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (int)t.hidden, R,
+                     p.batch, p.steps, p.chunk, p.k, cand, p.ngroups, p.max_groups);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return record_event(ev1, stream);
+}
+
+hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
+                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  return p.nimg == 1 ? launch_stream_nimg<1>(t, p, R, cand, stream, ev0, ev1)
+                     : launch_stream_nimg<2>(t, p, R, cand, stream, ev0, ev1);
+}
+
+int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
+  (void)why;
+    p->nimg = batch <= 4 ? 1 : 2;
+    p->nbc = p->nimg == 1 ? 4 : 8;
+    p->steps = (int32_t)cdiv(t.hidden, 64);
+    p->ngroups = cdiv(t.V, 8);
+    p->npass = (int32_t)cdiv(batch, p->nbc);
+    // one block per CU, unless a wave would then own more than kStreamMaxPairs pairs
+    const int64_t npairs_all = cdiv(p->ngroups, 2);
+    p->nblk = (int32_t)std::max<int64_t>(cdiv(npairs_all, (int64_t)kStreamWaves * kStreamMaxPairs),
+                                         std::min<int64_t>(kTargetBlocks, cdiv(npairs_all, kStreamWaves)));
+    p->max_groups = (int32_t)(2 * cdiv(npairs_all, (int64_t)p->nblk * kStreamWaves));
+    const size_t log_bytes = (size_t)kStreamWaves * p->max_groups * 8 * p->nbc * 4;
+    const size_t img_room = kMaxLds - 1024 - log_bytes;
+    const int64_t max_chunk = (int64_t)(img_room / ((size_t)p->nimg * 1024)) / kStreamUnroll * kStreamUnroll;
+    // equal chunks (multiples of the unroll), as few as fit
+    const int64_t nchunks = cdiv(p->steps, max_chunk);
+    p->chunk = (int32_t)std::min<int64_t>(max_chunk, cdiv(cdiv(p->steps, nchunks), kStreamUnroll) * kStreamUnroll);
+    p->lds_bytes = (size_t)p->chunk * p->nimg * 1024 + log_bytes;
+    p->img_bytes = 0;
+    p->ncand = p->nblk * k;
+  return 0;
+}
+
+}  // namespace etg

@@ -1,0 +1,358 @@
+// Wide stream path of the tied lm_head projection (bf16 tables, up to 64 residual
+// rows per table pass): ADR-0008 "POST /v1/logits", logits = residual @ lm_head.T
+// over every vocabulary row, fused with a per-block top-k.
+#include <algorithm>
+
+#include "etg_device.hpp"
+#include "etg_internal.hpp"
+
+namespace etg {
+
+// ---------------------------------------------------------------------------
+// Wide stream path: bf16 tables, batches beyond the stream path's 8 rows.
+//
+// Still one HBM pass over the table per pass of up to 64 residual rows, with
+// the table read straight into VGPRs; the residual operand comes from LDS.
+// A block owns 512 table rows (8 waves x 4 M-tiles of 16 rows).
+//
+// Loads: per 16-row M-tile and 64-value K step, two load instructions X (rows
+// 0-7) and Y (rows 8-15); lane l reads row l % 8 of its half, 16-byte chunk
+// l / 8 of the 128-byte step, so each instruction reads 8 whole 128-byte lines.
+// Two DPP moves per dword exchange the upper 8 lanes of each 16-lane row of X
+// with the lower 8 lanes of Y:
+//   P: lanes 0-7 of each row from X, lanes 8-15 from Y (row_shr:8)
+//   Q: lanes 0-7 from X (row_shl:8), lanes 8-15 from Y
+// after which lane l of P holds row l % 16, chunk 2 (l / 16) and lane l of Q the
+// same row, chunk 2 (l / 16) + 1.  P and Q are complete 16x16x32 A operands
+// over the even and odd 16-byte chunks of the step (values 64 s + 16 g + e and
+// 64 s + 16 g + 8 + e for K-group g), so no MFMA lane is wasted.
+//
+// The residual enters as hi + lo bf16 pairs (as on the stream path).  Per step
+// and 16-column N-tile there are four B fragments (P/Q x hi/lo), all four
+// accumulating into the same 16x16 tile: logit = D after the K loop.
+// The operand image [pass][step][nt][pq][hl][lane] x 16 bytes is built once per
+// call by wide_prep_kernel; blocks stage it through LDS kWideCK steps at a time
+// in two buffers, the next chunk's image being copied in while the current one is
+// used, with one LDS-only barrier per chunk (table loads stay in flight across it).
+// ---------------------------------------------------------------------------
+static constexpr int kWideWaves = 8;
+static constexpr int kWideMT = 4;                            // 16-row M-tiles per wave
+static constexpr int kWideRows = kWideWaves * kWideMT * 16;  // table rows per block
+static constexpr int kWideCK = 3;  // K steps per staged chunk = depth of the table-load ring
+static constexpr int kWideMaxTiles = 4;                      // 16-column N-tiles: 64 residual rows
+
+// Barrier that orders LDS accesses only: outstanding global loads are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Image slot i = ((((pass * steps_pad + s) * ntile + nt) * 2 + pq) * 2 + hl) * 64 + lane
+// holds residual row 16 (ntile pass + nt) + lane % 16, values
+// 64 s + 16 (lane / 16) + 8 pq + e (e = 0..7), as bf16 hi (hl = 0) or lo (hl = 1).
+// Rows past the batch and values past hidden are zero.
+// It also clears the per-row top-k lower bounds thr[B] (total >= B).
+__global__ void __launch_bounds__(256) wide_prep_kernel(const float* __restrict__ R, int64_t B, int hidden,
+                                                        int steps_pad, int ntile, int64_t total,
+                                                        u32x4* __restrict__ img, uint64_t* __restrict__ thr) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < B) thr[i] = 0;
+  if (i >= total) return;
+  const int lane = (int)(i & 63);
+  const int f = (int)((i >> 6) & 3);
+  int64_t q = i >> 8;
+  const int nt = (int)(q % ntile);
+  q /= ntile;
+  const int s = (int)(q % steps_pad);
+  const int64_t pass = q / steps_pad;
+  const int64_t b = (pass * ntile + nt) * 16 + (lane & 15);
+  const int c0 = 64 * s + 16 * (lane >> 4) + 8 * (f >> 1);
+  const bool lo = (f & 1) != 0;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const int c = c0 + e;
+    const float x = (b < B && c < hidden) ? R[b * hidden + c] : 0.0f;
+    const uint32_t hi = bf16_rne(x);
+    v[e] = lo ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;  // x - hi is exact in f32
+  }
+  img[i] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+}
+
+// One pass (blockIdx.y) over the table for 16 NTILE residual rows.
+//  table      bf16 [V][hidden], row_bytes = 2 hidden, a multiple of 16
+//  img        operand image (wide_prep_kernel), steps_pad K steps per pass
+//  steps_pad  ceil(hidden / 64) rounded up to kWideCK
+// Rows past V are read from row V - 1 and never ranked; 16-byte chunks past the
+// row end are read from the row's last 16 bytes and meet zero image values.
+template <int NTILE>
+__global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
+    const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, const u32x4* __restrict__ img, int64_t B,
+    int steps_pad, int k, uint64_t* __restrict__ cand, uint64_t* __restrict__ thr) {
+  constexpr int STEP_U4 = NTILE * 4 * 64;  // image slots per K step
+  constexpr int CHUNK_U4 = kWideCK * STEP_U4;
+  constexpr int NTHR = 64 * kWideWaves;
+  constexpr int NPER = (STEP_U4 + NTHR - 1) / NTHR;
+  constexpr int NC = NTILE * 16;
+  constexpr int LS = NC + 1;  // logit row stride in LDS (odd: conflict-free column reads)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  u32x4* sbuf = (u32x4*)smem;  // two chunk buffers
+  float* slog = (float*)smem;  // after the K loop: [kWideRows][LS]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t row0 = (int64_t)blockIdx.x * kWideRows;
+  const u32x4* pimg = img + (size_t)blockIdx.y * steps_pad * STEP_U4;
+  const uint8_t* tbase = table + (uint64_t)row0 * (uint64_t)row_bytes;
+  const int r8 = lane & 7, ck = lane >> 3;
+  const uint32_t last_off = (uint32_t)(row_bytes - 16);
+
+  // byte offsets of this lane's X and Y rows from the block's first row (32-bit:
+  // the planner bounds kWideRows * row_bytes)
+  uint32_t xoff[kWideMT], yoff[kWideMT];
+#pragma unroll
+  for (int mt = 0; mt < kWideMT; mt++) {
+    const int64_t rx = min(row0 + wv * (kWideMT * 16) + 16 * mt + r8, V - 1) - row0;
+    const int64_t ry = min(row0 + wv * (kWideMT * 16) + 16 * mt + 8 + r8, V - 1) - row0;
+    xoff[mt] = (uint32_t)(rx * row_bytes);
+    yoff[mt] = (uint32_t)(ry * row_bytes);
+  }
+  // offset of this lane's 16-byte chunk of K step s within a row
+  auto koff = [&](int s) { return min(128u * (uint32_t)s + 16u * (uint32_t)ck, last_off); };
+
+  f32x4 acc[kWideMT][NTILE];
+#pragma unroll
+  for (int mt = 0; mt < kWideMT; mt++)
+#pragma unroll
+    for (int nt = 0; nt < NTILE; nt++) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // first chunk of the image: loads issued before the table loads, so the LDS
+  // writes below do not wait for those
+  constexpr int NPRE = (CHUNK_U4 + NTHR - 1) / NTHR;
+  u32x4 pre[NPRE];
+#pragma unroll
+  for (int q = 0; q < NPRE; q++) pre[q] = pimg[min(tid + q * NTHR, CHUNK_U4 - 1)];
+
+  // ring of table loads: the j-th step of a chunk lives in slot j and is loaded
+  // kWideCK - 1 steps ahead of its use
+  u32x4 ax[kWideCK][kWideMT], ay[kWideCK][kWideMT];
+#pragma unroll
+  for (int r = 0; r < kWideCK - 1; r++) {
+    const uint32_t ko = koff(r);
+#pragma unroll
+    for (int mt = 0; mt < kWideMT; mt++) {
+      ax[r][mt] = __builtin_nontemporal_load((const u32x4*)(tbase + (xoff[mt] + ko)));
+      ay[r][mt] = __builtin_nontemporal_load((const u32x4*)(tbase + (yoff[mt] + ko)));
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NPRE; q++) sbuf[min(tid + q * NTHR, CHUNK_U4 - 1)] = pre[q];
+  lds_barrier();
+
+  const int nchunks = steps_pad / kWideCK;
+  for (int c = 0; c < nchunks; c++) {
+    const u32x4* cur = sbuf + (c & 1) * CHUNK_U4;
+    u32x4* nxt = sbuf + ((c + 1) & 1) * CHUNK_U4;
+    // the next chunk; past the last one these are spare loads of the last chunk
+    // (never used)
+    const int pn = min(c + 1, nchunks - 1);
+    const int pc = c;
+#pragma unroll
+    for (int j = 0; j < kWideCK; j++) {
+      const int cb = j, nb = (j + kWideCK - 1) % kWideCK;
+      // image piece j of the next chunk
+      u32x4 st[NPER];
+      const u32x4* ps = pimg + ((size_t)pn * kWideCK + j) * STEP_U4;
+#pragma unroll
+      for (int q = 0; q < NPER; q++) st[q] = ps[min(tid + q * NTHR, STEP_U4 - 1)];
+      // table loads of the step kWideCK - 1 ahead: the last step of this chunk for
+      // j = 0, else step j - 1 of the next chunk (clamped to the row end)
+      const uint32_t ko = koff(j == 0 ? pc * kWideCK + kWideCK - 1 : pn * kWideCK + j - 1);
+#pragma unroll
+      for (int mt = 0; mt < kWideMT; mt++) {
+        ax[nb][mt] = __builtin_nontemporal_load((const u32x4*)(tbase + (xoff[mt] + ko)));
+        ay[nb][mt] = __builtin_nontemporal_load((const u32x4*)(tbase + (yoff[mt] + ko)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 P[kWideMT], Q[kWideMT];
+#pragma unroll
+      for (int mt = 0; mt < kWideMT; mt++) {
+        const u32x4 x = ax[cb][mt], y = ay[cb][mt];
+        u32x4 p, qv;
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+          p[d] = __builtin_amdgcn_update_dpp(x[d], y[d], 0x118, 0xf, 0xc, false);   // row_shr:8 into lanes 8-15
+          qv[d] = __builtin_amdgcn_update_dpp(y[d], x[d], 0x108, 0xf, 0x3, false);  // row_shl:8 into lanes 0-7
+        }
+        P[mt] = __builtin_bit_cast(bf16x8, p);
+        Q[mt] = __builtin_bit_cast(bf16x8, qv);
+      }
+      const u32x4* bl = cur + j * STEP_U4 + lane;
+      // fragment f = 2 pq + hl of N-tile nt; consecutive MFMAs go to different
+      // accumulators
+#pragma unroll
+      for (int nt = 0; nt < NTILE; nt++) {
+#pragma unroll
+        for (int f = 0; f < 4; f++) {
+          const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[(4 * nt + f) * 64]);
+#pragma unroll
+          for (int mt = 0; mt < kWideMT; mt++)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f < 2 ? P[mt] : Q[mt], bop, acc[mt][nt], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NPER; q++) nxt[j * STEP_U4 + min(tid + q * NTHR, STEP_U4 - 1)] = st[q];
+    }
+    lds_barrier();
+  }
+
+  // Per residual row b: the block's k best keys, largest first, then empty (0)
+  // slots.  thr[b] is a running lower bound on the k-th best key of row b over
+  // the whole table (the largest k-th best any block has found so far), so
+  // entries whose order value is below its order value cannot be among the final
+  // k and are skipped.  Whatever value a block reads, every key of the final
+  // top k is still emitted, so the merged result does not depend on timing.
+  // Only the order value (the upper 32 bits) of each bound is used; the bounds
+  // of this wave's rows are loaded together, before the logits pass through LDS.
+  constexpr int PER_LANE = kWideRows / 64;
+  constexpr int MAXC = (NC + kWideWaves - 1) / kWideWaves;
+  const int64_t bcol0 = (int64_t)blockIdx.y * NC + wv;
+  uint32_t tords[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; i++)
+    tords[i] = __hip_atomic_load((const uint32_t*)(thr + min(bcol0 + i * kWideWaves, B - 1)) + 1, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+
+  // logits of the block's rows through LDS (the image buffers are free now)
+#pragma unroll
+  for (int mt = 0; mt < kWideMT; mt++)
+#pragma unroll
+    for (int nt = 0; nt < NTILE; nt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int rl = wv * (kWideMT * 16) + 16 * mt + 4 * (lane >> 4) + i;
+        slog[rl * LS + 16 * nt + (lane & 15)] = acc[mt][nt][i];
+      }
+  lds_barrier();
+
+  // into scalars before any store, so that no later wait covers the stores
+#pragma unroll
+  for (int i = 0; i < MAXC; i++) tords[i] = __builtin_amdgcn_readfirstlane(tords[i]);
+
+  // The wave's columns are selected together, round by round, so that their
+  // reduction chains interleave.  v[i][q]: order value (score_ord, > 0 for any
+  // score) of row lane + 64 q for column i if it passes the bound, else 0.
+  // Round t takes, per column, the largest order value left and the smallest row
+  // holding it, and removes that entry; a column whose largest value is 0 has no
+  // entries left.  The rounds stop after k or when no column has entries left.
+  uint32_t v[MAXC][PER_LANE];
+  bool live[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; i++) {
+    const int col = min(wv + i * kWideWaves, NC - 1);
+    live[i] = wv + i * kWideWaves < NC && bcol0 + i * kWideWaves < B;
+#pragma unroll
+    for (int q = 0; q < PER_LANE; q++) {
+      const int rl = lane + 64 * q;
+      const uint32_t o = score_ord(slog[rl * LS + col]);
+      v[i][q] = (row0 + rl < V && live[i] && o >= tords[i]) ? o : 0u;
+    }
+  }
+  int rnd[MAXC];  // keys emitted per column
+  uint64_t key[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; i++) rnd[i] = 0, key[i] = 0;
+  for (int t = 0; t < k; t++) {
+    uint32_t M[MAXC], Rw[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) {
+      uint32_t lm = v[i][0];
+#pragma unroll
+      for (int q = 1; q < PER_LANE; q++) lm = max(lm, v[i][q]);
+      M[i] = lm;
+    }
+    wave_minmax_u32_multi<true>(M);
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) any |= M[i] != 0u;
+    if (!any) break;
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) {
+      uint32_t rq = 0xffffffffu;
+#pragma unroll
+      for (int q = PER_LANE - 1; q >= 0; q--) rq = v[i][q] == M[i] ? (uint32_t)(lane + 64 * q) : rq;
+      Rw[i] = rq;
+    }
+    wave_minmax_u32_multi<false>(Rw);
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) {
+      const bool hit = M[i] != 0u;
+#pragma unroll
+      for (int q = 0; q < PER_LANE; q++) v[i][q] = (hit && lane + 64 * q == (int)Rw[i]) ? 0u : v[i][q];
+      key[i] = hit ? ((uint64_t)M[i] << 32) | (uint64_t)(~(uint32_t)(row0 + Rw[i])) : key[i];
+      rnd[i] += hit ? 1 : 0;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < MAXC; i++)
+        if (M[i] != 0u) cand[((bcol0 + i * kWideWaves) * gridDim.x + blockIdx.x) * (int64_t)k + t] = key[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MAXC; i++) {
+    if (!live[i]) break;
+    uint64_t* out = cand + ((bcol0 + i * kWideWaves) * gridDim.x + blockIdx.x) * (int64_t)k;
+    for (int t = rnd[i] + lane; t < k; t += 64) out[t] = 0;
+    if (rnd[i] == k && lane == 0)
+      atomicMax((unsigned long long*)(thr + bcol0 + i * kWideWaves), (unsigned long long)key[i]);
+  }
+}
+
+
+template <int NTILE>
+static hipError_t launch_wide_nt(const TableDesc& t, const LogitsPlan& p, const u32x4* img, uint64_t* cand,
+                                 uint64_t* thr, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  hipError_t e = set_dynamic_lds((const void*)wide_logits_kernel<NTILE>, p.lds_bytes);
+  if (e != hipSuccess) return e;
+  if ((e = record_event(ev0, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((wide_logits_kernel<NTILE>), dim3((unsigned)p.nblk, (unsigned)p.npass), dim3(64 * kWideWaves),
+                     p.lds_bytes, stream, t.rows, t.V, t.row_bytes, img, p.batch, p.steps, p.k, cand, thr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return record_event(ev1, stream);
+}
+
+hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* img,
+                              uint64_t* cand, uint64_t* thr, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const int64_t total = (int64_t)p.npass * p.steps * p.ntile * 256;  // >= 768 npass >= batch
+  hipLaunchKernelGGL(wide_prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, R, p.batch,
+                     (int)t.hidden, p.steps, p.ntile, total, (u32x4*)img, thr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (p.ntile) {
+    case 1: return launch_wide_nt<1>(t, p, (const u32x4*)img, cand, thr, stream, ev0, ev1);
+    case 2: return launch_wide_nt<2>(t, p, (const u32x4*)img, cand, thr, stream, ev0, ev1);
+    case 3: return launch_wide_nt<3>(t, p, (const u32x4*)img, cand, thr, stream, ev0, ev1);
+    case 4: return launch_wide_nt<4>(t, p, (const u32x4*)img, cand, thr, stream, ev0, ev1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
+    // passes of at most 64 residual rows, split evenly into 16-row N-tiles
+    if ((uint64_t)(kWideRows + 1) * (uint64_t)t.row_bytes >= (1ull << 32)) {
+      *why = "rows too long for the wide path";
+      return -5;
+    }
+    p->npass = (int32_t)cdiv(batch, kWideMaxTiles * 16);
+    p->ntile = (int32_t)cdiv(cdiv(batch, p->npass), 16);
+    p->steps = (int32_t)(cdiv(cdiv(t.hidden, 64), kWideCK) * kWideCK);
+    p->nblk = (int32_t)cdiv(t.V, kWideRows);
+    const size_t img_lds = (size_t)2 * kWideCK * p->ntile * 4 * 1024;
+    const size_t log_lds = (size_t)kWideRows * (16 * p->ntile + 1) * 4;
+    p->lds_bytes = std::max(img_lds, log_lds);
+    p->img_bytes = (size_t)p->npass * p->steps * p->ntile * 4 * 1024;
+    p->ncand = p->nblk * k;
+  p->aux_bytes = (size_t)batch * 8;
+  return 0;
+}
+
+}  // namespace etg
