@@ -29,8 +29,8 @@ struct LogitsPlan {
   int64_t ngroups;       // 8-row table groups = ceil(V / 8)
   int32_t max_groups;    // most 8-row groups one wave handles
   // gemm path
-  int32_t tn;            // split residual columns per column tile (128 or 256)
-  int32_t gemm_mw;       // waves along the vocabulary (2: 4 waves, 4: 8 waves)
+  int32_t tn;            // split residual columns per column tile (256)
+  int32_t gemm_wn;       // waves along the columns (2: 2 x 2 waves, 4: 2 x 4 waves)
   int32_t kpad;          // hidden rounded up to the K stage
   int32_t nct;           // column tiles of tn / 2 residual rows
   int32_t nvr;           // vocabulary ranges
