@@ -30,7 +30,8 @@ struct LogitsPlan {
   int32_t max_groups;    // most 8-row groups one wave handles
   // gemm path
   int32_t tn;            // split residual columns per column tile (256)
-  int32_t gemm_wn;       // waves along the columns (2: 2 x 2 waves, 4: 2 x 4 waves)
+  int32_t gemm_wn;       // waves along the columns (4: 2 x 4 waves)
+  int32_t gemm_ring;     // LDS ring depths, table x 10 + residual (33 or 34)
   int32_t kpad;          // hidden rounded up to the K stage
   int32_t nct;           // column tiles of tn / 2 residual rows
   int32_t nvr;           // vocabulary ranges

@@ -15,12 +15,16 @@ namespace etg {
 // rows, so logit[v][b] = C[v][hi(b)] + C[v][lo(b)].  A workgroup owns one
 // column tile of 256 split columns (128 residual rows) and walks a range of
 // 256-row vocabulary tiles.  Per tile the K loop runs in stages of 32 values:
-// the table and residual slices of a stage (2 x 256 rows x 64 bytes) are copied
-// HBM/L2 -> LDS by global_load_lds_dwordx4 (no staging registers) into a ring of
-// three LDS buffers, two stages ahead of the MFMAs (v_mfma_f32_32x32x16_bf16).
-// One barrier per stage, preceded by an explicit wait for the stage that is due
-// next (vmcnt counts loads in issue order, so the later stage stays in flight)
-// and for this wave's LDS reads.
+// the table and residual slices of a stage (256 rows x 64 bytes each) are
+// copied HBM/L2 -> LDS by global_load_lds_dwordx4 (no staging registers), the
+// table slices into a ring of NA buffers and the residual slices into a ring of
+// NB buffers, NA - 1 and NB - 1 stages ahead of the MFMAs
+// (v_mfma_f32_32x32x16_bf16); half of the waves issue each kind.  One barrier
+// per stage, preceded by an explicit wait for the stage that is due next
+// (vmcnt counts loads in issue order, so later stages stay in flight) and for
+// this wave's LDS reads.  Fragment reads are software-pipelined: each group of
+// six reads (one 16-value sub-step) overlaps the 8 MFMAs of the previous group,
+// across the barrier too.
 //
 // Waves form a WM x WN grid; wave (mw, nw) computes rows [WR mw, +WR) x split
 // columns [WC nw, +WC) as MT x NT 32x32 tiles.  N-tiles [0, NT/2) hold hi rows
@@ -46,7 +50,6 @@ namespace etg {
 static constexpr int kGemmBM = 256;                                   // vocabulary rows per tile
 static constexpr int kGemmBN = 256;                                   // split columns per tile
 static constexpr int kGemmBK = 32;                                    // K values per stage
-static constexpr int kGemmBuf = 3;                                    // LDS stage ring
 static constexpr int kGemmStage = (kGemmBM + kGemmBN) * kGemmBK * 2;  // bytes per stage
 static constexpr int kGemmCols = kGemmBN / 2;                         // residual rows per column tile
 static constexpr int kXcds = 8;
@@ -68,9 +71,20 @@ __device__ __forceinline__ int gemm_swz(int r, int piece) { return r * 64 + 16 *
 // vmcnt(n) lgkmcnt(0), then a workgroup barrier that no memory access crosses.
 template <int N>
 __device__ __forceinline__ void gemm_stage_barrier() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // expcnt(7) lgkmcnt(0) vmcnt(N)
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);  // expcnt(7) lgkmcnt(0) vmcnt(N)
   asm volatile("s_barrier" ::: "memory");
+}
+
+// gemm_stage_barrier<groups * G> for a run-time number of outstanding load groups.
+template <int G>
+__device__ __forceinline__ void gemm_stage_barrier_groups(int groups) {
+  switch (groups) {
+    case 0: gemm_stage_barrier<0>(); break;
+    case 1: gemm_stage_barrier<G>(); break;
+    case 2: gemm_stage_barrier<2 * G>(); break;
+    default: gemm_stage_barrier<3 * G>(); break;
+  }
 }
 
 // fp32 residual [B][hidden] -> split bf16 rows [nct][256][kpad].  Row j of column
@@ -130,15 +144,18 @@ __device__ __forceinline__ void heap_replace_root(uint64_t* h, int k, uint64_t k
 //         rounded up to 32
 // Table rows past V are read from row V - 1 and never ranked; table bytes past
 // the row end are read from the row's last 16 bytes and meet zero residual values.
-template <int WM, int WN>
+template <int WM, int WN, int NA, int NB>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, const uint8_t* __restrict__ Rs, int kpad,
     int64_t B, int k, uint64_t* __restrict__ cand, int nct, int nvr, int tiles_per_range) {
   using C = GemmCfg<WM, WN>;
   constexpr int MT = C::MT, NT = C::NT, WR = C::WR, WC = C::WC, DPW = C::DPW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint64_t* heaps = (uint64_t*)(smem + kGemmBuf * kGemmStage);  // [kGemmCols][k]
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  static_assert(NA >= 2 && NB >= 2 && NA <= 5 && NB <= 5, "ring depths");
+  constexpr int SLICE = kGemmBM * 64;                     // one stage of 256 table or residual rows
+  uint64_t* heaps = (uint64_t*)(smem + (NA + NB) * SLICE);  // [kGemmCols][k]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps wave choices scalar
   const int mw = wv / WN, nw = wv % WN;
 
   // XCD-aware placement: ids {x, x + 8, ...} run on XCD x.
@@ -173,9 +190,13 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     for (int j = 0; j < DPW; j++)
       src[j] = dma_a ? table + (uint64_t)min(v0 + 16 * ((wv * DPW + j) % 16) + lrow, V - 1) * (uint64_t)row_bytes
                      : bsrc[j];
-    auto issue = [&](int s, int buf) {
-      const uint32_t off = min((uint32_t)s * 64u + 16u * (uint32_t)lpiece, lim);
-      unsigned char* dst = smem + buf * kGemmStage + (dma_a ? 0 : kGemmBM * 64);
+    // Table slices go to a ring of NA buffers, residual slices to a ring of NB
+    // buffers after it; a wave issues only one kind, depth - 1 stages ahead.
+    const int depth = dma_a ? NA : NB;
+    unsigned char* ring = smem + (dma_a ? 0 : NA * SLICE);
+    auto issue = [&](int st, int slot) {
+      const uint32_t off = min((uint32_t)st * 64u + 16u * (uint32_t)lpiece, lim);
+      unsigned char* dst = ring + slot * SLICE;
 #pragma unroll
       for (int j = 0; j < DPW; j++)
         __builtin_amdgcn_global_load_lds((const void*)(src[j] + off),
@@ -188,39 +209,49 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
 #pragma unroll
       for (int t = 0; t < NT; t++) acc[a][t] = f32x16{};
 
-    issue(0, 0);
-    if (nstage > 1) {
-      issue(1, 1);
-      gemm_stage_barrier<DPW>();  // stage 0 has landed
-    } else {
-      gemm_stage_barrier<0>();
-    }
-    int cb = 0;  // buffer of stage s
-    for (int s = 0; s < nstage; s++) {
-      const int ib = cb == 0 ? 2 : cb - 1;  // buffer of stage s + 2 = (s + 2) % 3
-      if (s + 2 < nstage) issue(s + 2, ib);
-      const unsigned char* A = smem + cb * kGemmStage;
-      const unsigned char* Bt = A + kGemmBM * 64;
+    // Fragments of K sub-step ks (16 values) of the stage in ring slots (sa, sb).
+    bf16x8 fa0[MT], fb0[NT], fa1[MT], fb1[NT];
+    auto read = [&](int sa_, int sb_, int ks, bf16x8* fa, bf16x8* fb) {
+      const unsigned char* A = smem + sa_ * SLICE;
+      const unsigned char* Bt = smem + (NA + sb_) * SLICE;
+      const int piece = 2 * ks + (lane >> 5);
 #pragma unroll
-      for (int ks = 0; ks < kGemmBK / 16; ks++) {
-        const int piece = 2 * ks + (lane >> 5);
-        bf16x8 af[MT], bfr[NT];
+      for (int a = 0; a < MT; a++)
+        fa[a] = __builtin_bit_cast(bf16x8, *(const u32x4*)(A + gemm_swz(WR * mw + 32 * a + (lane & 31), piece)));
 #pragma unroll
-        for (int a = 0; a < MT; a++)
-          af[a] = __builtin_bit_cast(bf16x8, *(const u32x4*)(A + gemm_swz(WR * mw + 32 * a + (lane & 31), piece)));
+      for (int t = 0; t < NT; t++)
+        fb[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bt + gemm_swz(WC * nw + 32 * t + (lane & 31), piece)));
+    };
+    auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+      for (int a = 0; a < MT; a++)
 #pragma unroll
         for (int t = 0; t < NT; t++)
-          bfr[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bt + gemm_swz(WC * nw + 32 * t + (lane & 31), piece)));
-#pragma unroll
-        for (int a = 0; a < MT; a++)
-#pragma unroll
-          for (int t = 0; t < NT; t++)
-            acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[t], acc[a][t], 0, 0, 0);
-      }
-      // stage s + 1 due next: with stage s + 2 in flight, DPW loads may stay outstanding
-      if (s + 2 < nstage) gemm_stage_barrier<DPW>();
-      else gemm_stage_barrier<0>();
-      cb = cb == 2 ? 0 : cb + 1;
+          acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[t], acc[a][t], 0, 0, 0);
+    };
+
+    const int pre = min(depth - 1, nstage);
+    for (int st = 0; st < pre; st++) issue(st, st);
+    gemm_stage_barrier_groups<DPW>(pre - 1);  // stage 0 has landed
+    int sa = 0, sb = 0, sm = 0;  // ring slots of stage s (table, residual, this wave's ring)
+    read(0, 0, 0, fa0, fb0);
+    // Each group of fragment reads overlaps the 8 MFMAs of the previous group:
+    // stage s sub-step 1 is read while sub-step 0 computes, and after the barrier
+    // stage s + 1 sub-step 0 is read while stage s sub-step 1 computes.
+    for (int s = 0; s < nstage; s++) {
+      // stage s + depth - 1 goes to the slot stage s - 1 has left
+      if (s + depth - 1 < nstage) issue(s + depth - 1, sm == 0 ? depth - 1 : sm - 1);
+      read(sa, sb, 1, fa1, fb1);
+      mma(fa0, fb0);
+      // stage s + 1 is due next; the stages this wave issued after it may stay in
+      // flight.  The wait also covers this wave's reads of stage s, whose slot the
+      // next iteration refills.
+      gemm_stage_barrier_groups<DPW>(max(0, min(s + depth - 1, nstage - 1) - (s + 1)));
+      sa = sa == NA - 1 ? 0 : sa + 1;
+      sb = sb == NB - 1 ? 0 : sb + 1;
+      sm = sm == depth - 1 ? 0 : sm + 1;
+      if (s + 1 < nstage) read(sa, sb, 0, fa0, fb0);
+      mma(fa1, fb1);
     }
 
     // Epilogue.  Register i of tile (a, t) holds row WR mw + 32 a + 8 (i / 4) +
@@ -232,6 +263,64 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     // a time: the wave rows mw take turns (barrier between), and within a wave
     // the half-waves (lanes l and l + 32 share a column).
     static_assert(NT == 2, "one hi and one lo N-tile per wave");
+    if (vt == 0) {
+      // First tile: the heaps are empty, so each residual row's heap is built by
+      // selection.  In two halves of 64 residual rows the sums pass through LDS
+      // as [256 rows][65]; wave w then takes the k largest keys of columns
+      // w + 8 i (i < 8) in rounds (largest order value left, smallest row holding
+      // it) and stores them in ascending order, a valid min-heap; missing keys
+      // (rows past V) are 0 at the front.
+      static_assert(WN == 4 && WM == 2 && kGemmCols == 128, "tile-0 selection layout");
+      float* Lt = (float*)smem;
+      constexpr int TS = 65;
+#pragma unroll 1
+      for (int half = 0; half < 2; half++) {
+        if ((nw >> 1) == half) {
+#pragma unroll
+          for (int a = 0; a < MT; a++)
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+              Lt[(WR * mw + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * TS + (nw & 1) * 32 + (lane & 31)] =
+                  acc[a][0][i] + acc[a][1][i];
+        }
+        gemm_stage_barrier<0>();
+        uint32_t v[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int r = lane + 64 * q;
+            v[i][q] = v0 + r < V ? score_ord(Lt[r * TS + wv + 8 * i]) : 0u;
+          }
+        for (int t = 0; t < k; t++) {
+          uint32_t M[8], Rw[8];
+#pragma unroll
+          for (int i = 0; i < 8; i++) M[i] = max(max(v[i][0], v[i][1]), max(v[i][2], v[i][3]));
+          wave_minmax_u32_multi<true>(M);
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            uint32_t rq = 0xffffffffu;
+#pragma unroll
+            for (int q = 3; q >= 0; q--) rq = v[i][q] == M[i] ? (uint32_t)(lane + 64 * q) : rq;
+            Rw[i] = rq;
+          }
+          wave_minmax_u32_multi<false>(Rw);
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) v[i][q] = (M[i] != 0u && lane + 64 * q == (int)Rw[i]) ? 0u : v[i][q];
+          }
+          if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+              heaps[(size_t)(64 * half + wv + 8 * i) * k + (k - 1 - t)] =
+                  M[i] != 0u ? ((uint64_t)M[i] << 32) | (uint64_t)(~(uint32_t)(v0 + Rw[i])) : 0ull;
+          }
+        }
+        gemm_stage_barrier<0>();
+      }
+      continue;
+    }
     const int col = nw * (WC / 2) + (lane & 31);
     const bool col_ok = (int64_t)ct * kGemmCols + col < B;
     uint64_t* heap = heaps + (size_t)col * k;
@@ -286,7 +375,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
   }
 }
 
-template <int WM, int WN>
+template <int WM, int WN, int NA, int NB>
 static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs,
                                   uint64_t* cand, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   using C = GemmCfg<WM, WN>;
@@ -296,9 +385,9 @@ static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const
                      (int)t.hidden, p.kpad, C::WC, nrows, (u32x4*)rs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = set_dynamic_lds((const void*)gemm_logits_kernel<WM, WN>, p.lds_bytes)) != hipSuccess) return e;
+  if ((e = set_dynamic_lds((const void*)gemm_logits_kernel<WM, WN, NA, NB>, p.lds_bytes)) != hipSuccess) return e;
   if ((e = record_event(ev0, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_logits_kernel<WM, WN>), dim3((unsigned)p.nblk), dim3(C::THREADS), p.lds_bytes, stream,
+  hipLaunchKernelGGL((gemm_logits_kernel<WM, WN, NA, NB>), dim3((unsigned)p.nblk), dim3(C::THREADS), p.lds_bytes, stream,
                      t.rows, t.V, t.row_bytes, (const uint8_t*)rs, p.kpad, p.batch, p.k, cand, p.nct, p.nvr,
                      p.tiles_per_range);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -307,8 +396,9 @@ static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const
 
 hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs, uint64_t* cand,
                        hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  (void)p.gemm_wn;  // one layout: 2 x 4 waves of 128 x 64 (2 x 2 waves of 128 x 128 would spill)
-  return launch_gemm_cfg<2, 4>(t, p, R, rs, cand, stream, ev0, ev1);
+  // one wave layout: 2 x 4 waves of 128 x 64 (2 x 2 waves of 128 x 128 would spill)
+  if (p.gemm_ring == 34) return launch_gemm_cfg<2, 4, 3, 4>(t, p, R, rs, cand, stream, ev0, ev1);
+  return launch_gemm_cfg<2, 4, 3, 3>(t, p, R, rs, cand, stream, ev0, ev1);
 }
 
 int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
@@ -325,7 +415,10 @@ int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
   p->nvr = (int32_t)nvr;
   p->nblk = (int32_t)(p->nct * nvr);
   p->npass = 1;
-  p->lds_bytes = (size_t)kGemmBuf * kGemmStage + (size_t)kGemmCols * k * 8;
+  // the residual ring one stage deeper when the heaps leave room
+  const size_t heaps = (size_t)kGemmCols * k * 8;
+  p->gemm_ring = 7 * (size_t)kGemmBM * 64 + heaps <= kMaxLds ? 34 : 33;
+  p->lds_bytes = (p->gemm_ring == 34 ? 7 : 6) * (size_t)kGemmBM * 64 + heaps;
   if (p->lds_bytes > kMaxLds) {
     *why = "k too large for the gemm path's LDS heaps";
     return -5;
