@@ -90,8 +90,11 @@ def _ptr(t: torch.Tensor):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _event_handle(ev: torch.cuda.Event, device: torch.device) -> int:
-    """The hipEvent_t behind a torch event (created on first record)."""
+def _event_handle(ev, device: torch.device) -> int:
+    """The hipEvent_t behind a torch event (created on first record), or a raw
+    hipEvent_t handle passed as an int."""
+    if isinstance(ev, int):
+        return ev
     if ev.cuda_event == 0:
         ev.record(torch.cuda.current_stream(device))
     return ev.cuda_event

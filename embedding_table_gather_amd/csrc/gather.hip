@@ -8,9 +8,11 @@
 // Q8_0 rows by sqrt(768).
 //
 // One wavefront per output row.  f32 / bf16 rows are read with 16-byte loads
-// straight into registers; Q8_0 rows (34-byte blocks, so only 2-byte aligned)
-// are staged through the wave's slice of LDS with aligned dword loads and then
-// unpacked.  Stores are 16-byte f32x4, contiguous across the wave.
+// straight into registers; Q8_0 rows (34-byte blocks, so only 2-byte aligned in
+// general) are staged through the wave's slice of LDS with aligned dword loads
+// and then unpacked.  Q8_0 rows whose size is a multiple of 16 bytes take a
+// kernel that stages them with 16-byte loads, two rows per wave.  Stores are
+// 16-byte f32x4, contiguous across the wave.
 //
 // Bit-exactness: dequant is exact in f32 (copy; bf16 widening; int8 * f16 has at
 // most 19 significant bits) and the scale is one f32 multiply, so there is one
@@ -125,6 +127,74 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
   }
 }
 
+// Q8_0 rows whose size is a multiple of 16 bytes (d a multiple of 256, e.g. 768:
+// 816-byte rows) start 16-byte aligned, so a wave stages a row with one 16-byte
+// load per lane.  Each wave gathers kQ8Rows rows, issuing all of their loads
+// before unpacking any, so the loads of both rows are in flight together.
+static constexpr int kQ8Rows = 2;
+static constexpr int kQ8MaxChunks = 128;  // 16-byte chunks per row (row_bytes <= 2 KiB)
+
+template <bool SCALE>
+__global__ void __launch_bounds__(256) gather_q8_aligned_kernel(const uint8_t* __restrict__ table, uint32_t V,
+                                                                int hidden, int64_t row_bytes,
+                                                                const int32_t* __restrict__ ids, int64_t n,
+                                                                float scale, float* __restrict__ out,
+                                                                int32_t* __restrict__ bad) {
+  constexpr int IT = kQ8MaxChunks / 64;
+  __shared__ u32x4 stage[kGatherWaves][kQ8Rows][kQ8MaxChunks];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int64_t r0 = ((int64_t)blockIdx.x * kGatherWaves + wv) * kQ8Rows;
+  if (r0 >= n) return;  // whole wave; the kernel has no block-level barrier
+  const int nch = (int)(row_bytes >> 4);
+  const int n4 = hidden >> 2;
+  uint32_t id[kQ8Rows];
+  u32x4 v[kQ8Rows][IT];
+#pragma unroll
+  for (int r = 0; r < kQ8Rows; r++) {
+    id[r] = r0 + r < n ? (uint32_t)ids[r0 + r] : V;  // past the end: no load, no store
+    const u32x4* src = (const u32x4*)(table + (uint64_t)min(id[r], V - 1) * (uint64_t)row_bytes);
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+      const int c = lane + 64 * it;
+      if (id[r] < V && c < nch) v[r][it] = src[c];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kQ8Rows; r++)
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+      const int c = lane + 64 * it;
+      if (id[r] < V && c < nch) stage[wv][r][c] = v[r][it];
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int r = 0; r < kQ8Rows; r++) {
+    if (r0 + r >= n) break;
+    f32x4* o = (f32x4*)(out + (r0 + r) * (int64_t)hidden);
+    if (id[r] >= V) {
+      for (int c4 = lane; c4 < n4; c4 += 64) o[c4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (lane == 0 && bad != nullptr) atomicAdd(bad, 1);
+      continue;
+    }
+    const uint8_t* wb = (const uint8_t*)stage[wv][r];
+    for (int c4 = lane; c4 < n4; c4 += 64) {
+      const int c = 4 * c4;
+      const int off = 34 * (c >> 5);  // even
+      const float sc = f16_bits_to_f32(*(const uint16_t*)(wb + off));
+      const int qo = off + 2 + (c & 31);
+      const uint32_t q01 = *(const uint16_t*)(wb + qo);
+      const uint32_t q23 = *(const uint16_t*)(wb + qo + 2);
+      f32x4 x = {(float)(int8_t)(q01 & 0xffu) * sc, (float)(int8_t)(q01 >> 8) * sc,
+                 (float)(int8_t)(q23 & 0xffu) * sc, (float)(int8_t)(q23 >> 8) * sc};
+      if (SCALE) x = x * scale;
+      o[c4] = x;
+    }
+  }
+}
+
 template <int DT>
 static hipError_t launch_dt(const TableDesc& t, const int32_t* ids, int64_t n, float scale, float* out,
                             int32_t* bad, hipStream_t stream) {
@@ -134,6 +204,16 @@ static hipError_t launch_dt(const TableDesc& t, const int32_t* ids, int64_t n, f
   int lds_words = 0;
   size_t lds = 0;
   if (DT == DT_Q8_0) {
+    if (t.row_bytes % 16 == 0 && t.row_bytes <= 16 * kQ8MaxChunks) {
+      const dim3 g((unsigned)((n + kGatherWaves * kQ8Rows - 1) / (kGatherWaves * kQ8Rows)));
+      if (sc)
+        hipLaunchKernelGGL((gather_q8_aligned_kernel<true>), g, block, 0, stream, t.rows, (uint32_t)t.V,
+                           (int)t.hidden, t.row_bytes, ids, n, scale, out, bad);
+      else
+        hipLaunchKernelGGL((gather_q8_aligned_kernel<false>), g, block, 0, stream, t.rows, (uint32_t)t.V,
+                           (int)t.hidden, t.row_bytes, ids, n, scale, out, bad);
+      return hipGetLastError();
+    }
     lds_words = (int)((t.row_bytes + 8 + 3) / 4);
     lds = (size_t)kGatherWaves * lds_words * 4;
   }

@@ -99,6 +99,26 @@ __global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restr
 static constexpr int kMergeThreads = 1024;
 static constexpr int kMergeWaves = kMergeThreads / 64;
 
+// One selection round over keys held by a wave (N per lane, 0 = empty): returns
+// the largest key to every lane and removes it.  Keys are unique, so the round
+// takes the largest order value (upper 32 bits) and, among keys holding it, the
+// largest lower word (~id, so the smallest id); both are 32-bit DPP reductions.
+template <int N>
+__device__ __forceinline__ uint64_t wave_pop_max(uint64_t (&key)[N]) {
+  uint32_t hi = 0;
+#pragma unroll
+  for (int j = 0; j < N; j++) hi = max(hi, (uint32_t)(key[j] >> 32));
+  hi = wave_minmax_u32<true>(hi);
+  uint32_t lo = 0;
+#pragma unroll
+  for (int j = 0; j < N; j++) lo = (uint32_t)(key[j] >> 32) == hi ? max(lo, (uint32_t)key[j]) : lo;
+  lo = wave_minmax_u32<true>(lo);
+  const uint64_t best = ((uint64_t)hi << 32) | lo;
+#pragma unroll
+  for (int j = 0; j < N; j++) key[j] = key[j] == best ? 0 : key[j];
+  return best;
+}
+
 template <int KPT>
 __global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __restrict__ cand, int n, int k,
                                                           int32_t* __restrict__ ids, float* __restrict__ scores) {
@@ -112,14 +132,10 @@ __global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __rest
     const int i = tid + j * kMergeThreads;
     key[j] = i < n ? c[i] : 0;
   }
-  uint64_t prev = ~0ull;
+  // each wave's k best, then wave 0 merges the kMergeWaves lists
   for (int t = 0; t < k; t++) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; j++) best = (key[j] < prev && key[j] > best) ? key[j] : best;
-    best = wave_max_u64(best);
+    const uint64_t best = wave_pop_max(key);
     if (lane == 0) part[wv * k + t] = best;
-    prev = best;
   }
   __syncthreads();
   if (wv == 0) {
@@ -130,17 +146,12 @@ __global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __rest
       const int i = lane + 64 * j;
       key2[j] = i < kMergeWaves * k ? part[i] : 0;
     }
-    prev = ~0ull;
     for (int t = 0; t < k; t++) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int j = 0; j < kMergeWaves; j++) best = (key2[j] < prev && key2[j] > best) ? key2[j] : best;
-      best = wave_max_u64(best);
+      const uint64_t best = wave_pop_max(key2);
       if (lane == 0) {
         ids[b * k + t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
         scores[b * k + t] = ord_score((uint32_t)(best >> 32));
       }
-      prev = best;
     }
   }
 }

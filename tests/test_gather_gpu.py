@@ -78,8 +78,11 @@ def test_gather_special_values_bit_exact():
             assert np.array_equal(bits(out), bits(ref)), (dt, scaled)
 
 
-def test_gather_bad_ids_zero_and_count():
-    V, d = 500, 96
+# d = 96: 102-byte rows (2-byte aligned path); d = 256: 272-byte rows (16-byte
+# aligned path, two rows per wave, 7 ids so the last wave has one)
+@pytest.mark.parametrize("d", [96, 256])
+def test_gather_bad_ids_zero_and_count(d):
+    V = 500
     host = synth.make_table(Q8_0, V, d, seed=7)
     ids = np.array([3, -1, 500, 2 ** 31 - 1, 499, -(2 ** 31), 0], np.int32)
     t = table(host, Q8_0, V, d)
