@@ -8,6 +8,8 @@ fallback: if the library is missing, every call raises.
     t = Table(rows, BF16, vocab, hidden)          # rows: device tensor, borrowed
     x = t.embed_gather(ids)                       # ADR-0008 "POST /v1/embed"
     ids, scores = t.logits_topk(residual, k=10)   # ADR-0008 "POST /v1/logits"
+    ids, scores, probs = t.logits_topk_probs(residual, k=10, temperature=1.0)
+    logits = t.logits_raw(residual)               # raw logits mode, [B, vocab]
 """
 from __future__ import annotations
 
@@ -41,6 +43,9 @@ SIGNATURES = {
     "etg_logits_topk_ex": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP]),
     "etg_logits_topk_profiled": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP, _VP,
                                         _VP]),
+    "etg_logits_topk_probs": (_I32, [_VP, _VP, _I64, _I32, _F, _VP, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP]),
+    "etg_logits_raw_workspace": (_I64, [_VP, _I64, _I32]),
+    "etg_logits_raw": (_I32, [_VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _I32, _VP]),
     "etg_last_error": (ctypes.c_char_p, []),
 }
 
@@ -208,6 +213,48 @@ class Table:
                                                   _ptr(workspace), workspace.numel(), int(path), ev0, ev1,
                                                   _stream_ptr(self.device)))
         return out_ids, out_scores
+
+    def _residual(self, residual: torch.Tensor) -> torch.Tensor:
+        if residual.dtype != torch.float32 or residual.device != self.device:
+            raise ValueError("residual must be a float32 tensor on the table's device")
+        return residual.contiguous().view(-1, self.hidden)
+
+    def logits_topk_probs(self, residual: torch.Tensor, k: int, temperature: float = 1.0,
+                          path: int = PATH_AUTO, workspace: torch.Tensor | None = None):
+        """Top-k (ids int32 [B, k], logits f32 [B, k], probabilities f32 [B, k]); the
+        probabilities are the softmax of logits / temperature over the whole vocabulary."""
+        R = self._residual(residual)
+        B = R.shape[0]
+        if workspace is None:
+            workspace = self.workspace(B, k, path)
+        ids = torch.empty((B, k), dtype=torch.int32, device=self.device)
+        scores = torch.empty((B, k), dtype=torch.float32, device=self.device)
+        probs = torch.empty((B, k), dtype=torch.float32, device=self.device)
+        with torch.cuda.device(self.device):
+            _check(lib().etg_logits_topk_probs(self._h, _ptr(R), B, int(k), float(temperature), _ptr(ids),
+                                               _ptr(scores), _ptr(probs), _ptr(workspace), workspace.numel(),
+                                               int(path), _stream_ptr(self.device)))
+        return ids, scores, probs
+
+    def logits_raw(self, residual: torch.Tensor, path: int = PATH_AUTO, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+        """Raw logits mode: f32 [B, vocab] = residual @ table.T."""
+        R = self._residual(residual)
+        B = R.shape[0]
+        if workspace is None:
+            n = int(lib().etg_logits_raw_workspace(self._h, B, int(path)))
+            if n < 0:
+                _check(n)
+            workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        if out is None:
+            out = torch.empty((B, self.vocab), dtype=torch.float32, device=self.device)
+        elif out.dtype != torch.float32 or out.device != self.device or out.shape != (B, self.vocab) \
+                or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 [batch, vocab] tensor on the table's device")
+        with torch.cuda.device(self.device):
+            _check(lib().etg_logits_raw(self._h, _ptr(R), B, _ptr(out), _ptr(workspace), workspace.numel(),
+                                        int(path), _stream_ptr(self.device)))
+        return out
 
 
 def embed_gather(table: Table, ids: torch.Tensor, scale=None, **kw) -> torch.Tensor:

@@ -137,17 +137,32 @@ int64_t etg_logits_topk_workspace(const etg_table* t, int64_t batch, int32_t k) 
   return etg_logits_topk_workspace_ex(t, batch, k, ETG_PATH_AUTO);
 }
 
-int32_t etg_logits_topk_profiled(const etg_table* t, const float* d_residual, int64_t batch, int32_t k,
-                                 int32_t* d_topk_ids, float* d_topk_scores, void* d_workspace,
-                                 size_t workspace_bytes, int32_t path, void* event_before, void* event_after,
-                                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the logits entry points: argument checks, plan, launch.
+// ids == nullptr selects the raw logits mode (k = 1 internally, no merge).
+int32_t run_logits(const etg_table* t, const float* d_residual, int64_t batch, int32_t k, int32_t* d_topk_ids,
+                   float* d_topk_scores, float* d_topk_probs, float temperature, float* d_logits,
+                   void* d_workspace, size_t workspace_bytes, int32_t path, void* event_before, void* event_after,
+                   void* stream) {
   int32_t st = check_logits_args(t, batch, k);
   if (st != ETG_OK) return st;
-  if (d_residual == nullptr || d_topk_ids == nullptr || d_topk_scores == nullptr || d_workspace == nullptr)
+  const bool raw = d_topk_ids == nullptr;
+  if (d_residual == nullptr || d_workspace == nullptr || (raw ? d_logits == nullptr : d_topk_scores == nullptr))
     return fail(ETG_EINVAL, "a residual, output or workspace pointer is NULL");
-  if (!aligned(d_residual, 4) || !aligned(d_topk_ids, 4) || !aligned(d_topk_scores, 4))
+  if (!aligned(d_residual, 4) || (!raw && (!aligned(d_topk_ids, 4) || !aligned(d_topk_scores, 4))) ||
+      !aligned(d_topk_probs, 4) || !aligned(d_logits, 4))
     return fail(ETG_EALIGN, "residual and output pointers must be 4-byte aligned");
   if (!aligned(d_workspace, 256)) return fail(ETG_EALIGN, "workspace pointer is not 256-byte aligned");
+  float lse_scale = 0.f;
+  if (d_topk_probs != nullptr) {
+    // c = log2(e) / T must be a finite positive float
+    lse_scale = (float)(1.4426950408889634 / (double)temperature);
+    if (!(temperature > 0.f) || !std::isfinite(temperature) || !std::isfinite(lse_scale) || !(lse_scale > 0.f))
+      return fail(ETG_ERANGE, "temperature %g is not a finite value in [1e-37, 3.4e38]", (double)temperature);
+  }
   etg::LogitsPlan p;
   const char* why = "";
   st = etg::plan_logits(t->d, batch, k, path, &p, &why);
@@ -155,9 +170,42 @@ int32_t etg_logits_topk_profiled(const etg_table* t, const float* d_residual, in
   if (workspace_bytes < p.ws_bytes)
     return fail(ETG_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.ws_bytes);
   hipError_t e = etg::launch_logits_topk(t->d, p, d_residual, d_topk_ids, d_topk_scores, d_workspace,
-                                         (hipStream_t)stream, (hipEvent_t)event_before, (hipEvent_t)event_after);
+                                         (hipStream_t)stream, (hipEvent_t)event_before, (hipEvent_t)event_after,
+                                         d_logits, d_topk_probs, lse_scale);
   if (e != hipSuccess) return fail(ETG_EHIP, "logits launch failed: %s", hipGetErrorString(e));
   return ETG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t etg_logits_topk_profiled(const etg_table* t, const float* d_residual, int64_t batch, int32_t k,
+                                 int32_t* d_topk_ids, float* d_topk_scores, void* d_workspace,
+                                 size_t workspace_bytes, int32_t path, void* event_before, void* event_after,
+                                 void* stream) {
+  if (d_topk_ids == nullptr) return fail(ETG_EINVAL, "ids pointer is NULL");
+  return run_logits(t, d_residual, batch, k, d_topk_ids, d_topk_scores, nullptr, 0.f, nullptr, d_workspace,
+                    workspace_bytes, path, event_before, event_after, stream);
+}
+
+int32_t etg_logits_topk_probs(const etg_table* t, const float* d_residual, int64_t batch, int32_t k,
+                              float temperature, int32_t* d_topk_ids, float* d_topk_scores, float* d_topk_probs,
+                              void* d_workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  if (d_topk_ids == nullptr || d_topk_probs == nullptr) return fail(ETG_EINVAL, "ids or probs pointer is NULL");
+  return run_logits(t, d_residual, batch, k, d_topk_ids, d_topk_scores, d_topk_probs, temperature, nullptr,
+                    d_workspace, workspace_bytes, path, nullptr, nullptr, stream);
+}
+
+int64_t etg_logits_raw_workspace(const etg_table* t, int64_t batch, int32_t path) {
+  return etg_logits_topk_workspace_ex(t, batch, 1, path);
+}
+
+int32_t etg_logits_raw(const etg_table* t, const float* d_residual, int64_t batch, float* d_logits,
+                       void* d_workspace, size_t workspace_bytes, int32_t path, void* stream) {
+  if (d_logits == nullptr) return fail(ETG_EINVAL, "logits pointer is NULL");
+  return run_logits(t, d_residual, batch, 1, nullptr, nullptr, nullptr, 0.f, d_logits, d_workspace,
+                    workspace_bytes, path, nullptr, nullptr, stream);
 }
 
 int32_t etg_logits_topk_ex(const etg_table* t, const float* d_residual, int64_t batch, int32_t k,

@@ -102,6 +102,39 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Log-partition partials for probabilities at temperature T, c = log2(e) / T.
+// A set of logits x is summarised as (m, s) = (max x, sum exp2((x - m) c)), so
+// that ln sum exp(x / T) = (m c + log2 s) ln 2; the empty set is (-inf, 0).
+// Every term is <= 1 and the largest is exactly 1, so s never overflows.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float2 lse_combine(float2 a, float2 b, float c) {
+  const float m = fmaxf(a.x, b.x);
+  if (m == -__builtin_inff()) return a;  // both empty
+  // an empty side contributes 0 * exp2(-inf) = 0
+  return make_float2(m, a.y * exp2f((a.x - m) * c) + b.y * exp2f((b.x - m) * c));
+}
+
+// (m, s) over the wave of the values x[j] with ok[j], every lane getting the result.
+template <int N>
+__device__ __forceinline__ float2 wave_lse_part(const float (&x)[N], const bool (&ok)[N], float c) {
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < N; j++) m = ok[j] ? fmaxf(m, x[j]) : m;
+  m = wave_max_f32(m);
+  if (m == -__builtin_inff()) return make_float2(m, 0.f);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < N; j++) s += ok[j] ? exp2f((x[j] - m) * c) : 0.f;
+  return make_float2(m, wave_sum(s));
+}
+
 // float32 -> bfloat16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -48,8 +48,25 @@ struct LogitsPlan {
   size_t lds_bytes;      // dynamic LDS of the main kernel
   size_t img_offset, img_bytes;    // bf16 residual operand (gemm and wide paths)
   size_t cand_offset, cand_bytes;  // u64 keys [batch][nblk][k]
-  size_t aux_offset, aux_bytes;    // wide path: u64 top-k lower bound per residual row
+  size_t aux_offset, aux_bytes;    // wide path: u64 top-k lower bound per residual row;
+                                   // gemm path: per-thread running log-partition partials
+  int32_t nparts;                  // log-partition partials per residual row (= ncand / k)
+  size_t lse_offset, lse_bytes;    // float2 partials [batch][nparts]
   size_t ws_bytes;
+};
+
+// Optional outputs of a logits call besides the top-k.
+//  logits     [batch][V] f32 raw logits, the same values the top-k ranks (nullable)
+//  lse        [batch][nparts] log-partition partials (m, s) of each block's
+//             vocabulary slice: m = max logit, s = sum exp2((logit - m) lse_scale)
+//             (nullable; (-inf, 0) for a slice with no rows)
+//  lse_scale  log2(e) / temperature
+//  aux        the plan's aux area of the workspace
+struct LogitsExtras {
+  float* logits = nullptr;
+  float2* lse = nullptr;
+  float lse_scale = 0.f;
+  void* aux = nullptr;
 };
 
 // Returns 0 or a negative etg_status; fills *plan.  `why` receives a short reason.
@@ -60,9 +77,13 @@ hipError_t launch_gather(const TableDesc& t, const int32_t* ids, int64_t n, floa
                          float* out, int32_t* bad, hipStream_t stream);
 
 // ev_before / ev_after (nullable) are recorded around the table-streaming kernel.
+// With want_logits the raw logits go to `logits`; with `probs` (nullable) the
+// merge also writes the softmax probabilities at log2(e) / lse_scale temperature;
+// with ids == nullptr only the table kernel runs (raw logits mode).
 hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const float* R,
                               int32_t* ids, float* scores, void* ws, hipStream_t stream,
-                              hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr);
+                              hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr,
+                              float* logits = nullptr, float* probs = nullptr, float lse_scale = 0.f);
 
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kTargetBlocks = 256;  // one workgroup per MI355X compute unit
@@ -87,10 +108,10 @@ int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p,
 int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
-                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+                         const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* img, uint64_t* cand,
-                       uint64_t* thr, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+                       uint64_t* thr, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs, uint64_t* cand,
-                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+                       const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace etg

@@ -142,12 +142,18 @@ __device__ __forceinline__ void heap_replace_root(uint64_t* h, int k, uint64_t k
 //  table  bf16 [V][hidden], row_bytes = 2 hidden (a multiple of 16)
 //  Rs     split residual rows [nct][256][kpad] (gemm_prep_kernel), kpad = hidden
 //         rounded up to 32
+//  logits  nullable [B][V]: raw logits
+//  lse     nullable [B][nvr]: log-partition partial of each vocabulary range at
+//          lse_c = log2(e) / temperature
+//  lse_run [gridDim.x][64 WM WN]: each thread's running partial over the tiles
+//          of its range (kept in memory, not in registers, across the K loops)
 // Table rows past V are read from row V - 1 and never ranked; table bytes past
 // the row end are read from the row's last 16 bytes and meet zero residual values.
 template <int WM, int WN, int NA, int NB>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, const uint8_t* __restrict__ Rs, int kpad,
-    int64_t B, int k, uint64_t* __restrict__ cand, int nct, int nvr, int tiles_per_range) {
+    int64_t B, int k, uint64_t* __restrict__ cand, int nct, int nvr, int tiles_per_range,
+    float* __restrict__ logits, float2* __restrict__ lse, float lse_c, float2* __restrict__ lse_run) {
   using C = GemmCfg<WM, WN>;
   constexpr int MT = C::MT, NT = C::NT, WR = C::WR, WC = C::WC, DPW = C::DPW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -254,6 +260,52 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
       mma(fa1, fb1);
     }
 
+    // Raw logits and the log-partition partial (register layout below; rows
+    // as 32-bit offsets in the tile, stores at constant offsets from one base).
+    if (logits != nullptr || lse != nullptr) {
+      // an opaque copy of the thread index: the addresses below are recomputed
+      // per tile instead of being hoisted out of the tile loop (no free registers
+      // to keep them in across the K loop)
+      int xt = tid;
+      asm volatile("" : "+v"(xt));
+      const int xl = xt & 63;
+      const int64_t bx = (int64_t)ct * kGemmCols + nw * (WC / 2) + (xl & 31);
+      const int rbase = WR * mw + 4 * (xl >> 5);
+      const int vlim = (int)min((int64_t)kGemmBM, V - v0) - rbase;  // tile rows past rbase
+      if (bx < B) {
+        if (logits != nullptr) {
+          float* lp = logits + bx * V + v0 + rbase;
+#pragma unroll
+          for (int a = 0; a < MT; a++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+              const int r = 32 * a + 8 * (i >> 2) + (i & 3);
+              if (r < vlim) lp[r] = acc[a][0][i] + acc[a][1][i];
+            }
+        }
+        if (lse != nullptr) {
+          float2* run_slot = lse_run + (size_t)id * C::THREADS + xt;
+          float2 run = vt == 0 ? make_float2(-__builtin_inff(), 0.f) : *run_slot;
+          float tm = -__builtin_inff();
+#pragma unroll
+          for (int a = 0; a < MT; a++)
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+              tm = 32 * a + 8 * (i >> 2) + (i & 3) < vlim ? fmaxf(tm, acc[a][0][i] + acc[a][1][i]) : tm;
+          if (tm > -__builtin_inff()) {
+            const float m = fmaxf(run.x, tm);
+            float sum = run.y * exp2f((run.x - m) * lse_c);  // 0 while nothing was seen
+#pragma unroll
+            for (int a = 0; a < MT; a++)
+#pragma unroll
+              for (int i = 0; i < 16; i++)
+                sum += 32 * a + 8 * (i >> 2) + (i & 3) < vlim ? exp2f((acc[a][0][i] + acc[a][1][i] - m) * lse_c) : 0.f;
+            run = make_float2(m, sum);
+          }
+          *run_slot = run;
+        }
+      }
+    }
     // Epilogue.  Register i of tile (a, t) holds row WR mw + 32 a + 8 (i / 4) +
     // 4 (lane / 32) + i % 4 of split column WC nw + 32 t + lane % 32; with NT = 2
     // a lane sees 64 rows of one residual row.  Each lane marks its hi + lo sums
@@ -364,7 +416,24 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
       gemm_stage_barrier<0>();
     }
   }
-  // heaps -> candidates [B][nvr][k]
+  if (lse != nullptr) {
+    // lanes l and l + 32 hold the same residual row, then the WM = 2 wave rows
+    // (the stage ring is free after the last tile's barrier)
+    static_assert(WM == 2, "two wave rows");
+    // a thread's slot holds its partial once the range's first tile ran
+    const bool mine = (int64_t)vr * tiles_per_range * kGemmBM < V &&
+                      (int64_t)ct * kGemmCols + nw * (WC / 2) + (lane & 31) < B;
+    float2 run = mine ? lse_run[(size_t)id * C::THREADS + tid] : make_float2(-__builtin_inff(), 0.f);
+    run = lse_combine(run, make_float2(__shfl_xor(run.x, 32, 64), __shfl_xor(run.y, 32, 64)), lse_c);
+    float2* xl = (float2*)smem;  // [WN][32]
+    if (mw == 1 && lane < 32) xl[nw * 32 + lane] = run;
+    gemm_stage_barrier<0>();
+    const int64_t b = (int64_t)ct * kGemmCols + nw * (WC / 2) + lane;
+    if (mw == 0 && lane < 32 && b < B) lse[b * nvr + vr] = lse_combine(run, xl[nw * 32 + lane], lse_c);
+  }
+  // heaps -> candidates [B][nvr][k]; the barrier orders the heap writes (also
+  // the zeroing, for a range past the table that ran no tile) before the reads
+  gemm_stage_barrier<0>();
   if (tid < kGemmCols) {
     const int64_t b = (int64_t)ct * kGemmCols + tid;
     if (b < B) {
@@ -377,7 +446,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
 
 template <int WM, int WN, int NA, int NB>
 static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs,
-                                  uint64_t* cand, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                                  uint64_t* cand, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0,
+                                  hipEvent_t ev1) {
   using C = GemmCfg<WM, WN>;
   const int64_t nrows = (int64_t)p.nct * kGemmBN;
   const int64_t nprep = nrows * (p.kpad / 8);
@@ -389,16 +459,16 @@ static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const
   if ((e = record_event(ev0, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((gemm_logits_kernel<WM, WN, NA, NB>), dim3((unsigned)p.nblk), dim3(C::THREADS), p.lds_bytes, stream,
                      t.rows, t.V, t.row_bytes, (const uint8_t*)rs, p.kpad, p.batch, p.k, cand, p.nct, p.nvr,
-                     p.tiles_per_range);
+                     p.tiles_per_range, x.logits, x.lse, x.lse_scale, (float2*)x.aux);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev1, stream);
 }
 
 hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs, uint64_t* cand,
-                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                       const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   // one wave layout: 2 x 4 waves of 128 x 64 (2 x 2 waves of 128 x 128 would spill)
-  if (p.gemm_ring == 34) return launch_gemm_cfg<2, 4, 3, 4>(t, p, R, rs, cand, stream, ev0, ev1);
-  return launch_gemm_cfg<2, 4, 3, 3>(t, p, R, rs, cand, stream, ev0, ev1);
+  if (p.gemm_ring == 34) return launch_gemm_cfg<2, 4, 3, 4>(t, p, R, rs, cand, x, stream, ev0, ev1);
+  return launch_gemm_cfg<2, 4, 3, 3>(t, p, R, rs, cand, x, stream, ev0, ev1);
 }
 
 int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
@@ -425,6 +495,7 @@ int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
   }
   p->img_bytes = (size_t)p->nct * kGemmBN * p->kpad * 2;
   p->ncand = (int32_t)(nvr * k);
+  p->aux_bytes = (size_t)p->nblk * 64 * 8 * 8;  // running log-partition partial per thread
   return 0;
 }
 

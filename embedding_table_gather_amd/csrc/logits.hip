@@ -43,11 +43,14 @@ __device__ __forceinline__ float deq_value(const uint8_t* row, int c) {
   }
 }
 
+// logits (nullable [B][V]) receives the raw logits, lse (nullable [B][nblk]) the
+// log-partition partial of the block's rows at lse_c = log2(e) / temperature.
 template <int DT, int RB>
 __global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restrict__ table, int64_t V,
                                                           int64_t row_bytes, int hidden,
                                                           const float* __restrict__ R, int64_t B, int k,
-                                                          uint64_t* __restrict__ cand) {
+                                                          uint64_t* __restrict__ cand, float* __restrict__ logits,
+                                                          float2* __restrict__ lse, float lse_c) {
   extern __shared__ float vlog[];  // [rows of this block][RB]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t nblk = gridDim.x;
@@ -74,6 +77,18 @@ __global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restr
   }
   __syncthreads();
   for (int b = wv; b < nb; b += 4) {
+    if (logits != nullptr)
+      for (int i = lane; i < nrows; i += 64) logits[(b0 + b) * V + r_begin + i] = vlog[i * RB + b];
+    if (lse != nullptr) {
+      float m = -__builtin_inff();
+      for (int i = lane; i < nrows; i += 64) m = fmaxf(m, vlog[i * RB + b]);
+      m = wave_max_f32(m);
+      float sum = 0.f;
+      if (m > -__builtin_inff())
+        for (int i = lane; i < nrows; i += 64) sum += exp2f((vlog[i * RB + b] - m) * lse_c);
+      sum = wave_sum(sum);
+      if (lane == 0) lse[(b0 + b) * nblk + blockIdx.x] = make_float2(m, sum);
+    }
     uint64_t* out = cand + ((b0 + b) * nblk + blockIdx.x) * (int64_t)k;
     uint64_t prev = ~0ull;
     for (int t = 0; t < k; t++) {
@@ -119,12 +134,41 @@ __device__ __forceinline__ uint64_t wave_pop_max(uint64_t (&key)[N]) {
   return best;
 }
 
+// Log-partition of one residual row from its n partials (m_i, s_i), returned to
+// every thread as (M, log2 S), S = sum_i s_i exp2((m_i - M) c).  Each thread
+// combines a strided subset, each wave reduces (max, then rescaled sum) and
+// every thread combines the kMergeWaves wave results in the same order.
+__device__ float2 block_log_partition(const float2* __restrict__ part, int n, float c, float2* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  float2 a = make_float2(-__builtin_inff(), 0.f);
+  for (int i = tid; i < n; i += kMergeThreads) a = lse_combine(a, part[i], c);
+  const float m = wave_max_f32(a.x);
+  const float s = wave_sum(m > -__builtin_inff() ? a.y * exp2f((a.x - m) * c) : 0.f);
+  if (lane == 0) red[wv] = make_float2(m, s);
+  __syncthreads();
+  float2 r = red[0];
+  for (int w = 1; w < kMergeWaves; w++) r = lse_combine(r, red[w], c);
+  return make_float2(r.x, log2f(r.y));
+}
+
+// prob = exp(score / T - lse) with lse = (M c + log2 S) ln 2, computed as
+// exp2((score - M) c - log2 S).
+__device__ __forceinline__ float prob_of(float score, float2 ml, float c) {
+  return exp2f((score - ml.x) * c - ml.y);
+}
+
+// probs (nullable [B][k]): probabilities of the selected ids from the partials
+// lse [B][nparts] at c = log2(e) / temperature.
 template <int KPT>
 __global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __restrict__ cand, int n, int k,
-                                                          int32_t* __restrict__ ids, float* __restrict__ scores) {
+                                                          int32_t* __restrict__ ids, float* __restrict__ scores,
+                                                          const float2* __restrict__ lse, int nparts, float lc,
+                                                          float* __restrict__ probs) {
   __shared__ uint64_t part[kMergeWaves * 64];
+  __shared__ float2 red[kMergeWaves];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t b = blockIdx.x;
+  const float2 ml = probs != nullptr ? block_log_partition(lse + b * nparts, nparts, lc, red) : float2{};
   const uint64_t* c = cand + b * (int64_t)n;
   uint64_t key[KPT];
 #pragma unroll
@@ -149,8 +193,10 @@ __global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __rest
     for (int t = 0; t < k; t++) {
       const uint64_t best = wave_pop_max(key2);
       if (lane == 0) {
+        const float sc = ord_score((uint32_t)(best >> 32));
         ids[b * k + t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
-        scores[b * k + t] = ord_score((uint32_t)(best >> 32));
+        scores[b * k + t] = sc;
+        if (probs != nullptr) probs[b * k + t] = prob_of(sc, ml, lc);
       }
     }
   }
@@ -158,10 +204,14 @@ __global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __rest
 
 // Same, for more keys than fit in registers: every round rescans global memory.
 __global__ void __launch_bounds__(1024) topk_merge_wide_kernel(const uint64_t* __restrict__ cand, int n, int k,
-                                                               int32_t* __restrict__ ids, float* __restrict__ scores) {
+                                                               int32_t* __restrict__ ids, float* __restrict__ scores,
+                                                               const float2* __restrict__ lse, int nparts, float lc,
+                                                               float* __restrict__ probs) {
   __shared__ uint64_t red[2][kMergeWaves];
+  __shared__ float2 lred[kMergeWaves];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t b = blockIdx.x;
+  const float2 ml = probs != nullptr ? block_log_partition(lse + b * nparts, nparts, lc, lred) : float2{};
   const uint64_t* c = cand + b * (int64_t)n;
   uint64_t prev = ~0ull;
   for (int t = 0; t < k; t++) {
@@ -176,23 +226,28 @@ __global__ void __launch_bounds__(1024) topk_merge_wide_kernel(const uint64_t* _
     uint64_t m = red[t & 1][0];
     for (int w = 1; w < kMergeWaves; w++) m = red[t & 1][w] > m ? red[t & 1][w] : m;
     if (tid == 0) {
+      const float sc = ord_score((uint32_t)(m >> 32));
       ids[b * k + t] = (int32_t)(~(uint32_t)(m & 0xffffffffu));
-      scores[b * k + t] = ord_score((uint32_t)(m >> 32));
+      scores[b * k + t] = sc;
+      if (probs != nullptr) probs[b * k + t] = prob_of(sc, ml, lc);
     }
     prev = m;
   }
 }
 
 static hipError_t launch_merge(const uint64_t* cand, int64_t batch, int n, int k, int32_t* ids, float* scores,
-                               hipStream_t stream) {
+                               const float2* lse, int nparts, float c, float* probs, hipStream_t stream) {
   const dim3 grid((unsigned)batch), block(kMergeThreads);
   const int kpt = (n + kMergeThreads - 1) / kMergeThreads;
-#define ETG_MERGE_CASE(KV) \
-  if (kpt <= KV) { hipLaunchKernelGGL((topk_merge_kernel<KV>), grid, block, 0, stream, cand, n, k, ids, scores); }
+#define ETG_MERGE_CASE(KV)                                                                                     \
+  if (kpt <= KV) {                                                                                             \
+    hipLaunchKernelGGL((topk_merge_kernel<KV>), grid, block, 0, stream, cand, n, k, ids, scores, lse, nparts, c, \
+                       probs);                                                                                 \
+  }
   ETG_MERGE_CASE(1)
   else ETG_MERGE_CASE(2) else ETG_MERGE_CASE(4) else ETG_MERGE_CASE(8) else ETG_MERGE_CASE(16)
   else ETG_MERGE_CASE(32) else hipLaunchKernelGGL(topk_merge_wide_kernel, grid, block, 0, stream, cand, n, k, ids,
-                                                   scores);
+                                                   scores, lse, nparts, c, probs);
 #undef ETG_MERGE_CASE
   return hipGetLastError();
 }
@@ -200,7 +255,7 @@ static hipError_t launch_merge(const uint64_t* cand, int64_t batch, int n, int k
 
 template <int DT>
 static hipError_t launch_valu(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
-                              hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                              const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const dim3 grid((unsigned)p.nblk, (unsigned)p.npass), block(256);
   hipError_t e = set_dynamic_lds((const void*)valu_logits_kernel<DT, 1>, p.lds_bytes);
   if (e == hipSuccess) e = set_dynamic_lds((const void*)valu_logits_kernel<DT, 2>, p.lds_bytes);
@@ -212,7 +267,7 @@ static hipError_t launch_valu(const TableDesc& t, const LogitsPlan& p, const flo
 #define ETG_VALU_CASE(RBV)                                                                          \
   case RBV:                                                                                         \
     hipLaunchKernelGGL((valu_logits_kernel<DT, RBV>), grid, block, p.lds_bytes, stream, t.rows, t.V, \
-                       t.row_bytes, (int)t.hidden, R, p.batch, p.k, cand);                          \
+                       t.row_bytes, (int)t.hidden, R, p.batch, p.k, cand, x.logits, x.lse, x.lse_scale);  \
     break;
     ETG_VALU_CASE(1)
     ETG_VALU_CASE(2)
@@ -226,25 +281,31 @@ static hipError_t launch_valu(const TableDesc& t, const LogitsPlan& p, const flo
 }
 
 hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const float* R, int32_t* ids,
-                              float* scores, void* ws, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                              float* scores, void* ws, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
+                              float* logits, float* probs, float lse_scale) {
   uint8_t* base = (uint8_t*)ws;
   uint64_t* cand = (uint64_t*)(base + p.cand_offset);
+  LogitsExtras x;
+  x.logits = logits;
+  x.lse = probs != nullptr ? (float2*)(base + p.lse_offset) : nullptr;
+  x.lse_scale = lse_scale;
+  x.aux = base + p.aux_offset;
   hipError_t e;
   if (p.path == 2) {
-    e = launch_stream(t, p, R, cand, stream, ev0, ev1);
+    e = launch_stream(t, p, R, cand, x, stream, ev0, ev1);
   } else if (p.path == 3) {
-    e = launch_gemm(t, p, R, base + p.img_offset, cand, stream, ev0, ev1);
+    e = launch_gemm(t, p, R, base + p.img_offset, cand, x, stream, ev0, ev1);
   } else if (p.path == 4) {
-    e = launch_wide(t, p, R, base + p.img_offset, cand, (uint64_t*)(base + p.aux_offset), stream, ev0, ev1);
+    e = launch_wide(t, p, R, base + p.img_offset, cand, (uint64_t*)(base + p.aux_offset), x, stream, ev0, ev1);
   } else {
     switch (t.dtype) {
-      case DT_F32: e = launch_valu<DT_F32>(t, p, R, cand, stream, ev0, ev1); break;
-      case DT_BF16: e = launch_valu<DT_BF16>(t, p, R, cand, stream, ev0, ev1); break;
-      default: e = launch_valu<DT_Q8_0>(t, p, R, cand, stream, ev0, ev1); break;
+      case DT_F32: e = launch_valu<DT_F32>(t, p, R, cand, x, stream, ev0, ev1); break;
+      case DT_BF16: e = launch_valu<DT_BF16>(t, p, R, cand, x, stream, ev0, ev1); break;
+      default: e = launch_valu<DT_Q8_0>(t, p, R, cand, x, stream, ev0, ev1); break;
     }
   }
-  if (e != hipSuccess) return e;
-  return launch_merge(cand, p.batch, p.ncand, p.k, ids, scores, stream);
+  if (e != hipSuccess || ids == nullptr) return e;
+  return launch_merge(cand, p.batch, p.ncand, p.k, ids, scores, x.lse, p.nparts, lse_scale, probs, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -292,7 +353,10 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
   p->cand_offset = align_up(p->img_bytes, 256);
   p->cand_bytes = (size_t)batch * p->ncand * 8;
   p->aux_offset = align_up(p->cand_offset + p->cand_bytes, 256);
-  p->ws_bytes = align_up(p->aux_offset + p->aux_bytes, 256);
+  p->nparts = p->ncand / k;
+  p->lse_offset = align_up(p->aux_offset + p->aux_bytes, 256);
+  p->lse_bytes = (size_t)batch * p->nparts * 8;
+  p->ws_bytes = align_up(p->lse_offset + p->lse_bytes, 256);
   return 0;
 }
 

@@ -121,6 +121,9 @@ __device__ void stream_block_topk(const float* slog, const int64_t* sg0, const i
 //  R          fp32 [B][hidden]
 //  steps      64-value K steps, ceil(hidden / 64)
 //  chunk      K steps staged in LDS at a time (a multiple of the unroll)
+//  logits     nullable [B][V]: the block's raw logits
+//  lse        nullable [B][gridDim.x]: log-partition partial of the block's rows
+//             at lse_c = log2(e) / temperature
 // Out-of-range rows and K positions are read from clamped in-range addresses and
 // meet zero residual values or are never ranked, so no load is predicated (table
 // entries are assumed finite).
@@ -128,7 +131,7 @@ template <int NIMG>
 __global__ void __launch_bounds__(1024) stream_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden,
     const float* __restrict__ R, int64_t B, int steps, int chunk, int k, uint64_t* __restrict__ cand,
-    int64_t ngroups, int max_groups) {
+    int64_t ngroups, int max_groups, float* __restrict__ logits, float2* __restrict__ lse, float lse_c) {
   constexpr int NBC = NIMG == 1 ? 4 : 8;
   constexpr int U = NIMG == 1 ? kStreamUnroll : kStreamUnroll / 2;
   const int steps_full = hidden / 64;
@@ -225,30 +228,54 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
   }
   __syncthreads();
 
+  // raw logits: each wave writes the rows it computed (64 consecutive per store)
+  if (logits != nullptr) {
+    for (int i = lane; i < ng * 8; i += 64) {
+      const int64_t row = g_begin * 8 + i;
+      if (row < V) {
+#pragma unroll
+        for (int b = 0; b < NBC; b++)
+          if (b0 + b < B) logits[(b0 + b) * V + row] = mylog[i * NBC + b];
+      }
+    }
+  }
   if (wv < NBC && b0 + wv < B) {
     uint64_t* out = cand + ((b0 + wv) * gridDim.x + blockIdx.x) * (int64_t)k;
     stream_block_topk<NBC>(slog, sg0, sng, wv, lane, max_groups, V, k, out);
+  } else if (lse != nullptr && wv >= NBC && wv < 2 * NBC && b0 + (wv - NBC) < B) {
+    // waves NBC .. 2 NBC - 1: log-partition partial of column wv - NBC over the
+    // block's rows (lane holds row lane of every wave's run, as in the top-k)
+    const int b = wv - NBC, per_wave = max_groups * 8;
+    float x[kStreamWaves];
+    bool ok[kStreamWaves];
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; w++) {
+      ok[w] = lane < sng[w] * 8 && sg0[w] * 8 + lane < V;
+      x[w] = ok[w] ? slog[(w * per_wave + lane) * NBC + b] : 0.f;
+    }
+    const float2 part = wave_lse_part(x, ok, lse_c);
+    if (lane == 0) lse[(b0 + b) * gridDim.x + blockIdx.x] = part;
   }
 }
 
 
 template <int NIMG>
 static hipError_t launch_stream_nimg(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
-                                hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                                     const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e = set_dynamic_lds((const void*)stream_logits_kernel<NIMG>, p.lds_bytes);
   if (e != hipSuccess) return e;
   if ((e = record_event(ev0, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((stream_logits_kernel<NIMG>), dim3((unsigned)p.nblk, (unsigned)p.npass),
                      dim3(64 * kStreamWaves), p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (int)t.hidden, R,
-                     p.batch, p.steps, p.chunk, p.k, cand, p.ngroups, p.max_groups);
+                     p.batch, p.steps, p.chunk, p.k, cand, p.ngroups, p.max_groups, x.logits, x.lse, x.lse_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev1, stream);
 }
 
 hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
-                         hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  return p.nimg == 1 ? launch_stream_nimg<1>(t, p, R, cand, stream, ev0, ev1)
-                     : launch_stream_nimg<2>(t, p, R, cand, stream, ev0, ev1);
+                         const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  return p.nimg == 1 ? launch_stream_nimg<1>(t, p, R, cand, x, stream, ev0, ev1)
+                     : launch_stream_nimg<2>(t, p, R, cand, x, stream, ev0, ev1);
 }
 
 int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {

@@ -84,12 +84,16 @@ __global__ void __launch_bounds__(256) wide_prep_kernel(const float* __restrict_
 //  table      bf16 [V][hidden], row_bytes = 2 hidden, a multiple of 16
 //  img        operand image (wide_prep_kernel), steps_pad K steps per pass
 //  steps_pad  ceil(hidden / 64) rounded up to kWideCK
+//  logits     nullable [B][V]: the block's raw logits
+//  lse        nullable [B][gridDim.x]: log-partition partial of the block's rows
+//             at lse_c = log2(e) / temperature
 // Rows past V are read from row V - 1 and never ranked; 16-byte chunks past the
 // row end are read from the row's last 16 bytes and meet zero image values.
 template <int NTILE>
 __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, const u32x4* __restrict__ img, int64_t B,
-    int steps_pad, int k, uint64_t* __restrict__ cand, uint64_t* __restrict__ thr) {
+    int steps_pad, int k, uint64_t* __restrict__ cand, uint64_t* __restrict__ thr, float* __restrict__ logits,
+    float2* __restrict__ lse, float lse_c) {
   constexpr int STEP_U4 = NTILE * 4 * 64;  // image slots per K step
   constexpr int CHUNK_U4 = kWideCK * STEP_U4;
   constexpr int NTHR = 64 * kWideWaves;
@@ -238,6 +242,29 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
 #pragma unroll
   for (int i = 0; i < MAXC; i++) tords[i] = __builtin_amdgcn_readfirstlane(tords[i]);
 
+  // raw logits and log-partition partials of the wave's columns
+  if (logits != nullptr || lse != nullptr) {
+#pragma unroll
+    for (int i = 0; i < MAXC; i++) {
+      const int col = wv + i * kWideWaves;
+      const int64_t b = bcol0 + i * kWideWaves;
+      if (col >= NC || b >= B) break;
+      float x[PER_LANE];
+      bool ok[PER_LANE];
+#pragma unroll
+      for (int q = 0; q < PER_LANE; q++) {
+        const int rl = lane + 64 * q;
+        ok[q] = row0 + rl < V;
+        x[q] = slog[rl * LS + col];
+        if (logits != nullptr && ok[q]) logits[b * V + row0 + rl] = x[q];
+      }
+      if (lse != nullptr) {
+        const float2 part = wave_lse_part(x, ok, lse_c);
+        if (lane == 0) lse[b * gridDim.x + blockIdx.x] = part;
+      }
+    }
+  }
+
   // The wave's columns are selected together, round by round, so that their
   // reduction chains interleave.  v[i][q]: order value (score_ord, > 0 for any
   // score) of row lane + 64 q for column i if it passes the bound, else 0.
@@ -310,28 +337,30 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
 
 template <int NTILE>
 static hipError_t launch_wide_nt(const TableDesc& t, const LogitsPlan& p, const u32x4* img, uint64_t* cand,
-                                 uint64_t* thr, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                                 uint64_t* thr, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0,
+                                 hipEvent_t ev1) {
   hipError_t e = set_dynamic_lds((const void*)wide_logits_kernel<NTILE>, p.lds_bytes);
   if (e != hipSuccess) return e;
   if ((e = record_event(ev0, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((wide_logits_kernel<NTILE>), dim3((unsigned)p.nblk, (unsigned)p.npass), dim3(64 * kWideWaves),
-                     p.lds_bytes, stream, t.rows, t.V, t.row_bytes, img, p.batch, p.steps, p.k, cand, thr);
+                     p.lds_bytes, stream, t.rows, t.V, t.row_bytes, img, p.batch, p.steps, p.k, cand, thr,
+                     x.logits, x.lse, x.lse_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev1, stream);
 }
 
-hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* img,
-                              uint64_t* cand, uint64_t* thr, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* img, uint64_t* cand,
+                       uint64_t* thr, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t total = (int64_t)p.npass * p.steps * p.ntile * 256;  // >= 768 npass >= batch
   hipLaunchKernelGGL(wide_prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, R, p.batch,
                      (int)t.hidden, p.steps, p.ntile, total, (u32x4*)img, thr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (p.ntile) {
-    case 1: return launch_wide_nt<1>(t, p, (const u32x4*)img, cand, thr, stream, ev0, ev1);
-    case 2: return launch_wide_nt<2>(t, p, (const u32x4*)img, cand, thr, stream, ev0, ev1);
-    case 3: return launch_wide_nt<3>(t, p, (const u32x4*)img, cand, thr, stream, ev0, ev1);
-    case 4: return launch_wide_nt<4>(t, p, (const u32x4*)img, cand, thr, stream, ev0, ev1);
+    case 1: return launch_wide_nt<1>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+    case 2: return launch_wide_nt<2>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+    case 3: return launch_wide_nt<3>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+    case 4: return launch_wide_nt<4>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -53,7 +53,8 @@ typedef enum {
                           outside [1, 65536]; vocab outside [1, 2^31 - 1]; seq_len or
                           batch outside the supported range                            */
   ETG_EALIGN = -4,     /* a device pointer lacks the alignment its argument states     */
-  ETG_ERANGE = -5,     /* k outside [1, min(vocab, 64)], or an unknown path            */
+  ETG_ERANGE = -5,     /* k outside [1, min(vocab, 64)], an unknown path, or a
+                          temperature out of range                                     */
   ETG_EWORKSPACE = -6, /* workspace smaller than etg_logits_topk_workspace() bytes     */
   ETG_EHIP = -8        /* a HIP runtime call failed (the message names it)             */
 } etg_status;
@@ -167,6 +168,42 @@ int32_t etg_logits_topk_profiled(const etg_table* lm_head, const float* d_residu
                                  int32_t k, int32_t* d_topk_ids, float* d_topk_scores,
                                  void* d_workspace, size_t workspace_bytes, int32_t path,
                                  void* event_before, void* event_after, void* stream);
+
+/*
+ * Top-k with probabilities (ADR-0008 "POST /v1/logits": every listed token carries
+ * its probability at the request's temperature).  As etg_logits_topk_ex, and
+ *
+ *   d_topk_probs[b][j] = exp(L[b][id_j] / T - lse_b),  lse_b = ln sum_v exp(L[b][v] / T)
+ *
+ * the softmax of L / T over the WHOLE vocabulary (so the k listed values need not
+ * sum to 1).  The normaliser is fused into the same table pass: every block
+ * summarises its slice of logits as (max, sum of exp) and the merge combines the
+ * summaries, so no V-wide vector is written.
+ *   temperature    T > 0, finite, with log2(e) / T a finite float (ETG_ERANGE
+ *                  otherwise); it changes the probabilities, never the ids.
+ *   d_topk_probs   f32 [batch][k], 4-byte aligned.
+ * Accuracy: with every logit within its bound above (tol_v), the log of each
+ * probability is within (tol_{id_j} + max_v tol_v) / T of the exact value, plus
+ * about 1e-5 for the f32 exp2 / log2 and sums.  Workspace: as etg_logits_topk_ex.
+ */
+int32_t etg_logits_topk_probs(const etg_table* lm_head, const float* d_residual, int64_t batch,
+                              int32_t k, float temperature, int32_t* d_topk_ids,
+                              float* d_topk_scores, float* d_topk_probs, void* d_workspace,
+                              size_t workspace_bytes, int32_t path, void* stream);
+
+/*
+ * Raw logits mode (ADR-0008 "POST /v1/logits": the full vector of vocab_size f32
+ * logits, for beam search and sampling).
+ *   d_logits   f32 [batch][vocab] row-major, 4-byte aligned, caller-owned:
+ *              L[b][v] as defined for etg_logits_topk, with the same accuracy; on
+ *              a given path these are bitwise the values its top-k ranks.
+ *   d_workspace  at least etg_logits_raw_workspace() bytes, 256-byte aligned.
+ * Writes batch * vocab * 4 bytes of HBM besides reading the table once per pass.
+ */
+int64_t etg_logits_raw_workspace(const etg_table* lm_head, int64_t batch, int32_t path);
+int32_t etg_logits_raw(const etg_table* lm_head, const float* d_residual, int64_t batch,
+                       float* d_logits, void* d_workspace, size_t workspace_bytes, int32_t path,
+                       void* stream);
 
 /* Message of the calling thread's last failed call ("" if none). */
 const char* etg_last_error(void);

@@ -57,6 +57,8 @@ def _load():
     L.orc_logits.argtypes = [vp, ctypes.c_int, i64, i64, vp, i64, vp, vp]
     L.orc_topk.argtypes = [vp, i64, i64, i32, vp, vp]
     L.orc_logits_at.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, i64, vp, vp]
+    L.orc_log_partition.argtypes = [vp, i64, i64, ctypes.c_double, vp]
+    L.orc_probs_at.argtypes = [vp, vp, i64, i64, ctypes.c_double, vp, i32, vp]
     L.orc_set_threads.argtypes = [ctypes.c_int]
     L.orc_max_threads.restype = ctypes.c_int
     _lib = L
@@ -171,3 +173,30 @@ def logits_at(table, dtype: int, V: int, hidden: int, R, bs, vids):
     _load().orc_logits_at(_p(raw), int(dtype), int(V), int(hidden), _p(R), _p(bs), _p(vids),
                           bs.size, _p(oL), _p(oA))
     return oL, oA
+
+
+def log_partition(L, T: float) -> np.ndarray:
+    """lse[b] = log(sum_v exp(L[b][v] / T)) in float64 (softmax normaliser at temperature T)."""
+    L = np.ascontiguousarray(L, dtype=np.float64)
+    if L.ndim == 1:
+        L = L[None, :]
+    if not T > 0:
+        raise ValueError("temperature must be > 0")
+    B, V = L.shape
+    out = np.empty(B, np.float64)
+    _load().orc_log_partition(_p(L), B, V, float(T), _p(out))
+    return out
+
+
+def probs_at(L, ids, T: float) -> np.ndarray:
+    """prob[b][j] = exp(L[b][ids[b][j]] / T - lse[b]): softmax of L / T over the vocabulary."""
+    L = np.ascontiguousarray(L, dtype=np.float64)
+    if L.ndim == 1:
+        L = L[None, :]
+    B, V = L.shape
+    ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(B, -1)
+    k = ids.shape[1]
+    lse = log_partition(L, T)
+    out = np.empty((B, k), np.float64)
+    _load().orc_probs_at(_p(L), _p(lse), B, V, float(T), _p(ids), int(k), _p(out))
+    return out

@@ -63,6 +63,48 @@ def check_row(gids, gscores, V: int, c: float, L_at_g, A_at_g, L_at_o=None, A_at
     return fails
 
 
+# Probabilities (softmax of L / T over the vocabulary).  With S_j within tol(G_j)
+# of the exact logit and every logit within its tol, the log-partition moves by
+# at most max_v tol(v) / T (it is 1-Lipschitz in the max norm of L / T), so
+#   |ln P_j - ln p(G_j)| <= (tol(G_j) + max_v tol(v)) / T + slack,
+# slack covering the f32 arithmetic of the probabilities themselves: exp2 and
+# log2 to a few ulps, sums of at most a few hundred rounded non-negative terms
+# (relative error <= 2^-24 each) and the rounding of exponent arguments
+# (<= 2^-22 |ln p| in all).
+PROB_SLACK_ABS = 5e-5
+PROB_SLACK_REL = 2.0 ** -20
+# Below this the f32 probability may underflow; such entries only need to be tiny.
+PROB_LN_FLOOR = -80.0
+
+
+def check_probs(gids, gprobs, T: float, c: float, L, A):
+    """Failure strings for GPU probabilities of the GPU's ids, against the oracle's
+    full [B, V] logits L and sums A at temperature T."""
+    import oracle
+    gids = np.asarray(gids, dtype=np.int64)
+    gp = np.asarray(gprobs, dtype=np.float64)
+    B, V = L.shape
+    ref = oracle.probs_at(L, np.clip(gids, 0, V - 1).astype(np.int32), T)
+    fails = []
+    for b in range(B):
+        tmax = c * float(np.max(A[b]))
+        for j in range(gids.shape[1]):
+            v = int(gids[b, j])
+            lnp = float(np.log(ref[b, j])) if ref[b, j] > 0 else -np.inf
+            if not 0.0 <= gp[b, j] <= 1.0:
+                fails.append(f"row {b} pos {j}: probability {gp[b, j]!r} outside [0, 1]")
+                continue
+            if lnp < PROB_LN_FLOOR:
+                if gp[b, j] > 1e-30:
+                    fails.append(f"row {b} pos {j}: probability {gp[b, j]!r} for ln p = {lnp!r}")
+                continue
+            lim = (c * float(A[b, v]) + tmax) / T + PROB_SLACK_ABS + PROB_SLACK_REL * abs(lnp)
+            err = abs(np.log(gp[b, j]) - lnp) if gp[b, j] > 0 else np.inf
+            if err > lim:
+                fails.append(f"row {b} pos {j} (id {v}): |ln {gp[b, j]!r} - ({lnp!r})| > {lim!r}")
+    return fails
+
+
 def check_full(gids, gscores, L, A, oids, c: float):
     """All rows, with the oracle's full [B, V] logits L, sums A and top-k ids oids."""
     gids = np.asarray(gids)

@@ -21,6 +21,9 @@
  *                   "Open Questions", item 1; HELIX proposal section 5(a)).
  *   top-k           ADR-0008 "POST /v1/logits": the response lists the top_k
  *                   tokens in descending order.
+ *   probabilities   ADR-0008 "POST /v1/logits": each listed token with its
+ *                   probability at the request's temperature (softmax of L / T
+ *                   over the whole vocabulary).
  *
  * Every function here has a pin in tests/test_oracle.py against values fixed
  * by the pages or by mathematics; none is "parity unpinned".
@@ -274,6 +277,45 @@ void orc_logits_at(const uint8_t* table, int dtype, int64_t V, int64_t hidden, c
     out_A[j] = sa;
     free(x);
   }
+}
+
+/*
+ * Probabilities at a temperature (ADR-0008 "POST /v1/logits": each listed token
+ * carries its probability at the request's temperature).  Reading: the softmax
+ * of L / T over the whole vocabulary, so the listed probabilities are those of
+ * the full distribution (they need not sum to 1 over the top k).
+ *
+ *   lse[b] = log(sum_v exp(L[b][v] / T))
+ *          = M / T + log(sum_v exp((L[b][v] - M) / T)),  M = max_v L[b][v]
+ *
+ * (the shift by M is an identity that keeps every exp argument <= 0).  The sum
+ * runs in double in vocabulary order.  T > 0.
+ */
+void orc_log_partition(const double* L, int64_t B, int64_t V, double T, double* lse) {
+  int64_t b;
+#pragma omp parallel for schedule(static)
+  for (b = 0; b < B; b++) {
+    const double* x = L + b * V;
+    double m = x[0], s = 0.0;
+    int64_t v;
+    for (v = 1; v < V; v++)
+      if (x[v] > m) m = x[v];
+    for (v = 0; v < V; v++) s += exp((x[v] - m) / T);
+    lse[b] = m / T + log(s);
+  }
+}
+
+/* prob[b][j] = exp(L[b][ids[b][j]] / T - lse[b]) for k ids per row (NAN for an id
+ * outside [0, V)). */
+void orc_probs_at(const double* L, const double* lse, int64_t B, int64_t V, double T, const int32_t* ids,
+                  int32_t k, double* prob) {
+  int64_t b;
+  int32_t j;
+  for (b = 0; b < B; b++)
+    for (j = 0; j < k; j++) {
+      const uint32_t v = (uint32_t)ids[b * k + j];
+      prob[b * k + j] = (uint64_t)v < (uint64_t)V ? exp(L[b * V + v] / T - lse[b]) : NAN;
+    }
 }
 
 /* Element-wise decoders over arrays (for the decoder pins). */

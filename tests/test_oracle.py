@@ -354,6 +354,70 @@ def test_permuting_rows_permutes_ids():
     assert np.array_equal(inv[i1], i2)
 
 
+# ---------------------------------------------------------------- probabilities
+def test_uniform_logits_give_one_over_v():
+    for V in (1, 7, 262144):
+        L = np.zeros((1, V))
+        assert oracle.log_partition(L, 1.0)[0] == pytest.approx(math.log(V), rel=0, abs=1e-12)
+        p = oracle.probs_at(L, [[0]], 0.37)
+        assert p[0, 0] == pytest.approx(1.0 / V, rel=1e-12)
+
+
+def test_two_token_probabilities_are_logistic():
+    # p(v0) = 1 / (1 + exp((L1 - L0) / T)); a temperature that multiplied instead
+    # of dividing, or a dropped shift, would miss it
+    for l0, l1, T in ((0.3, -1.2, 1.0), (2.0, 5.0, 2.5), (-7.0, -7.5, 0.25), (1000.0, 999.0, 1.0)):
+        L = np.array([[l0, l1]])
+        p = oracle.probs_at(L, [[0, 1]], T)
+        want0 = 1.0 / (1.0 + math.exp((l1 - l0) / T))
+        assert p[0, 0] == pytest.approx(want0, rel=1e-13)
+        assert p[0, 1] == pytest.approx(1.0 - want0, rel=1e-12)
+
+
+def test_probabilities_of_log_weights_are_the_weights():
+    w = np.array([1.0, 2.0, 3.0, 4.0, 10.0])
+    L = np.log(w)[None, :]
+    p = oracle.probs_at(L, [[4, 3, 2, 1, 0]], 1.0)
+    assert np.allclose(p[0], w[::-1] / w.sum(), rtol=1e-13, atol=0)
+    # at T = 1/2 the weights are squared
+    p2 = oracle.probs_at(L, [[4, 0]], 0.5)
+    assert np.allclose(p2[0], np.array([100.0, 1.0]) / (w ** 2).sum(), rtol=1e-13, atol=0)
+
+
+def test_log_partition_matches_scipy_and_probabilities_sum_to_one():
+    from scipy.special import logsumexp
+    g = np.random.default_rng(31)
+    L = g.standard_normal((3, 5000)) * 4.0 + 50.0          # shifted: a naive sum would still fit,
+    for T in (0.3, 1.0, 7.0):                               # the shift must cancel exactly
+        lse = oracle.log_partition(L, T)
+        assert np.allclose(lse, logsumexp(L / T, axis=1), rtol=1e-13, atol=0)
+        p = oracle.probs_at(L, np.tile(np.arange(5000, dtype=np.int32), (3, 1)), T)
+        assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_large_logits_do_not_overflow():
+    L = np.array([[800.0, 799.0, -800.0]])
+    p = oracle.probs_at(L, [[0, 1, 2]], 1.0)
+    e = math.exp(-1.0)
+    assert p[0, 0] == pytest.approx(1.0 / (1.0 + e), rel=1e-13)
+    assert p[0, 1] == pytest.approx(e / (1.0 + e), rel=1e-12)
+    assert 0.0 <= p[0, 2] < 1e-300
+
+
+def test_probability_check_accepts_oracle_and_rejects_shifted():
+    V, d = 300, 64
+    t = _table(BF16, V, d, seed=19)
+    R = np.random.default_rng(20).standard_normal((2, d)).astype(np.float32)
+    L, A = oracle.logits(t, BF16, V, d, R)
+    ids, _ = oracle.topk(L, 5)
+    for T in (0.5, 1.0):
+        p = oracle.probs_at(L, ids, T)
+        assert accept.check_probs(ids, p, T, 2e-3, L, A) == []
+        # beyond the logit tolerance: a probability off by a factor e^(3 max tol / T)
+        off = p * np.exp(3.0 * 2e-3 * A.max() / T)
+        assert accept.check_probs(ids, off, T, 2e-3, L, A)
+
+
 # ---------------------------------------------------------------- acceptance rule
 def test_acceptance_rule_accepts_exact_and_rejects_wrong():
     V, d = 300, 64
