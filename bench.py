@@ -10,8 +10,9 @@ seeded synthetic arrays (synth/), resident in HBM before the timed region.
 value = algorithmic bytes of the step / time per step, in GB/s.  The roofline
 object times the table-streaming kernel alone with HIP events recorded on the
 stream it runs on.  The other workloads of the page set (batches of 8 to 64,
-the 1,024-row contraction, the EmbeddingGemma-shaped Q8_0 gather) are measured
-after the timed steps and reported under "also".  The CPU oracle is timed on a
+the response with probabilities, the raw logits mode, the 1,024-row
+contraction, the EmbeddingGemma-shaped Q8_0 gather) are measured after the
+timed steps and reported under "also".  The CPU oracle is timed on a
 bounded sample of the same workload under "cpu_baseline".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -220,7 +221,26 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     hev = _HipEvents()
+    # eager steps, with the table kernel timed alone by events around it
     ms, kms = _timed(torch, step, args.steps, events=hev)
+    ms_graph = None
+    if not args.no_extras:
+        # the same step captured once in a HIP graph and replayed (one launch per
+        # step instead of three); reported beside the eager steps
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        ms_graph, _ = _timed(torch, graph.replay, args.steps)
+        del graph
+        log(f"eager {ms * 1e3:.1f} us/step, graph replay {ms_graph * 1e3:.1f} us/step")
 
     gather_bytes = B * cfg.row_bytes + B * cfg.d * 4 + B * 4
     logits_bytes = cfg.table_bytes + B * cfg.d * 4 + B * k * 8
@@ -263,6 +283,10 @@ def main() -> int:
     log(f"step {ms * 1e3:.1f} us, table kernel {kms * 1e3:.1f} us -> {achieved:.0f} GB/s")
 
     also = {}
+    if ms_graph is not None:
+        also["decode_step_hipgraph_replay"] = {
+            "ms_per_step": round(ms_graph, 4),
+            "GBps": round(step_bytes / (ms_graph * 1e-3) / 1e9, 1)}
     if not args.no_extras:
         for b in (8, 16, 32, 64):
             Rb = torch.from_numpy(cfg.residuals(b)).to(dev)
@@ -275,6 +299,25 @@ def main() -> int:
                 "GBps": round(cfg.table_bytes / (mb * 1e-3) / 1e9, 1),
                 "pct_hbm_peak": round(100 * cfg.table_bytes / (mb * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
             log(f"B={b}: {mb * 1e3:.1f} us")
+        # the logits response with probabilities at T = 1, and the raw logits mode
+        R1 = torch.from_numpy(cfg.residuals(1)).to(dev)
+        ws1 = table.workspace(1, k)
+        f = lambda: table.logits_topk_probs(R1, k, temperature=1.0, workspace=ws1)
+        f()
+        mq, _ = _timed(torch, f, 20)
+        also["lm31b_logits_top10_probs_B1"] = {
+            "us_per_call": round(mq * 1e3, 1), "GBps": round(cfg.table_bytes / (mq * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * cfg.table_bytes / (mq * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
+        raw = torch.empty((1, cfg.V), dtype=torch.float32, device=dev)
+        wsr = torch.empty(max(table.workspace_bytes(1, 1), 256), dtype=torch.uint8, device=dev)
+        f = lambda: table.logits_raw(R1, out=raw, workspace=wsr)
+        f()
+        mr, _ = _timed(torch, f, 20)
+        rbytes = cfg.table_bytes + cfg.V * 4
+        also["lm31b_logits_raw_B1"] = {
+            "us_per_call": round(mr * 1e3, 1), "GBps": round(rbytes / (mr * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * rbytes / (mr * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
+        log(f"probs B=1: {mq * 1e3:.1f} us, raw B=1: {mr * 1e3:.1f} us")
     del table, rows
     torch.cuda.empty_cache()
 

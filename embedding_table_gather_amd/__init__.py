@@ -18,7 +18,7 @@ import os
 
 import torch
 
-F32, BF16, Q8_0 = 0, 1, 2
+F32, BF16, Q8_0, F16 = 0, 1, 2, 3
 PATH_AUTO, PATH_VALU, PATH_STREAM, PATH_GEMM, PATH_WIDE = 0, 1, 2, 3, 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libetg.so")
@@ -106,10 +106,10 @@ def _event_handle(ev, device: torch.device) -> int:
 
 
 class Table:
-    """A V x hidden table already in device memory (f32, bf16 or Q8_0 rows).
+    """A V x hidden table already in device memory (f32, bf16, f16 or Q8_0 rows).
 
     ``rows`` is any contiguous CUDA tensor holding exactly vocab * row_bytes bytes
-    (e.g. uint16 [V, d] bf16 bits, float32 [V, d], uint8 [V, 34 d / 32]).  It is
+    (e.g. uint16 [V, d] bf16 or f16 bits, float32 [V, d], uint8 [V, 34 d / 32]).  It is
     borrowed: the handle keeps a reference but never copies it.
     """
 

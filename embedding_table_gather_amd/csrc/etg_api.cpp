@@ -39,6 +39,7 @@ const char* dtype_name(int32_t dt) {
     case ETG_F32: return "f32";
     case ETG_BF16: return "bf16";
     case ETG_Q8_0: return "q8_0";
+    case ETG_F16: return "f16";
     default: return "?";
   }
 }
@@ -65,6 +66,7 @@ int64_t etg_row_bytes(int32_t dtype, int64_t hidden) {
   switch (dtype) {
     case ETG_F32: return hidden % 4 ? -1 : 4 * hidden;
     case ETG_BF16: return hidden % 8 ? -1 : 2 * hidden;
+    case ETG_F16: return hidden % 8 ? -1 : 2 * hidden;
     case ETG_Q8_0: return hidden % 32 ? -1 : 34 * (hidden / 32);
     default: return -1;
   }
@@ -81,13 +83,14 @@ int32_t etg_table_create(const void* d_rows, int32_t dtype, int64_t vocab, int64
   if (out == nullptr) return fail(ETG_EINVAL, "out handle pointer is NULL");
   *out = nullptr;
   if (d_rows == nullptr) return fail(ETG_EINVAL, "table rows pointer is NULL");
-  if (dtype != ETG_F32 && dtype != ETG_BF16 && dtype != ETG_Q8_0) return fail(ETG_EDTYPE, "unknown dtype %d", dtype);
+  if (dtype != ETG_F32 && dtype != ETG_BF16 && dtype != ETG_Q8_0 && dtype != ETG_F16)
+    return fail(ETG_EDTYPE, "unknown dtype %d", dtype);
   if (vocab < 1 || vocab > kMaxVocab)
     return fail(ETG_ESHAPE, "vocab %lld outside [1, %lld]", (long long)vocab, (long long)kMaxVocab);
   const int64_t rb = etg_row_bytes(dtype, hidden);
   if (rb < 0)
     return fail(ETG_ESHAPE, "hidden %lld not storable as %s (multiple of %d, at most %lld)", (long long)hidden,
-                dtype_name(dtype), dtype == ETG_F32 ? 4 : dtype == ETG_BF16 ? 8 : 32, (long long)kMaxHidden);
+                dtype_name(dtype), dtype == ETG_F32 ? 4 : dtype == ETG_Q8_0 ? 32 : 8, (long long)kMaxHidden);
   if (!aligned(d_rows, 16)) return fail(ETG_EALIGN, "table rows pointer is not 16-byte aligned");
   etg_table* t = new (std::nothrow) etg_table;
   if (t == nullptr) return fail(ETG_EINVAL, "out of host memory");

@@ -9,7 +9,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-enum { DT_F32 = 0, DT_BF16 = 1, DT_Q8_0 = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_Q8_0 = 2, DT_F16 = 3 };
 
 // ---------------------------------------------------------------------------
 // Top-k ordering key.  A larger key is a better candidate: higher logit first,

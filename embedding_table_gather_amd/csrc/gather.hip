@@ -7,14 +7,17 @@
 // embeddinggemma.c port specification ("Forward graph") scales the gathered
 // Q8_0 rows by sqrt(768).
 //
-// One wavefront per output row.  f32 / bf16 rows are read with 16-byte loads
+// f16 rows are the embed slice's binary16 store, widened per lookup (ADR-0008
+// "Vindex Slice: embed" and "Memory footprint").
+//
+// One wavefront per output row.  f32 / bf16 / f16 rows are read with 16-byte loads
 // straight into registers; Q8_0 rows (34-byte blocks, so only 2-byte aligned in
 // general) are staged through the wave's slice of LDS with aligned dword loads
 // and then unpacked.  Q8_0 rows whose size is a multiple of 16 bytes take a
 // kernel that stages them with 16-byte loads, two rows per wave.  Stores are
 // 16-byte f32x4, contiguous across the wave.
 //
-// Bit-exactness: dequant is exact in f32 (copy; bf16 widening; int8 * f16 has at
+// Bit-exactness: dequant is exact in f32 (copy; bf16 and f16 widening; int8 * f16 has at
 // most 19 significant bits) and the scale is one f32 multiply, so there is one
 // rounding at most.  FP contraction is off in this file.
 #include "etg_device.hpp"
@@ -65,7 +68,7 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
         if (c4 < n4) o[c4] = SCALE ? v[u] * scale : v[u];
       }
     }
-  } else if constexpr (DT == DT_BF16) {
+  } else if constexpr (DT == DT_BF16 || DT == DT_F16) {
     const u32x4* s8 = (const u32x4*)src;
     const int n8 = hidden >> 3;
     for (int c0 = lane; c0 < n8; c0 += 64 * kGatherUnroll) {
@@ -79,8 +82,16 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
       for (int u = 0; u < kGatherUnroll; u++) {
         const int c8 = c0 + 64 * u;
         if (c8 < n8) {
-          f32x4 a = {bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y)};
-          f32x4 b = {bf16_lo(w[u].z), bf16_hi(w[u].z), bf16_lo(w[u].w), bf16_hi(w[u].w)};
+          f32x4 a, b;
+          if constexpr (DT == DT_BF16) {
+            a = f32x4{bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y)};
+            b = f32x4{bf16_lo(w[u].z), bf16_hi(w[u].z), bf16_lo(w[u].w), bf16_hi(w[u].w)};
+          } else {
+            a = f32x4{f16_bits_to_f32(w[u].x & 0xffffu), f16_bits_to_f32(w[u].x >> 16),
+                      f16_bits_to_f32(w[u].y & 0xffffu), f16_bits_to_f32(w[u].y >> 16)};
+            b = f32x4{f16_bits_to_f32(w[u].z & 0xffffu), f16_bits_to_f32(w[u].z >> 16),
+                      f16_bits_to_f32(w[u].w & 0xffffu), f16_bits_to_f32(w[u].w >> 16)};
+          }
           if (SCALE) {
             a = a * scale;
             b = b * scale;
@@ -231,6 +242,7 @@ hipError_t launch_gather(const TableDesc& t, const int32_t* ids, int64_t n, floa
   switch (t.dtype) {
     case DT_F32: return launch_dt<DT_F32>(t, ids, n, scale, out, bad, stream);
     case DT_BF16: return launch_dt<DT_BF16>(t, ids, n, scale, out, bad, stream);
+    case DT_F16: return launch_dt<DT_F16>(t, ids, n, scale, out, bad, stream);
     default: return launch_dt<DT_Q8_0>(t, ids, n, scale, out, bad, stream);
   }
 }

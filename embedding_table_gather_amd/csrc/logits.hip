@@ -16,7 +16,7 @@
 //    up to 64 residual rows, still streamed into VGPRs; the residual operand is
 //    staged through LDS and no MFMA lane is idle.
 //  * gemm:   bf16 tables, large batches: a tiled MFMA contraction.
-//  * valu:   any dtype (f32, bf16, Q8_0); f32 FMAs per lane, one table pass per
+//  * valu:   any dtype (f32, bf16, f16, Q8_0); f32 FMAs per lane, one table pass per
 //    up to 8 residual rows.
 #include <algorithm>
 
@@ -36,6 +36,8 @@ __device__ __forceinline__ float deq_value(const uint8_t* row, int c) {
     return ((const float*)row)[c];
   } else if constexpr (DT == DT_BF16) {
     return __uint_as_float((uint32_t)((const uint16_t*)row)[c] << 16);
+  } else if constexpr (DT == DT_F16) {
+    return f16_bits_to_f32(((const uint16_t*)row)[c]);
   } else {
     const uint8_t* blk = row + 34 * (c >> 5);
     const float s = f16_bits_to_f32(*(const uint16_t*)blk);
@@ -301,6 +303,7 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const flo
     switch (t.dtype) {
       case DT_F32: e = launch_valu<DT_F32>(t, p, R, cand, x, stream, ev0, ev1); break;
       case DT_BF16: e = launch_valu<DT_BF16>(t, p, R, cand, x, stream, ev0, ev1); break;
+      case DT_F16: e = launch_valu<DT_F16>(t, p, R, cand, x, stream, ev0, ev1); break;
       default: e = launch_valu<DT_Q8_0>(t, p, R, cand, x, stream, ev0, ev1); break;
     }
   }

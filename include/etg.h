@@ -39,17 +39,20 @@ extern "C" {
 typedef enum {
   ETG_F32 = 0,  /* little-endian IEEE binary32; row_bytes = 4 * hidden             */
   ETG_BF16 = 1, /* bfloat16 (upper half of a binary32); row_bytes = 2 * hidden       */
-  ETG_Q8_0 = 2  /* blocks of 32 values: little-endian binary16 scale, then 32 int8;
+  ETG_Q8_0 = 2, /* blocks of 32 values: little-endian binary16 scale, then 32 int8;
                    value = int8 * scale; row_bytes = 34 * hidden / 32.  (The
                    embeddinggemma.c port specification, "Tensor inventory": the Q8_0
                    token_embd is used by row-gather + dequant only.) */
+  ETG_F16 = 3   /* little-endian IEEE binary16; row_bytes = 2 * hidden.  (ADR-0008
+                   "Vindex Slice: embed": embeddings.bin is vocab x hidden f16, and
+                   "Memory footprint": decoded to f32 per lookup.) */
 } etg_dtype;
 
 typedef enum {
   ETG_OK = 0,
   ETG_EINVAL = -1,     /* null pointer or handle                                       */
   ETG_EDTYPE = -2,     /* unknown dtype                                                */
-  ETG_ESHAPE = -3,     /* hidden not a multiple of 4 (f32) / 8 (bf16) / 32 (Q8_0), or
+  ETG_ESHAPE = -3,     /* hidden not a multiple of 4 (f32) / 8 (bf16, f16) / 32 (Q8_0), or
                           outside [1, 65536]; vocab outside [1, 2^31 - 1]; seq_len or
                           batch outside the supported range                            */
   ETG_EALIGN = -4,     /* a device pointer lacks the alignment its argument states     */
@@ -93,7 +96,7 @@ int32_t etg_table_destroy(etg_table* table);
  *   out[n][c] = deq(row ids[n])[c]                  when scale == 1.0f
  *   out[n][c] = round_f32(deq(row ids[n])[c] * scale) otherwise
  *
- * deq is exact: f32 rows are copied, bf16 rows widened, Q8_0 values are int8 * the
+ * deq is exact: f32 rows are copied, bf16 and f16 rows widened, Q8_0 values are int8 * the
  * block's binary16 scale (exact in f32).  The optional scale is applied after the
  * dequant with one round-to-nearest-even f32 multiply; pass etg_sqrt_d(hidden) for
  * the x * sqrt(d) of the embeddinggemma.c "Forward graph".
@@ -113,7 +116,7 @@ int32_t etg_embed_gather(const etg_table* table, const int32_t* d_ids, int64_t s
 
 /* Kernel path for etg_logits_topk_ex (ETG_PATH_AUTO is what etg_logits_topk uses). */
 typedef enum {
-  ETG_PATH_AUTO = 0,   /* f32 and Q8_0 tables: VALU; bf16 tables: STREAM up to 8 rows,
+  ETG_PATH_AUTO = 0,   /* f32, f16 and Q8_0 tables: VALU; bf16 tables: STREAM up to 8 rows,
                           WIDE up to 64, GEMM beyond                                      */
   ETG_PATH_VALU = 1,   /* any dtype: f32 vector FMAs, one table pass per 8 residuals     */
   ETG_PATH_STREAM = 2, /* bf16 tables: one HBM pass per 8 residuals, bf16 MFMA dot engine;
@@ -145,7 +148,7 @@ int64_t etg_logits_topk_workspace_ex(const etg_table* lm_head, int64_t batch, in
  *   d_topk_scores  f32 [batch][k]: the logits of those ids.
  *   d_workspace    at least etg_logits_topk_workspace() bytes, 256-byte aligned.
  * Accuracy: |score - exact logit| <= 2e-3 * sum_i |r_i e_i| for bf16 and Q8_0
- * tables and <= 1e-5 * sum_i |r_i e_i| for f32 tables; ids can differ from the
+ * tables and <= 1e-5 * sum_i |r_i e_i| for f32 and f16 tables; ids can differ from the
  * exact order only among logits that tie within that bound.  Results are
  * deterministic (bitwise repeatable) for a given path.
  */

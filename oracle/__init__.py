@@ -13,7 +13,7 @@ import subprocess
 
 import numpy as np
 
-F32, BF16, Q8_0 = 0, 1, 2
+F32, BF16, Q8_0, F16 = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "etg_oracle.c")

@@ -38,8 +38,10 @@
 #include <omp.h>
 #endif
 
-/* Storage dtype codes of the oracle's interface. */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8_0 = 2 };
+/* Storage dtype codes of the oracle's interface.  f16: the embed slice's
+ * embeddings.bin stores vocab x hidden binary16 values, decoded per lookup
+ * (ADR-0008 "Vindex Slice: embed" and "Memory footprint"). */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8_0 = 2, ORC_F16 = 3 };
 
 /* Q8_0 block: a little-endian binary16 scale, then 32 signed 8-bit values
  * (reading of the "blocks of 32 int8 with one f16 scale" layout; the pages
@@ -63,13 +65,14 @@ int orc_max_threads(void) {
 #endif
 }
 
-/* Bytes of one stored row: hidden * itemsize for f32 (4) and bf16 (2); for Q8_0,
+/* Bytes of one stored row: hidden * itemsize for f32 (4), bf16 and f16 (2); for Q8_0,
  * 34 bytes per 32 values.  -1 when the dtype is unknown or hidden does not fit. */
 int64_t orc_row_bytes(int dtype, int64_t hidden) {
   if (hidden <= 0) return -1;
   switch (dtype) {
     case ORC_F32: return 4 * hidden;
     case ORC_BF16: return 2 * hidden;
+    case ORC_F16: return 2 * hidden;
     case ORC_Q8_0:
       if (hidden % ORC_Q8_VALUES) return -1;
       return (hidden / ORC_Q8_VALUES) * ORC_Q8_BYTES;
@@ -124,6 +127,9 @@ void orc_dequant_row(const uint8_t* row, int dtype, int64_t hidden, double* out)
       break;
     case ORC_BF16:
       for (c = 0; c < hidden; c++) out[c] = orc_bf16_to_f64(rd_u16le(row + 2 * c));
+      break;
+    case ORC_F16:
+      for (c = 0; c < hidden; c++) out[c] = orc_f16_to_f64(rd_u16le(row + 2 * c));
       break;
     case ORC_Q8_0:
       for (c = 0; c < hidden; c++) {

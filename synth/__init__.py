@@ -31,8 +31,8 @@ import numpy as np
 
 # Storage dtype codes (the same small integers are used by both sides'
 # public interfaces; each side defines them on its own).
-F32, BF16, Q8_0 = 0, 1, 2
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", Q8_0: "q8_0"}
+F32, BF16, Q8_0, F16 = 0, 1, 2, 3
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", Q8_0: "q8_0", F16: "f16"}
 
 Q8_BLOCK = 32          # values per Q8_0 block
 Q8_BLOCK_BYTES = 34    # 2-byte f16 scale + 32 int8 values
@@ -44,7 +44,7 @@ def storage_row_bytes(dtype: int, d: int) -> int:
     """Bytes of one stored row (used only to size buffers)."""
     if dtype == F32:
         return 4 * d
-    if dtype == BF16:
+    if dtype in (BF16, F16):
         return 2 * d
     if dtype == Q8_0:
         return Q8_BLOCK_BYTES * (d // Q8_BLOCK)
@@ -103,6 +103,19 @@ def normal_bf16_table(V: int, d: int, std: float, seed: int) -> np.ndarray:
     return _chunked(V, fill, out, seed)
 
 
+def normal_f16_table(V: int, d: int, std: float, seed: int) -> np.ndarray:
+    """binary16 bit patterns (uint16 [V, d]) of N(0, std^2) float32 draws (numpy's
+    round-to-nearest-even conversion)."""
+    out = np.empty((V, d), np.uint16)
+
+    def fill(g, blk):
+        tmp = g.standard_normal(size=blk.shape, dtype=np.float32)
+        tmp *= np.float32(std)
+        blk[...] = tmp.astype(np.float16).view(np.uint16)
+
+    return _chunked(V, fill, out, seed)
+
+
 def q8_0_table(V: int, d: int, seed: int, scale_std: float = 0.01,
                qlo: int = -127, qhi: int = 127) -> np.ndarray:
     """Q8_0 rows (uint8 [V, 34*d/32]).
@@ -135,6 +148,8 @@ def make_table(dtype: int, V: int, d: int, seed: int, std: float = 0.02) -> np.n
         return normal_bf16_table(V, d, std, seed)
     if dtype == Q8_0:
         return q8_0_table(V, d, seed)
+    if dtype == F16:
+        return normal_f16_table(V, d, std, seed)
     raise ValueError(f"unknown dtype {dtype}")
 
 

@@ -37,13 +37,15 @@ def test_version(L):
 
 
 def test_row_bytes_matches_page_sizes(L):
-    dts = {"f32": etg.F32, "bf16": etg.BF16, "q8_0": etg.Q8_0}
+    dts = {"f32": etg.F32, "bf16": etg.BF16, "q8_0": etg.Q8_0, "f16": etg.F16}
     for name, dt, V, d, qty, expected, unit, src in read_golden("sizes.txt"):
         if unit == "B" and int(V) == 1:
             assert L.etg_row_bytes(dts[dt], int(d)) == int(expected), (name, src)
     assert L.etg_row_bytes(etg.BF16, 5376) == 10752
     assert L.etg_row_bytes(etg.Q8_0, 768) == 816
-    for dt, d in [(etg.F32, 6), (etg.BF16, 12), (etg.Q8_0, 48), (etg.BF16, 0), (etg.F32, 65540), (9, 64)]:
+    assert L.etg_row_bytes(etg.F16, 2560) == 5120
+    for dt, d in [(etg.F32, 6), (etg.BF16, 12), (etg.F16, 12), (etg.Q8_0, 48), (etg.BF16, 0), (etg.F32, 65540),
+                  (9, 64)]:
         assert L.etg_row_bytes(dt, d) == -1, (dt, d)
 
 
@@ -150,6 +152,36 @@ def test_logits_errors_without_launch(L, table):
     assert f(table, p, 2, 10, p, p, ctypes.c_void_p(FAKE + 16), ws_n, None) == -4
     assert f(table, p, 2, 10, p, p, p, ws_n - 1, None) == -6 and "workspace" in _err(L)
     assert L.etg_logits_topk_ex(table, p, 2, 10, p, p, p, ws_n, 9, None) == -5
+
+
+def test_probs_and_raw_errors_without_launch(L, table):
+    p = ctypes.c_void_p(FAKE)
+    ws_n = L.etg_logits_topk_workspace(table, 2, 10)
+    f = L.etg_logits_topk_probs
+    for T in (0.0, -1.0, float("inf"), float("nan"), 1e-39):
+        assert f(table, p, 2, 10, T, p, p, p, p, ws_n, 0, None) == -5, T
+        assert "temperature" in _err(L)
+    assert f(table, p, 2, 10, 1.0, p, p, None, p, ws_n, 0, None) == -1
+    assert f(table, p, 2, 10, 1.0, None, p, p, p, ws_n, 0, None) == -1
+    assert f(table, p, 2, 10, 1.0, p, p, ctypes.c_void_p(FAKE + 2), p, ws_n, 0, None) == -4
+    assert f(table, p, 2, 10, 1.0, p, p, p, p, ws_n - 1, 0, None) == -6
+    rn = L.etg_logits_raw_workspace(table, 3, 0)
+    assert rn == L.etg_logits_topk_workspace_ex(table, 3, 1, 0) > 0
+    g = L.etg_logits_raw
+    assert g(table, p, 3, None, p, rn, 0, None) == -1
+    assert g(table, p, 3, ctypes.c_void_p(FAKE + 1), p, rn, 0, None) == -4
+    assert g(table, p, 3, p, p, rn - 1, 0, None) == -6
+    assert g(table, p, 0, p, p, rn, 0, None) == -3
+    assert g(None, p, 3, p, p, rn, 0, None) == -1
+
+
+def test_f16_tables_take_the_valu_path(L):
+    st, h = _create(L, FAKE, etg.F16, 1000, 64)
+    assert st == 0
+    assert L.etg_logits_topk_workspace_ex(h, 1, 5, etg.PATH_STREAM) == -5
+    assert L.etg_logits_topk_workspace_ex(h, 4, 5, etg.PATH_AUTO) == L.etg_logits_topk_workspace_ex(
+        h, 4, 5, etg.PATH_VALU) > 0
+    L.etg_table_destroy(h)
 
 
 def test_python_binding_rejects_host_tensors():

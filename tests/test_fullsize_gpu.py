@@ -88,3 +88,40 @@ def test_lm31b_tied_gather_then_logits():
     torch.cuda.synchronize()
     # a row's dot product with itself is its squared norm, by far the largest logit here
     assert gids.cpu().numpy()[:, 0].tolist() == ids.tolist()
+
+
+@pytest.mark.parametrize("B,T", [(1, 1.0), (8, 0.7)])
+def test_lm31b_probs_full_pass(B, T):
+    # probabilities at the bench's shape: the oracle's full log-partition of row 0
+    cfg, host, t = _table("lm31b")
+    R = synth.residuals(B, cfg.d, cfg.residual_seed(B))
+    note(f"logits_topk_probs lm31b B={B} T={T}")
+    ids, sc, pr = t.logits_topk_probs(to_dev(R), 10, temperature=T)
+    torch.cuda.synchronize()
+    ids, sc, pr = ids.cpu().numpy(), sc.cpu().numpy(), pr.cpu().numpy()
+    L, A = oracle.logits(host, cfg.dtype, cfg.V, cfg.d, R[:1])
+    oids, _ = oracle.topk(L, 10)
+    c = accept.tol_coeff(cfg.dtype)
+    fails = accept.check_full(ids[:1], sc[:1], L, A, oids, c)
+    fails += accept.check_probs(ids[:1], pr[:1], T, c, L, A)
+    assert not fails, fails[:5]
+    assert np.all((pr > 0) & (pr <= 1)) and np.all(np.diff(pr, axis=1) <= 0)
+
+
+def test_lm31b_raw_logits_b1():
+    # raw logits mode at the bench's shape: sampled entries against the oracle,
+    # and the top-k of the vector against the top-k call
+    cfg, host, t = _table("lm31b")
+    R = synth.residuals(1, cfg.d, cfg.residual_seed(1))
+    note("logits_raw lm31b B=1")
+    raw = t.logits_raw(to_dev(R))
+    ids, sc = t.logits_topk(to_dev(R), 10)
+    torch.cuda.synchronize()
+    raw, ids, sc = raw.cpu().numpy()[0], ids.cpu().numpy()[0], sc.cpu().numpy()[0]
+    g = np.random.default_rng(5)
+    vids = np.concatenate([g.integers(0, cfg.V, 2000), [0, cfg.V - 1], ids]).astype(np.int32)
+    Lv, Av = oracle.logits_at(host, cfg.dtype, cfg.V, cfg.d, R, np.zeros(vids.size, np.int64), vids)
+    assert np.all(np.abs(raw[vids].astype(np.float64) - Lv) <= accept.tol_coeff(cfg.dtype) * Av)
+    assert np.array_equal(raw[ids].view(np.uint32), sc.view(np.uint32))
+    order = np.lexsort((np.arange(cfg.V), -(raw.astype(np.float64) + 0.0)))
+    assert np.array_equal(order[:10], ids)

@@ -10,7 +10,7 @@ from tests.gpu_util import bits, ids_dev, note, table
 
 pytestmark = pytest.mark.gpu
 
-F32, BF16, Q8_0 = etg.F32, etg.BF16, etg.Q8_0
+F32, BF16, Q8_0, F16 = etg.F32, etg.BF16, etg.Q8_0, etg.F16
 
 
 def _gather_both(host, dtype, V, d, ids, scaled):
@@ -40,7 +40,8 @@ def test_scale_constants_agree():
 
 
 @pytest.mark.parametrize("dtype,d", [(F32, 4), (F32, 100), (BF16, 8), (BF16, 200), (BF16, 896),
-                                     (Q8_0, 32), (Q8_0, 96), (Q8_0, 768), (Q8_0, 896), (Q8_0, 4096)])
+                                     (Q8_0, 32), (Q8_0, 96), (Q8_0, 768), (Q8_0, 896), (Q8_0, 4096),
+                                     (F16, 8), (F16, 200), (F16, 2560)])
 @pytest.mark.parametrize("n", [1, 65, 1000])
 def test_gather_shapes_bit_exact(dtype, d, n):
     V = 3001
@@ -71,8 +72,12 @@ def test_gather_special_values_bit_exact():
     blk[0, 0, 2:4] = np.array([-128, 127], np.int8).view(np.uint8)
     blk[0, 1, 2:4] = np.array([-128, 127], np.int8).view(np.uint8)
     blk[1, 0, :2] = [0x00, 0x80]                          # scale = -0
+    h = np.clip(f, -60000, 60000).astype(np.float16).view(np.uint16)
+    h[0, :6] = [0x0001, 0x8001, 0x03FF, 0x7BFF, 0xFBFF, 0x8000]  # subnormals, max finite, -0
+    h[1, :2] = [0x0400, 0x3C00]                           # smallest normal, 1.0
+    h[2] = np.linspace(-5, 5, d, dtype=np.float32).astype(np.float16).view(np.uint16)
     ids = np.arange(V, dtype=np.int32)
-    for host, dt in ((f, F32), (b, BF16), (q, Q8_0)):
+    for host, dt in ((f, F32), (b, BF16), (q, Q8_0), (h, F16)):
         for scaled in (False, True):
             out, ref, _ = _gather_both(host, dt, V, d, ids, scaled)
             assert np.array_equal(bits(out), bits(ref)), (dt, scaled)

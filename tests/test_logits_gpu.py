@@ -17,7 +17,7 @@ from tests.gpu_util import note, table, to_dev
 
 pytestmark = pytest.mark.gpu
 
-F32, BF16, Q8_0 = etg.F32, etg.BF16, etg.Q8_0
+F32, BF16, Q8_0, F16 = etg.F32, etg.BF16, etg.Q8_0, etg.F16
 VALU, STREAM, GEMM, WIDE = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE
 ALL = [VALU, STREAM, GEMM, WIDE]
 
@@ -47,7 +47,7 @@ def test_tiny_config_f32():
 
 
 @pytest.mark.parametrize("dtype,V,d", [(F32, 2049, 100), (BF16, 5003, 200), (BF16, 4099, 896),
-                                       (Q8_0, 3001, 96), (Q8_0, 2000, 768)])
+                                       (Q8_0, 3001, 96), (Q8_0, 2000, 768), (F16, 2049, 104), (F16, 4099, 896)])
 @pytest.mark.parametrize("B", [1, 3, 9])
 def test_valu_path_ragged(dtype, V, d, B):
     host = synth.make_table(dtype, V, d, seed=100 + V)
@@ -197,3 +197,24 @@ def test_residual_at_bf16_midpoints_stays_within_tolerance(path, B, d):
         exact = R[b].astype(np.float64) @ row
         assert abs(single - exact) > 2e-3 * (np.abs(R[b]).astype(np.float64) @ np.abs(row))
     full_check(host, BF16, V, d, R, 5, path)
+
+
+def test_untied_lm_head_is_a_second_handle():
+    # ADR-0008 "Vindex Slice: embed": lm_head.bin is the embeddings when tied, else
+    # its own matrix.  Gather from an f16 embedding table, project through a
+    # separate bf16 lm_head table of another vocabulary size.
+    Ve, Vh, d = 3000, 4099, 256
+    emb = synth.make_table(F16, Ve, d, seed=90)
+    head = synth.make_table(BF16, Vh, d, seed=91)
+    te, th = table(emb, F16, Ve, d), table(head, BF16, Vh, d)
+    ids = synth.uniform_ids(5, Ve, seed=92)
+    note("untied: gather f16, logits bf16")
+    x = te.embed_gather(torch.from_numpy(ids).cuda())
+    gids, gsc = th.logits_topk(x, 10)
+    torch.cuda.synchronize()
+    xr, _ = oracle.embed_gather(emb, F16, Ve, d, ids)
+    assert np.array_equal(x.cpu().numpy().view(np.uint32), xr.view(np.uint32))
+    L, A = oracle.logits(head, BF16, Vh, d, xr)
+    oids, _ = oracle.topk(L, 10)
+    fails = accept.check_full(gids.cpu().numpy(), gsc.cpu().numpy(), L, A, oids, accept.tol_coeff(BF16))
+    assert not fails, fails[:3]

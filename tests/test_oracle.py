@@ -17,8 +17,8 @@ import oracle
 from oracle import accept
 from tests.conftest import read_golden
 
-F32, BF16, Q8_0 = oracle.F32, oracle.BF16, oracle.Q8_0
-DT = {"f32": F32, "bf16": BF16, "q8_0": Q8_0}
+F32, BF16, Q8_0, F16 = oracle.F32, oracle.BF16, oracle.Q8_0, oracle.F16
+DT = {"f32": F32, "bf16": BF16, "q8_0": Q8_0, "f16": F16}
 
 
 # ---------------------------------------------------------------- sizes (pages)
@@ -130,6 +130,11 @@ def _table(dtype, V, d, seed=0):
     if dtype == BF16:
         x = torch.from_numpy((g.standard_normal((V, d)) * 0.02).astype(np.float32))
         return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if dtype == F16:
+        # N(0, 0.02) plus subnormal and extreme binary16 patterns
+        h = (g.standard_normal((V, d)) * 0.02).astype(np.float16).view(np.uint16)
+        h.reshape(-1)[:6] = [0x0001, 0x03ff, 0x8001, 0x7bff, 0xfbff, 0x8000]
+        return h
     nb = d // 32
     out = np.empty((V, nb, 34), np.uint8)
     sc = np.abs(g.standard_normal((V, nb)) * 0.01).astype(np.float16)
@@ -144,13 +149,15 @@ def _library_dequant(table, dtype, V, d):
         return table.astype(np.float64)
     if dtype == BF16:
         return torch.from_numpy(table.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    if dtype == F16:
+        return table.view(np.float16).astype(np.float64)
     blk = table.reshape(V, d // 32, 34)
     s = blk[:, :, :2].copy().view("<f2").astype(np.float64)          # [V, nb, 1]
     q = blk[:, :, 2:].view(np.int8).astype(np.float64)                # [V, nb, 32]
     return (q * s).reshape(V, d)
 
 
-@pytest.mark.parametrize("dtype", [F32, BF16, Q8_0])
+@pytest.mark.parametrize("dtype", [F32, BF16, Q8_0, F16])
 def test_gather_equals_library_dequant_rows(dtype):
     V, d = 300, 96
     t = _table(dtype, V, d, seed=dtype)
@@ -161,7 +168,7 @@ def test_gather_equals_library_dequant_rows(dtype):
     assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("dtype", [F32, BF16, Q8_0])
+@pytest.mark.parametrize("dtype", [F32, BF16, Q8_0, F16])
 def test_gather_scale_is_one_f32_rounding(dtype):
     V, d = 64, 768
     t = _table(dtype, V, d, seed=10 + dtype)
@@ -230,7 +237,7 @@ def test_gather_empty():
 
 
 # ---------------------------------------------------------------- logits
-@pytest.mark.parametrize("dtype", [F32, BF16, Q8_0])
+@pytest.mark.parametrize("dtype", [F32, BF16, Q8_0, F16])
 def test_logits_match_numpy_float64(dtype):
     V, d, B = 517, 256, 3
     t = _table(dtype, V, d, seed=20 + dtype)
