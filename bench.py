@@ -11,8 +11,8 @@ value = algorithmic bytes of the step / time per step, in GB/s.  The roofline
 object times the table-streaming kernel alone with HIP events recorded on the
 stream it runs on.  The other workloads of the page set (batches of 8 to 64,
 the response with probabilities, the raw logits mode, the 1,024-row
-contraction, the EmbeddingGemma-shaped Q8_0 gather) are measured after the
-timed steps and reported under "also".  The CPU oracle is timed on a
+contraction, the EmbeddingGemma-shaped Q8_0 gather with f32, f16 and i8
+output rows) are measured after the timed steps and reported under "also".  The CPU oracle is timed on a
 bounded sample of the same workload under "cpu_baseline".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -338,6 +338,17 @@ def main() -> int:
             "rows_per_s": round(gids.numel() / (mg * 1e-3)), "alg_GBps": round(alg / (mg * 1e-3) / 1e9, 1)}
         out["gather_rows_per_s"] = also["gemma_embed_gather_q8_0_x_sqrt_d"]["rows_per_s"]
         log(f"gather: {mg * 1e3:.1f} us")
+        # the same gather with its output in the f16 and i8 residual wire formats
+        for wname, wire in (("f16", etg.WIRE_F16), ("i8", etg.WIRE_I8)):
+            wb = torch.empty((gids.numel(), etg.wire_row_bytes(wire, g.d)), dtype=torch.uint8, device=dev)
+            f = lambda: gt.embed_gather_wire(gids, wire, scale="sqrt_d", out=wb)
+            f()
+            mw, _ = _timed(torch, f, 100)
+            algw = U * g.row_bytes + gids.numel() * wb.shape[1] + gids.numel() * 4
+            also[f"gemma_embed_gather_q8_0_x_sqrt_d_{wname}_wire"] = {
+                "us_per_call": round(mw * 1e3, 2), "rows_per_s": round(gids.numel() / (mw * 1e-3)),
+                "bytes_per_row_out": int(wb.shape[1]), "alg_GBps": round(algw / (mw * 1e-3) / 1e9, 1)}
+            del wb
         del gt
         torch.cuda.empty_cache()
 

@@ -19,6 +19,7 @@ import os
 import torch
 
 F32, BF16, Q8_0, F16 = 0, 1, 2, 3
+WIRE_F32, WIRE_F16, WIRE_I8 = 0, 1, 2
 PATH_AUTO, PATH_VALU, PATH_STREAM, PATH_GEMM, PATH_WIDE = 0, 1, 2, 3, 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libetg.so")
@@ -46,6 +47,9 @@ SIGNATURES = {
     "etg_logits_topk_probs": (_I32, [_VP, _VP, _I64, _I32, _F, _VP, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP]),
     "etg_logits_raw_workspace": (_I64, [_VP, _I64, _I32]),
     "etg_logits_raw": (_I32, [_VP, _VP, _I64, _VP, _VP, ctypes.c_size_t, _I32, _VP]),
+    "etg_wire_row_bytes": (_I64, [_I32, _I64]),
+    "etg_embed_gather_wire": (_I32, [_VP, _VP, _I64, _F, _I32, _VP, _VP, _VP]),
+    "etg_logits_topk_wire": (_I32, [_VP, _VP, _I32, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP]),
     "etg_last_error": (ctypes.c_char_p, []),
 }
 
@@ -172,6 +176,27 @@ class Table:
                     raise ValueError(f"bad token id: {nbad} of {n} ids are not in [0, {self.vocab})")
         return out
 
+    def embed_gather_wire(self, ids: torch.Tensor, wire: int, scale=None, out: torch.Tensor | None = None,
+                          bad_count: torch.Tensor | None = None) -> torch.Tensor:
+        """Rows encoded in a residual wire format: uint8 [n, wire_row_bytes(wire, hidden)]
+        (ADR-0009: f16, or per-position [scale][zero point][int8 x hidden]).  No check
+        of bad ids beyond counting them into ``bad_count`` if one is given."""
+        if ids.dtype != torch.int32 or ids.device != self.device:
+            raise ValueError("ids must be an int32 tensor on the table's device")
+        ids = ids.contiguous().view(-1)
+        n = ids.numel()
+        rb = wire_row_bytes(wire, self.hidden)
+        sc = 1.0 if scale is None else (sqrt_d(self.hidden) if scale == "sqrt_d" else float(scale))
+        if out is None:
+            out = torch.empty((n, rb), dtype=torch.uint8, device=self.device)
+        elif out.numel() * out.element_size() != n * rb or not out.is_contiguous():
+            raise ValueError("out must be a contiguous buffer of n * wire_row_bytes bytes")
+        bad_ptr = _ptr(bad_count) if bad_count is not None else None
+        with torch.cuda.device(self.device):
+            _check(lib().etg_embed_gather_wire(self._h, _ptr(ids), n, sc, int(wire), _ptr(out), bad_ptr,
+                                               _stream_ptr(self.device)))
+        return out
+
     # ------------------------------------------------------------------ logits
     def workspace_bytes(self, batch: int, k: int, path: int = PATH_AUTO) -> int:
         n = int(lib().etg_logits_topk_workspace_ex(self._h, int(batch), int(k), int(path)))
@@ -236,6 +261,25 @@ class Table:
                                                int(path), _stream_ptr(self.device)))
         return ids, scores, probs
 
+    def logits_topk_wire(self, residual: torch.Tensor, wire: int, k: int, path: int = PATH_AUTO,
+                         workspace: torch.Tensor | None = None):
+        """Top-k (ids, logits) of residual rows given in a wire format: a contiguous
+        device buffer of batch * wire_row_bytes(wire, hidden) bytes."""
+        rb = wire_row_bytes(wire, self.hidden)
+        nbytes = residual.numel() * residual.element_size()
+        if residual.device != self.device or not residual.is_contiguous() or nbytes % rb:
+            raise ValueError("residual must be a contiguous device buffer of whole wire rows")
+        B = nbytes // rb
+        if workspace is None:
+            workspace = self.workspace(B, k, path)
+        ids = torch.empty((B, k), dtype=torch.int32, device=self.device)
+        scores = torch.empty((B, k), dtype=torch.float32, device=self.device)
+        with torch.cuda.device(self.device):
+            _check(lib().etg_logits_topk_wire(self._h, _ptr(residual), int(wire), B, int(k), _ptr(ids), _ptr(scores),
+                                              _ptr(workspace), workspace.numel(), int(path),
+                                              _stream_ptr(self.device)))
+        return ids, scores
+
     def logits_raw(self, residual: torch.Tensor, path: int = PATH_AUTO, out: torch.Tensor | None = None,
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
         """Raw logits mode: f32 [B, vocab] = residual @ table.T."""
@@ -255,6 +299,13 @@ class Table:
             _check(lib().etg_logits_raw(self._h, _ptr(R), B, _ptr(out), _ptr(workspace), workspace.numel(),
                                         int(path), _stream_ptr(self.device)))
         return out
+
+
+def wire_row_bytes(wire: int, hidden: int) -> int:
+    n = int(lib().etg_wire_row_bytes(int(wire), int(hidden)))
+    if n < 0:
+        raise ValueError(f"unknown wire format {wire} or hidden {hidden}")
+    return n
 
 
 def embed_gather(table: Table, ids: torch.Tensor, scale=None, **kw) -> torch.Tensor:

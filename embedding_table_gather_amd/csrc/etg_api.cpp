@@ -126,6 +126,37 @@ int32_t etg_embed_gather(const etg_table* t, const int32_t* d_ids, int64_t seq_l
   return ETG_OK;
 }
 
+int64_t etg_wire_row_bytes(int32_t wire, int64_t hidden) {
+  if (hidden < 1 || hidden > kMaxHidden) return -1;
+  switch (wire) {
+    case ETG_WIRE_F32: return 4 * hidden;
+    case ETG_WIRE_F16: return 2 * hidden;
+    case ETG_WIRE_I8: return hidden + 8;
+    default: return -1;
+  }
+}
+
+int32_t etg_embed_gather_wire(const etg_table* t, const int32_t* d_ids, int64_t seq_len, float scale, int32_t wire,
+                              void* d_out, int32_t* d_bad_count, void* stream) {
+  if (wire == ETG_WIRE_F32) return etg_embed_gather(t, d_ids, seq_len, scale, (float*)d_out, d_bad_count, stream);
+  if (wire != ETG_WIRE_F16 && wire != ETG_WIRE_I8) return fail(ETG_ERANGE, "unknown wire format %d", wire);
+  if (t == nullptr) return fail(ETG_EINVAL, "table handle is NULL");
+  if (seq_len < 0 || seq_len > 2147483647LL)
+    return fail(ETG_ESHAPE, "seq_len %lld outside [0, 2^31 - 1]", (long long)seq_len);
+  if (seq_len == 0) return ETG_OK;
+  if (d_ids == nullptr) return fail(ETG_EINVAL, "ids pointer is NULL");
+  if (d_out == nullptr) return fail(ETG_EINVAL, "output pointer is NULL");
+  if (!aligned(d_ids, 4)) return fail(ETG_EALIGN, "ids pointer is not 4-byte aligned");
+  if (!aligned(d_out, 4)) return fail(ETG_EALIGN, "output pointer is not 4-byte aligned");
+  if (d_bad_count != nullptr && !aligned(d_bad_count, 4))
+    return fail(ETG_EALIGN, "bad-count pointer is not 4-byte aligned");
+  if (!std::isfinite(scale)) return fail(ETG_ERANGE, "scale is not finite");
+  hipError_t e = etg::launch_gather_wire(t->d, d_ids, seq_len, scale, wire, (uint8_t*)d_out, d_bad_count,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ETG_EHIP, "gather launch failed: %s", hipGetErrorString(e));
+  return ETG_OK;
+}
+
 int64_t etg_logits_topk_workspace_ex(const etg_table* t, int64_t batch, int32_t k, int32_t path) {
   int32_t st = check_logits_args(t, batch, k);
   if (st != ETG_OK) return st;
@@ -146,16 +177,21 @@ namespace {
 
 // Shared body of the logits entry points: argument checks, plan, launch.
 // ids == nullptr selects the raw logits mode (k = 1 internally, no merge).
-int32_t run_logits(const etg_table* t, const float* d_residual, int64_t batch, int32_t k, int32_t* d_topk_ids,
+int32_t run_logits(const etg_table* t, const void* d_residual, int64_t batch, int32_t k, int32_t* d_topk_ids,
                    float* d_topk_scores, float* d_topk_probs, float temperature, float* d_logits,
                    void* d_workspace, size_t workspace_bytes, int32_t path, void* event_before, void* event_after,
-                   void* stream) {
+                   void* stream, int32_t wire = ETG_WIRE_F32) {
   int32_t st = check_logits_args(t, batch, k);
   if (st != ETG_OK) return st;
+  if (wire != ETG_WIRE_F32 && wire != ETG_WIRE_F16 && wire != ETG_WIRE_I8)
+    return fail(ETG_ERANGE, "unknown wire format %d", wire);
+  if (wire == ETG_WIRE_F16 && !aligned(d_residual, 2))
+    return fail(ETG_EALIGN, "f16 residual pointer is not 2-byte aligned");
   const bool raw = d_topk_ids == nullptr;
   if (d_residual == nullptr || d_workspace == nullptr || (raw ? d_logits == nullptr : d_topk_scores == nullptr))
     return fail(ETG_EINVAL, "a residual, output or workspace pointer is NULL");
-  if (!aligned(d_residual, 4) || (!raw && (!aligned(d_topk_ids, 4) || !aligned(d_topk_scores, 4))) ||
+  if ((wire != ETG_WIRE_F16 && !aligned(d_residual, 4)) ||
+      (!raw && (!aligned(d_topk_ids, 4) || !aligned(d_topk_scores, 4))) ||
       !aligned(d_topk_probs, 4) || !aligned(d_logits, 4))
     return fail(ETG_EALIGN, "residual and output pointers must be 4-byte aligned");
   if (!aligned(d_workspace, 256)) return fail(ETG_EALIGN, "workspace pointer is not 256-byte aligned");
@@ -174,7 +210,7 @@ int32_t run_logits(const etg_table* t, const float* d_residual, int64_t batch, i
     return fail(ETG_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.ws_bytes);
   hipError_t e = etg::launch_logits_topk(t->d, p, d_residual, d_topk_ids, d_topk_scores, d_workspace,
                                          (hipStream_t)stream, (hipEvent_t)event_before, (hipEvent_t)event_after,
-                                         d_logits, d_topk_probs, lse_scale);
+                                         d_logits, d_topk_probs, lse_scale, wire);
   if (e != hipSuccess) return fail(ETG_EHIP, "logits launch failed: %s", hipGetErrorString(e));
   return ETG_OK;
 }
@@ -198,6 +234,14 @@ int32_t etg_logits_topk_probs(const etg_table* t, const float* d_residual, int64
   if (d_topk_ids == nullptr || d_topk_probs == nullptr) return fail(ETG_EINVAL, "ids or probs pointer is NULL");
   return run_logits(t, d_residual, batch, k, d_topk_ids, d_topk_scores, d_topk_probs, temperature, nullptr,
                     d_workspace, workspace_bytes, path, nullptr, nullptr, stream);
+}
+
+int32_t etg_logits_topk_wire(const etg_table* t, const void* d_residual, int32_t wire, int64_t batch, int32_t k,
+                             int32_t* d_topk_ids, float* d_topk_scores, void* d_workspace, size_t workspace_bytes,
+                             int32_t path, void* stream) {
+  if (d_topk_ids == nullptr) return fail(ETG_EINVAL, "ids pointer is NULL");
+  return run_logits(t, d_residual, batch, k, d_topk_ids, d_topk_scores, nullptr, 0.f, nullptr, d_workspace,
+                    workspace_bytes, path, nullptr, nullptr, stream, wire);
 }
 
 int64_t etg_logits_raw_workspace(const etg_table* t, int64_t batch, int32_t path) {

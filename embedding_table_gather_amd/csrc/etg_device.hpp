@@ -149,4 +149,40 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h16) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)h16);
 }
 
+// f32 -> binary16 bits, round to nearest even, clamped to +-65504 (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_f16_sat(float x) {
+  return __builtin_bit_cast(unsigned short, (_Float16)fminf(fmaxf(x, -65504.f), 65504.f));
+}
+
+// Exact value c of a stored row (f32 copy, bf16 / f16 widening, Q8_0 int8 * scale).
+template <int DT>
+__device__ __forceinline__ float deq_value(const uint8_t* row, int c) {
+  if constexpr (DT == DT_F32) {
+    return ((const float*)row)[c];
+  } else if constexpr (DT == DT_BF16) {
+    return __uint_as_float((uint32_t)((const uint16_t*)row)[c] << 16);
+  } else if constexpr (DT == DT_F16) {
+    return f16_bits_to_f32(((const uint16_t*)row)[c]);
+  } else {
+    const uint8_t* blk = row + 34 * (c >> 5);
+    const float s = f16_bits_to_f32(*(const uint16_t*)blk);
+    return (float)(int8_t)blk[2 + (c & 31)] * s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Residual wire formats (ADR-0009 "Wire Layout"), for rows of `hidden` values:
+//   WIRE_F32  binary32 [B][hidden]
+//   WIRE_F16  binary16 [B][hidden]
+//   WIRE_I8   per row: [scale f32][zero point f32 (0)][int8 x hidden], value = q * scale
+// ---------------------------------------------------------------------------
+enum { WIRE_F32 = 0, WIRE_F16 = 1, WIRE_I8 = 2 };
+
+__device__ __forceinline__ float residual_value(const void* R, int wire, int64_t b, int hidden, int c) {
+  if (wire == WIRE_F32) return ((const float*)R)[b * hidden + c];
+  if (wire == WIRE_F16) return f16_bits_to_f32(((const uint16_t*)R)[b * hidden + c]);
+  const uint8_t* row = (const uint8_t*)R + b * (int64_t)(hidden + 8);
+  return (float)(int8_t)row[8 + c] * *(const float*)row;
+}
+
 }  // namespace etg

@@ -62,11 +62,13 @@ struct LogitsPlan {
 //             (nullable; (-inf, 0) for a slice with no rows)
 //  lse_scale  log2(e) / temperature
 //  aux        the plan's aux area of the workspace
+//  wire       encoding of the residual rows (0 f32, 1 f16, 2 per-row symmetric i8)
 struct LogitsExtras {
   float* logits = nullptr;
   float2* lse = nullptr;
   float lse_scale = 0.f;
   void* aux = nullptr;
+  int32_t wire = 0;
 };
 
 // Returns 0 or a negative etg_status; fills *plan.  `why` receives a short reason.
@@ -75,15 +77,19 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
 
 hipError_t launch_gather(const TableDesc& t, const int32_t* ids, int64_t n, float scale,
                          float* out, int32_t* bad, hipStream_t stream);
+// Gather with the rows written in wire format 1 (f16) or 2 (i8) to `out`.
+hipError_t launch_gather_wire(const TableDesc& t, const int32_t* ids, int64_t n, float scale, int32_t wire,
+                              uint8_t* out, int32_t* bad, hipStream_t stream);
 
 // ev_before / ev_after (nullable) are recorded around the table-streaming kernel.
 // With want_logits the raw logits go to `logits`; with `probs` (nullable) the
 // merge also writes the softmax probabilities at log2(e) / lse_scale temperature;
 // with ids == nullptr only the table kernel runs (raw logits mode).
-hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const float* R,
+hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const void* R,
                               int32_t* ids, float* scores, void* ws, hipStream_t stream,
                               hipEvent_t ev_before = nullptr, hipEvent_t ev_after = nullptr,
-                              float* logits = nullptr, float* probs = nullptr, float lse_scale = 0.f);
+                              float* logits = nullptr, float* probs = nullptr, float lse_scale = 0.f,
+                              int32_t wire = 0);
 
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kTargetBlocks = 256;  // one workgroup per MI355X compute unit
@@ -107,11 +113,11 @@ inline hipError_t record_event(hipEvent_t ev, hipStream_t stream) {
 int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
-hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
+hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
                          const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
-hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* img, uint64_t* cand,
+hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
                        uint64_t* thr, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
-hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs, uint64_t* cand,
+hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs, uint64_t* cand,
                        const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace etg

@@ -206,6 +206,80 @@ __global__ void __launch_bounds__(256) gather_q8_aligned_kernel(const uint8_t* _
   }
 }
 
+// Gather with the output rows in a residual wire format (ADR-0009 "Wire Layout";
+// the embed output may travel as f16 or as per-position symmetric i8).  x is the
+// value the f32 gather writes (exact dequant, then the optional scale):
+//   wire 1 (f16): binary16 of x, round to nearest even, clamped to +-65504;
+//   wire 2 (i8):  [scale f32][zero point 0 f32][int8 x hidden] per row with
+//                 scale = max|x| / 127 and q = round-half-even(x / scale), all in
+//                 f32, clamped to [-127, 127]; a row with scale 0 is all zeros.
+// A bad id gives an all-zero record.  One wave per row; the i8 codes take a second
+// pass over the source row (L1/L2 hits) once the row maximum is known.
+template <int DT, bool SCALE>
+__global__ void __launch_bounds__(256) gather_wire_kernel(const uint8_t* __restrict__ table, uint32_t V,
+                                                          int hidden, int64_t row_bytes,
+                                                          const int32_t* __restrict__ ids, int64_t n, float scale,
+                                                          int wire, uint8_t* __restrict__ out,
+                                                          int32_t* __restrict__ bad) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kGatherWaves + (threadIdx.x >> 6);
+  if (row >= n) return;  // whole wave; no block-level barrier
+  const uint32_t id = (uint32_t)ids[row];
+  const int64_t orb = wire == WIRE_F16 ? 2 * (int64_t)hidden : (int64_t)hidden + 8;  // a multiple of 4
+  uint8_t* o = out + row * orb;
+  if (id >= V) {
+    for (int i = lane; i < (int)(orb >> 2); i += 64) ((uint32_t*)o)[i] = 0u;
+    if (lane == 0 && bad != nullptr) atomicAdd(bad, 1);
+    return;
+  }
+  const uint8_t* src = table + (uint64_t)id * (uint64_t)row_bytes;
+  auto value = [&](int c) {
+    const float x = deq_value<DT>(src, c);
+    return SCALE ? x * scale : x;
+  };
+  if (wire == WIRE_F16) {
+    uint16_t* o16 = (uint16_t*)o;
+    for (int c = lane; c < hidden; c += 64) o16[c] = (uint16_t)f32_to_f16_sat(value(c));
+    return;
+  }
+  float m = 0.f;
+  for (int c = lane; c < hidden; c += 64) m = fmaxf(m, fabsf(value(c)));
+  m = wave_max_f32(m);
+  const float sc = m / 127.0f;  // correctly rounded f32 division
+  if (lane == 0) {
+    ((float*)o)[0] = sc;
+    ((float*)o)[1] = 0.f;
+  }
+  int8_t* q = (int8_t*)(o + 8);
+  for (int c = lane; c < hidden; c += 64) {
+    const float v = sc != 0.f ? fminf(fmaxf(rintf(value(c) / sc), -127.f), 127.f) : 0.f;
+    q[c] = (int8_t)(int)v;
+  }
+}
+
+template <int DT>
+static hipError_t launch_wire_dt(const TableDesc& t, const int32_t* ids, int64_t n, float scale, int32_t wire,
+                                 uint8_t* out, int32_t* bad, hipStream_t stream) {
+  const dim3 grid((unsigned)((n + kGatherWaves - 1) / kGatherWaves)), block(64 * kGatherWaves);
+  if (!(scale == 1.0f))
+    hipLaunchKernelGGL((gather_wire_kernel<DT, true>), grid, block, 0, stream, t.rows, (uint32_t)t.V,
+                       (int)t.hidden, t.row_bytes, ids, n, scale, (int)wire, out, bad);
+  else
+    hipLaunchKernelGGL((gather_wire_kernel<DT, false>), grid, block, 0, stream, t.rows, (uint32_t)t.V,
+                       (int)t.hidden, t.row_bytes, ids, n, scale, (int)wire, out, bad);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_wire(const TableDesc& t, const int32_t* ids, int64_t n, float scale, int32_t wire,
+                              uint8_t* out, int32_t* bad, hipStream_t stream) {
+  switch (t.dtype) {
+    case DT_F32: return launch_wire_dt<DT_F32>(t, ids, n, scale, wire, out, bad, stream);
+    case DT_BF16: return launch_wire_dt<DT_BF16>(t, ids, n, scale, wire, out, bad, stream);
+    case DT_F16: return launch_wire_dt<DT_F16>(t, ids, n, scale, wire, out, bad, stream);
+    default: return launch_wire_dt<DT_Q8_0>(t, ids, n, scale, wire, out, bad, stream);
+  }
+}
+
 template <int DT>
 static hipError_t launch_dt(const TableDesc& t, const int32_t* ids, int64_t n, float scale, float* out,
                             int32_t* bad, hipStream_t stream) {

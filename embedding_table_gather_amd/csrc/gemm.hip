@@ -87,11 +87,12 @@ __device__ __forceinline__ void gemm_stage_barrier_groups(int groups) {
   }
 }
 
-// fp32 residual [B][hidden] -> split bf16 rows [nct][256][kpad].  Row j of column
+// residual [B][hidden] (f32, or decoded from its wire format) -> split bf16 rows [nct][256][kpad].  Row j of column
 // tile ct belongs to wave column nw = j / WC, N-tile t = (j % WC) / 32; it is the
 // hi (t < NT/2) or lo part of residual row 128 ct + nw WC/2 + (t % (NT/2)) 32 + j % 32.
 // Rows past the batch and values past hidden are zero.
-__global__ void __launch_bounds__(256) gemm_prep_kernel(const float* __restrict__ R, int64_t B, int hidden, int kpad,
+__global__ void __launch_bounds__(256) gemm_prep_kernel(const void* __restrict__ R, int wire, int64_t B, int hidden,
+                                                        int kpad,
                                                         int wc, int64_t nrows, u32x4* __restrict__ Rs) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int kc = kpad / 8;
@@ -108,7 +109,7 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(const float* __restrict_
 #pragma unroll
   for (int e = 0; e < 8; e++) {
     const int c = c0 + e;
-    const float x = (b < B && c < hidden) ? R[b * hidden + c] : 0.0f;
+    const float x = (b < B && c < hidden) ? residual_value(R, wire, b, hidden, c) : 0.0f;
     const uint32_t hi = bf16_rne(x);
     v[e] = part == 1 ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;  // x - hi is exact in f32
   }
@@ -445,13 +446,14 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
 }
 
 template <int WM, int WN, int NA, int NB>
-static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs,
+static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs,
                                   uint64_t* cand, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0,
                                   hipEvent_t ev1) {
   using C = GemmCfg<WM, WN>;
   const int64_t nrows = (int64_t)p.nct * kGemmBN;
   const int64_t nprep = nrows * (p.kpad / 8);
-  hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream, R, p.batch,
+  hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream, R, (int)x.wire,
+                     p.batch,
                      (int)t.hidden, p.kpad, C::WC, nrows, (u32x4*)rs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -464,7 +466,7 @@ static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const
   return record_event(ev1, stream);
 }
 
-hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* rs, uint64_t* cand,
+hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs, uint64_t* cand,
                        const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   // one wave layout: 2 x 4 waves of 128 x 64 (2 x 2 waves of 128 x 128 would spill)
   if (p.gemm_ring == 34) return launch_gemm_cfg<2, 4, 3, 4>(t, p, R, rs, cand, x, stream, ev0, ev1);

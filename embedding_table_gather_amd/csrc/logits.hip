@@ -30,27 +30,12 @@ namespace etg {
 // takes one row at a time, each lane accumulates RB residual rows over values
 // lane, lane + 64, ... with f32 FMAs, then a butterfly sum per residual row.
 // ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ float deq_value(const uint8_t* row, int c) {
-  if constexpr (DT == DT_F32) {
-    return ((const float*)row)[c];
-  } else if constexpr (DT == DT_BF16) {
-    return __uint_as_float((uint32_t)((const uint16_t*)row)[c] << 16);
-  } else if constexpr (DT == DT_F16) {
-    return f16_bits_to_f32(((const uint16_t*)row)[c]);
-  } else {
-    const uint8_t* blk = row + 34 * (c >> 5);
-    const float s = f16_bits_to_f32(*(const uint16_t*)blk);
-    return (float)(int8_t)blk[2 + (c & 31)] * s;
-  }
-}
-
 // logits (nullable [B][V]) receives the raw logits, lse (nullable [B][nblk]) the
 // log-partition partial of the block's rows at lse_c = log2(e) / temperature.
 template <int DT, int RB>
 __global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restrict__ table, int64_t V,
                                                           int64_t row_bytes, int hidden,
-                                                          const float* __restrict__ R, int64_t B, int k,
+                                                          const void* __restrict__ R, int wire, int64_t B, int k,
                                                           uint64_t* __restrict__ cand, float* __restrict__ logits,
                                                           float2* __restrict__ lse, float lse_c) {
   extern __shared__ float vlog[];  // [rows of this block][RB]
@@ -65,11 +50,21 @@ __global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restr
     float acc[RB];
 #pragma unroll
     for (int b = 0; b < RB; b++) acc[b] = 0.f;
-    for (int c = lane; c < hidden; c += 64) {
-      const float x = deq_value<DT>(row, c);
+    if (wire == WIRE_F32) {
+      const float* Rf = (const float*)R;
+      for (int c = lane; c < hidden; c += 64) {
+        const float x = deq_value<DT>(row, c);
 #pragma unroll
-      for (int b = 0; b < RB; b++)
-        if (b < nb) acc[b] = __builtin_fmaf(x, R[(b0 + b) * hidden + c], acc[b]);
+        for (int b = 0; b < RB; b++)
+          if (b < nb) acc[b] = __builtin_fmaf(x, Rf[(b0 + b) * hidden + c], acc[b]);
+      }
+    } else {
+      for (int c = lane; c < hidden; c += 64) {
+        const float x = deq_value<DT>(row, c);
+#pragma unroll
+        for (int b = 0; b < RB; b++)
+          if (b < nb) acc[b] = __builtin_fmaf(x, residual_value(R, wire, b0 + b, hidden, c), acc[b]);
+      }
     }
 #pragma unroll
     for (int b = 0; b < RB; b++) {
@@ -256,7 +251,7 @@ static hipError_t launch_merge(const uint64_t* cand, int64_t batch, int n, int k
 
 
 template <int DT>
-static hipError_t launch_valu(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
+static hipError_t launch_valu(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
                               const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const dim3 grid((unsigned)p.nblk, (unsigned)p.npass), block(256);
   hipError_t e = set_dynamic_lds((const void*)valu_logits_kernel<DT, 1>, p.lds_bytes);
@@ -269,7 +264,8 @@ static hipError_t launch_valu(const TableDesc& t, const LogitsPlan& p, const flo
 #define ETG_VALU_CASE(RBV)                                                                          \
   case RBV:                                                                                         \
     hipLaunchKernelGGL((valu_logits_kernel<DT, RBV>), grid, block, p.lds_bytes, stream, t.rows, t.V, \
-                       t.row_bytes, (int)t.hidden, R, p.batch, p.k, cand, x.logits, x.lse, x.lse_scale);  \
+                       t.row_bytes, (int)t.hidden, R, (int)x.wire, p.batch, p.k, cand, x.logits, x.lse,    \
+                       x.lse_scale);                                                                        \
     break;
     ETG_VALU_CASE(1)
     ETG_VALU_CASE(2)
@@ -282,9 +278,9 @@ static hipError_t launch_valu(const TableDesc& t, const LogitsPlan& p, const flo
   return record_event(ev1, stream);
 }
 
-hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const float* R, int32_t* ids,
+hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const void* R, int32_t* ids,
                               float* scores, void* ws, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
-                              float* logits, float* probs, float lse_scale) {
+                              float* logits, float* probs, float lse_scale, int32_t wire) {
   uint8_t* base = (uint8_t*)ws;
   uint64_t* cand = (uint64_t*)(base + p.cand_offset);
   LogitsExtras x;
@@ -292,6 +288,7 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const flo
   x.lse = probs != nullptr ? (float2*)(base + p.lse_offset) : nullptr;
   x.lse_scale = lse_scale;
   x.aux = base + p.aux_offset;
+  x.wire = wire;
   hipError_t e;
   if (p.path == 2) {
     e = launch_stream(t, p, R, cand, x, stream, ev0, ev1);

@@ -46,10 +46,10 @@ static constexpr int kStreamUnroll = 6;  // K steps per load group (half of it w
 static constexpr int kStreamMaxPairs = 4;  // a wave handles at most 8 groups (64 rows)
 
 // Fill LDS with steps [c0, c0 + n) of the bf16 hi/lo operand image, converted from
-// the fp32 residual rows of this pass.  Image slot (s, im, lane) holds the 8
+// the residual rows of this pass (f32, or decoded from their wire format).  Image slot (s, im, lane) holds the 8
 // values of B column n = lane % 16, K-group g = lane / 16 (layout above).
 template <int NIMG>
-__device__ __forceinline__ void stream_stage_image(u32x4* simg, const float* __restrict__ R, int64_t B,
+__device__ __forceinline__ void stream_stage_image(u32x4* simg, const void* __restrict__ R, int wire, int64_t B,
                                                    int hidden, int64_t b0, int c0, int n) {
   constexpr int NBC = NIMG == 1 ? 4 : 8;
   for (int i = threadIdx.x; i < n * NIMG * 64; i += blockDim.x) {
@@ -66,7 +66,7 @@ __device__ __forceinline__ void stream_stage_image(u32x4* simg, const float* __r
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const int c = cbase + e;
-      const float x = (b < B && c < hidden) ? R[b * hidden + c] : 0.0f;
+      const float x = (b < B && c < hidden) ? residual_value(R, wire, b, hidden, c) : 0.0f;
       const uint32_t hi = bf16_rne(x);
       // part 1 carries the remainder x - hi (exact in f32), rounded to bf16
       v[e] = part == 1 ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;
@@ -118,7 +118,7 @@ __device__ void stream_block_topk(const float* slog, const int64_t* sg0, const i
 
 // One pass over the table for NBC residual rows (pass = blockIdx.y).
 //  table      bf16 [V][hidden], row_bytes = 2 * hidden
-//  R          fp32 [B][hidden]
+//  R          residual rows [B][hidden] in wire format `wire` (0 = fp32)
 //  steps      64-value K steps, ceil(hidden / 64)
 //  chunk      K steps staged in LDS at a time (a multiple of the unroll)
 //  logits     nullable [B][V]: the block's raw logits
@@ -130,7 +130,7 @@ __device__ void stream_block_topk(const float* slog, const int64_t* sg0, const i
 template <int NIMG>
 __global__ void __launch_bounds__(1024) stream_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden,
-    const float* __restrict__ R, int64_t B, int steps, int chunk, int k, uint64_t* __restrict__ cand,
+    const void* __restrict__ R, int wire, int64_t B, int steps, int chunk, int k, uint64_t* __restrict__ cand,
     int64_t ngroups, int max_groups, float* __restrict__ logits, float2* __restrict__ lse, float lse_c) {
   constexpr int NBC = NIMG == 1 ? 4 : 8;
   constexpr int U = NIMG == 1 ? kStreamUnroll : kStreamUnroll / 2;
@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
   for (int c0 = 0; c0 < steps; c0 += chunk) {
     const int c1 = min(steps, c0 + chunk);
     if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
-    stream_stage_image<NIMG>(simg, R, B, hidden, b0, c0, c1 - c0);
+    stream_stage_image<NIMG>(simg, R, wire, B, hidden, b0, c0, c1 - c0);
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kStreamMaxPairs; p++) {
@@ -260,19 +260,19 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
 
 
 template <int NIMG>
-static hipError_t launch_stream_nimg(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
+static hipError_t launch_stream_nimg(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
                                      const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   hipError_t e = set_dynamic_lds((const void*)stream_logits_kernel<NIMG>, p.lds_bytes);
   if (e != hipSuccess) return e;
   if ((e = record_event(ev0, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((stream_logits_kernel<NIMG>), dim3((unsigned)p.nblk, (unsigned)p.npass),
                      dim3(64 * kStreamWaves), p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (int)t.hidden, R,
-                     p.batch, p.steps, p.chunk, p.k, cand, p.ngroups, p.max_groups, x.logits, x.lse, x.lse_scale);
+                     (int)x.wire, p.batch, p.steps, p.chunk, p.k, cand, p.ngroups, p.max_groups, x.logits, x.lse, x.lse_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev1, stream);
 }
 
-hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const float* R, uint64_t* cand,
+hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
                          const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   return p.nimg == 1 ? launch_stream_nimg<1>(t, p, R, cand, x, stream, ev0, ev1)
                      : launch_stream_nimg<2>(t, p, R, cand, x, stream, ev0, ev1);

@@ -53,7 +53,7 @@ __device__ __forceinline__ void lds_barrier() {
 // 64 s + 16 (lane / 16) + 8 pq + e (e = 0..7), as bf16 hi (hl = 0) or lo (hl = 1).
 // Rows past the batch and values past hidden are zero.
 // It also clears the per-row top-k lower bounds thr[B] (total >= B).
-__global__ void __launch_bounds__(256) wide_prep_kernel(const float* __restrict__ R, int64_t B, int hidden,
+__global__ void __launch_bounds__(256) wide_prep_kernel(const void* __restrict__ R, int wire, int64_t B, int hidden,
                                                         int steps_pad, int ntile, int64_t total,
                                                         u32x4* __restrict__ img, uint64_t* __restrict__ thr) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -73,7 +73,7 @@ __global__ void __launch_bounds__(256) wide_prep_kernel(const float* __restrict_
 #pragma unroll
   for (int e = 0; e < 8; e++) {
     const int c = c0 + e;
-    const float x = (b < B && c < hidden) ? R[b * hidden + c] : 0.0f;
+    const float x = (b < B && c < hidden) ? residual_value(R, wire, b, hidden, c) : 0.0f;
     const uint32_t hi = bf16_rne(x);
     v[e] = lo ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;  // x - hi is exact in f32
   }
@@ -349,10 +349,11 @@ static hipError_t launch_wide_nt(const TableDesc& t, const LogitsPlan& p, const 
   return record_event(ev1, stream);
 }
 
-hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const float* R, uint8_t* img, uint64_t* cand,
+hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
                        uint64_t* thr, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const int64_t total = (int64_t)p.npass * p.steps * p.ntile * 256;  // >= 768 npass >= batch
-  hipLaunchKernelGGL(wide_prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, R, p.batch,
+  hipLaunchKernelGGL(wide_prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, R, (int)x.wire,
+                     p.batch,
                      (int)t.hidden, p.steps, p.ntile, total, (u32x4*)img, thr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

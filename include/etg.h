@@ -114,6 +114,34 @@ int32_t etg_table_destroy(etg_table* table);
 int32_t etg_embed_gather(const etg_table* table, const int32_t* d_ids, int64_t seq_len,
                          float scale, float* d_out, int32_t* d_bad_count, void* stream);
 
+/*
+ * Residual wire formats (ADR-0009 "Wire Layout": residuals travel as f32, f16 or
+ * per-position symmetric i8).  A row of `hidden` values is encoded as
+ *   ETG_WIRE_F32  hidden little-endian binary32 (4 * hidden bytes)
+ *   ETG_WIRE_F16  hidden little-endian binary16 (2 * hidden bytes): round to nearest
+ *                 even, clamped to +-65504 (the page's clamp-to-max overflow)
+ *   ETG_WIRE_I8   [scale f32][zero_point f32 = 0][hidden int8] (hidden + 8 bytes):
+ *                 scale = max|x| / 127, q = round-half-even(x / scale), both in f32,
+ *                 clamped to [-127, 127]; decoded as q * scale.  A row with scale 0
+ *                 is all zeros.
+ * Rows are contiguous.
+ */
+typedef enum { ETG_WIRE_F32 = 0, ETG_WIRE_F16 = 1, ETG_WIRE_I8 = 2 } etg_wire;
+
+/* Bytes of one encoded row; -1 for an unknown format or hidden outside [1, 65536]. */
+int64_t etg_wire_row_bytes(int32_t wire, int64_t hidden);
+
+/* etg_embed_gather with the output rows encoded in `wire` (the embed response on the
+ * wire, ADR-0009).  The encoded values are those etg_embed_gather writes (dequant,
+ * then the optional scale); encoding is bit-exact to the definition above.
+ *   d_out   seq_len * etg_wire_row_bytes(wire, hidden) bytes, 4-byte aligned
+ *           (16-byte aligned for ETG_WIRE_F32, which is etg_embed_gather itself).
+ * A bad id gives an all-zero record and is counted as in etg_embed_gather.
+ * Errors: as etg_embed_gather; ETG_ERANGE for an unknown format. */
+int32_t etg_embed_gather_wire(const etg_table* table, const int32_t* d_ids, int64_t seq_len,
+                              float scale, int32_t wire, void* d_out, int32_t* d_bad_count,
+                              void* stream);
+
 /* Kernel path for etg_logits_topk_ex (ETG_PATH_AUTO is what etg_logits_topk uses). */
 typedef enum {
   ETG_PATH_AUTO = 0,   /* f32, f16 and Q8_0 tables: VALU; bf16 tables: STREAM up to 8 rows,
@@ -207,6 +235,17 @@ int64_t etg_logits_raw_workspace(const etg_table* lm_head, int64_t batch, int32_
 int32_t etg_logits_raw(const etg_table* lm_head, const float* d_residual, int64_t batch,
                        float* d_logits, void* d_workspace, size_t workspace_bytes, int32_t path,
                        void* stream);
+
+/* etg_logits_topk_ex with the residual rows in a wire format (the logits request on
+ * the wire, ADR-0009): each value is decoded (f16 widened, i8 as q * scale) where
+ * the kernels read the residual, so the result is bitwise that of etg_logits_topk_ex
+ * on the decoded f32 rows.
+ *   d_residual  batch * etg_wire_row_bytes(wire, hidden) bytes; 2-byte aligned for
+ *               ETG_WIRE_F16, 4-byte aligned otherwise.
+ * Workspace: as etg_logits_topk_ex.  ETG_ERANGE for an unknown format. */
+int32_t etg_logits_topk_wire(const etg_table* lm_head, const void* d_residual, int32_t wire,
+                             int64_t batch, int32_t k, int32_t* d_topk_ids, float* d_topk_scores,
+                             void* d_workspace, size_t workspace_bytes, int32_t path, void* stream);
 
 /* Message of the calling thread's last failed call ("" if none). */
 const char* etg_last_error(void);

@@ -14,6 +14,7 @@ import subprocess
 import numpy as np
 
 F32, BF16, Q8_0, F16 = 0, 1, 2, 3
+WIRE_F32, WIRE_F16, WIRE_I8 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "etg_oracle.c")
@@ -59,6 +60,12 @@ def _load():
     L.orc_logits_at.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, i64, vp, vp]
     L.orc_log_partition.argtypes = [vp, i64, i64, ctypes.c_double, vp]
     L.orc_probs_at.argtypes = [vp, vp, i64, i64, ctypes.c_double, vp, i32, vp]
+    L.orc_wire_row_bytes.restype = i64
+    L.orc_wire_row_bytes.argtypes = [ctypes.c_int, i64]
+    L.orc_f32_to_f16_sat.restype = ctypes.c_uint16
+    L.orc_f32_to_f16_sat.argtypes = [ctypes.c_float]
+    L.orc_wire_encode.argtypes = [vp, i64, i64, ctypes.c_int, vp]
+    L.orc_wire_decode.argtypes = [vp, i64, i64, ctypes.c_int, vp]
     L.orc_set_threads.argtypes = [ctypes.c_int]
     L.orc_max_threads.restype = ctypes.c_int
     _lib = L
@@ -199,4 +206,32 @@ def probs_at(L, ids, T: float) -> np.ndarray:
     lse = log_partition(L, T)
     out = np.empty((B, k), np.float64)
     _load().orc_probs_at(_p(L), _p(lse), B, V, float(T), _p(ids), int(k), _p(out))
+    return out
+
+
+def wire_row_bytes(wire: int, hidden: int) -> int:
+    return int(_load().orc_wire_row_bytes(int(wire), int(hidden)))
+
+
+def f32_to_f16_sat(x: float) -> int:
+    return int(_load().orc_f32_to_f16_sat(float(np.float32(x))))
+
+
+def wire_encode(x, wire: int) -> np.ndarray:
+    """uint8 [n, wire_row_bytes] encoding of float32 rows x [n, hidden]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    n, hidden = x.shape
+    out = np.empty((n, wire_row_bytes(wire, hidden)), np.uint8)
+    _load().orc_wire_encode(_p(x), n, hidden, int(wire), _p(out))
+    return out
+
+
+def wire_decode(rows, hidden: int, wire: int) -> np.ndarray:
+    """float32 [n, hidden] values of wire rows."""
+    rb = wire_row_bytes(wire, hidden)
+    raw = np.ascontiguousarray(rows, dtype=np.uint8).reshape(-1, rb)
+    out = np.empty((raw.shape[0], hidden), np.float32)
+    _load().orc_wire_decode(_p(raw), raw.shape[0], hidden, int(wire), _p(out))
     return out

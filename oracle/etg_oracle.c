@@ -24,6 +24,8 @@
  *   probabilities   ADR-0008 "POST /v1/logits": each listed token with its
  *                   probability at the request's temperature (softmax of L / T
  *                   over the whole vocabulary).
+ *   wire codecs     ADR-0009 "Wire Layout": f16 and per-position symmetric i8
+ *                   encodings of residual rows.
  *
  * Every function here has a pin in tests/test_oracle.py against values fixed
  * by the pages or by mathematics; none is "parity unpinned".
@@ -322,6 +324,117 @@ void orc_probs_at(const double* L, const double* lse, int64_t B, int64_t V, doub
       const uint32_t v = (uint32_t)ids[b * k + j];
       prob[b * k + j] = (uint64_t)v < (uint64_t)V ? exp(L[b * V + v] / T - lse[b]) : NAN;
     }
+}
+
+/*
+ * Residual wire codecs (ADR-0009 "Wire Layout"): the embed output and the
+ * logits input may travel as
+ *   wire 0  f32: hidden little-endian binary32 values per row (4 hidden bytes);
+ *   wire 1  f16: hidden little-endian binary16 values per row (2 hidden bytes);
+ *   wire 2  i8 symmetric, per position: [scale f32][zero_point f32 = 0]
+ *           [hidden int8] (hidden + 8 bytes), scale = max|x| / 127 and
+ *           x^ = q * scale.
+ * Readings: f16 rounds to nearest even and clamps to +-65504 (the page's
+ * clamp-to-max overflow); the i8 code is q = round-half-even(x / scale) taken
+ * in f32, as are max|x| and scale = max|x| / 127.0f (the codes are integers
+ * decided by floating point, so both sides decide in f32), clamped to
+ * [-127, 127]; a row with scale 0 encodes as all zeros.
+ */
+enum { ORC_WIRE_F32 = 0, ORC_WIRE_F16 = 1, ORC_WIRE_I8 = 2 };
+
+int64_t orc_wire_row_bytes(int wire, int64_t hidden) {
+  switch (wire) {
+    case ORC_WIRE_F32: return 4 * hidden;
+    case ORC_WIRE_F16: return 2 * hidden;
+    case ORC_WIRE_I8: return hidden + 8;
+    default: return -1;
+  }
+}
+
+/* Round-half-even of a non-negative double holding an exact small value. */
+static double orc_rne(double m) {
+  double f = floor(m), d = m - f;
+  if (d > 0.5) return f + 1.0;
+  if (d < 0.5) return f;
+  return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+/* Nearest binary16 (ties to even) of a finite float, clamped to +-65504. */
+uint16_t orc_f32_to_f16_sat(float x) {
+  const uint16_t sign = signbit(x) ? 0x8000 : 0;
+  const double a = fabs((double)x);
+  int ex;
+  double q;
+  if (a >= 65504.0) return sign | 0x7BFF;
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: multiples of 2^-24; q = 1024 is the smallest normal */
+    q = orc_rne(ldexp(a, 24));
+    return sign | (uint16_t)q;
+  }
+  frexp(a, &ex);                           /* a = m 2^ex, m in [0.5, 1) */
+  ex -= 1;                                 /* a in [2^ex, 2^(ex+1)), ex >= -14 */
+  q = orc_rne(ldexp(a, 10 - ex));          /* in [1024, 2048] */
+  if (q == 2048.0) {
+    q = 1024.0;
+    ex += 1;
+  }
+  if (ex + 15 >= 31) return sign | 0x7BFF; /* cannot happen below 65504 */
+  return sign | (uint16_t)(((ex + 15) << 10) | ((int)q - 1024));
+}
+
+/* Encode n rows of hidden f32 values into wire rows (orc_wire_row_bytes each). */
+void orc_wire_encode(const float* x, int64_t n, int64_t hidden, int wire, uint8_t* out) {
+  const int64_t rb = orc_wire_row_bytes(wire, hidden);
+  int64_t r, c;
+  for (r = 0; r < n; r++) {
+    const float* xr = x + r * hidden;
+    uint8_t* o = out + r * rb;
+    if (wire == ORC_WIRE_F32) {
+      memcpy(o, xr, (size_t)(4 * hidden));
+    } else if (wire == ORC_WIRE_F16) {
+      for (c = 0; c < hidden; c++) {
+        const uint16_t h = orc_f32_to_f16_sat(xr[c]);
+        o[2 * c] = (uint8_t)(h & 0xFF);
+        o[2 * c + 1] = (uint8_t)(h >> 8);
+      }
+    } else {
+      float m = 0.0f, scale, zero = 0.0f;
+      for (c = 0; c < hidden; c++)
+        if (fabsf(xr[c]) > m) m = fabsf(xr[c]);
+      scale = m / 127.0f;
+      memcpy(o, &scale, 4);
+      memcpy(o + 4, &zero, 4);
+      for (c = 0; c < hidden; c++) {
+        float q = 0.0f;
+        if (scale != 0.0f) {
+          q = rintf(xr[c] / scale);
+          if (q > 127.0f) q = 127.0f;
+          if (q < -127.0f) q = -127.0f;
+        }
+        o[8 + c] = (uint8_t)(int8_t)q;
+      }
+    }
+  }
+}
+
+/* Decode n wire rows into f32 values: f16 widened exactly, i8 as q * scale (one
+ * f32 rounding). */
+void orc_wire_decode(const uint8_t* in, int64_t n, int64_t hidden, int wire, float* out) {
+  const int64_t rb = orc_wire_row_bytes(wire, hidden);
+  int64_t r, c;
+  for (r = 0; r < n; r++) {
+    const uint8_t* row = in + r * rb;
+    float* o = out + r * hidden;
+    if (wire == ORC_WIRE_F32) {
+      memcpy(o, row, (size_t)(4 * hidden));
+    } else if (wire == ORC_WIRE_F16) {
+      for (c = 0; c < hidden; c++) o[c] = (float)orc_f16_to_f64(rd_u16le(row + 2 * c));
+    } else {
+      float scale;
+      memcpy(&scale, row, 4);
+      for (c = 0; c < hidden; c++) o[c] = (float)(int8_t)row[8 + c] * scale;
+    }
+  }
 }
 
 /* Element-wise decoders over arrays (for the decoder pins). */

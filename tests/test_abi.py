@@ -188,3 +188,22 @@ def test_python_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         etg.Table(torch.zeros(16, dtype=torch.int16), etg.BF16, 1, 16)
+
+
+def test_wire_formats(L, table):
+    assert L.etg_wire_row_bytes(etg.WIRE_F32, 5376) == 21504
+    assert L.etg_wire_row_bytes(etg.WIRE_F16, 5120) == 10240        # ADR-0009: half of 20 KB
+    assert L.etg_wire_row_bytes(etg.WIRE_I8, 5120) == 5128          # 8-byte header + one byte per value
+    assert L.etg_wire_row_bytes(3, 64) == -1 and L.etg_wire_row_bytes(etg.WIRE_I8, 0) == -1
+    p = ctypes.c_void_p(FAKE)
+    g = L.etg_embed_gather_wire
+    assert g(table, p, 4, 1.0, 3, p, None, None) == -5
+    assert g(table, p, 4, 1.0, etg.WIRE_I8, ctypes.c_void_p(FAKE + 2), None, None) == -4
+    assert g(table, p, 4, 1.0, etg.WIRE_I8, None, None, None) == -1
+    assert g(table, p, 0, 1.0, etg.WIRE_F16, None, None, None) == 0
+    ws_n = L.etg_logits_topk_workspace(table, 2, 10)
+    f = L.etg_logits_topk_wire
+    assert f(table, p, 3, 2, 10, p, p, p, ws_n, 0, None) == -5
+    assert f(table, ctypes.c_void_p(FAKE + 1), etg.WIRE_F16, 2, 10, p, p, p, ws_n, 0, None) == -4
+    assert f(table, ctypes.c_void_p(FAKE + 2), etg.WIRE_I8, 2, 10, p, p, p, ws_n, 0, None) == -4
+    assert f(table, p, etg.WIRE_I8, 2, 10, None, p, p, ws_n, 0, None) == -1

@@ -425,6 +425,71 @@ def test_probability_check_accepts_oracle_and_rejects_shifted():
         assert accept.check_probs(ids, off, T, 2e-3, L, A)
 
 
+# ---------------------------------------------------------------- wire codecs
+def _f16_edge_values():
+    g = np.random.default_rng(33)
+    x = np.concatenate([
+        g.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** g.integers(-9, 5, 20000),
+        np.array([0.0, -0.0, 1.0, -1.0, 65504.0, 65519.0, 65520.0, 1e30, -1e30, 6.1035156e-05,
+                  5.9604645e-08, 2.9802322e-08, 2.9802326e-08, 8.940697e-08, 1e-45, 3.4028235e38,
+                  1.0009766, 1.0004883, 1.0014648, -2048.5, 2049.0, 4097.0], np.float32)])
+    # exact halfway points between neighbouring binary16 values (ties to even)
+    h = np.arange(0x0000, 0x7BFF, 97, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)
+    return np.concatenate([x, mid, -mid])
+
+
+def test_f16_encoder_matches_numpy_with_saturation():
+    x = _f16_edge_values()
+    got = np.array([oracle.f32_to_f16_sat(v) for v in x], np.uint16)
+    want = np.clip(x, -65504, 65504).astype(np.float16).view(np.uint16)   # numpy: round to nearest even
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (x[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def test_f16_wire_round_trip():
+    x = _f16_edge_values()[None, :5000]
+    enc = oracle.wire_encode(x, oracle.WIRE_F16)
+    assert enc.shape == (1, 2 * 5000)
+    assert np.array_equal(enc.view(np.uint16)[0], np.clip(x[0], -65504, 65504).astype(np.float16).view(np.uint16))
+    dec = oracle.wire_decode(enc, 5000, oracle.WIRE_F16)
+    assert np.array_equal(dec, np.clip(x, -65504, 65504).astype(np.float16).astype(np.float32))
+
+
+def test_i8_wire_hand_worked_row():
+    # max |x| = 127 -> scale 1; codes round half to even: -63.5 -> -64, 0.5 -> 0, 2.5 -> 2
+    x = np.array([[127, -63.5, 0.5, 2.5, -0.49, 0, 126.5, -127]], np.float32)
+    enc = oracle.wire_encode(x, oracle.WIRE_I8)
+    assert enc.shape == (1, 8 + 8)
+    assert enc[0, :4].view(np.float32)[0] == 1.0 and enc[0, 4:8].view(np.float32)[0] == 0.0
+    assert enc[0, 8:].view(np.int8).tolist() == [127, -64, 0, 2, 0, 0, 126, -127]
+    # max 254 -> scale 2
+    enc = oracle.wire_encode(np.array([[254.0, 1.0, -3.0, 5.0]], np.float32), oracle.WIRE_I8)
+    assert enc[0, :4].view(np.float32)[0] == 2.0
+    assert enc[0, 8:].view(np.int8).tolist() == [127, 0, -2, 2]
+    dec = oracle.wire_decode(enc, 4, oracle.WIRE_I8)
+    assert dec.tolist() == [[254.0, 0.0, -4.0, 4.0]]
+
+
+def test_i8_wire_zero_row_and_scale_in_f32():
+    enc = oracle.wire_encode(np.zeros((2, 16), np.float32), oracle.WIRE_I8)
+    assert np.all(enc == 0)
+    g = np.random.default_rng(34)
+    x = g.standard_normal((5, 333)).astype(np.float32) * np.float32([[1e-3], [1.0], [7.0], [1e4], [3e-30]])
+    enc = oracle.wire_encode(x, oracle.WIRE_I8)
+    for r in range(5):
+        m = np.max(np.abs(x[r]))
+        scale = np.float32(m) / np.float32(127.0)                 # numpy f32 division
+        assert enc[r, :4].view(np.float32)[0] == scale
+        q = np.clip(np.rint(x[r] / scale), -127, 127)             # numpy f32 division, round half even
+        assert np.array_equal(enc[r, 8:].view(np.int8), q.astype(np.int8))
+        dec = oracle.wire_decode(enc[r:r + 1], 333, oracle.WIRE_I8)[0]
+        assert np.array_equal(dec, q.astype(np.float32) * scale)
+        assert np.all(np.abs(dec.astype(np.float64) - x[r]) <= 0.5 * scale * (1 + 1e-6) + 1e-45)
+
+
 # ---------------------------------------------------------------- acceptance rule
 def test_acceptance_rule_accepts_exact_and_rejects_wrong():
     V, d = 300, 64
