@@ -10,9 +10,10 @@ seeded synthetic arrays (synth/), resident in HBM before the timed region.
 value = algorithmic bytes of the step / time per step, in GB/s.  The roofline
 object times the table-streaming kernel alone with HIP events recorded on the
 stream it runs on.  The other workloads of the page set (batches of 8 to 64,
-the response with probabilities, the raw logits mode, the 1,024-row
-contraction, the EmbeddingGemma-shaped Q8_0 gather with f32, f16 and i8
-output rows) are measured after the timed steps and reported under "also".  The CPU oracle is timed on a
+the response with probabilities, the raw logits mode, the same lm_head stored
+as Q8_0, the 1,024-row contraction, the EmbeddingGemma-shaped Q8_0 gather with
+f32, f16 and i8 output rows) are measured after the timed steps and reported
+under "also".  The CPU oracle is timed on a
 bounded sample of the same workload under "cpu_baseline".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -350,6 +351,25 @@ def main() -> int:
                 "bytes_per_row_out": int(wb.shape[1]), "alg_GBps": round(algw / (mw * 1e-3) / 1e9, 1)}
             del wb
         del gt
+        torch.cuda.empty_cache()
+
+        # the Q8_0 lm_head (31B-shaped, 1.50 GB): the q8 stream path
+        q = synth.CONFIGS["lm31b_q8"]
+        qh = q.table()
+        qt = etg.Table(torch.from_numpy(qh).to(dev), q.dtype, q.V, q.d)
+        del qh
+        for b in q.batches:
+            Rq = torch.from_numpy(q.residuals(b)).to(dev)
+            wsq = qt.workspace(b, q.k)
+            f = lambda evs=None: qt.logits_topk(Rq, q.k, workspace=wsq, events=evs)
+            f()
+            mq8, kq8 = _timed(torch, f, 20, events=hev)
+            also[f"lm31b_q8_0_logits_top10_B{b}"] = {
+                "us_per_call": round(mq8 * 1e3, 1), "kernel_us": round(kq8 * 1e3, 1),
+                "GBps": round(q.table_bytes / (mq8 * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100 * q.table_bytes / (mq8 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
+            log(f"q8_0 B={b}: {mq8 * 1e3:.1f} us")
+        del qt
         torch.cuda.empty_cache()
 
         p = synth.CONFIGS["prefill"]

@@ -258,5 +258,8 @@ CONFIGS = {
     "lm31b": Config(4, "lm31b", BF16, 262144, 5376, batches=(1, 8, 64), k=10),
     # bf16 262,144 x 5,120; logits + top-40 for 1,024 residuals (dense contraction)
     "prefill": Config(5, "prefill", BF16, 262144, 5120, batches=(1024,), k=40),
+    # the 31B-shaped lm_head stored as Q8_0 (1.50 GB; a timed Q8_0 lm_head): int8 uniform
+    # [-127, 127], f16(|N(0, 0.01)|) scales as for gemma_embed; logits + top-10, B = 1, 2, 8
+    "lm31b_q8": Config(6, "lm31b_q8", Q8_0, 262144, 5376, batches=(1, 2, 8), k=10),
 }
 

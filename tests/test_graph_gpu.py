@@ -35,6 +35,7 @@ def _eager(t, ids, R, k, path, T):
     (etg.BF16, 5003, 896, 16, etg.PATH_WIDE),
     (etg.BF16, 5003, 896, 70, etg.PATH_GEMM),
     (etg.Q8_0, 3001, 768, 3, etg.PATH_VALU),
+    (etg.Q8_0, 3001, 768, 3, etg.PATH_Q8),
 ])
 def test_captured_step_replays_match_eager(dtype, V, d, B, path):
     host = synth.make_table(dtype, V, d, seed=1200 + V)

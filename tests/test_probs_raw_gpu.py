@@ -24,7 +24,7 @@ from tests.gpu_util import bits, note, table, to_dev
 pytestmark = pytest.mark.gpu
 
 F32, BF16, Q8_0 = etg.F32, etg.BF16, etg.Q8_0
-VALU, STREAM, GEMM, WIDE = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE
+VALU, STREAM, GEMM, WIDE, Q8 = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE, etg.PATH_Q8
 ALL = [VALU, STREAM, GEMM, WIDE]
 
 # (dtype, V, d, B, path): ragged vocabularies, several blocks and passes per path
@@ -34,6 +34,7 @@ CASES = [
     (BF16, 20000, 5376, 3, STREAM),
     (BF16, 5003, 200, 17, WIDE), (BF16, 1536, 1032, 64, WIDE), (BF16, 70000, 512, 33, WIDE),
     (BF16, 5003, 200, 65, GEMM), (BF16, 1001, 64, 130, GEMM), (BF16, 20000, 5376, 70, GEMM),
+    (Q8_0, 3001, 768, 3, Q8), (Q8_0, 4099, 5376, 2, Q8), (Q8_0, 777, 288, 1, Q8),
 ]
 
 
