@@ -213,8 +213,30 @@ __global__ void __launch_bounds__(256) gather_q8_aligned_kernel(const uint8_t* _
 //   wire 2 (i8):  [scale f32][zero point 0 f32][int8 x hidden] per row with
 //                 scale = max|x| / 127 and q = round-half-even(x / scale), all in
 //                 f32, clamped to [-127, 127]; a row with scale 0 is all zeros.
-// A bad id gives an all-zero record.  One wave per row; the i8 codes take a second
-// pass over the source row (L1/L2 hits) once the row maximum is known.
+// A bad id gives an all-zero record.  One wave per row, four consecutive values
+// per lane (hidden is a multiple of 4): one load of the four stored values and
+// one 8-byte (f16) or 4-byte (i8) store.  The i8 codes take a second pass over
+// the source row (L1/L2 hits) once the row maximum is known.
+template <int DT>
+__device__ __forceinline__ f32x4 deq4(const uint8_t* row, int c) {  // values c .. c + 3, c % 4 == 0
+  if constexpr (DT == DT_F32) {
+    return *(const f32x4*)(row + 4 * c);
+  } else if constexpr (DT == DT_BF16 || DT == DT_F16) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = *(const u32x2*)(row + 2 * c);
+    if constexpr (DT == DT_BF16) return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+    return f32x4{f16_bits_to_f32(w.x & 0xffffu), f16_bits_to_f32(w.x >> 16), f16_bits_to_f32(w.y & 0xffffu),
+                 f16_bits_to_f32(w.y >> 16)};
+  } else {
+    typedef uint32_t u32a2 __attribute__((aligned(2)));
+    const uint8_t* blk = row + 34 * (c >> 5);
+    const float sc = f16_bits_to_f32(*(const uint16_t*)blk);
+    const uint32_t q = *(const u32a2*)(blk + 2 + (c & 31));  // 2-byte aligned, inside the block
+    return f32x4{(float)(int8_t)(q & 0xffu) * sc, (float)(int8_t)((q >> 8) & 0xffu) * sc,
+                 (float)(int8_t)((q >> 16) & 0xffu) * sc, (float)(int8_t)(q >> 24) * sc};
+  }
+}
+
 template <int DT, bool SCALE>
 __global__ void __launch_bounds__(256) gather_wire_kernel(const uint8_t* __restrict__ table, uint32_t V,
                                                           int hidden, int64_t row_bytes,
@@ -233,27 +255,39 @@ __global__ void __launch_bounds__(256) gather_wire_kernel(const uint8_t* __restr
     return;
   }
   const uint8_t* src = table + (uint64_t)id * (uint64_t)row_bytes;
-  auto value = [&](int c) {
-    const float x = deq_value<DT>(src, c);
+  auto value4 = [&](int c) {
+    const f32x4 x = deq4<DT>(src, c);
     return SCALE ? x * scale : x;
   };
   if (wire == WIRE_F16) {
-    uint16_t* o16 = (uint16_t*)o;
-    for (int c = lane; c < hidden; c += 64) o16[c] = (uint16_t)f32_to_f16_sat(value(c));
+    typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));  // the output is 4-byte aligned
+    for (int c = 4 * lane; c < hidden; c += 256) {
+      const f32x4 x = value4(c);
+      *(u32x2a4*)(o + 2 * c) = u32x2a4{f32_to_f16_sat(x[0]) | (f32_to_f16_sat(x[1]) << 16),
+                                   f32_to_f16_sat(x[2]) | (f32_to_f16_sat(x[3]) << 16)};
+    }
     return;
   }
   float m = 0.f;
-  for (int c = lane; c < hidden; c += 64) m = fmaxf(m, fabsf(value(c)));
+  for (int c = 4 * lane; c < hidden; c += 256) {
+    const f32x4 x = value4(c);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+  }
   m = wave_max_f32(m);
   const float sc = m / 127.0f;  // correctly rounded f32 division
   if (lane == 0) {
     ((float*)o)[0] = sc;
     ((float*)o)[1] = 0.f;
   }
-  int8_t* q = (int8_t*)(o + 8);
-  for (int c = lane; c < hidden; c += 64) {
-    const float v = sc != 0.f ? fminf(fmaxf(rintf(value(c) / sc), -127.f), 127.f) : 0.f;
-    q[c] = (int8_t)(int)v;
+  for (int c = 4 * lane; c < hidden; c += 256) {
+    const f32x4 x = value4(c);
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float v = sc != 0.f ? fminf(fmaxf(rintf(x[e] / sc), -127.f), 127.f) : 0.f;
+      w |= ((uint32_t)(int32_t)v & 0xffu) << (8 * e);
+    }
+    *(uint32_t*)(o + 8 + c) = w;
   }
 }
 

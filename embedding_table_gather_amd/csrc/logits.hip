@@ -154,6 +154,28 @@ __device__ __forceinline__ float prob_of(float score, float2 ml, float c) {
   return exp2f((score - ml.x) * c - ml.y);
 }
 
+// Wave 0's final rounds over the kMergeWaves * k per-wave bests in part (N per lane).
+template <int N>
+__device__ __forceinline__ void merge_final(const uint64_t* part, int k, int32_t* ids, float* scores, float* probs,
+                                            float2 ml, float lc) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key2[N];
+#pragma unroll
+  for (int j = 0; j < N; j++) {
+    const int i = lane + 64 * j;
+    key2[j] = i < kMergeWaves * k ? part[i] : 0;
+  }
+  for (int t = 0; t < k; t++) {
+    const uint64_t best = wave_pop_max(key2);
+    if (lane == 0) {
+      const float sc = ord_score((uint32_t)(best >> 32));
+      ids[t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
+      scores[t] = sc;
+      if (probs != nullptr) probs[t] = prob_of(sc, ml, lc);
+    }
+  }
+}
+
 // probs (nullable [B][k]): probabilities of the selected ids from the partials
 // lse [B][nparts] at c = log2(e) / temperature.
 template <int KPT>
@@ -180,21 +202,12 @@ __global__ void __launch_bounds__(1024) topk_merge_kernel(const uint64_t* __rest
   }
   __syncthreads();
   if (wv == 0) {
-    // kMergeWaves * k <= 1024 keys: 16 per lane
-    uint64_t key2[kMergeWaves];
-#pragma unroll
-    for (int j = 0; j < kMergeWaves; j++) {
-      const int i = lane + 64 * j;
-      key2[j] = i < kMergeWaves * k ? part[i] : 0;
-    }
-    for (int t = 0; t < k; t++) {
-      const uint64_t best = wave_pop_max(key2);
-      if (lane == 0) {
-        const float sc = ord_score((uint32_t)(best >> 32));
-        ids[b * k + t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
-        scores[b * k + t] = sc;
-        if (probs != nullptr) probs[b * k + t] = prob_of(sc, ml, lc);
-      }
+    // kMergeWaves * k keys: 4 per lane for k <= 16, else up to 16
+    if (k <= 16) {
+      merge_final<4>(part, k, ids + b * k, scores + b * k, probs != nullptr ? probs + b * k : nullptr, ml, lc);
+    } else {
+      merge_final<kMergeWaves>(part, k, ids + b * k, scores + b * k, probs != nullptr ? probs + b * k : nullptr,
+                               ml, lc);
     }
   }
 }
