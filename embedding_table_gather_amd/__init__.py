@@ -10,6 +10,8 @@ fallback: if the library is missing, every call raises.
     ids, scores = t.logits_topk(residual, k=10)   # ADR-0008 "POST /v1/logits"
     ids, scores, probs = t.logits_topk_probs(residual, k=10, temperature=1.0)
     logits = t.logits_raw(residual)               # raw logits mode, [B, vocab]
+    rows = t.embed_gather_wire(ids, WIRE_I8)      # ADR-0009 wire rows (f16 or i8)
+    ids, scores = t.logits_topk_wire(rows, WIRE_I8, k=10)
 """
 from __future__ import annotations
 

@@ -16,8 +16,12 @@
 //    up to 64 residual rows, still streamed into VGPRs; the residual operand is
 //    staged through LDS and no MFMA lane is idle.
 //  * gemm:   bf16 tables, large batches: a tiled MFMA contraction.
+//  * q8:     Q8_0 tables: lanes split each row's 34-byte blocks, f32 FMAs, one
+//    table pass per up to 2 residual rows (q8.hip).
 //  * valu:   any dtype (f32, bf16, f16, Q8_0); f32 FMAs per lane, one table pass per
 //    up to 8 residual rows.
+// Every path can also write its raw logits and per-block log-partition partials
+// (probabilities at a temperature), and reads the residual in any wire format.
 #include <algorithm>
 
 #include "etg_device.hpp"

@@ -7,6 +7,11 @@
  *   etg_embed_gather   token ids -> f32 residual_0 rows        ("POST /v1/embed")
  *   etg_logits_topk    residuals -> top-k (id, logit) per row  ("POST /v1/logits")
  *
+ * with the rest of that endpoint's response (etg_logits_topk_probs: probabilities
+ * at a temperature; etg_logits_raw: the raw logits mode) and the residual wire
+ * formats of "ADR-0009 -- Wire Format Evolution" (etg_embed_gather_wire,
+ * etg_logits_topk_wire).
+ *
  * The table is row-major and row-addressed: row i occupies bytes
  * [i * row_bytes, (i + 1) * row_bytes) of the table (HELIX Columnar Embedding
  * proposal, section 3, "Wire format" and "Index").  The lm_head is tied: the
