@@ -18,7 +18,7 @@ struct TableDesc {
 // function of (table shape, batch, k, path): the workspace size can be queried
 // without a device.
 struct LogitsPlan {
-  int32_t path;          // 1 valu, 2 stream, 3 gemm, 4 wide, 5 q8
+  int32_t path;          // 1 valu, 2 stream, 3 gemm, 4 wide, 5 q8, 6 row
   int32_t k;
   int64_t batch;
   // stream path
@@ -38,6 +38,8 @@ struct LogitsPlan {
   int32_t tiles_per_range;
   // wide path
   int32_t ntile;         // 16-column N-tiles per pass (residual rows per pass / 16)
+  // row path
+  int32_t row_ni;        // KiB loads per table row
   // q8 path
   int32_t lpr_log2;      // log2 of the lanes that split one row's blocks
   int32_t q8_t;          // blocks per lane per row
@@ -113,11 +115,12 @@ inline hipError_t record_event(hipEvent_t ev, hipStream_t stream) {
 
 // Per-path geometry (fill the path's fields and nblk, npass, lds_bytes,
 // img_bytes, aux_bytes, ncand) and launchers of the table-streaming kernel
-// (recording ev0 / ev1 around it).  stream.hip, wide.hip, gemm.hip, q8.hip.
+// (recording ev0 / ev1 around it).  stream.hip, wide.hip, gemm.hip, q8.hip, row.hip.
 int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_q8(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
+int32_t plan_row(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
                          const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
@@ -126,5 +129,7 @@ hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const void* R, u
                        const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_q8(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand, const LogitsExtras& x,
                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_row(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand, const LogitsExtras& x,
+                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace etg

@@ -18,6 +18,9 @@
 //  * gemm:   bf16 tables, large batches: a tiled MFMA contraction.
 //  * q8:     Q8_0 tables: lanes split each row's 34-byte blocks, f32 FMAs, one
 //    table pass per up to 2 residual rows (q8.hip).
+//  * row:    f32 / bf16 / f16 tables, one or two residual rows per table pass: a
+//    wave reads a row as 1 KiB contiguous loads, f32 FMAs against the residual in
+//    LDS (row.hip).
 //  * valu:   any dtype (f32, bf16, f16, Q8_0); f32 FMAs per lane, one table pass per
 //    up to 8 residual rows.
 // Every path can also write its raw logits and per-block log-partition partials
@@ -315,6 +318,8 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const voi
     e = launch_wide(t, p, R, base + p.img_offset, cand, (uint64_t*)(base + p.aux_offset), x, stream, ev0, ev1);
   } else if (p.path == 5) {
     e = launch_q8(t, p, R, cand, x, stream, ev0, ev1);
+  } else if (p.path == 6) {
+    e = launch_row(t, p, R, cand, x, stream, ev0, ev1);
   } else {
     switch (t.dtype) {
       case DT_F32: e = launch_valu<DT_F32>(t, p, R, cand, x, stream, ev0, ev1); break;
@@ -337,12 +342,13 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
   p->batch = batch;
   // auto: bf16 tables stream for up to 64 residual rows (one table pass per 8
   // or per 64 rows), then switch to the tiled contraction
-  // auto: Q8_0 tables take the q8 stream path (passes of 2 residual rows) when the
-  // row fits it, other f32 / f16 / Q8_0 tables the VALU path
-  if (path == 0 && t.dtype == DT_Q8_0) {
+  // auto: Q8_0 tables take the q8 path and f32 / f16 tables the row path (passes of
+  // 2 residual rows) when the row fits it, else the VALU path
+  if (path == 0 && t.dtype != DT_BF16) {
     LogitsPlan q;
     const char* w = "";
-    path = plan_q8(t, batch, k, &q, &w) == 0 ? 5 : 1;
+    if (t.dtype == DT_Q8_0) path = plan_q8(t, batch, k, &q, &w) == 0 ? 5 : 1;
+    else path = plan_row(t, batch, k, &q, &w) == 0 ? 6 : 1;
   }
   if (path == 0) path = (t.dtype != DT_BF16) ? 1 : (batch <= 8 ? 2 : batch <= 64 ? 4 : 3);
   if ((path == 2 || path == 3 || path == 4) && t.dtype != DT_BF16) {
@@ -353,7 +359,7 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     *why = "the q8 path needs a Q8_0 table";
     return -5;
   }
-  if (path != 1 && path != 2 && path != 3 && path != 4 && path != 5) {
+  if (path < 1 || path > 6) {
     *why = "unknown path";
     return -5;
   }
@@ -367,6 +373,8 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     st = plan_gemm(t, batch, k, p, why);
   } else if (path == 5) {
     st = plan_q8(t, batch, k, p, why);
+  } else if (path == 6) {
+    st = plan_row(t, batch, k, p, why);
   } else {
     p->rb = batch >= 8 ? 8 : batch >= 4 ? 4 : batch >= 2 ? 2 : 1;
     p->npass = (int32_t)cdiv(batch, p->rb);

@@ -149,16 +149,20 @@ int32_t etg_embed_gather_wire(const etg_table* table, const int32_t* d_ids, int6
 
 /* Kernel path for etg_logits_topk_ex (ETG_PATH_AUTO is what etg_logits_topk uses). */
 typedef enum {
-  ETG_PATH_AUTO = 0,   /* f32 and f16 tables: VALU; Q8_0 tables: Q8 (VALU past hidden 8192);
-                          bf16 tables: STREAM up to 8 rows, WIDE up to 64, GEMM beyond    */
+  ETG_PATH_AUTO = 0,   /* f32 and f16 tables: ROW; Q8_0 tables: Q8 (both VALU past their
+                          row limits); bf16 tables: STREAM up to 8 rows, WIDE up to 64,
+                          GEMM beyond                                                     */
   ETG_PATH_VALU = 1,   /* any dtype: f32 vector FMAs, one table pass per 8 residuals     */
   ETG_PATH_STREAM = 2, /* bf16 tables: one HBM pass per 8 residuals, bf16 MFMA dot engine;
                           batches of <= 4 use a hi+lo bf16 split of the residual          */
   ETG_PATH_GEMM = 3,   /* bf16 tables: tiled bf16 MFMA contraction for large batches     */
   ETG_PATH_WIDE = 4,   /* bf16 tables: one HBM pass per 64 residuals, bf16 MFMA dot engine,
                           hi+lo bf16 split of the residual                                */
-  ETG_PATH_Q8 = 5      /* Q8_0 tables with hidden <= 8192: one HBM pass per 2 residuals,
+  ETG_PATH_Q8 = 5,     /* Q8_0 tables with hidden <= 8192: one HBM pass per 2 residuals,
                           lanes split each row's blocks, f32 FMAs                         */
+  ETG_PATH_ROW = 6     /* f32 / bf16 / f16 tables with rows <= 16 KiB: one HBM pass per
+                          2 residuals, a wave per row, f32 FMAs (no bf16 rounding of the
+                          residual)                                                       */
 } etg_path;
 
 /* Device workspace bytes etg_logits_topk(_ex) needs for this table, batch and k

@@ -67,6 +67,11 @@ def test_lm31b_logits(B, sample):
     _check("lm31b", B, 10, sample)
 
 
+@pytest.mark.parametrize("path", [etg.PATH_STREAM, etg.PATH_ROW])
+def test_lm31b_logits_b1_paths(path):
+    _check("lm31b", 1, 10, [0], path)
+
+
 @pytest.mark.parametrize("path", [etg.PATH_GEMM, etg.PATH_WIDE])
 def test_lm31b_logits_b64_mfma_paths(path):
     _check("lm31b", 64, 10, [31], path)

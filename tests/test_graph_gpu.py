@@ -36,6 +36,7 @@ def _eager(t, ids, R, k, path, T):
     (etg.BF16, 5003, 896, 70, etg.PATH_GEMM),
     (etg.Q8_0, 3001, 768, 3, etg.PATH_VALU),
     (etg.Q8_0, 3001, 768, 3, etg.PATH_Q8),
+    (etg.BF16, 5003, 896, 1, etg.PATH_ROW),
 ])
 def test_captured_step_replays_match_eager(dtype, V, d, B, path):
     host = synth.make_table(dtype, V, d, seed=1200 + V)

@@ -18,8 +18,8 @@ from tests.gpu_util import note, table, to_dev
 pytestmark = pytest.mark.gpu
 
 F32, BF16, Q8_0, F16 = etg.F32, etg.BF16, etg.Q8_0, etg.F16
-VALU, STREAM, GEMM, WIDE = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE
-ALL = [VALU, STREAM, GEMM, WIDE]
+VALU, STREAM, GEMM, WIDE, ROW = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE, etg.PATH_ROW
+ALL = [VALU, STREAM, GEMM, WIDE, ROW]
 
 
 def run(t, R, k, path):
@@ -70,6 +70,18 @@ def test_gemm_path_ragged(V, d, B):
     host = synth.make_table(BF16, V, d, seed=500 + V)
     R = synth.residuals(B, d, seed=600 + B)
     full_check(host, BF16, V, d, R, min(10, V), GEMM)
+
+
+# the row path: rows of 16 bytes to 16 KiB (1 to 16 KiB loads, the last one partial),
+# f32 / bf16 / f16 tables, one table pass per residual row
+@pytest.mark.parametrize("dtype,V,d", [(BF16, 5003, 200), (BF16, 4099, 896), (BF16, 37, 8), (BF16, 20000, 5376),
+                                       (BF16, 1500, 8192), (F32, 2049, 100), (F32, 3000, 4096), (F16, 2049, 104),
+                                       (F16, 4099, 2560)])
+@pytest.mark.parametrize("B", [1, 3])
+def test_row_path_ragged(dtype, V, d, B):
+    host = synth.make_table(dtype, V, d, seed=700 + V + d)
+    R = synth.residuals(B, d, seed=800 + B)
+    full_check(host, dtype, V, d, R, min(10, V), ROW)
 
 
 # the wide path: 512-row blocks (ragged last block), 4-step K chunks (ragged last

@@ -23,9 +23,10 @@ from tests.gpu_util import bits, note, table, to_dev
 
 pytestmark = pytest.mark.gpu
 
-F32, BF16, Q8_0 = etg.F32, etg.BF16, etg.Q8_0
-VALU, STREAM, GEMM, WIDE, Q8 = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE, etg.PATH_Q8
-ALL = [VALU, STREAM, GEMM, WIDE]
+F32, BF16, Q8_0, F16 = etg.F32, etg.BF16, etg.Q8_0, etg.F16
+VALU, STREAM, GEMM, WIDE, Q8, ROW = (etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE, etg.PATH_Q8,
+                                    etg.PATH_ROW)
+ALL = [VALU, STREAM, GEMM, WIDE, ROW]
 
 # (dtype, V, d, B, path): ragged vocabularies, several blocks and passes per path
 CASES = [
@@ -35,6 +36,7 @@ CASES = [
     (BF16, 5003, 200, 17, WIDE), (BF16, 1536, 1032, 64, WIDE), (BF16, 70000, 512, 33, WIDE),
     (BF16, 5003, 200, 65, GEMM), (BF16, 1001, 64, 130, GEMM), (BF16, 20000, 5376, 70, GEMM),
     (Q8_0, 3001, 768, 3, Q8), (Q8_0, 4099, 5376, 2, Q8), (Q8_0, 777, 288, 1, Q8),
+    (BF16, 20000, 5376, 1, ROW), (F32, 2049, 100, 2, ROW), (F16, 4099, 2560, 1, ROW),
 ]
 
 
