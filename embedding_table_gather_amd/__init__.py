@@ -22,7 +22,7 @@ import torch
 
 F32, BF16, Q8_0, F16 = 0, 1, 2, 3
 WIRE_F32, WIRE_F16, WIRE_I8 = 0, 1, 2
-PATH_AUTO, PATH_VALU, PATH_STREAM, PATH_GEMM, PATH_WIDE, PATH_Q8, PATH_ROW = 0, 1, 2, 3, 4, 5, 6
+PATH_AUTO, PATH_VALU, PATH_STREAM, PATH_GEMM, PATH_WIDE, PATH_Q8, PATH_ROW, PATH_RANK = 0, 1, 2, 3, 4, 5, 6, 7
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libetg.so")
 

@@ -204,7 +204,7 @@ int32_t run_logits(const etg_table* t, const void* d_residual, int64_t batch, in
   }
   etg::LogitsPlan p;
   const char* why = "";
-  st = etg::plan_logits(t->d, batch, k, path, &p, &why);
+  st = etg::plan_logits(t->d, batch, k, path, &p, &why, raw || d_topk_probs != nullptr);
   if (st != ETG_OK) return fail(st, "%s", why);
   if (workspace_bytes < p.ws_bytes)
     return fail(ETG_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, p.ws_bytes);

@@ -94,6 +94,26 @@ __device__ __forceinline__ void wave_minmax_u32_multi(uint32_t (&v)[N]) {
   for (int i = 0; i < N; i++) v[i] = __builtin_amdgcn_readlane(v[i], 63);
 }
 
+// One selection round over keys held by a wave (N per lane, 0 = empty): returns
+// the largest key to every lane and removes it.  Keys are unique, so the round
+// takes the largest order value (upper 32 bits) and, among keys holding it, the
+// largest lower word (~id, so the smallest id); both are 32-bit DPP reductions.
+template <int N>
+__device__ __forceinline__ uint64_t wave_pop_max(uint64_t (&key)[N]) {
+  uint32_t hi = 0;
+#pragma unroll
+  for (int j = 0; j < N; j++) hi = max(hi, (uint32_t)(key[j] >> 32));
+  hi = wave_minmax_u32<true>(hi);
+  uint32_t lo = 0;
+#pragma unroll
+  for (int j = 0; j < N; j++) lo = (uint32_t)(key[j] >> 32) == hi ? max(lo, (uint32_t)key[j]) : lo;
+  lo = wave_minmax_u32<true>(lo);
+  const uint64_t best = ((uint64_t)hi << 32) | lo;
+#pragma unroll
+  for (int j = 0; j < N; j++) key[j] = key[j] == best ? 0 : key[j];
+  return best;
+}
+
 // Butterfly sum: every lane ends with the same (bitwise) value because each
 // pairwise add is commutative.
 __device__ __forceinline__ float wave_sum(float v) {

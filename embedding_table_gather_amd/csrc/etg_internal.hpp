@@ -8,7 +8,7 @@ namespace etg {
 
 struct TableDesc {
   const uint8_t* rows;  // device pointer, 16-byte aligned
-  int32_t dtype;        // 0 f32, 1 bf16, 2 Q8_0
+  int32_t dtype;        // 0 f32, 1 bf16, 2 Q8_0, 3 f16
   int64_t V;            // rows
   int64_t hidden;       // values per row
   int64_t row_bytes;
@@ -18,7 +18,7 @@ struct TableDesc {
 // function of (table shape, batch, k, path): the workspace size can be queried
 // without a device.
 struct LogitsPlan {
-  int32_t path;          // 1 valu, 2 stream, 3 gemm, 4 wide, 5 q8, 6 row
+  int32_t path;          // 1 valu, 2 stream, 3 gemm, 4 wide, 5 q8, 6 row, 7 rank
   int32_t k;
   int64_t batch;
   // stream path
@@ -36,6 +36,9 @@ struct LogitsPlan {
   int32_t nct;           // column tiles of tn / 2 residual rows
   int32_t nvr;           // vocabulary ranges
   int32_t tiles_per_range;
+  // rank path (the gemm kernel in ranking mode, then exact rescoring)
+  int32_t kb;            // keys per vocabulary-range heap
+  size_t rescore_lds;    // dynamic LDS of the rescoring kernel
   // wide path
   int32_t ntile;         // 16-column N-tiles per pass (residual rows per pass / 16)
   // row path
@@ -55,7 +58,8 @@ struct LogitsPlan {
   size_t img_offset, img_bytes;    // bf16 residual operand (gemm and wide paths)
   size_t cand_offset, cand_bytes;  // u64 keys [batch][nblk][k]
   size_t aux_offset, aux_bytes;    // wide path: u64 top-k lower bound per residual row;
-                                   // gemm path: per-thread running log-partition partials
+                                   // gemm path: per-thread running log-partition partials;
+                                   // rank path: f32 largest squared row norm per vocabulary range
   int32_t nparts;                  // log-partition partials per residual row (= ncand / k)
   size_t lse_offset, lse_bytes;    // float2 partials [batch][nparts]
   size_t ws_bytes;
@@ -78,8 +82,10 @@ struct LogitsExtras {
 };
 
 // Returns 0 or a negative etg_status; fills *plan.  `why` receives a short reason.
+// `extras`: the call also wants probabilities or raw logits (which the rank path
+// does not produce).  With path 0 (auto) the workspace size covers both answers.
 int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, LogitsPlan* plan,
-                    const char** why);
+                    const char** why, bool extras = false);
 
 hipError_t launch_gather(const TableDesc& t, const int32_t* ids, int64_t n, float scale,
                          float* out, int32_t* bad, hipStream_t stream);
@@ -115,12 +121,13 @@ inline hipError_t record_event(hipEvent_t ev, hipStream_t stream) {
 
 // Per-path geometry (fill the path's fields and nblk, npass, lds_bytes,
 // img_bytes, aux_bytes, ncand) and launchers of the table-streaming kernel
-// (recording ev0 / ev1 around it).  stream.hip, wide.hip, gemm.hip, q8.hip, row.hip.
+// (recording ev0 / ev1 around it).  stream.hip, wide.hip, gemm.hip (gemm and rank), q8.hip, row.hip.
 int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_q8(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_row(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
+int32_t plan_rank(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
                          const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
@@ -131,5 +138,9 @@ hipError_t launch_q8(const TableDesc& t, const LogitsPlan& p, const void* R, uin
                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_row(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand, const LogitsExtras& x,
                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+// The rank path writes ids / scores itself (its rescoring kernel replaces the merge).
+hipError_t launch_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs, uint64_t* cand,
+                       const LogitsExtras& x, int32_t* ids, float* scores, hipStream_t stream, hipEvent_t ev0,
+                       hipEvent_t ev1);
 
 }  // namespace etg

@@ -116,7 +116,39 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(const void* __restrict__
   Rs[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
 }
 
+// residual [B][hidden] -> bf16 rows [nct][256][kpad] for the ranking mode: image
+// row j of column tile ct is bf16(residual row 256 ct + j) (round to nearest
+// even); rows past the batch and values past hidden are zero.
+__global__ void __launch_bounds__(256) gemm_prep_hi_kernel(const void* __restrict__ R, int wire, int64_t B,
+                                                           int hidden, int kpad, int64_t nrows,
+                                                           u32x4* __restrict__ Rs) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int kc = kpad / 8;
+  if (t >= nrows * kc) return;
+  const int64_t b = t / kc;
+  const int c0 = (int)(t % kc) * 8;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const int c = c0 + e;
+    v[e] = (b < B && c < hidden) ? bf16_rne(residual_value(R, wire, b, hidden, c)) : 0u;
+  }
+  Rs[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+}
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// s + the squares of 8 bf16 values, f32 FMAs in element order.
+__device__ __forceinline__ float sumsq_bf16x8(bf16x8 f, float s) {
+  const u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+    s = __builtin_fmaf(lo, lo, s);
+    s = __builtin_fmaf(hi, hi, s);
+  }
+  return s;
+}
 
 // Min-heap of k keys in LDS (root = smallest kept key = admission threshold).
 // Replacing the root and sifting down costs at most log2(k) levels.
@@ -150,17 +182,27 @@ __device__ __forceinline__ void heap_replace_root(uint64_t* h, int k, uint64_t k
 //          of its range (kept in memory, not in registers, across the K loops)
 // Table rows past V are read from row V - 1 and never ranked; table bytes past
 // the row end are read from the row's last 16 bytes and meet zero residual values.
-template <int WM, int WN, int NA, int NB>
+template <int WM, int WN, int NA, int NB, bool SPLIT>
 __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, const uint8_t* __restrict__ Rs, int kpad,
     int64_t B, int k, uint64_t* __restrict__ cand, int nct, int nvr, int tiles_per_range,
-    float* __restrict__ logits, float2* __restrict__ lse, float lse_c, float2* __restrict__ lse_run) {
+    float* __restrict__ logits, float2* __restrict__ lse, float lse_c, float2* __restrict__ lse_run,
+    float* __restrict__ nrm2) {
   using C = GemmCfg<WM, WN>;
   constexpr int MT = C::MT, NT = C::NT, WR = C::WR, WC = C::WC, DPW = C::DPW;
+  constexpr int COLS = SPLIT ? kGemmCols : kGemmBN;  // residual rows per column tile
+  constexpr int WCR = SPLIT ? WC / 2 : WC;            // residual rows per wave column
+  constexpr int NTR = SPLIT ? 1 : NT;                 // N-tiles holding distinct residual rows
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   static_assert(NA >= 2 && NB >= 2 && NA <= 5 && NB <= 5, "ring depths");
+  static_assert(NT == 2 && MT == WN, "one hi and one lo N-tile (split) or two N-tiles; one M-tile per wave column");
   constexpr int SLICE = kGemmBM * 64;                     // one stage of 256 table or residual rows
-  uint64_t* heaps = (uint64_t*)(smem + (NA + NB) * SLICE);  // [kGemmCols][k]
+  uint64_t* heaps = (uint64_t*)(smem + (NA + NB) * SLICE);  // [COLS][k]
+  // logit of register i of tile a, N-tile t (hi + lo for split columns)
+  auto val = [&](const f32x16 (&ac)[MT][NT], int a, int t, int i) -> float {
+    if constexpr (SPLIT) return ac[a][0][i] + ac[a][1][i];
+    else return ac[a][t][i];
+  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps wave choices scalar
   const int mw = wv / WN, nw = wv % WN;
@@ -172,7 +214,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
   const int vr = xcd + kXcds * (local / nct);
   if (vr >= nvr) return;  // whole workgroup; no barrier has been reached
 
-  for (int i = tid; i < kGemmCols * k; i += C::THREADS) heaps[i] = 0;
+  for (int i = tid; i < COLS * k; i += C::THREADS) heaps[i] = 0;
+  // ranking mode: squared norms of this wave's table rows (M-tile nw, one K half per
+  // lane half) over the current tile, and their running maximum over the range
+  float nsq = 0.f, nmax = 0.f;
 
   const int nstage = kpad / kGemmBK;
   const uint8_t* rs_tile = Rs + (size_t)ct * kGemmBN * kpad * 2;
@@ -235,6 +280,11 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
 #pragma unroll
         for (int t = 0; t < NT; t++)
           acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[t], acc[a][t], 0, 0, 0);
+      if constexpr (!SPLIT) {
+#pragma unroll
+        for (int a = 0; a < MT; a++)
+          if (a == nw) nsq = sumsq_bf16x8(fa[a], nsq);
+      }
     };
 
     const int pre = min(depth - 1, nstage);
@@ -263,7 +313,13 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
 
     // Raw logits and the log-partition partial (register layout below; rows
     // as 32-bit offsets in the tile, stores at constant offsets from one base).
-    if (logits != nullptr || lse != nullptr) {
+    if constexpr (!SPLIT) {
+      // rows past V are copies of row V - 1 and K values past hidden copies of
+      // stored values: the maximum can only grow, so it stays an upper bound
+      nmax = fmaxf(nmax, nsq + __shfl_xor(nsq, 32, 64));
+      nsq = 0.f;
+    }
+    if (SPLIT && (logits != nullptr || lse != nullptr)) {
       // an opaque copy of the thread index: the addresses below are recomputed
       // per tile instead of being hoisted out of the tile loop (no free registers
       // to keep them in across the K loop)
@@ -308,33 +364,36 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
       }
     }
     // Epilogue.  Register i of tile (a, t) holds row WR mw + 32 a + 8 (i / 4) +
-    // 4 (lane / 32) + i % 4 of split column WC nw + 32 t + lane % 32; with NT = 2
-    // a lane sees 64 rows of one residual row.  Each lane marks its hi + lo sums
-    // whose order value reaches the heap root of that residual row (rare after
-    // the first tiles).  A wave with marks writes its sums to LDS and its lanes
-    // insert the marked entries that beat the root.  Each heap has one writer at
-    // a time: the wave rows mw take turns (barrier between), and within a wave
-    // the half-waves (lanes l and l + 32 share a column).
-    static_assert(NT == 2, "one hi and one lo N-tile per wave");
+    // 4 (lane / 32) + i % 4 of operand column WC nw + 32 t + lane % 32.  Split
+    // columns: N-tile 0 is hi and 1 is lo, so a lane sees 64 rows of one residual
+    // row; ranking columns: each N-tile is its own residual row.  Each lane marks
+    // its logits whose order value reaches the heap root of that residual row
+    // (rare after the first tiles).  A wave with marks writes its logits to LDS
+    // and its lanes insert the marked entries that beat the root.  Each heap has
+    // one writer at a time: the wave rows mw take turns (barrier between), and
+    // within a wave the half-waves (lanes l and l + 32 share a column).
     if (vt == 0) {
       // First tile: the heaps are empty, so each residual row's heap is built by
-      // selection.  In two halves of 64 residual rows the sums pass through LDS
-      // as [256 rows][65]; wave w then takes the k largest keys of columns
-      // w + 8 i (i < 8) in rounds (largest order value left, smallest row holding
-      // it) and stores them in ascending order, a valid min-heap; missing keys
-      // (rows past V) are 0 at the front.
-      static_assert(WN == 4 && WM == 2 && kGemmCols == 128, "tile-0 selection layout");
+      // selection.  In groups of 64 residual rows (one wave column pair when split,
+      // one wave column otherwise) the logits pass through LDS as [256 rows][65];
+      // wave w then takes the k largest keys of columns w + 8 i (i < 8) in rounds
+      // (largest order value left, smallest row holding it) and stores them in
+      // ascending order, a valid min-heap; missing keys (rows past V) are 0 at the
+      // front.
+      static_assert(WN == 4 && WM == 2 && COLS % 64 == 0, "tile-0 selection layout");
       float* Lt = (float*)smem;
       constexpr int TS = 65;
 #pragma unroll 1
-      for (int half = 0; half < 2; half++) {
-        if ((nw >> 1) == half) {
+      for (int grp = 0; grp < COLS / 64; grp++) {
+        if (SPLIT ? (nw >> 1) == grp : nw == grp) {
 #pragma unroll
-          for (int a = 0; a < MT; a++)
+          for (int t = 0; t < NTR; t++)
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-              Lt[(WR * mw + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * TS + (nw & 1) * 32 + (lane & 31)] =
-                  acc[a][0][i] + acc[a][1][i];
+            for (int a = 0; a < MT; a++)
+#pragma unroll
+              for (int i = 0; i < 16; i++)
+                Lt[(WR * mw + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * TS +
+                   (SPLIT ? (nw & 1) * 32 : 32 * t) + (lane & 31)] = val(acc, a, t, i);
         }
         gemm_stage_barrier<0>();
         uint32_t v[8][4];
@@ -366,7 +425,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
           if (lane == 0) {
 #pragma unroll
             for (int i = 0; i < 8; i++)
-              heaps[(size_t)(64 * half + wv + 8 * i) * k + (k - 1 - t)] =
+              heaps[(size_t)(64 * grp + wv + 8 * i) * k + (k - 1 - t)] =
                   M[i] != 0u ? ((uint64_t)M[i] << 32) | (uint64_t)(~(uint32_t)(v0 + Rw[i])) : 0ull;
           }
         }
@@ -374,50 +433,52 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
       }
       continue;
     }
-    const int col = nw * (WC / 2) + (lane & 31);
-    const bool col_ok = (int64_t)ct * kGemmCols + col < B;
-    uint64_t* heap = heaps + (size_t)col * k;
-    float* xs = (float*)smem + (size_t)(nw * 64 + lane) * 64;  // [WN waves][64 lanes][64], 64 KiB
 #pragma unroll
-    for (int p = 0; p < WM; p++) {
-      if (mw == p) {
-        const uint32_t tord = col_ok ? (uint32_t)(heap[0] >> 32) : 0xffffffffu;
-        uint64_t mask = 0;
+    for (int t = 0; t < NTR; t++) {
+      const int col = nw * WCR + 32 * t + (lane & 31);
+      const bool col_ok = (int64_t)ct * COLS + col < B;
+      uint64_t* heap = heaps + (size_t)col * k;
+      float* xs = (float*)smem + (size_t)(nw * 64 + lane) * 64;  // [WN waves][64 lanes][64], 64 KiB
 #pragma unroll
-        for (int a = 0; a < MT; a++)
-#pragma unroll
-          for (int i = 0; i < 16; i++)
-            mask |= (uint64_t)(score_ord(acc[a][0][i] + acc[a][1][i]) >= tord) << (16 * a + i);
-        if (__ballot(mask != 0) != 0) {
+      for (int p = 0; p < WM; p++) {
+        if (mw == p) {
+          const uint32_t tord = col_ok ? (uint32_t)(heap[0] >> 32) : 0xffffffffu;
+          uint64_t mask = 0;
 #pragma unroll
           for (int a = 0; a < MT; a++)
 #pragma unroll
-            for (int i = 0; i < 16; i += 4)
-              *(f32x4*)(xs + 16 * a + i) = f32x4{acc[a][0][i] + acc[a][1][i], acc[a][0][i + 1] + acc[a][1][i + 1],
-                                                 acc[a][0][i + 2] + acc[a][1][i + 2], acc[a][0][i + 3] + acc[a][1][i + 3]};
-          const int64_t r0 = v0 + WR * p + 4 * (lane >> 5);
-          for (int h = 0; h < 2; h++) {
-            if ((lane >> 5) == h && mask != 0) {
-              uint64_t thr = heap[0];
-              while (mask != 0) {
-                const int j = __builtin_ctzll(mask);
-                mask &= mask - 1;
-                const int64_t row = r0 + 32 * (j >> 4) + 8 * ((j & 15) >> 2) + (j & 3);
-                const uint64_t key = row < V ? make_key(xs[j], (uint32_t)row) : 0;
-                if (key > thr) {
-                  heap_replace_root(heap, k, key);
-                  thr = heap[0];
+            for (int i = 0; i < 16; i++) mask |= (uint64_t)(score_ord(val(acc, a, t, i)) >= tord) << (16 * a + i);
+          if (__ballot(mask != 0) != 0) {
+#pragma unroll
+            for (int a = 0; a < MT; a++)
+#pragma unroll
+              for (int i = 0; i < 16; i += 4)
+                *(f32x4*)(xs + 16 * a + i) =
+                    f32x4{val(acc, a, t, i), val(acc, a, t, i + 1), val(acc, a, t, i + 2), val(acc, a, t, i + 3)};
+            const int64_t r0 = v0 + WR * p + 4 * (lane >> 5);
+            for (int h = 0; h < 2; h++) {
+              if ((lane >> 5) == h && mask != 0) {
+                uint64_t thr = heap[0];
+                while (mask != 0) {
+                  const int j = __builtin_ctzll(mask);
+                  mask &= mask - 1;
+                  const int64_t row = r0 + 32 * (j >> 4) + 8 * ((j & 15) >> 2) + (j & 3);
+                  const uint64_t key = row < V ? make_key(xs[j], (uint32_t)row) : 0;
+                  if (key > thr) {
+                    heap_replace_root(heap, k, key);
+                    thr = heap[0];
+                  }
                 }
               }
+              __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this half-wave's heap writes are done
             }
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this half-wave's heap writes are done
           }
         }
+        gemm_stage_barrier<0>();
       }
-      gemm_stage_barrier<0>();
     }
   }
-  if (lse != nullptr) {
+  if (SPLIT && lse != nullptr) {
     // lanes l and l + 32 hold the same residual row, then the WM = 2 wave rows
     // (the stage ring is free after the last tile's barrier)
     static_assert(WM == 2, "two wave rows");
@@ -432,11 +493,24 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     const int64_t b = (int64_t)ct * kGemmCols + nw * (WC / 2) + lane;
     if (mw == 0 && lane < 32 && b < B) lse[b * nvr + vr] = lse_combine(run, xl[nw * 32 + lane], lse_c);
   }
+  if constexpr (!SPLIT) {
+    // the range's largest squared row norm (column tile 0 writes it); the ring
+    // is free after the last tile's barrier
+    float* xn = (float*)smem;
+    const float m = wave_max_f32(nmax);
+    if (lane == 0) xn[wv] = m;
+    gemm_stage_barrier<0>();
+    if (ct == 0 && tid == 0) {
+      float mm = xn[0];
+      for (int w = 1; w < C::NW; w++) mm = fmaxf(mm, xn[w]);
+      nrm2[vr] = mm;
+    }
+  }
   // heaps -> candidates [B][nvr][k]; the barrier orders the heap writes (also
   // the zeroing, for a range past the table that ran no tile) before the reads
   gemm_stage_barrier<0>();
-  if (tid < kGemmCols) {
-    const int64_t b = (int64_t)ct * kGemmCols + tid;
+  if (tid < COLS) {
+    const int64_t b = (int64_t)ct * COLS + tid;
     if (b < B) {
       const uint64_t* heap = heaps + (size_t)tid * k;
       uint64_t* out = cand + (b * nvr + vr) * (int64_t)k;
@@ -445,39 +519,299 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
   }
 }
 
-template <int WM, int WN, int NA, int NB>
+// ---------------------------------------------------------------------------
+// Ranking mode: exact rescoring with a certificate.
+//
+// In ranking mode the contraction sees hi = bf16(r) only, so its value a_v for
+// table row e_v misses lo . e_v (lo = r - hi, exact in f32) and carries the f32
+// accumulation error of hi . e_v (its products of two bf16 values are exact).
+// By Cauchy-Schwarz, with N >= max_v |e_v| measured by the contraction,
+//   |a_v - r . e_v| <= (|lo| + g |hi|) N = slack,   g = kpad 2^-22
+// (g allows a few ulp of accumulation error per term).  Each candidate is then
+// rescored from the f32 residual (lane-strided f32 FMAs and a butterfly sum),
+// which is within eps = (hidden / 64 + 8) 2^-23 |r| N of r . e_v.
+//
+// One workgroup per residual row:
+//  * U = the heap keys of every vocabulary range (kb per range, approximate);
+//  * A = the k-th largest approximate logit in U (-inf with fewer than k keys);
+//  * thr = A - 2 (slack + eps);
+//  * a range whose heap is full and whose smallest kept key reaches thr may have
+//    dropped a row above thr: all its rows are rescored;
+//  * every other key of U with a_v >= thr is rescored;
+//  * the answer is the k best rescored keys (logit desc, id asc).
+// Why this is the top-k: the k best keys of U are rescored (directly or through
+// their range), so the k-th rescored value T >= A - slack - eps.  A row that is
+// not rescored has a_v < thr (dropped rows lie at or below their range's
+// smallest kept key), so r . e_v < thr + slack = A - slack - 2 eps <= T - eps,
+// below the exact logit of every selected row.
+// ---------------------------------------------------------------------------
+static constexpr int kRescoreThreads = 512;
+static constexpr int kRescoreWaves = kRescoreThreads / 64;
+static constexpr int kRankMaxHidden = 16384;  // the residual row is kept in LDS
+static constexpr int kRankMaxKeys = 4096;     // heap keys per residual row (nvr kb)
+
+// LDS of gemm_rescore_kernel: U [n] keys, heaps [waves][k] keys, the residual
+// [hidden rounded up to 8] f32, S [n] rows, flags [nvr], rescan list [nvr].
+static size_t rescore_lds_bytes(int64_t hidden, int n, int nvr, int k) {
+  return (size_t)n * 8 + (size_t)kRescoreWaves * k * 8 + (size_t)((hidden + 7) & ~7) * 4 + (size_t)n * 4 +
+         (size_t)nvr * 8;
+}
+
+// Order value of the k-th largest key among the nonzero keys U[0, n) (counted
+// with multiplicity), or 0 with fewer than k.  Radix selection, 8 bits per
+// pass from the top, counts in an LDS histogram.
+__device__ uint32_t block_kth_ord(const uint64_t* U, int n, int k, uint32_t* hist, uint32_t* sel) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t prefix = 0, pmask = 0, kk = (uint32_t)k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kRescoreThreads) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kRescoreThreads) {
+      const uint64_t key = U[i];
+      const uint32_t o = (uint32_t)(key >> 32);
+      if (key != 0 && (o & pmask) == prefix) atomicAdd(&hist[(o >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l takes bins 255 - 4 l - j (j < 4), largest first
+      uint32_t c[4], sum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        c[j] = hist[255 - 4 * lane - j];
+        sum += c[j];
+      }
+      uint32_t inc = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += o;
+      }
+      const uint64_t m = __ballot(inc >= kk);
+      if (m == 0) {
+        if (lane == 0) sel[0] = 0xffffffffu;
+      } else if (lane == __builtin_ctzll(m)) {
+        uint32_t cum = inc - sum;
+        int j = 0;
+        while (j < 3 && cum + c[j] < kk) cum += c[j++];
+        sel[0] = (uint32_t)(255 - 4 * lane - j);
+        sel[1] = kk - cum;
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = sel[0], rest = sel[1];
+    __syncthreads();  // sel and hist are rewritten by the next pass
+    if (bin == 0xffffffffu) return 0u;
+    prefix |= bin << shift;
+    pmask |= 255u << shift;
+    kk = rest;
+  }
+  return prefix;
+}
+
+// f32 value rounded toward -inf from a finite double.
+__device__ __forceinline__ float f32_round_down(double x) {
+  float f = (float)x;
+  if ((double)f > x) {
+    const uint32_t u = __float_as_uint(f);
+    f = f > 0.f ? __uint_as_float(u - 1u) : f < 0.f ? __uint_as_float(u + 1u) : -__uint_as_float(1u);
+  }
+  return f;
+}
+
+//  table   bf16 [V][hidden], row_bytes = 2 hidden (a multiple of 16)
+//  R       residual rows (wire format `wire`)
+//  cand    [B][nvr][kb] heap keys of the ranking contraction (unordered, 0 = empty)
+//  nrm2    [nvr] largest squared row norm of each vocabulary range
+//  ids, scores  [B][k] the answer, best first
+__global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
+    const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden, int kpad,
+    const void* __restrict__ R, int wire, const uint64_t* __restrict__ cand, int nvr, int kb, int64_t range_rows,
+    const float* __restrict__ nrm2, int k, int32_t* __restrict__ ids, float* __restrict__ scores) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ float red[kRescoreWaves][4];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t cnt[2];  // rows in S, ranges to rescan
+  const int n = nvr * kb;
+  uint64_t* U = (uint64_t*)smem;
+  uint64_t* heaps = U + n;                                     // [waves][k]
+  float* r = (float*)(heaps + kRescoreWaves * k);              // [hidden]
+  uint32_t* S = (uint32_t*)(r + ((hidden + 7) & ~7));          // [n]
+  uint32_t* flag = S + n;                                      // [nvr] 1: rescanned
+  uint32_t* rl = flag + nvr;                                   // [nvr]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t b = blockIdx.x;
+
+  // residual row and the squared norms of lo, hi and r
+  float s_lo = 0.f, s_hi = 0.f, s_r = 0.f, n2 = 0.f;
+  for (int c = tid; c < hidden; c += kRescoreThreads) {
+    const float x = residual_value(R, wire, b, hidden, c);
+    r[c] = x;
+    const float hi = __uint_as_float(bf16_rne(x) << 16);
+    const float lo = x - hi;  // exact
+    s_lo = __builtin_fmaf(lo, lo, s_lo);
+    s_hi = __builtin_fmaf(hi, hi, s_hi);
+    s_r = __builtin_fmaf(x, x, s_r);
+  }
+  for (int i = tid; i < nvr; i += kRescoreThreads) n2 = fmaxf(n2, nrm2[i]);
+  for (int i = tid; i < n; i += kRescoreThreads) U[i] = cand[b * n + i];
+  for (int i = tid; i < kRescoreWaves * k; i += kRescoreThreads) heaps[i] = 0;
+  if (tid == 0) cnt[0] = cnt[1] = 0;
+  s_lo = wave_sum(s_lo);
+  s_hi = wave_sum(s_hi);
+  s_r = wave_sum(s_r);
+  n2 = wave_max_f32(n2);
+  if (lane == 0) {
+    red[wv][0] = s_lo;
+    red[wv][1] = s_hi;
+    red[wv][2] = s_r;
+    red[wv][3] = n2;
+  }
+  __syncthreads();
+  double lo2 = 0, hi2 = 0, r2 = 0, nn2 = 0;
+  for (int w = 0; w < kRescoreWaves; w++) {
+    lo2 += red[w][0];
+    hi2 += red[w][1];
+    r2 += red[w][2];
+    nn2 = fmax(nn2, (double)red[w][3]);
+  }
+  // the f32 sums above are within a few hundred ulp of the exact ones: inflate
+  // them by 2^-10 (sums of squares) before the square roots
+  const double inf2 = 1.0 + 0x1p-10;
+  const double N = sqrt(nn2 * inf2);
+  // inputs or products below the f32 normal range (flushed to zero or not)
+  const double tiny = 0x1p-100 * ((double)kpad + sqrt((double)kpad) * (N + sqrt(hi2 * inf2) + sqrt(r2 * inf2)));
+  const double slack = (sqrt(lo2 * inf2) + (double)kpad * 0x1p-22 * sqrt(hi2 * inf2)) * N + tiny;
+  const double eps = ((double)hidden / 64.0 + 8.0) * 0x1p-23 * sqrt(r2 * inf2) * N + tiny;
+
+  const uint32_t a_ord = block_kth_ord(U, n, k, hist, sel);
+  const float thr = a_ord == 0u ? -__builtin_inff() : f32_round_down((double)ord_score(a_ord) - 2.0 * (slack + eps));
+
+  // ranges to rescan: a full heap whose smallest key reaches thr
+  for (int vr = tid; vr < nvr; vr += kRescoreThreads) {
+    uint64_t mn = ~0ull;
+    for (int j = 0; j < kb; j++) mn = min(mn, U[vr * kb + j]);
+    const bool rescan = mn != 0 && ord_score((uint32_t)(mn >> 32)) >= thr;
+    flag[vr] = rescan;
+    if (rescan) rl[atomicAdd(&cnt[1], 1u)] = (uint32_t)vr;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kRescoreThreads) {
+    const uint64_t key = U[i];
+    if (key != 0 && flag[i / kb] == 0 && ord_score((uint32_t)(key >> 32)) >= thr)
+      S[atomicAdd(&cnt[0], 1u)] = ~(uint32_t)key;
+  }
+  __syncthreads();
+  const int ns = (int)cnt[0], nres = (int)cnt[1];
+
+  // one wave per row: f32 FMAs over values 8 lane + 512 j + e, then a butterfly
+  uint64_t* hp = heaps + wv * k;
+  auto rescore = [&](int64_t v) {
+    const uint8_t* row = table + (uint64_t)v * (uint64_t)row_bytes;
+    float acc = 0.f;
+#pragma unroll 4
+    for (int c = 8 * lane; c < hidden; c += 512) {
+      const u32x4 w = *(const u32x4*)(row + 2 * c);
+      const f32x4 ra = *(const f32x4*)(r + c), rb = *(const f32x4*)(r + c + 4);
+      acc = __builtin_fmaf(bf16_lo(w.x), ra.x, acc);
+      acc = __builtin_fmaf(bf16_hi(w.x), ra.y, acc);
+      acc = __builtin_fmaf(bf16_lo(w.y), ra.z, acc);
+      acc = __builtin_fmaf(bf16_hi(w.y), ra.w, acc);
+      acc = __builtin_fmaf(bf16_lo(w.z), rb.x, acc);
+      acc = __builtin_fmaf(bf16_hi(w.z), rb.y, acc);
+      acc = __builtin_fmaf(bf16_lo(w.w), rb.z, acc);
+      acc = __builtin_fmaf(bf16_hi(w.w), rb.w, acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      const uint64_t key = make_key(acc, (uint32_t)v);
+      if (key > hp[0]) heap_replace_root(hp, k, key);
+    }
+  };
+  for (int i = wv; i < ns; i += kRescoreWaves) rescore(S[i]);
+  for (int q = 0; q < nres; q++) {
+    const int64_t v0 = (int64_t)rl[q] * range_rows, v1 = min(V, v0 + range_rows);
+    for (int64_t v = v0 + wv; v < v1; v += kRescoreWaves) rescore(v);
+  }
+  __syncthreads();
+  if (wv == 0) {
+    uint64_t key[kRescoreWaves];  // up to 8 k <= 512 keys, 8 per lane
+#pragma unroll
+    for (int j = 0; j < kRescoreWaves; j++) {
+      const int i = lane + 64 * j;
+      key[j] = i < kRescoreWaves * k ? heaps[i] : 0;
+    }
+    for (int t = 0; t < k; t++) {
+      const uint64_t best = wave_pop_max(key);
+      if (lane == 0) {
+        ids[b * k + t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
+        scores[b * k + t] = ord_score((uint32_t)(best >> 32));
+      }
+    }
+  }
+}
+
+template <int WM, int WN, int NA, int NB, bool SPLIT>
 static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs,
-                                  uint64_t* cand, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0,
-                                  hipEvent_t ev1) {
+                                  uint64_t* cand, const LogitsExtras& x, int32_t* ids, float* scores,
+                                  hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   using C = GemmCfg<WM, WN>;
   const int64_t nrows = (int64_t)p.nct * kGemmBN;
   const int64_t nprep = nrows * (p.kpad / 8);
-  hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream, R, (int)x.wire,
-                     p.batch,
-                     (int)t.hidden, p.kpad, C::WC, nrows, (u32x4*)rs);
+  if constexpr (SPLIT) {
+    hipLaunchKernelGGL(gemm_prep_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream, R, (int)x.wire,
+                       p.batch, (int)t.hidden, p.kpad, C::WC, nrows, (u32x4*)rs);
+  } else {
+    hipLaunchKernelGGL(gemm_prep_hi_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream, R,
+                       (int)x.wire, p.batch, (int)t.hidden, p.kpad, nrows, (u32x4*)rs);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if ((e = set_dynamic_lds((const void*)gemm_logits_kernel<WM, WN, NA, NB>, p.lds_bytes)) != hipSuccess) return e;
+  if ((e = set_dynamic_lds((const void*)gemm_logits_kernel<WM, WN, NA, NB, SPLIT>, p.lds_bytes)) != hipSuccess)
+    return e;
   if ((e = record_event(ev0, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((gemm_logits_kernel<WM, WN, NA, NB>), dim3((unsigned)p.nblk), dim3(C::THREADS), p.lds_bytes, stream,
-                     t.rows, t.V, t.row_bytes, (const uint8_t*)rs, p.kpad, p.batch, p.k, cand, p.nct, p.nvr,
-                     p.tiles_per_range, x.logits, x.lse, x.lse_scale, (float2*)x.aux);
+  hipLaunchKernelGGL((gemm_logits_kernel<WM, WN, NA, NB, SPLIT>), dim3((unsigned)p.nblk), dim3(C::THREADS),
+                     p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (const uint8_t*)rs, p.kpad, p.batch,
+                     SPLIT ? p.k : p.kb, cand, p.nct, p.nvr, p.tiles_per_range, x.logits, x.lse, x.lse_scale,
+                     (float2*)x.aux, (float*)x.aux);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return record_event(ev1, stream);
+  if ((e = record_event(ev1, stream)) != hipSuccess) return e;
+  if constexpr (!SPLIT) {
+    if ((e = set_dynamic_lds((const void*)gemm_rescore_kernel, p.rescore_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_rescore_kernel, dim3((unsigned)p.batch), dim3(kRescoreThreads), p.rescore_lds, stream,
+                       t.rows, t.V, t.row_bytes, (int)t.hidden, p.kpad, R, (int)x.wire, (const uint64_t*)cand, p.nvr,
+                       p.kb, (int64_t)p.tiles_per_range * kGemmBM, (const float*)x.aux, p.k, ids, scores);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs, uint64_t* cand,
                        const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   // one wave layout: 2 x 4 waves of 128 x 64 (2 x 2 waves of 128 x 128 would spill)
-  if (p.gemm_ring == 34) return launch_gemm_cfg<2, 4, 3, 4>(t, p, R, rs, cand, x, stream, ev0, ev1);
-  return launch_gemm_cfg<2, 4, 3, 3>(t, p, R, rs, cand, x, stream, ev0, ev1);
+  if (p.gemm_ring == 34)
+    return launch_gemm_cfg<2, 4, 3, 4, true>(t, p, R, rs, cand, x, nullptr, nullptr, stream, ev0, ev1);
+  return launch_gemm_cfg<2, 4, 3, 3, true>(t, p, R, rs, cand, x, nullptr, nullptr, stream, ev0, ev1);
 }
 
-int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
+hipError_t launch_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs, uint64_t* cand,
+                       const LogitsExtras& x, int32_t* ids, float* scores, hipStream_t stream, hipEvent_t ev0,
+                       hipEvent_t ev1) {
+  if (p.gemm_ring == 34) return launch_gemm_cfg<2, 4, 3, 4, false>(t, p, R, rs, cand, x, ids, scores, stream, ev0, ev1);
+  return launch_gemm_cfg<2, 4, 3, 3, false>(t, p, R, rs, cand, x, ids, scores, stream, ev0, ev1);
+}
+
+// Column tiles, vocabulary ranges and LDS rings shared by both modes.  Split
+// mode: 128 residual rows per column tile and heaps of k keys (the exact k best);
+// ranking mode: 256 rows and heaps of hk_max keys, fewer when there are many
+// ranges (at most kRankMaxKeys per residual row).  *hk receives the heap size.
+static int32_t plan_gemm_common(const TableDesc& t, int64_t batch, bool split, int hk_max, LogitsPlan* p,
+                                int32_t* hk, const char** why) {
+  const int cols = split ? kGemmCols : kGemmBN;
   p->gemm_wn = 4;
   p->tn = kGemmBN;
   p->kpad = (int32_t)(cdiv(t.hidden, kGemmBK) * kGemmBK);
-  p->nct = (int32_t)cdiv(batch, kGemmCols);
+  p->nct = (int32_t)cdiv(batch, cols);
   const int64_t vtiles = cdiv(t.V, kGemmBM);
   // about one workgroup per CU; vocabulary ranges in multiples of the XCD count
   int64_t nvr = std::max<int64_t>(1, kTargetBlocks / p->nct);
@@ -487,8 +821,9 @@ int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
   p->nvr = (int32_t)nvr;
   p->nblk = (int32_t)(p->nct * nvr);
   p->npass = 1;
+  *hk = split ? hk_max : std::min<int32_t>(hk_max, std::max<int32_t>(1, kRankMaxKeys / (int32_t)nvr));
   // the residual ring one stage deeper when the heaps leave room
-  const size_t heaps = (size_t)kGemmCols * k * 8;
+  const size_t heaps = (size_t)cols * *hk * 8;
   p->gemm_ring = 7 * (size_t)kGemmBM * 64 + heaps <= kMaxLds ? 34 : 33;
   p->lds_bytes = (p->gemm_ring == 34 ? 7 : 6) * (size_t)kGemmBM * 64 + heaps;
   if (p->lds_bytes > kMaxLds) {
@@ -496,8 +831,34 @@ int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
     return -5;
   }
   p->img_bytes = (size_t)p->nct * kGemmBN * p->kpad * 2;
-  p->ncand = (int32_t)(nvr * k);
+  return 0;
+}
+
+int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
+  int32_t hk = 0;
+  const int32_t st = plan_gemm_common(t, batch, true, k, p, &hk, why);
+  if (st != 0) return st;
+  p->ncand = (int32_t)(p->nvr * k);
   p->aux_bytes = (size_t)p->nblk * 64 * 8 * 8;  // running log-partition partial per thread
+  return 0;
+}
+
+int32_t plan_rank(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
+  if (t.hidden > kRankMaxHidden) {
+    *why = "hidden too large for the rank path (the residual row is kept in LDS)";
+    return -5;
+  }
+  int32_t hk = 0;
+  const int32_t st = plan_gemm_common(t, batch, false, std::min<int32_t>(k, 32), p, &hk, why);
+  if (st != 0) return st;
+  p->kb = hk;
+  p->ncand = (int32_t)(p->nvr * hk);
+  p->aux_bytes = (size_t)p->nvr * 4;  // largest squared row norm per vocabulary range
+  p->rescore_lds = rescore_lds_bytes(t.hidden, p->ncand, p->nvr, k);
+  if (p->rescore_lds > kMaxLds - 2048) {  // static LDS besides
+    *why = "the rank path's rescoring does not fit in LDS";
+    return -5;
+  }
   return 0;
 }
 

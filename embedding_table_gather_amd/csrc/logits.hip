@@ -118,26 +118,6 @@ __global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restr
 static constexpr int kMergeThreads = 1024;
 static constexpr int kMergeWaves = kMergeThreads / 64;
 
-// One selection round over keys held by a wave (N per lane, 0 = empty): returns
-// the largest key to every lane and removes it.  Keys are unique, so the round
-// takes the largest order value (upper 32 bits) and, among keys holding it, the
-// largest lower word (~id, so the smallest id); both are 32-bit DPP reductions.
-template <int N>
-__device__ __forceinline__ uint64_t wave_pop_max(uint64_t (&key)[N]) {
-  uint32_t hi = 0;
-#pragma unroll
-  for (int j = 0; j < N; j++) hi = max(hi, (uint32_t)(key[j] >> 32));
-  hi = wave_minmax_u32<true>(hi);
-  uint32_t lo = 0;
-#pragma unroll
-  for (int j = 0; j < N; j++) lo = (uint32_t)(key[j] >> 32) == hi ? max(lo, (uint32_t)key[j]) : lo;
-  lo = wave_minmax_u32<true>(lo);
-  const uint64_t best = ((uint64_t)hi << 32) | lo;
-#pragma unroll
-  for (int j = 0; j < N; j++) key[j] = key[j] == best ? 0 : key[j];
-  return best;
-}
-
 // Log-partition of one residual row from its n partials (m_i, s_i), returned to
 // every thread as (M, log2 S), S = sum_i s_i exp2((m_i - M) c).  Each thread
 // combines a strided subset, each wave reduces (max, then rescaled sum) and
@@ -320,6 +300,9 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const voi
     e = launch_q8(t, p, R, cand, x, stream, ev0, ev1);
   } else if (p.path == 6) {
     e = launch_row(t, p, R, cand, x, stream, ev0, ev1);
+  } else if (p.path == 7) {
+    if (ids == nullptr || probs != nullptr || logits != nullptr) return hipErrorInvalidValue;
+    return launch_rank(t, p, R, base + p.img_offset, cand, x, ids, scores, stream, ev0, ev1);
   } else {
     switch (t.dtype) {
       case DT_F32: e = launch_valu<DT_F32>(t, p, R, cand, x, stream, ev0, ev1); break;
@@ -336,10 +319,23 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const voi
 // Planning (host only, no device calls).
 // ---------------------------------------------------------------------------
 int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, LogitsPlan* p,
-                    const char** why) {
+                    const char** why, bool extras) {
   *p = LogitsPlan{};
   p->k = k;
   p->batch = batch;
+  // auto, bf16 tables past 64 residual rows: the rank path for the top-k alone,
+  // the split contraction when probabilities or raw logits are wanted; the
+  // workspace covers both
+  if (path == 0 && t.dtype == DT_BF16 && batch > 64) {
+    LogitsPlan r, g;
+    const char* w = "";
+    const bool rank_ok = plan_logits(t, batch, k, 7, &r, &w, false) == 0;
+    const int32_t st = plan_logits(t, batch, k, 3, &g, why, false);
+    if (st != 0) return st;
+    *p = (rank_ok && !extras) ? r : g;
+    if (rank_ok) p->ws_bytes = std::max(r.ws_bytes, g.ws_bytes);
+    return 0;
+  }
   // auto: bf16 tables stream for up to 64 residual rows (one table pass per 8
   // or per 64 rows), then switch to the tiled contraction
   // auto: Q8_0 tables take the q8 path and f32 / f16 tables the row path (passes of
@@ -350,7 +346,7 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     if (t.dtype == DT_Q8_0) path = plan_q8(t, batch, k, &q, &w) == 0 ? 5 : 1;
     else path = plan_row(t, batch, k, &q, &w) == 0 ? 6 : 1;
   }
-  if (path == 0) path = (t.dtype != DT_BF16) ? 1 : (batch <= 8 ? 2 : batch <= 64 ? 4 : 3);
+  if (path == 0) path = (t.dtype != DT_BF16) ? 1 : (batch <= 8 ? 2 : 4);
   if ((path == 2 || path == 3 || path == 4) && t.dtype != DT_BF16) {
     *why = "the stream, gemm and wide paths need a bf16 table";
     return -5;
@@ -359,7 +355,15 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     *why = "the q8 path needs a Q8_0 table";
     return -5;
   }
-  if (path < 1 || path > 6) {
+  if (path == 7 && t.dtype != DT_BF16) {
+    *why = "the rank path needs a bf16 table";
+    return -5;
+  }
+  if (path == 7 && extras) {
+    *why = "the rank path returns neither probabilities nor raw logits";
+    return -5;
+  }
+  if (path < 1 || path > 7) {
     *why = "unknown path";
     return -5;
   }
@@ -375,6 +379,8 @@ int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, 
     st = plan_q8(t, batch, k, p, why);
   } else if (path == 6) {
     st = plan_row(t, batch, k, p, why);
+  } else if (path == 7) {
+    st = plan_rank(t, batch, k, p, why);
   } else {
     p->rb = batch >= 8 ? 8 : batch >= 4 ? 4 : batch >= 2 ? 2 : 1;
     p->npass = (int32_t)cdiv(batch, p->rb);

@@ -61,8 +61,9 @@ typedef enum {
                           outside [1, 65536]; vocab outside [1, 2^31 - 1]; seq_len or
                           batch outside the supported range                            */
   ETG_EALIGN = -4,     /* a device pointer lacks the alignment its argument states     */
-  ETG_ERANGE = -5,     /* k outside [1, min(vocab, 64)], an unknown path, or a
-                          temperature out of range                                     */
+  ETG_ERANGE = -5,     /* k outside [1, min(vocab, 64)], an unknown path, a path that
+                          cannot serve the call (dtype, hidden, probabilities or raw
+                          logits on ETG_PATH_RANK), or a temperature out of range      */
   ETG_EWORKSPACE = -6, /* workspace smaller than etg_logits_topk_workspace() bytes     */
   ETG_EHIP = -8        /* a HIP runtime call failed (the message names it)             */
 } etg_status;
@@ -151,7 +152,8 @@ int32_t etg_embed_gather_wire(const etg_table* table, const int32_t* d_ids, int6
 typedef enum {
   ETG_PATH_AUTO = 0,   /* f32 and f16 tables: ROW; Q8_0 tables: Q8 (both VALU past their
                           row limits); bf16 tables: STREAM up to 8 rows, WIDE up to 64,
-                          GEMM beyond                                                     */
+                          RANK beyond (GEMM when probabilities or raw logits are asked
+                          for, or hidden > 16384)                                         */
   ETG_PATH_VALU = 1,   /* any dtype: f32 vector FMAs, one table pass per 8 residuals     */
   ETG_PATH_STREAM = 2, /* bf16 tables: one HBM pass per 8 residuals, bf16 MFMA dot engine;
                           batches of <= 4 use a hi+lo bf16 split of the residual          */
@@ -160,9 +162,13 @@ typedef enum {
                           hi+lo bf16 split of the residual                                */
   ETG_PATH_Q8 = 5,     /* Q8_0 tables with hidden <= 8192: one HBM pass per 2 residuals,
                           lanes split each row's blocks, f32 FMAs                         */
-  ETG_PATH_ROW = 6     /* f32 / bf16 / f16 tables with rows <= 16 KiB: one HBM pass per
+  ETG_PATH_ROW = 6,    /* f32 / bf16 / f16 tables with rows <= 16 KiB: one HBM pass per
                           2 residuals, a wave per row, f32 FMAs (no bf16 rounding of the
                           residual)                                                       */
+  ETG_PATH_RANK = 7    /* bf16 tables with hidden <= 16384, top-k only: the GEMM tiles
+                          rank with the residual rounded once to bf16, then every row
+                          that a rigorous error bound cannot rule out is rescored with
+                          f32 FMAs from the f32 residual (half the MFMA work of GEMM)     */
 } etg_path;
 
 /* Device workspace bytes etg_logits_topk(_ex) needs for this table, batch and k
@@ -227,6 +233,8 @@ int32_t etg_logits_topk_profiled(const etg_table* lm_head, const float* d_residu
  * Accuracy: with every logit within its bound above (tol_v), the log of each
  * probability is within (tol_{id_j} + max_v tol_v) / T of the exact value, plus
  * about 1e-5 for the f32 exp2 / log2 and sums.  Workspace: as etg_logits_topk_ex.
+ * ETG_PATH_RANK is rejected (ETG_ERANGE); ETG_PATH_AUTO takes GEMM where top-k
+ * alone would take RANK.
  */
 int32_t etg_logits_topk_probs(const etg_table* lm_head, const float* d_residual, int64_t batch,
                               int32_t k, float temperature, int32_t* d_topk_ids,
@@ -241,6 +249,7 @@ int32_t etg_logits_topk_probs(const etg_table* lm_head, const float* d_residual,
  *              a given path these are bitwise the values its top-k ranks.
  *   d_workspace  at least etg_logits_raw_workspace() bytes, 256-byte aligned.
  * Writes batch * vocab * 4 bytes of HBM besides reading the table once per pass.
+ * ETG_PATH_RANK is rejected (ETG_ERANGE), as for etg_logits_topk_probs.
  */
 int64_t etg_logits_raw_workspace(const etg_table* lm_head, int64_t batch, int32_t path);
 int32_t etg_logits_raw(const etg_table* lm_head, const float* d_residual, int64_t batch,

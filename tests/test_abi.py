@@ -175,6 +175,30 @@ def test_probs_and_raw_errors_without_launch(L, table):
     assert g(None, p, 3, p, p, rn, 0, None) == -1
 
 
+def test_rank_path_planning(L, table):
+    # the rank path: bf16 tables, top-k only; the auto workspace covers it and the
+    # split contraction that probabilities / raw logits take at the same batch
+    p = ctypes.c_void_p(FAKE)
+    rank = L.etg_logits_topk_workspace_ex(table, 1024, 40, etg.PATH_RANK)
+    gemm = L.etg_logits_topk_workspace_ex(table, 1024, 40, etg.PATH_GEMM)
+    auto = L.etg_logits_topk_workspace(table, 1024, 40)
+    assert rank > 0 and gemm > 0 and auto == max(rank, gemm)
+    assert L.etg_logits_topk_probs(table, p, 1024, 40, 1.0, p, p, p, p, auto, etg.PATH_RANK, None) == -5
+    assert "rank" in _err(L)
+    assert L.etg_logits_raw(table, p, 1024, p, p, auto, etg.PATH_RANK, None) == -5
+    for dtype, d in ((etg.F32, 64), (etg.Q8_0, 64), (etg.F16, 64)):
+        st, h = _create(L, FAKE, dtype, 1000, d)
+        assert st == 0
+        assert L.etg_logits_topk_workspace_ex(h, 100, 5, etg.PATH_RANK) == -5 and "bf16" in _err(L)
+        L.etg_table_destroy(h)
+    # hidden past 16384: the residual row no longer fits the rescoring's LDS
+    st, h = _create(L, FAKE, etg.BF16, 1000, 16392)
+    assert st == 0
+    assert L.etg_logits_topk_workspace_ex(h, 100, 5, etg.PATH_RANK) == -5 and "hidden" in _err(L)
+    assert L.etg_logits_topk_workspace(h, 100, 5) == L.etg_logits_topk_workspace_ex(h, 100, 5, etg.PATH_GEMM) > 0
+    L.etg_table_destroy(h)
+
+
 def test_f16_tables_take_the_valu_path(L):
     st, h = _create(L, FAKE, etg.F16, 1000, 64)
     assert st == 0

@@ -72,13 +72,18 @@ def test_lm31b_logits_b1_paths(path):
     _check("lm31b", 1, 10, [0], path)
 
 
-@pytest.mark.parametrize("path", [etg.PATH_GEMM, etg.PATH_WIDE])
+@pytest.mark.parametrize("path", [etg.PATH_GEMM, etg.PATH_WIDE, etg.PATH_RANK])
 def test_lm31b_logits_b64_mfma_paths(path):
     _check("lm31b", 64, 10, [31], path)
 
 
 def test_prefill_logits_b1024():
+    # the automatic choice here is the rank path
     _check("prefill", 1024, 40, [0, 1023])
+
+
+def test_prefill_logits_b1024_split_gemm():
+    _check("prefill", 1024, 40, [511], etg.PATH_GEMM)
 
 
 def test_lm31b_tied_gather_then_logits():

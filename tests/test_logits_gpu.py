@@ -18,8 +18,9 @@ from tests.gpu_util import note, table, to_dev
 pytestmark = pytest.mark.gpu
 
 F32, BF16, Q8_0, F16 = etg.F32, etg.BF16, etg.Q8_0, etg.F16
-VALU, STREAM, GEMM, WIDE, ROW = etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE, etg.PATH_ROW
-ALL = [VALU, STREAM, GEMM, WIDE, ROW]
+VALU, STREAM, GEMM, WIDE, ROW, RANK = (etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE, etg.PATH_ROW,
+                                       etg.PATH_RANK)
+ALL = [VALU, STREAM, GEMM, WIDE, ROW, RANK]
 
 
 def run(t, R, k, path):
@@ -70,6 +71,32 @@ def test_gemm_path_ragged(V, d, B):
     host = synth.make_table(BF16, V, d, seed=500 + V)
     R = synth.residuals(B, d, seed=600 + B)
     full_check(host, BF16, V, d, R, min(10, V), GEMM)
+
+
+# the rank path: 256-row column tiles (ragged last one), one or many vocabulary
+# ranges per column tile, heaps of fewer keys than k when ranges are many
+@pytest.mark.parametrize("V,d", [(5003, 200), (4099, 896), (1001, 64), (20000, 5376), (37, 8), (70000, 512)])
+@pytest.mark.parametrize("B", [1, 9, 65, 130, 257])
+def test_rank_path_ragged(V, d, B):
+    host = synth.make_table(BF16, V, d, seed=500 + V)
+    R = synth.residuals(B, d, seed=600 + B)
+    full_check(host, BF16, V, d, R, min(10, V), RANK)
+
+
+@pytest.mark.parametrize("k", [10, 40, 64])
+def test_rank_path_rescans_a_range_holding_many_winners(k):
+    # 80 planted winners in rows 256..335, one 256-row vocabulary range: its heap
+    # keeps at most 32 of them, so the certificate must send the whole range to
+    # exact rescoring for the answer to hold the other winners
+    V, d, B = 30000, 512, 2
+    host = synth.make_table(BF16, V, d, seed=23)
+    R = synth.residuals(B, d, seed=24)
+    u = R[0] / np.linalg.norm(R[0])
+    for j in range(80):
+        host[256 + j] = synth.f32_to_bf16_bits((u * (0.9 - 0.005 * j)).astype(np.float32))
+    gids, _, oids, _ = full_check(host, BF16, V, d, R, k, RANK)
+    assert np.array_equal(gids[0], np.arange(256, 256 + k))
+    assert np.array_equal(gids, oids)
 
 
 # the row path: rows of 16 bytes to 16 KiB (1 to 16 KiB loads, the last one partial),
