@@ -38,6 +38,7 @@ struct LogitsPlan {
   int32_t tiles_per_range;
   // rank path (the gemm kernel in ranking mode, then exact rescoring)
   int32_t kb;            // keys per vocabulary-range heap
+  int32_t ngrp;          // column tiles that measure table row norms (a share of K each)
   size_t rescore_lds;    // dynamic LDS of the rescoring kernel
   // wide path
   int32_t ntile;         // 16-column N-tiles per pass (residual rows per pass / 16)
@@ -59,7 +60,7 @@ struct LogitsPlan {
   size_t cand_offset, cand_bytes;  // u64 keys [batch][nblk][k]
   size_t aux_offset, aux_bytes;    // wide path: u64 top-k lower bound per residual row;
                                    // gemm path: per-thread running log-partition partials;
-                                   // rank path: f32 largest squared row norm per vocabulary range
+                                   // rank path: f32 squared row norm parts [ngrp][V] and block maxima
   int32_t nparts;                  // log-partition partials per residual row (= ncand / k)
   size_t lse_offset, lse_bytes;    // float2 partials [batch][nparts]
   size_t ws_bytes;

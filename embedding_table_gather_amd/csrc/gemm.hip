@@ -138,14 +138,16 @@ __global__ void __launch_bounds__(256) gemm_prep_hi_kernel(const void* __restric
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// s + the squares of 8 bf16 values, f32 FMAs in element order.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// s + the squares of 8 bf16 values: four v_dot2c_f32_bf16 (two exact products
+// and one f32 accumulation each), in element-pair order.
 __device__ __forceinline__ float sumsq_bf16x8(bf16x8 f, float s) {
   const u32x4 w = __builtin_bit_cast(u32x4, f);
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
-    s = __builtin_fmaf(lo, lo, s);
-    s = __builtin_fmaf(hi, hi, s);
+    const bf16x2 v = __builtin_bit_cast(bf16x2, w[j]);
+    s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
   }
   return s;
 }
@@ -187,7 +189,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, const uint8_t* __restrict__ Rs, int kpad,
     int64_t B, int k, uint64_t* __restrict__ cand, int nct, int nvr, int tiles_per_range,
     float* __restrict__ logits, float2* __restrict__ lse, float lse_c, float2* __restrict__ lse_run,
-    float* __restrict__ nrm2) {
+    float* __restrict__ npart, int ngrp) {
   using C = GemmCfg<WM, WN>;
   constexpr int MT = C::MT, NT = C::NT, WR = C::WR, WC = C::WC, DPW = C::DPW;
   constexpr int COLS = SPLIT ? kGemmCols : kGemmBN;  // residual rows per column tile
@@ -215,9 +217,11 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
   if (vr >= nvr) return;  // whole workgroup; no barrier has been reached
 
   for (int i = tid; i < COLS * k; i += C::THREADS) heaps[i] = 0;
-  // ranking mode: squared norms of this wave's table rows (M-tile nw, one K half per
-  // lane half) over the current tile, and their running maximum over the range
-  float nsq = 0.f, nmax = 0.f;
+  // ranking mode: partial squared norms of this wave's table rows (M-tile nw, one
+  // K half per lane half) over the K stages s with s % ngrp == ct; column tiles
+  // ct >= ngrp measure none
+  float nsq = 0.f;
+  bool nrm_on = false;
 
   const int nstage = kpad / kGemmBK;
   const uint8_t* rs_tile = Rs + (size_t)ct * kGemmBN * kpad * 2;
@@ -283,7 +287,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
       if constexpr (!SPLIT) {
 #pragma unroll
         for (int a = 0; a < MT; a++)
-          if (a == nw) nsq = sumsq_bf16x8(fa[a], nsq);
+          if (nrm_on && a == nw) nsq = sumsq_bf16x8(fa[a], nsq);
       }
     };
 
@@ -296,6 +300,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     // stage s sub-step 1 is read while sub-step 0 computes, and after the barrier
     // stage s + 1 sub-step 0 is read while stage s sub-step 1 computes.
     for (int s = 0; s < nstage; s++) {
+      if constexpr (!SPLIT) nrm_on = s % ngrp == ct;
       // stage s + depth - 1 goes to the slot stage s - 1 has left
       if (s + depth - 1 < nstage) issue(s + depth - 1, sm == 0 ? depth - 1 : sm - 1);
       read(sa, sb, 1, fa1, fb1);
@@ -314,10 +319,12 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     // Raw logits and the log-partition partial (register layout below; rows
     // as 32-bit offsets in the tile, stores at constant offsets from one base).
     if constexpr (!SPLIT) {
-      // rows past V are copies of row V - 1 and K values past hidden copies of
-      // stored values: the maximum can only grow, so it stays an upper bound
-      nmax = fmaxf(nmax, nsq + __shfl_xor(nsq, 32, 64));
+      // this column tile's part of the squared norm of row WR mw + 32 nw + lane % 32
+      // (K values past hidden are copies of stored values: the sum can only grow)
+      const float part = nsq + __shfl_xor(nsq, 32, 64);
       nsq = 0.f;
+      const int64_t row = v0 + WR * mw + 32 * nw + (lane & 31);
+      if (ct < ngrp && lane < 32 && row < V) npart[(int64_t)ct * V + row] = part;
     }
     if (SPLIT && (logits != nullptr || lse != nullptr)) {
       // an opaque copy of the thread index: the addresses below are recomputed
@@ -433,15 +440,16 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
       }
       continue;
     }
+    // per lane and N-tile t: its residual row's heap and the marks
+    float* xs = (float*)smem + (size_t)(nw * 64 + lane) * 64;  // [WN waves][64 lanes][64], 64 KiB
 #pragma unroll
-    for (int t = 0; t < NTR; t++) {
-      const int col = nw * WCR + 32 * t + (lane & 31);
-      const bool col_ok = (int64_t)ct * COLS + col < B;
-      uint64_t* heap = heaps + (size_t)col * k;
-      float* xs = (float*)smem + (size_t)(nw * 64 + lane) * 64;  // [WN waves][64 lanes][64], 64 KiB
+    for (int p = 0; p < WM; p++) {
+      if (mw == p) {
 #pragma unroll
-      for (int p = 0; p < WM; p++) {
-        if (mw == p) {
+        for (int t = 0; t < NTR; t++) {
+          const int col = nw * WCR + 32 * t + (lane & 31);
+          const bool col_ok = (int64_t)ct * COLS + col < B;
+          uint64_t* heap = heaps + (size_t)col * k;
           const uint32_t tord = col_ok ? (uint32_t)(heap[0] >> 32) : 0xffffffffu;
           uint64_t mask = 0;
 #pragma unroll
@@ -449,6 +457,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
 #pragma unroll
             for (int i = 0; i < 16; i++) mask |= (uint64_t)(score_ord(val(acc, a, t, i)) >= tord) << (16 * a + i);
           if (__ballot(mask != 0) != 0) {
+            // a lane's own 64 logits of N-tile t; the lane reads them back itself
 #pragma unroll
             for (int a = 0; a < MT; a++)
 #pragma unroll
@@ -474,8 +483,8 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
             }
           }
         }
-        gemm_stage_barrier<0>();
       }
+      gemm_stage_barrier<0>();
     }
   }
   if (SPLIT && lse != nullptr) {
@@ -493,19 +502,6 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     const int64_t b = (int64_t)ct * kGemmCols + nw * (WC / 2) + lane;
     if (mw == 0 && lane < 32 && b < B) lse[b * nvr + vr] = lse_combine(run, xl[nw * 32 + lane], lse_c);
   }
-  if constexpr (!SPLIT) {
-    // the range's largest squared row norm (column tile 0 writes it); the ring
-    // is free after the last tile's barrier
-    float* xn = (float*)smem;
-    const float m = wave_max_f32(nmax);
-    if (lane == 0) xn[wv] = m;
-    gemm_stage_barrier<0>();
-    if (ct == 0 && tid == 0) {
-      float mm = xn[0];
-      for (int w = 1; w < C::NW; w++) mm = fmaxf(mm, xn[w]);
-      nrm2[vr] = mm;
-    }
-  }
   // heaps -> candidates [B][nvr][k]; the barrier orders the heap writes (also
   // the zeroing, for a range past the table that ran no tile) before the reads
   gemm_stage_barrier<0>();
@@ -517,6 +513,28 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
       for (int j = 0; j < k; j++) out[j] = heap[j];
     }
   }
+}
+
+// Squared row norms from the column tiles' parts npart [ngrp][V]; block x writes
+// the largest of its rows' norms to nrm2[x].
+static constexpr int kNormRows = 1024;  // rows per block of rank_norm_kernel
+__global__ void __launch_bounds__(256) rank_norm_kernel(const float* __restrict__ npart, int ngrp, int64_t V,
+                                                        float* __restrict__ nrm2) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  float m = 0.f;
+  for (int j = 0; j < kNormRows / 256; j++) {
+    const int64_t v = (int64_t)blockIdx.x * kNormRows + j * 256 + tid;
+    if (v < V) {
+      float sum = 0.f;
+      for (int g = 0; g < ngrp; g++) sum += npart[(int64_t)g * V + v];
+      m = fmaxf(m, sum);
+    }
+  }
+  m = wave_max_f32(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) nrm2[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // ---------------------------------------------------------------------------
@@ -534,21 +552,28 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
 // One workgroup per residual row:
 //  * U = the heap keys of every vocabulary range (kb per range, approximate);
 //  * A = the k-th largest approximate logit in U (-inf with fewer than k keys);
-//  * thr = A - 2 (slack + eps);
+//  * phase 1 rescores the keys of U with a_v >= A, and T1 is the k-th largest
+//    rescored value (-inf with fewer than k);
+//  * thr = T1 - slack - 2 eps;
 //  * a range whose heap is full and whose smallest kept key reaches thr may have
 //    dropped a row above thr: all its rows are rescored;
-//  * every other key of U with a_v >= thr is rescored;
-//  * the answer is the k best rescored keys (logit desc, id asc).
-// Why this is the top-k: the k best keys of U are rescored (directly or through
-// their range), so the k-th rescored value T >= A - slack - eps.  A row that is
+//  * every other key of U with thr <= a_v < A is rescored;
+//  * the answer is the k best rescored keys (logit desc, id asc; a row rescored
+//    twice enters a heap once).
+// Why this is the top-k: the final k-th rescored value T >= T1.  A row that is
 // not rescored has a_v < thr (dropped rows lie at or below their range's
-// smallest kept key), so r . e_v < thr + slack = A - slack - 2 eps <= T - eps,
-// below the exact logit of every selected row.
+// smallest kept key), so r . e_v < thr + slack = T1 - 2 eps <= T - 2 eps, below
+// the exact logit of every selected row (each >= T - eps).
 // ---------------------------------------------------------------------------
 static constexpr int kRescoreThreads = 512;
 static constexpr int kRescoreWaves = kRescoreThreads / 64;
 static constexpr int kRankMaxHidden = 16384;  // the residual row is kept in LDS
 static constexpr int kRankMaxKeys = 4096;     // heap keys per residual row (nvr kb)
+// Keys per vocabulary-range heap in ranking mode.  A range keeps its 16 best
+// approximate keys; the answer's k rows are spread over the ranges, and a range
+// holding more of the candidates than that is rescanned.  Small heaps leave LDS
+// for the deeper residual ring and shorten the first tile's selection.
+static constexpr int kRankHeapKeys = 16;
 
 // LDS of gemm_rescore_kernel: U [n] keys, heaps [waves][k] keys, the residual
 // [hidden rounded up to 8] f32, S [n] rows, flags [nvr], rescan list [nvr].
@@ -621,12 +646,12 @@ __device__ __forceinline__ float f32_round_down(double x) {
 //  table   bf16 [V][hidden], row_bytes = 2 hidden (a multiple of 16)
 //  R       residual rows (wire format `wire`)
 //  cand    [B][nvr][kb] heap keys of the ranking contraction (unordered, 0 = empty)
-//  nrm2    [nvr] largest squared row norm of each vocabulary range
+//  nrm2    [nnrm] largest squared row norms of blocks of table rows
 //  ids, scores  [B][k] the answer, best first
 __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden, int kpad,
     const void* __restrict__ R, int wire, const uint64_t* __restrict__ cand, int nvr, int kb, int64_t range_rows,
-    const float* __restrict__ nrm2, int k, int32_t* __restrict__ ids, float* __restrict__ scores) {
+    const float* __restrict__ nrm2, int nnrm, int k, int32_t* __restrict__ ids, float* __restrict__ scores) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ float red[kRescoreWaves][4];
   __shared__ uint32_t hist[256];
@@ -653,7 +678,7 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
     s_hi = __builtin_fmaf(hi, hi, s_hi);
     s_r = __builtin_fmaf(x, x, s_r);
   }
-  for (int i = tid; i < nvr; i += kRescoreThreads) n2 = fmaxf(n2, nrm2[i]);
+  for (int i = tid; i < nnrm; i += kRescoreThreads) n2 = fmaxf(n2, nrm2[i]);
   for (int i = tid; i < n; i += kRescoreThreads) U[i] = cand[b * n + i];
   for (int i = tid; i < kRescoreWaves * k; i += kRescoreThreads) heaps[i] = 0;
   if (tid == 0) cnt[0] = cnt[1] = 0;
@@ -676,40 +701,25 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
     nn2 = fmax(nn2, (double)red[w][3]);
   }
   // the f32 sums above are within a few hundred ulp of the exact ones: inflate
-  // them by 2^-10 (sums of squares) before the square roots
+  // them by 2^-10 (sums of squares) before the square roots; the row norms
+  // (up to kpad / 4 roundings per lane) by 2^-9
   const double inf2 = 1.0 + 0x1p-10;
-  const double N = sqrt(nn2 * inf2);
+  const double N = sqrt(nn2 * (1.0 + 0x1p-9));
   // inputs or products below the f32 normal range (flushed to zero or not)
   const double tiny = 0x1p-100 * ((double)kpad + sqrt((double)kpad) * (N + sqrt(hi2 * inf2) + sqrt(r2 * inf2)));
   const double slack = (sqrt(lo2 * inf2) + (double)kpad * 0x1p-22 * sqrt(hi2 * inf2)) * N + tiny;
   const double eps = ((double)hidden / 64.0 + 8.0) * 0x1p-23 * sqrt(r2 * inf2) * N + tiny;
 
   const uint32_t a_ord = block_kth_ord(U, n, k, hist, sel);
-  const float thr = a_ord == 0u ? -__builtin_inff() : f32_round_down((double)ord_score(a_ord) - 2.0 * (slack + eps));
+  const float A = a_ord == 0u ? -__builtin_inff() : ord_score(a_ord);
 
-  // ranges to rescan: a full heap whose smallest key reaches thr
-  for (int vr = tid; vr < nvr; vr += kRescoreThreads) {
-    uint64_t mn = ~0ull;
-    for (int j = 0; j < kb; j++) mn = min(mn, U[vr * kb + j]);
-    const bool rescan = mn != 0 && ord_score((uint32_t)(mn >> 32)) >= thr;
-    flag[vr] = rescan;
-    if (rescan) rl[atomicAdd(&cnt[1], 1u)] = (uint32_t)vr;
-  }
-  __syncthreads();
-  for (int i = tid; i < n; i += kRescoreThreads) {
-    const uint64_t key = U[i];
-    if (key != 0 && flag[i / kb] == 0 && ord_score((uint32_t)(key >> 32)) >= thr)
-      S[atomicAdd(&cnt[0], 1u)] = ~(uint32_t)key;
-  }
-  __syncthreads();
-  const int ns = (int)cnt[0], nres = (int)cnt[1];
-
-  // one wave per row: f32 FMAs over values 8 lane + 512 j + e, then a butterfly
+  // one wave per row: f32 FMAs over values 8 lane + 512 j + e, then a butterfly;
+  // every lane holds the same key, and the wave checks its heap for it
   uint64_t* hp = heaps + wv * k;
   auto rescore = [&](int64_t v) {
     const uint8_t* row = table + (uint64_t)v * (uint64_t)row_bytes;
     float acc = 0.f;
-#pragma unroll 4
+#pragma unroll 8
     for (int c = 8 * lane; c < hidden; c += 512) {
       const u32x4 w = *(const u32x4*)(row + 2 * c);
       const f32x4 ra = *(const f32x4*)(r + c), rb = *(const f32x4*)(r + c + 4);
@@ -723,11 +733,42 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
       acc = __builtin_fmaf(bf16_hi(w.w), rb.w, acc);
     }
     acc = wave_sum(acc);
-    if (lane == 0) {
-      const uint64_t key = make_key(acc, (uint32_t)v);
-      if (key > hp[0]) heap_replace_root(hp, k, key);
-    }
+    const uint64_t key = make_key(acc, (uint32_t)v);
+    if (key > hp[0] && __ballot(lane < k && hp[lane] == key) == 0 && lane == 0) heap_replace_root(hp, k, key);
   };
+
+  // phase 1: the keys of U at or above A
+  for (int i = tid; i < n; i += kRescoreThreads) {
+    const uint64_t key = U[i];
+    if (key != 0 && ord_score((uint32_t)(key >> 32)) >= A) S[atomicAdd(&cnt[0], 1u)] = ~(uint32_t)key;
+  }
+  __syncthreads();
+  const int ns1 = (int)cnt[0];
+  for (int i = wv; i < ns1; i += kRescoreWaves) rescore(S[i]);
+  __syncthreads();
+  if (tid == 0) cnt[0] = 0;
+  const uint32_t t_ord = block_kth_ord(heaps, kRescoreWaves * k, k, hist, sel);
+  const float thr =
+      t_ord == 0u ? -__builtin_inff() : f32_round_down((double)ord_score(t_ord) - slack - 2.0 * eps);
+
+  // phase 2: ranges to rescan (a full heap whose smallest key reaches thr), then
+  // the keys of U in [thr, A) outside them
+  for (int vr = tid; vr < nvr; vr += kRescoreThreads) {
+    uint64_t mn = ~0ull;
+    for (int j = 0; j < kb; j++) mn = min(mn, U[vr * kb + j]);
+    const bool rescan = mn != 0 && ord_score((uint32_t)(mn >> 32)) >= thr;
+    flag[vr] = rescan;
+    if (rescan) rl[atomicAdd(&cnt[1], 1u)] = (uint32_t)vr;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kRescoreThreads) {
+    const uint64_t key = U[i];
+    if (key == 0 || flag[i / kb] != 0) continue;
+    const float a = ord_score((uint32_t)(key >> 32));
+    if (a >= thr && a < A) S[atomicAdd(&cnt[0], 1u)] = ~(uint32_t)key;
+  }
+  __syncthreads();
+  const int ns = (int)cnt[0], nres = (int)cnt[1];
   for (int i = wv; i < ns; i += kRescoreWaves) rescore(S[i]);
   for (int q = 0; q < nres; q++) {
     const int64_t v0 = (int64_t)rl[q] * range_rows, v1 = min(V, v0 + range_rows);
@@ -773,14 +814,20 @@ static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const
   hipLaunchKernelGGL((gemm_logits_kernel<WM, WN, NA, NB, SPLIT>), dim3((unsigned)p.nblk), dim3(C::THREADS),
                      p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (const uint8_t*)rs, p.kpad, p.batch,
                      SPLIT ? p.k : p.kb, cand, p.nct, p.nvr, p.tiles_per_range, x.logits, x.lse, x.lse_scale,
-                     (float2*)x.aux, (float*)x.aux);
+                     (float2*)x.aux, (float*)x.aux, p.ngrp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record_event(ev1, stream)) != hipSuccess) return e;
   if constexpr (!SPLIT) {
+    // aux: npart [ngrp][V], then nrm2 [nnrm]
+    const int nnrm = (int)cdiv(t.V, kNormRows);
+    float* nrm2 = (float*)x.aux + align_up((size_t)p.ngrp * t.V, 64);
+    hipLaunchKernelGGL(rank_norm_kernel, dim3((unsigned)nnrm), dim3(256), 0, stream, (const float*)x.aux, p.ngrp, t.V,
+                       nrm2);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = set_dynamic_lds((const void*)gemm_rescore_kernel, p.rescore_lds)) != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_rescore_kernel, dim3((unsigned)p.batch), dim3(kRescoreThreads), p.rescore_lds, stream,
                        t.rows, t.V, t.row_bytes, (int)t.hidden, p.kpad, R, (int)x.wire, (const uint64_t*)cand, p.nvr,
-                       p.kb, (int64_t)p.tiles_per_range * kGemmBM, (const float*)x.aux, p.k, ids, scores);
+                       p.kb, (int64_t)p.tiles_per_range * kGemmBM, (const float*)nrm2, nnrm, p.k, ids, scores);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -849,11 +896,13 @@ int32_t plan_rank(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
     return -5;
   }
   int32_t hk = 0;
-  const int32_t st = plan_gemm_common(t, batch, false, std::min<int32_t>(k, 32), p, &hk, why);
+  const int32_t st = plan_gemm_common(t, batch, false, std::min<int32_t>(k, kRankHeapKeys), p, &hk, why);
   if (st != 0) return st;
   p->kb = hk;
   p->ncand = (int32_t)(p->nvr * hk);
-  p->aux_bytes = (size_t)p->nvr * 4;  // largest squared row norm per vocabulary range
+  // row norms: up to 8 column tiles each measure a share of the K stages
+  p->ngrp = (int32_t)std::min<int64_t>(p->nct, 8);
+  p->aux_bytes = (align_up((size_t)p->ngrp * t.V, 64) + (size_t)cdiv(t.V, kNormRows)) * 4;
   p->rescore_lds = rescore_lds_bytes(t.hidden, p->ncand, p->nvr, k);
   if (p->rescore_lds > kMaxLds - 2048) {  // static LDS besides
     *why = "the rank path's rescoring does not fit in LDS";

@@ -86,7 +86,7 @@ def test_rank_path_ragged(V, d, B):
 @pytest.mark.parametrize("k", [10, 40, 64])
 def test_rank_path_rescans_a_range_holding_many_winners(k):
     # 80 planted winners in rows 256..335, one 256-row vocabulary range: its heap
-    # keeps at most 32 of them, so the certificate must send the whole range to
+    # keeps only 16 of them, so the certificate must send the whole range to
     # exact rescoring for the answer to hold the other winners
     V, d, B = 30000, 512, 2
     host = synth.make_table(BF16, V, d, seed=23)
