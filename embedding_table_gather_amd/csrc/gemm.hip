@@ -565,8 +565,11 @@ __global__ void __launch_bounds__(256) rank_norm_kernel(const float* __restrict_
 // smallest kept key), so r . e_v < thr + slack = T1 - 2 eps <= T - 2 eps, below
 // the exact logit of every selected row (each >= T - eps).
 // ---------------------------------------------------------------------------
-static constexpr int kRescoreThreads = 512;
+// 4 waves per residual row: with the LDS below, four or more rows share a CU, so
+// a 1,024-row batch is rescored in one round (the rescoring is bound by HBM).
+static constexpr int kRescoreThreads = 256;
 static constexpr int kRescoreWaves = kRescoreThreads / 64;
+static constexpr int kRescoreChunks = 6;  // 1 KiB loads per row in flight per wave
 static constexpr int kRankMaxHidden = 16384;  // the residual row is kept in LDS
 static constexpr int kRankMaxKeys = 4096;     // heap keys per residual row (nvr kb)
 // Keys per vocabulary-range heap in ranking mode.  A range keeps its 16 best
@@ -713,28 +716,61 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
   const uint32_t a_ord = block_kth_ord(U, n, k, hist, sel);
   const float A = a_ord == 0u ? -__builtin_inff() : ord_score(a_ord);
 
-  // one wave per row: f32 FMAs over values 8 lane + 512 j + e, then a butterfly;
-  // every lane holds the same key, and the wave checks its heap for it
+  // One wave per row: f32 FMAs over values 8 lane + 512 j + e (j ascending), then
+  // a butterfly; every lane holds the same key, and the wave checks its heap for
+  // it.  A wave takes two rows at a time and issues kRescoreChunks 1 KiB loads of
+  // each together (the last block's loads past hidden read the row's last chunk
+  // and are not used), so each row's sum has the same order either way.
   uint64_t* hp = heaps + wv * k;
-  auto rescore = [&](int64_t v) {
-    const uint8_t* row = table + (uint64_t)v * (uint64_t)row_bytes;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int c = 8 * lane; c < hidden; c += 512) {
-      const u32x4 w = *(const u32x4*)(row + 2 * c);
-      const f32x4 ra = *(const f32x4*)(r + c), rb = *(const f32x4*)(r + c + 4);
-      acc = __builtin_fmaf(bf16_lo(w.x), ra.x, acc);
-      acc = __builtin_fmaf(bf16_hi(w.x), ra.y, acc);
-      acc = __builtin_fmaf(bf16_lo(w.y), ra.z, acc);
-      acc = __builtin_fmaf(bf16_hi(w.y), ra.w, acc);
-      acc = __builtin_fmaf(bf16_lo(w.z), rb.x, acc);
-      acc = __builtin_fmaf(bf16_hi(w.z), rb.y, acc);
-      acc = __builtin_fmaf(bf16_lo(w.w), rb.z, acc);
-      acc = __builtin_fmaf(bf16_hi(w.w), rb.w, acc);
-    }
-    acc = wave_sum(acc);
+  auto insert = [&](float acc, int64_t v) {
     const uint64_t key = make_key(acc, (uint32_t)v);
     if (key > hp[0] && __ballot(lane < k && hp[lane] == key) == 0 && lane == 0) heap_replace_root(hp, k, key);
+  };
+  auto rescore2 = [&](int64_t va, int64_t vb) {  // vb < 0: one row
+    const uint8_t* rowa = table + (uint64_t)va * (uint64_t)row_bytes;
+    const uint8_t* rowb = table + (uint64_t)(vb >= 0 ? vb : va) * (uint64_t)row_bytes;
+    float acca = 0.f, accb = 0.f;
+    for (int c0 = 8 * lane; c0 < hidden; c0 += 512 * kRescoreChunks) {
+      u32x4 wa[kRescoreChunks], wb[kRescoreChunks];
+#pragma unroll
+      for (int j = 0; j < kRescoreChunks; j++) {
+        const int c = min(c0 + 512 * j, hidden - 8);
+        wa[j] = *(const u32x4*)(rowa + 2 * c);
+        wb[j] = *(const u32x4*)(rowb + 2 * c);
+      }
+#pragma unroll
+      for (int j = 0; j < kRescoreChunks; j++) {
+        const int c = c0 + 512 * j;
+        if (c < hidden) {
+          const f32x4 x0 = *(const f32x4*)(r + c), x1 = *(const f32x4*)(r + c + 4);
+          acca = __builtin_fmaf(bf16_lo(wa[j].x), x0.x, acca);
+          acca = __builtin_fmaf(bf16_hi(wa[j].x), x0.y, acca);
+          acca = __builtin_fmaf(bf16_lo(wa[j].y), x0.z, acca);
+          acca = __builtin_fmaf(bf16_hi(wa[j].y), x0.w, acca);
+          acca = __builtin_fmaf(bf16_lo(wa[j].z), x1.x, acca);
+          acca = __builtin_fmaf(bf16_hi(wa[j].z), x1.y, acca);
+          acca = __builtin_fmaf(bf16_lo(wa[j].w), x1.z, acca);
+          acca = __builtin_fmaf(bf16_hi(wa[j].w), x1.w, acca);
+          accb = __builtin_fmaf(bf16_lo(wb[j].x), x0.x, accb);
+          accb = __builtin_fmaf(bf16_hi(wb[j].x), x0.y, accb);
+          accb = __builtin_fmaf(bf16_lo(wb[j].y), x0.z, accb);
+          accb = __builtin_fmaf(bf16_hi(wb[j].y), x0.w, accb);
+          accb = __builtin_fmaf(bf16_lo(wb[j].z), x1.x, accb);
+          accb = __builtin_fmaf(bf16_hi(wb[j].z), x1.y, accb);
+          accb = __builtin_fmaf(bf16_lo(wb[j].w), x1.z, accb);
+          accb = __builtin_fmaf(bf16_hi(wb[j].w), x1.w, accb);
+        }
+      }
+    }
+    acca = wave_sum(acca);
+    accb = wave_sum(accb);
+    insert(acca, va);
+    if (vb >= 0) insert(accb, vb);
+  };
+  // rows S[i0], S[i0 + W], ... of a list, two at a time
+  auto rescore_list = [&](int cnt) {
+    for (int i = wv; i < cnt; i += 2 * kRescoreWaves)
+      rescore2(S[i], i + kRescoreWaves < cnt ? (int64_t)S[i + kRescoreWaves] : -1);
   };
 
   // phase 1: the keys of U at or above A
@@ -744,7 +780,7 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
   }
   __syncthreads();
   const int ns1 = (int)cnt[0];
-  for (int i = wv; i < ns1; i += kRescoreWaves) rescore(S[i]);
+  rescore_list(ns1);
   __syncthreads();
   if (tid == 0) cnt[0] = 0;
   const uint32_t t_ord = block_kth_ord(heaps, kRescoreWaves * k, k, hist, sel);
@@ -769,14 +805,15 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
   }
   __syncthreads();
   const int ns = (int)cnt[0], nres = (int)cnt[1];
-  for (int i = wv; i < ns; i += kRescoreWaves) rescore(S[i]);
+  rescore_list(ns);
   for (int q = 0; q < nres; q++) {
     const int64_t v0 = (int64_t)rl[q] * range_rows, v1 = min(V, v0 + range_rows);
-    for (int64_t v = v0 + wv; v < v1; v += kRescoreWaves) rescore(v);
+    for (int64_t v = v0 + wv; v < v1; v += 2 * kRescoreWaves)
+      rescore2(v, v + kRescoreWaves < v1 ? v + kRescoreWaves : -1);
   }
   __syncthreads();
   if (wv == 0) {
-    uint64_t key[kRescoreWaves];  // up to 8 k <= 512 keys, 8 per lane
+    uint64_t key[kRescoreWaves];  // the waves' heaps, kRescoreWaves keys per lane (k <= 64)
 #pragma unroll
     for (int j = 0; j < kRescoreWaves; j++) {
       const int i = lane + 64 * j;
