@@ -378,16 +378,21 @@ def main() -> int:
         del ph
         Bp = p.batches[0]
         Rp = torch.from_numpy(p.residuals(Bp)).to(dev)
-        wsp = pt.workspace(Bp, p.k)
-        f = lambda evs=None: pt.logits_topk(Rp, p.k, workspace=wsp, events=evs)
-        f()
-        mp, kp = _timed(torch, f, 5, events=hev)
         flops = 2.0 * Bp * p.V * p.d
-        also["prefill_logits_top40_B1024"] = {
-            "ms_per_call": round(mp, 3), "kernel_ms": round(kp, 3),
-            "TFLOPs": round(flops / (mp * 1e-3) / 1e12, 1),
-            "pct_bf16_mfma_peak": round(100 * flops / (mp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1)}
-        log(f"prefill B=1024: {mp:.2f} ms")
+        # the automatic choice (rank path: bf16-residual tiles + exact rescoring),
+        # then the hi + lo split contraction that probabilities and raw logits use
+        for key, path in (("prefill_logits_top40_B1024", etg.PATH_AUTO),
+                          ("prefill_logits_top40_B1024_split_gemm", etg.PATH_GEMM)):
+            wsp = pt.workspace(Bp, p.k, path)
+            f = lambda evs=None: pt.logits_topk(Rp, p.k, path=path, workspace=wsp, events=evs)
+            for _ in range(5):  # the clocks settle over the first calls of this contraction
+                f()
+            mp, kp = _timed(torch, f, 10, events=hev)
+            also[key] = {
+                "ms_per_call": round(mp, 3), "kernel_ms": round(kp, 3),
+                "TFLOPs": round(flops / (mp * 1e-3) / 1e12, 1),
+                "pct_bf16_mfma_peak": round(100 * flops / (mp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1)}
+            log(f"prefill B=1024 path={path}: {mp:.2f} ms")
         del pt
         torch.cuda.empty_cache()
     if also:
