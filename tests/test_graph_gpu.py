@@ -88,3 +88,50 @@ def test_captured_step_replays_match_eager(dtype, V, d, B, path):
                 assert np.array_equal(a, b), (rep, j)
             else:
                 assert np.array_equal(bits(a), bits(b)), (rep, j)
+
+
+@pytest.mark.parametrize("B", [70, 300])
+def test_captured_rank_path_replays_match_eager(B):
+    # the rank path answers the top-k alone (no probabilities or raw logits):
+    # gather + top-k captured, replayed with new inputs, against eager calls
+    V, d, k, n = 5003, 896, 10, 37
+    host = synth.make_table(etg.BF16, V, d, seed=1250)
+    t = table(host, etg.BF16, V, d)
+    dev = torch.device("cuda")
+    ids_buf = torch.zeros(n, dtype=torch.int32, device=dev)
+    R_buf = torch.zeros((B, d), dtype=torch.float32, device=dev)
+    ws = t.workspace(B, k, etg.PATH_RANK)
+    x_buf = torch.empty((n, d), dtype=torch.float32, device=dev)
+    oi = torch.empty((B, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((B, k), device=dev)
+
+    def step():
+        t.embed_gather(ids_buf, scale="sqrt_d", out=x_buf, check=False)
+        t.logits_topk(R_buf, k, path=etg.PATH_RANK, workspace=ws, out_ids=oi, out_scores=osc)
+
+    note(f"graph capture rank path V={V} d={d} B={B}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ids = synth.uniform_ids(n, V, seed=1350 + rep)
+        R = synth.residuals(B, d, seed=1450 + rep)
+        ids_buf.copy_(torch.from_numpy(ids))
+        R_buf.copy_(torch.from_numpy(R))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [a.cpu().numpy().copy() for a in (x_buf, oi, osc)]
+        x = t.embed_gather(ids_buf, scale="sqrt_d", check=False)
+        i, s = t.logits_topk(R_buf, k, path=etg.PATH_RANK)
+        torch.cuda.synchronize()
+        assert np.array_equal(got[1], i.cpu().numpy()), f"replay {rep}: ids differ from eager"
+        for a, b in ((got[0], x), (got[2], s)):
+            assert np.array_equal(bits(a), bits(b)), f"replay {rep} differs from eager"
