@@ -37,7 +37,8 @@ struct LogitsPlan {
   int32_t nvr;           // vocabulary ranges
   int32_t tiles_per_range;
   // rank path (the gemm kernel in ranking mode, then exact rescoring)
-  int32_t kb;            // keys per vocabulary-range heap
+  int32_t kb;            // keys per vocabulary-range heap (or per wide-kernel block)
+  int32_t rank_wide;     // 1: the wide kernel ranks (batch <= 64), 0: the gemm kernel
   int32_t ngrp;          // column tiles that measure table row norms (a share of K each)
   size_t rescore_lds;    // dynamic LDS of the rescoring kernel
   // wide path
@@ -124,7 +125,7 @@ inline hipError_t record_event(hipEvent_t ev, hipStream_t stream) {
 // img_bytes, aux_bytes, ncand) and launchers of the table-streaming kernel
 // (recording ev0 / ev1 around it).  stream.hip, wide.hip, gemm.hip (gemm and rank), q8.hip, row.hip.
 int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
-int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
+int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why, bool rank = false);
 int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_q8(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_row(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
@@ -139,7 +140,20 @@ hipError_t launch_q8(const TableDesc& t, const LogitsPlan& p, const void* R, uin
                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_row(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand, const LogitsExtras& x,
                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
-// The rank path writes ids / scores itself (its rescoring kernel replaces the merge).
+// The rank path writes ids / scores itself (its rescoring kernel replaces the merge):
+// the gemm kernel ranks past 64 residual rows, the wide kernel up to 64.
+hipError_t launch_wide_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
+                            const LogitsExtras& x, int32_t* ids, float* scores, hipStream_t stream, hipEvent_t ev0,
+                            hipEvent_t ev1);
+// Rescoring and certificate of the rank path (gemm.hip): candidate keys [batch][nranges][p.kb]
+// of ranges of range_rows table rows, nrm2 [nnrm] upper bounds of the squared row norms,
+// kpad the terms the ranking kernel accumulated per logit; sorted: each range's keys
+// are in descending order.
+hipError_t launch_rescore(const TableDesc& t, const LogitsPlan& p, const void* R, int wire, const uint64_t* cand,
+                          int nranges, int64_t range_rows, const float* nrm2, int nnrm, int kpad, int32_t* ids,
+                          float* scores, hipStream_t stream, int sorted);
+int32_t rescore_waves(int64_t batch);
+size_t rescore_lds(int64_t hidden, int n, int nvr, int k, int64_t batch);
 hipError_t launch_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs, uint64_t* cand,
                        const LogitsExtras& x, int32_t* ids, float* scores, hipStream_t stream, hipEvent_t ev0,
                        hipEvent_t ev1);

@@ -552,12 +552,14 @@ __global__ void __launch_bounds__(256) rank_norm_kernel(const float* __restrict_
 // One workgroup per residual row:
 //  * U = the heap keys of every vocabulary range (kb per range, approximate);
 //  * A = the k-th largest approximate logit in U (-inf with fewer than k keys);
-//  * phase 1 rescores the keys of U with a_v >= A, and T1 is the k-th largest
+//  * phase 1 rescores the keys of U with a_v >= lo1 = A - 9/8 slack - 2 eps (the
+//    window phase 2 will want, guessed from A), and T1 is the k-th largest
 //    rescored value (-inf with fewer than k);
 //  * thr = T1 - slack - 2 eps;
 //  * a range whose heap is full and whose smallest kept key reaches thr may have
 //    dropped a row above thr: all its rows are rescored;
-//  * every other key of U with thr <= a_v < A is rescored;
+//  * every other key of U with thr <= a_v < lo1 is rescored (none unless T1 fell
+//    more than slack / 8 below A);
 //  * the answer is the k best rescored keys (logit desc, id asc; a row rescored
 //    twice enters a heap once).
 // Why this is the top-k: the final k-th rescored value T >= T1.  A row that is
@@ -565,10 +567,11 @@ __global__ void __launch_bounds__(256) rank_norm_kernel(const float* __restrict_
 // smallest kept key), so r . e_v < thr + slack = T1 - 2 eps <= T - 2 eps, below
 // the exact logit of every selected row (each >= T - eps).
 // ---------------------------------------------------------------------------
-// 4 waves per residual row: with the LDS below, four or more rows share a CU, so
-// a 1,024-row batch is rescored in one round (the rescoring is bound by HBM).
-static constexpr int kRescoreThreads = 256;
-static constexpr int kRescoreWaves = kRescoreThreads / 64;
+// Waves per residual row: 4 for large batches (with the LDS below, four or more
+// rows share a CU, so a 1,024-row batch is rescored in one round, bound by HBM),
+// 16 for batches of up to kRescoreWideBatch rows (few workgroups: each row's
+// rescoring is latency-bound and the extra waves shorten it).
+static constexpr int kRescoreWideBatch = 256;
 static constexpr int kRescoreChunks = 6;  // 1 KiB loads per row in flight per wave
 static constexpr int kRankMaxHidden = 16384;  // the residual row is kept in LDS
 static constexpr int kRankMaxKeys = 4096;     // heap keys per residual row (nvr kb)
@@ -578,23 +581,29 @@ static constexpr int kRankMaxKeys = 4096;     // heap keys per residual row (nvr
 // for the deeper residual ring and shorten the first tile's selection.
 static constexpr int kRankHeapKeys = 16;
 
-// LDS of gemm_rescore_kernel: U [n] keys, heaps [waves][k] keys, the residual
+// LDS of rank_rescore_kernel: U [n] keys, heaps [waves][k] keys, the residual
 // [hidden rounded up to 8] f32, S [n] rows, flags [nvr], rescan list [nvr].
-static size_t rescore_lds_bytes(int64_t hidden, int n, int nvr, int k) {
-  return (size_t)n * 8 + (size_t)kRescoreWaves * k * 8 + (size_t)((hidden + 7) & ~7) * 4 + (size_t)n * 4 +
-         (size_t)nvr * 8;
+static size_t rescore_lds_bytes(int64_t hidden, int n, int nvr, int k, int nw) {
+  return (size_t)n * 8 + (size_t)nw * k * 8 + (size_t)((hidden + 7) & ~7) * 4 + (size_t)n * 4 + (size_t)nvr * 8;
+}
+
+int32_t rescore_waves(int64_t batch) { return batch <= kRescoreWideBatch ? 16 : 4; }
+
+size_t rescore_lds(int64_t hidden, int n, int nvr, int k, int64_t batch) {
+  return rescore_lds_bytes(hidden, n, nvr, k, rescore_waves(batch));
 }
 
 // Order value of the k-th largest key among the nonzero keys U[0, n) (counted
 // with multiplicity), or 0 with fewer than k.  Radix selection, 8 bits per
-// pass from the top, counts in an LDS histogram.
+// pass from the top, counts in an LDS histogram; NT threads.
+template <int NT>
 __device__ uint32_t block_kth_ord(const uint64_t* U, int n, int k, uint32_t* hist, uint32_t* sel) {
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t prefix = 0, pmask = 0, kk = (uint32_t)k;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kRescoreThreads) hist[i] = 0;
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kRescoreThreads) {
+    for (int i = tid; i < n; i += NT) {
       const uint64_t key = U[i];
       const uint32_t o = (uint32_t)(key >> 32);
       if (key != 0 && (o & pmask) == prefix) atomicAdd(&hist[(o >> shift) & 255u], 1u);
@@ -636,6 +645,39 @@ __device__ uint32_t block_kth_ord(const uint64_t* U, int n, int k, uint32_t* his
   return prefix;
 }
 
+// Order value of the k-th largest key of nl lists of kb keys each (each list in
+// descending order, empty slots 0 at its end), or 0 with fewer than k keys: k
+// rounds of taking the largest list head (keys are unique, so one list owns it).
+// One wave; lane l keeps the heads of lists l + 64 j, j < PL.
+template <int PL>
+__device__ uint32_t wave_kth_sorted(const uint64_t* U, int nl, int kb, int k) {
+  const int lane = threadIdx.x & 63;
+  uint64_t head[PL];
+  int pos[PL];
+#pragma unroll
+  for (int j = 0; j < PL; j++) {
+    const int l = lane + 64 * j;
+    pos[j] = 0;
+    head[j] = l < nl ? U[l * kb] : 0;
+  }
+  uint64_t best = 0;
+  for (int t = 0; t < k; t++) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int j = 0; j < PL; j++) m = head[j] > m ? head[j] : m;
+    best = wave_max_u64(m);
+    if (best == 0) return 0u;
+#pragma unroll
+    for (int j = 0; j < PL; j++) {
+      if (head[j] == best) {
+        pos[j]++;
+        head[j] = pos[j] < kb ? U[(lane + 64 * j) * kb + pos[j]] : 0;
+      }
+    }
+  }
+  return (uint32_t)(best >> 32);
+}
+
 // f32 value rounded toward -inf from a finite double.
 __device__ __forceinline__ float f32_round_down(double x) {
   float f = (float)x;
@@ -648,22 +690,28 @@ __device__ __forceinline__ float f32_round_down(double x) {
 
 //  table   bf16 [V][hidden], row_bytes = 2 hidden (a multiple of 16)
 //  R       residual rows (wire format `wire`)
-//  cand    [B][nvr][kb] heap keys of the ranking contraction (unordered, 0 = empty)
+//  cand    [B][nvr][kb] candidate keys of the ranking kernel per range of
+//          range_rows table rows (unordered, 0 = empty; a range with fewer than kb
+//          keys kept every row it has)
 //  nrm2    [nnrm] largest squared row norms of blocks of table rows
+//  kpad    terms the ranking kernel accumulated per logit
+//  sorted  each range's keys are in descending order (the wide kernel's lists)
 //  ids, scores  [B][k] the answer, best first
-__global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden, int kpad,
     const void* __restrict__ R, int wire, const uint64_t* __restrict__ cand, int nvr, int kb, int64_t range_rows,
-    const float* __restrict__ nrm2, int nnrm, int k, int32_t* __restrict__ ids, float* __restrict__ scores) {
+    const float* __restrict__ nrm2, int nnrm, int k, int32_t* __restrict__ ids, float* __restrict__ scores,
+    int sorted) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ float red[kRescoreWaves][4];
+  __shared__ float red[NW][4];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sel[2];
   __shared__ uint32_t cnt[2];  // rows in S, ranges to rescan
   const int n = nvr * kb;
   uint64_t* U = (uint64_t*)smem;
   uint64_t* heaps = U + n;                                     // [waves][k]
-  float* r = (float*)(heaps + kRescoreWaves * k);              // [hidden]
+  float* r = (float*)(heaps + NW * k);              // [hidden]
   uint32_t* S = (uint32_t*)(r + ((hidden + 7) & ~7));          // [n]
   uint32_t* flag = S + n;                                      // [nvr] 1: rescanned
   uint32_t* rl = flag + nvr;                                   // [nvr]
@@ -672,18 +720,29 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
 
   // residual row and the squared norms of lo, hi and r
   float s_lo = 0.f, s_hi = 0.f, s_r = 0.f, n2 = 0.f;
-  for (int c = tid; c < hidden; c += kRescoreThreads) {
-    const float x = residual_value(R, wire, b, hidden, c);
+  auto take = [&](int c, float x) {
     r[c] = x;
     const float hi = __uint_as_float(bf16_rne(x) << 16);
     const float lo = x - hi;  // exact
     s_lo = __builtin_fmaf(lo, lo, s_lo);
     s_hi = __builtin_fmaf(hi, hi, s_hi);
     s_r = __builtin_fmaf(x, x, s_r);
+  };
+  if (wire == WIRE_F32 && ((uintptr_t)R & 15) == 0) {  // hidden is a multiple of 8: 16-byte rows
+    const f32x4* src = (const f32x4*)((const float*)R + b * hidden);
+    for (int c4 = tid; c4 < hidden / 4; c4 += (64 * NW)) {
+      const f32x4 x = src[c4];
+      take(4 * c4, x.x);
+      take(4 * c4 + 1, x.y);
+      take(4 * c4 + 2, x.z);
+      take(4 * c4 + 3, x.w);
+    }
+  } else {
+    for (int c = tid; c < hidden; c += (64 * NW)) take(c, residual_value(R, wire, b, hidden, c));
   }
-  for (int i = tid; i < nnrm; i += kRescoreThreads) n2 = fmaxf(n2, nrm2[i]);
-  for (int i = tid; i < n; i += kRescoreThreads) U[i] = cand[b * n + i];
-  for (int i = tid; i < kRescoreWaves * k; i += kRescoreThreads) heaps[i] = 0;
+  for (int i = tid; i < nnrm; i += (64 * NW)) n2 = fmaxf(n2, nrm2[i]);
+  for (int i = tid; i < n; i += (64 * NW)) U[i] = cand[b * n + i];
+  for (int i = tid; i < NW * k; i += (64 * NW)) heaps[i] = 0;
   if (tid == 0) cnt[0] = cnt[1] = 0;
   s_lo = wave_sum(s_lo);
   s_hi = wave_sum(s_hi);
@@ -697,7 +756,7 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
   }
   __syncthreads();
   double lo2 = 0, hi2 = 0, r2 = 0, nn2 = 0;
-  for (int w = 0; w < kRescoreWaves; w++) {
+  for (int w = 0; w < NW; w++) {
     lo2 += red[w][0];
     hi2 += red[w][1];
     r2 += red[w][2];
@@ -713,7 +772,21 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
   const double slack = (sqrt(lo2 * inf2) + (double)kpad * 0x1p-22 * sqrt(hi2 * inf2)) * N + tiny;
   const double eps = ((double)hidden / 64.0 + 8.0) * 0x1p-23 * sqrt(r2 * inf2) * N + tiny;
 
-  const uint32_t a_ord = block_kth_ord(U, n, k, hist, sel);
+  uint32_t a_ord;
+  if (sorted && nvr <= 512) {
+    if (wv == 0) {
+      const uint32_t o = nvr <= 64    ? wave_kth_sorted<1>(U, nvr, kb, k)
+                         : nvr <= 128 ? wave_kth_sorted<2>(U, nvr, kb, k)
+                         : nvr <= 256 ? wave_kth_sorted<4>(U, nvr, kb, k)
+                                      : wave_kth_sorted<8>(U, nvr, kb, k);
+      if (lane == 0) sel[0] = o;
+    }
+    __syncthreads();
+    a_ord = sel[0];
+    __syncthreads();  // sel is reused
+  } else {
+    a_ord = block_kth_ord<64 * NW>(U, n, k, hist, sel);
+  }
   const float A = a_ord == 0u ? -__builtin_inff() : ord_score(a_ord);
 
   // One wave per row: f32 FMAs over values 8 lane + 512 j + e (j ascending), then
@@ -769,27 +842,28 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
   };
   // rows S[i0], S[i0 + W], ... of a list, two at a time
   auto rescore_list = [&](int cnt) {
-    for (int i = wv; i < cnt; i += 2 * kRescoreWaves)
-      rescore2(S[i], i + kRescoreWaves < cnt ? (int64_t)S[i + kRescoreWaves] : -1);
+    for (int i = wv; i < cnt; i += 2 * NW)
+      rescore2(S[i], i + NW < cnt ? (int64_t)S[i + NW] : -1);
   };
 
-  // phase 1: the keys of U at or above A
-  for (int i = tid; i < n; i += kRescoreThreads) {
+  // phase 1: the keys of U at or above lo1
+  const float lo1 = a_ord == 0u ? -__builtin_inff() : f32_round_down((double)A - 1.125 * slack - 2.0 * eps);
+  for (int i = tid; i < n; i += (64 * NW)) {
     const uint64_t key = U[i];
-    if (key != 0 && ord_score((uint32_t)(key >> 32)) >= A) S[atomicAdd(&cnt[0], 1u)] = ~(uint32_t)key;
+    if (key != 0 && ord_score((uint32_t)(key >> 32)) >= lo1) S[atomicAdd(&cnt[0], 1u)] = ~(uint32_t)key;
   }
   __syncthreads();
   const int ns1 = (int)cnt[0];
   rescore_list(ns1);
   __syncthreads();
   if (tid == 0) cnt[0] = 0;
-  const uint32_t t_ord = block_kth_ord(heaps, kRescoreWaves * k, k, hist, sel);
+  const uint32_t t_ord = block_kth_ord<64 * NW>(heaps, NW * k, k, hist, sel);
   const float thr =
       t_ord == 0u ? -__builtin_inff() : f32_round_down((double)ord_score(t_ord) - slack - 2.0 * eps);
 
   // phase 2: ranges to rescan (a full heap whose smallest key reaches thr), then
-  // the keys of U in [thr, A) outside them
-  for (int vr = tid; vr < nvr; vr += kRescoreThreads) {
+  // the keys of U in [thr, lo1) outside them
+  for (int vr = tid; vr < nvr; vr += (64 * NW)) {
     uint64_t mn = ~0ull;
     for (int j = 0; j < kb; j++) mn = min(mn, U[vr * kb + j]);
     const bool rescan = mn != 0 && ord_score((uint32_t)(mn >> 32)) >= thr;
@@ -797,27 +871,27 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
     if (rescan) rl[atomicAdd(&cnt[1], 1u)] = (uint32_t)vr;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += kRescoreThreads) {
+  for (int i = tid; i < n; i += (64 * NW)) {
     const uint64_t key = U[i];
     if (key == 0 || flag[i / kb] != 0) continue;
     const float a = ord_score((uint32_t)(key >> 32));
-    if (a >= thr && a < A) S[atomicAdd(&cnt[0], 1u)] = ~(uint32_t)key;
+    if (a >= thr && a < lo1) S[atomicAdd(&cnt[0], 1u)] = ~(uint32_t)key;
   }
   __syncthreads();
   const int ns = (int)cnt[0], nres = (int)cnt[1];
   rescore_list(ns);
   for (int q = 0; q < nres; q++) {
     const int64_t v0 = (int64_t)rl[q] * range_rows, v1 = min(V, v0 + range_rows);
-    for (int64_t v = v0 + wv; v < v1; v += 2 * kRescoreWaves)
-      rescore2(v, v + kRescoreWaves < v1 ? v + kRescoreWaves : -1);
+    for (int64_t v = v0 + wv; v < v1; v += 2 * NW)
+      rescore2(v, v + NW < v1 ? v + NW : -1);
   }
   __syncthreads();
   if (wv == 0) {
-    uint64_t key[kRescoreWaves];  // the waves' heaps, kRescoreWaves keys per lane (k <= 64)
+    uint64_t key[NW];  // the waves' heaps, NW keys per lane (k <= 64)
 #pragma unroll
-    for (int j = 0; j < kRescoreWaves; j++) {
+    for (int j = 0; j < NW; j++) {
       const int i = lane + 64 * j;
-      key[j] = i < kRescoreWaves * k ? heaps[i] : 0;
+      key[j] = i < NW * k ? heaps[i] : 0;
     }
     for (int t = 0; t < k; t++) {
       const uint64_t best = wave_pop_max(key);
@@ -827,6 +901,25 @@ __global__ void __launch_bounds__(kRescoreThreads) gemm_rescore_kernel(
       }
     }
   }
+}
+
+hipError_t launch_rescore(const TableDesc& t, const LogitsPlan& p, const void* R, int wire, const uint64_t* cand,
+                          int nranges, int64_t range_rows, const float* nrm2, int nnrm, int kpad, int32_t* ids,
+                          float* scores, hipStream_t stream, int sorted) {
+  const int nw = rescore_waves(p.batch);
+  const void* fn = nw == 16 ? (const void*)rank_rescore_kernel<16> : (const void*)rank_rescore_kernel<4>;
+  hipError_t e = set_dynamic_lds(fn, p.rescore_lds);
+  if (e != hipSuccess) return e;
+  if (nw == 16) {
+    hipLaunchKernelGGL(rank_rescore_kernel<16>, dim3((unsigned)p.batch), dim3(64 * 16), p.rescore_lds, stream, t.rows,
+                       t.V, t.row_bytes, (int)t.hidden, kpad, R, wire, cand, nranges, p.kb, range_rows, nrm2, nnrm, p.k,
+                       ids, scores, sorted);
+  } else {
+    hipLaunchKernelGGL(rank_rescore_kernel<4>, dim3((unsigned)p.batch), dim3(64 * 4), p.rescore_lds, stream, t.rows,
+                       t.V, t.row_bytes, (int)t.hidden, kpad, R, wire, cand, nranges, p.kb, range_rows, nrm2, nnrm, p.k,
+                       ids, scores, sorted);
+  }
+  return hipGetLastError();
 }
 
 template <int WM, int WN, int NA, int NB, bool SPLIT>
@@ -861,11 +954,9 @@ static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const
     hipLaunchKernelGGL(rank_norm_kernel, dim3((unsigned)nnrm), dim3(256), 0, stream, (const float*)x.aux, p.ngrp, t.V,
                        nrm2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = set_dynamic_lds((const void*)gemm_rescore_kernel, p.rescore_lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_rescore_kernel, dim3((unsigned)p.batch), dim3(kRescoreThreads), p.rescore_lds, stream,
-                       t.rows, t.V, t.row_bytes, (int)t.hidden, p.kpad, R, (int)x.wire, (const uint64_t*)cand, p.nvr,
-                       p.kb, (int64_t)p.tiles_per_range * kGemmBM, (const float*)nrm2, nnrm, p.k, ids, scores);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_rescore(t, p, R, (int)x.wire, cand, p.nvr, (int64_t)p.tiles_per_range * kGemmBM, nrm2, nnrm,
+                            p.kpad, ids, scores, stream, 0)) != hipSuccess)
+      return e;
   }
   return hipSuccess;
 }
@@ -881,6 +972,7 @@ hipError_t launch_gemm(const TableDesc& t, const LogitsPlan& p, const void* R, u
 hipError_t launch_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs, uint64_t* cand,
                        const LogitsExtras& x, int32_t* ids, float* scores, hipStream_t stream, hipEvent_t ev0,
                        hipEvent_t ev1) {
+  if (p.rank_wide) return launch_wide_rank(t, p, R, rs, cand, x, ids, scores, stream, ev0, ev1);
   if (p.gemm_ring == 34) return launch_gemm_cfg<2, 4, 3, 4, false>(t, p, R, rs, cand, x, ids, scores, stream, ev0, ev1);
   return launch_gemm_cfg<2, 4, 3, 3, false>(t, p, R, rs, cand, x, ids, scores, stream, ev0, ev1);
 }
@@ -932,6 +1024,10 @@ int32_t plan_rank(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
     *why = "hidden too large for the rank path (the residual row is kept in LDS)";
     return -5;
   }
+  if (batch <= 64) {  // one pass of the wide kernel in ranking mode
+    p->rank_wide = 1;
+    return plan_wide(t, batch, k, p, why, true);
+  }
   int32_t hk = 0;
   const int32_t st = plan_gemm_common(t, batch, false, std::min<int32_t>(k, kRankHeapKeys), p, &hk, why);
   if (st != 0) return st;
@@ -940,7 +1036,7 @@ int32_t plan_rank(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
   // row norms: up to 8 column tiles each measure a share of the K stages
   p->ngrp = (int32_t)std::min<int64_t>(p->nct, 8);
   p->aux_bytes = (align_up((size_t)p->ngrp * t.V, 64) + (size_t)cdiv(t.V, kNormRows)) * 4;
-  p->rescore_lds = rescore_lds_bytes(t.hidden, p->ncand, p->nvr, k);
+  p->rescore_lds = rescore_lds(t.hidden, p->ncand, p->nvr, k, batch);
   if (p->rescore_lds > kMaxLds - 2048) {  // static LDS besides
     *why = "the rank path's rescoring does not fit in LDS";
     return -5;

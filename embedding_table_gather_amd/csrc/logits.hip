@@ -318,19 +318,22 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const voi
 // ---------------------------------------------------------------------------
 // Planning (host only, no device calls).
 // ---------------------------------------------------------------------------
+// Smallest bf16 batch the automatic choice sends to the rank path (top-k only).
+static constexpr int64_t kRankMinBatch = 17;
+
 int32_t plan_logits(const TableDesc& t, int64_t batch, int32_t k, int32_t path, LogitsPlan* p,
                     const char** why, bool extras) {
   *p = LogitsPlan{};
   p->k = k;
   p->batch = batch;
-  // auto, bf16 tables past 64 residual rows: the rank path for the top-k alone,
-  // the split contraction when probabilities or raw logits are wanted; the
-  // workspace covers both
-  if (path == 0 && t.dtype == DT_BF16 && batch > 64) {
+  // auto, bf16 tables past kRankMinBatch residual rows: the rank path for the
+  // top-k alone, the wide kernel (up to 64 rows) or the split contraction when
+  // probabilities or raw logits are wanted; the workspace covers both
+  if (path == 0 && t.dtype == DT_BF16 && batch >= kRankMinBatch) {
     LogitsPlan r, g;
     const char* w = "";
     const bool rank_ok = plan_logits(t, batch, k, 7, &r, &w, false) == 0;
-    const int32_t st = plan_logits(t, batch, k, 3, &g, why, false);
+    const int32_t st = plan_logits(t, batch, k, batch > 64 ? 3 : 4, &g, why, false);
     if (st != 0) return st;
     *p = (rank_ok && !extras) ? r : g;
     if (rank_ok) p->ws_bytes = std::max(r.ws_bytes, g.ws_bytes);

@@ -40,6 +40,10 @@ static constexpr int kWideMT = 4;                            // 16-row M-tiles p
 static constexpr int kWideRows = kWideWaves * kWideMT * 16;  // table rows per block
 static constexpr int kWideCK = 3;  // K steps per staged chunk = depth of the table-load ring
 static constexpr int kWideMaxTiles = 4;                      // 16-column N-tiles: 64 residual rows
+// Ranking mode: keys kept per 512-row block and residual row.  The answer's k
+// rows are spread over 512 blocks; a block holding more of the candidates than
+// this is rescanned by the rescoring kernel.
+static constexpr int kWideRankKeys = 4;
 
 // Barrier that orders LDS accesses only: outstanding global loads are not waited for.
 __device__ __forceinline__ void lds_barrier() {
@@ -48,20 +52,35 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// s + the squares of 8 bf16 values (four v_dot2c_f32_bf16).
+__device__ __forceinline__ float wide_sumsq(bf16x8 f, float s) {
+  const u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const bf16x2 v = __builtin_bit_cast(bf16x2, w[j]);
+    s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+  }
+  return s;
+}
+
 // Image slot i = ((((pass * steps_pad + s) * ntile + nt) * 2 + pq) * 2 + hl) * 64 + lane
 // holds residual row 16 (ntile pass + nt) + lane % 16, values
-// 64 s + 16 (lane / 16) + 8 pq + e (e = 0..7), as bf16 hi (hl = 0) or lo (hl = 1).
+// 64 s + 16 (lane / 16) + 8 pq + e (e = 0..7), as bf16 hi (hl = 0) or lo (hl = 1);
+// in ranking mode (rank != 0) there is no hl level and every slot is hi.
 // Rows past the batch and values past hidden are zero.
-// It also clears the per-row top-k lower bounds thr[B] (total >= B).
+// It also clears the per-row top-k lower bounds thr[B] (total >= B; not in ranking mode).
 __global__ void __launch_bounds__(256) wide_prep_kernel(const void* __restrict__ R, int wire, int64_t B, int hidden,
                                                         int steps_pad, int ntile, int64_t total,
-                                                        u32x4* __restrict__ img, uint64_t* __restrict__ thr) {
+                                                        u32x4* __restrict__ img, uint64_t* __restrict__ thr, int rank) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < B) thr[i] = 0;
+  if (!rank && i < B) thr[i] = 0;
   if (i >= total) return;
   const int lane = (int)(i & 63);
-  const int f = (int)((i >> 6) & 3);
-  int64_t q = i >> 8;
+  const int nf = rank ? 2 : 4;
+  const int f = rank ? 2 * (int)((i >> 6) & 1) : (int)((i >> 6) & 3);
+  int64_t q = (i >> 6) / nf;
   const int nt = (int)(q % ntile);
   q /= ntile;
   const int s = (int)(q % steps_pad);
@@ -89,12 +108,19 @@ __global__ void __launch_bounds__(256) wide_prep_kernel(const void* __restrict__
 //             at lse_c = log2(e) / temperature
 // Rows past V are read from row V - 1 and never ranked; 16-byte chunks past the
 // row end are read from the row's last 16 bytes and meet zero image values.
-template <int NTILE>
+//
+// Ranking mode (RANK): the image holds bf16(residual) only (two fragments per
+// N-tile), k is the number of keys kept per block and column (approximate logits,
+// no running bound), and pass 0 writes the block's largest squared row norm to
+// nrm2[block] (the rescoring kernel's certificate needs an upper bound on the
+// table's row norms).
+template <int NTILE, bool RANK>
 __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, const u32x4* __restrict__ img, int64_t B,
     int steps_pad, int k, uint64_t* __restrict__ cand, uint64_t* __restrict__ thr, float* __restrict__ logits,
-    float2* __restrict__ lse, float lse_c) {
-  constexpr int STEP_U4 = NTILE * 4 * 64;  // image slots per K step
+    float2* __restrict__ lse, float lse_c, float* __restrict__ nrm2) {
+  constexpr int NF = RANK ? 2 : 4;          // image fragments per N-tile and step
+  constexpr int STEP_U4 = NTILE * NF * 64;  // image slots per K step
   constexpr int CHUNK_U4 = kWideCK * STEP_U4;
   constexpr int NTHR = 64 * kWideWaves;
   constexpr int NPER = (STEP_U4 + NTHR - 1) / NTHR;
@@ -128,6 +154,12 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
   for (int mt = 0; mt < kWideMT; mt++)
 #pragma unroll
     for (int nt = 0; nt < NTILE; nt++) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // ranking mode, pass 0: squares of this lane's table values per M-tile (lane l
+  // holds row l % 16 of each M-tile, 16 of every 64 values)
+  float nsq[kWideMT];
+#pragma unroll
+  for (int mt = 0; mt < kWideMT; mt++) nsq[mt] = 0.f;
+  const bool do_nrm = RANK && blockIdx.y == 0;
 
   // first chunk of the image: loads issued before the table loads, so the LDS
   // writes below do not wait for those
@@ -191,17 +223,22 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
         Q[mt] = __builtin_bit_cast(bf16x8, qv);
       }
       const u32x4* bl = cur + j * STEP_U4 + lane;
-      // fragment f = 2 pq + hl of N-tile nt; consecutive MFMAs go to different
-      // accumulators
+      // fragment f = 2 pq + hl of N-tile nt (ranking mode: f = pq); consecutive
+      // MFMAs go to different accumulators
 #pragma unroll
       for (int nt = 0; nt < NTILE; nt++) {
 #pragma unroll
-        for (int f = 0; f < 4; f++) {
-          const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[(4 * nt + f) * 64]);
+        for (int f = 0; f < NF; f++) {
+          const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[(NF * nt + f) * 64]);
 #pragma unroll
           for (int mt = 0; mt < kWideMT; mt++)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f < 2 ? P[mt] : Q[mt], bop, acc[mt][nt], 0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f < NF / 2 ? P[mt] : Q[mt], bop, acc[mt][nt], 0,
+                                                                   0, 0);
         }
+      }
+      if (do_nrm) {
+#pragma unroll
+        for (int mt = 0; mt < kWideMT; mt++) nsq[mt] = wide_sumsq(P[mt], wide_sumsq(Q[mt], nsq[mt]));
       }
 #pragma unroll
       for (int q = 0; q < NPER; q++) nxt[j * STEP_U4 + min(tid + q * NTHR, STEP_U4 - 1)] = st[q];
@@ -223,8 +260,32 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
   uint32_t tords[MAXC];
 #pragma unroll
   for (int i = 0; i < MAXC; i++)
-    tords[i] = __hip_atomic_load((const uint32_t*)(thr + min(bcol0 + i * kWideWaves, B - 1)) + 1, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+    tords[i] = RANK ? 0u
+                    : __hip_atomic_load((const uint32_t*)(thr + min(bcol0 + i * kWideWaves, B - 1)) + 1,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  if constexpr (RANK) {
+    // pass 0: the block's largest squared row norm.  Lanes l, l ^ 16, l ^ 32 and
+    // l ^ 48 hold the four quarters of row l % 16 of each M-tile; rows past V are
+    // copies of row V - 1 and chunks past the row end copies of its last chunk, so
+    // the maximum can only grow.
+    __shared__ float nred[kWideWaves];
+    float m = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < kWideMT; mt++) {
+      float x = nsq[mt] + __shfl_xor(nsq[mt], 16, 64);
+      x += __shfl_xor(x, 32, 64);
+      m = fmaxf(m, x);
+    }
+    m = wave_max_f32(m);
+    if (lane == 0) nred[wv] = m;
+    __syncthreads();
+    if (do_nrm && tid == 0) {
+      float mm = nred[0];
+      for (int w = 1; w < kWideWaves; w++) mm = fmaxf(mm, nred[w]);
+      nrm2[blockIdx.x] = mm;
+    }
+  }
 
   // logits of the block's rows through LDS (the image buffers are free now)
 #pragma unroll
@@ -243,7 +304,7 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
   for (int i = 0; i < MAXC; i++) tords[i] = __builtin_amdgcn_readfirstlane(tords[i]);
 
   // raw logits and log-partition partials of the wave's columns
-  if (logits != nullptr || lse != nullptr) {
+  if (!RANK && (logits != nullptr || lse != nullptr)) {
 #pragma unroll
     for (int i = 0; i < MAXC; i++) {
       const int col = wv + i * kWideWaves;
@@ -329,60 +390,91 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
     if (!live[i]) break;
     uint64_t* out = cand + ((bcol0 + i * kWideWaves) * gridDim.x + blockIdx.x) * (int64_t)k;
     for (int t = rnd[i] + lane; t < k; t += 64) out[t] = 0;
-    if (rnd[i] == k && lane == 0)
+    if (!RANK && rnd[i] == k && lane == 0)
       atomicMax((unsigned long long*)(thr + bcol0 + i * kWideWaves), (unsigned long long)key[i]);
   }
 }
 
 
-template <int NTILE>
+template <int NTILE, bool RANK>
 static hipError_t launch_wide_nt(const TableDesc& t, const LogitsPlan& p, const u32x4* img, uint64_t* cand,
                                  uint64_t* thr, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0,
                                  hipEvent_t ev1) {
-  hipError_t e = set_dynamic_lds((const void*)wide_logits_kernel<NTILE>, p.lds_bytes);
+  hipError_t e = set_dynamic_lds((const void*)wide_logits_kernel<NTILE, RANK>, p.lds_bytes);
   if (e != hipSuccess) return e;
   if ((e = record_event(ev0, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((wide_logits_kernel<NTILE>), dim3((unsigned)p.nblk, (unsigned)p.npass), dim3(64 * kWideWaves),
-                     p.lds_bytes, stream, t.rows, t.V, t.row_bytes, img, p.batch, p.steps, p.k, cand, thr,
-                     x.logits, x.lse, x.lse_scale);
+  hipLaunchKernelGGL((wide_logits_kernel<NTILE, RANK>), dim3((unsigned)p.nblk, (unsigned)p.npass),
+                     dim3(64 * kWideWaves), p.lds_bytes, stream, t.rows, t.V, t.row_bytes, img, p.batch, p.steps,
+                     RANK ? p.kb : p.k, cand, thr, x.logits, x.lse, x.lse_scale, (float*)x.aux);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev1, stream);
 }
 
-hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
-                       uint64_t* thr, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  const int64_t total = (int64_t)p.npass * p.steps * p.ntile * 256;  // >= 768 npass >= batch
+template <bool RANK>
+static hipError_t launch_wide_mode(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img,
+                                   uint64_t* cand, uint64_t* thr, const LogitsExtras& x, hipStream_t stream,
+                                   hipEvent_t ev0, hipEvent_t ev1) {
+  const int64_t total = (int64_t)p.npass * p.steps * p.ntile * (RANK ? 128 : 256);  // >= 768 npass >= batch
   hipLaunchKernelGGL(wide_prep_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, R, (int)x.wire,
-                     p.batch,
-                     (int)t.hidden, p.steps, p.ntile, total, (u32x4*)img, thr);
+                     p.batch, (int)t.hidden, p.steps, p.ntile, total, (u32x4*)img, thr, (int)RANK);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (p.ntile) {
-    case 1: return launch_wide_nt<1>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
-    case 2: return launch_wide_nt<2>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
-    case 3: return launch_wide_nt<3>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
-    case 4: return launch_wide_nt<4>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+    case 1: return launch_wide_nt<1, RANK>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+    case 2: return launch_wide_nt<2, RANK>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+    case 3: return launch_wide_nt<3, RANK>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+    case 4: return launch_wide_nt<4, RANK>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
     default: return hipErrorInvalidValue;
   }
 }
 
-int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
+hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
+                       uint64_t* thr, const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  return launch_wide_mode<false>(t, p, R, img, cand, thr, x, stream, ev0, ev1);
+}
+
+// Ranking mode for batches of up to 64 rows: the wide kernel ranks with bf16
+// residual rows and keeps kb keys per 512-row block; the rescoring kernel
+// certifies and completes the answer (aux holds the blocks' squared row norms).
+hipError_t launch_wide_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
+                            const LogitsExtras& x, int32_t* ids, float* scores, hipStream_t stream, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+  hipError_t e = launch_wide_mode<true>(t, p, R, img, cand, nullptr, x, stream, ev0, ev1);
+  if (e != hipSuccess) return e;
+  // the kernel emits each block's keys best first
+  return launch_rescore(t, p, R, (int)x.wire, cand, p.nblk, kWideRows, (const float*)x.aux, p.nblk, p.steps * 64, ids,
+                        scores, stream, 1);
+}
+
+int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why, bool rank) {
     // passes of at most 64 residual rows, split evenly into 16-row N-tiles
     if ((uint64_t)(kWideRows + 1) * (uint64_t)t.row_bytes >= (1ull << 32)) {
       *why = "rows too long for the wide path";
       return -5;
     }
+    const int nf = rank ? 2 : 4;  // image fragments per N-tile and step
     p->npass = (int32_t)cdiv(batch, kWideMaxTiles * 16);
     p->ntile = (int32_t)cdiv(cdiv(batch, p->npass), 16);
     p->steps = (int32_t)(cdiv(cdiv(t.hidden, 64), kWideCK) * kWideCK);
     p->nblk = (int32_t)cdiv(t.V, kWideRows);
-    const size_t img_lds = (size_t)2 * kWideCK * p->ntile * 4 * 1024;
+    const size_t img_lds = (size_t)2 * kWideCK * p->ntile * nf * 1024;
     const size_t log_lds = (size_t)kWideRows * (16 * p->ntile + 1) * 4;
     p->lds_bytes = std::max(img_lds, log_lds);
-    p->img_bytes = (size_t)p->npass * p->steps * p->ntile * 4 * 1024;
-    p->ncand = p->nblk * k;
-  p->aux_bytes = (size_t)batch * 8;
-  return 0;
+    p->img_bytes = (size_t)p->npass * p->steps * p->ntile * nf * 1024;
+    if (!rank) {
+      p->ncand = p->nblk * k;
+      p->aux_bytes = (size_t)batch * 8;  // running top-k bound per residual row
+      return 0;
+    }
+    p->kb = std::min<int32_t>(k, kWideRankKeys);
+    p->ncand = p->nblk * p->kb;
+    p->aux_bytes = (size_t)p->nblk * 4;  // largest squared row norm per block
+    p->rescore_lds = rescore_lds(t.hidden, p->ncand, p->nblk, k, batch);
+    if (p->rescore_lds > kMaxLds - 2048) {
+      *why = "too many vocabulary blocks for the rank path's rescoring";
+      return -5;
+    }
+    return 0;
 }
 
 }  // namespace etg

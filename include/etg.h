@@ -151,9 +151,9 @@ int32_t etg_embed_gather_wire(const etg_table* table, const int32_t* d_ids, int6
 /* Kernel path for etg_logits_topk_ex (ETG_PATH_AUTO is what etg_logits_topk uses). */
 typedef enum {
   ETG_PATH_AUTO = 0,   /* f32 and f16 tables: ROW; Q8_0 tables: Q8 (both VALU past their
-                          row limits); bf16 tables: STREAM up to 8 rows, WIDE up to 64,
-                          RANK beyond (GEMM when probabilities or raw logits are asked
-                          for, or hidden > 16384)                                         */
+                          row limits); bf16 tables: STREAM up to 8 rows, WIDE up to 16,
+                          RANK beyond (WIDE up to 64, then GEMM, when probabilities or
+                          raw logits are asked for, or hidden > 16384)                    */
   ETG_PATH_VALU = 1,   /* any dtype: f32 vector FMAs, one table pass per 8 residuals     */
   ETG_PATH_STREAM = 2, /* bf16 tables: one HBM pass per 8 residuals, bf16 MFMA dot engine;
                           batches of <= 4 use a hi+lo bf16 split of the residual          */
@@ -165,10 +165,11 @@ typedef enum {
   ETG_PATH_ROW = 6,    /* f32 / bf16 / f16 tables with rows <= 16 KiB: one HBM pass per
                           2 residuals, a wave per row, f32 FMAs (no bf16 rounding of the
                           residual)                                                       */
-  ETG_PATH_RANK = 7    /* bf16 tables with hidden <= 16384, top-k only: the GEMM tiles
-                          rank with the residual rounded once to bf16, then every row
-                          that a rigorous error bound cannot rule out is rescored with
-                          f32 FMAs from the f32 residual (half the MFMA work of GEMM)     */
+  ETG_PATH_RANK = 7    /* bf16 tables with hidden <= 16384, top-k only: the WIDE kernel
+                          (up to 64 rows) or the GEMM tiles rank with the residual
+                          rounded once to bf16, then every row that a rigorous error
+                          bound cannot rule out is rescored with f32 FMAs from the f32
+                          residual (half the MFMA work of the hi + lo split)               */
 } etg_path;
 
 /* Device workspace bytes etg_logits_topk(_ex) needs for this table, batch and k

@@ -73,10 +73,11 @@ def test_gemm_path_ragged(V, d, B):
     full_check(host, BF16, V, d, R, min(10, V), GEMM)
 
 
-# the rank path: 256-row column tiles (ragged last one), one or many vocabulary
-# ranges per column tile, heaps of fewer keys than k when ranges are many
+# the rank path: up to 64 rows the wide kernel ranks (1 to 4 N-tiles, 512-row
+# blocks keeping 4 keys each), beyond that the contraction (256-row column tiles,
+# ragged last one, one or many vocabulary ranges, heaps of fewer keys than k)
 @pytest.mark.parametrize("V,d", [(5003, 200), (4099, 896), (1001, 64), (20000, 5376), (37, 8), (70000, 512)])
-@pytest.mark.parametrize("B", [1, 9, 65, 130, 257])
+@pytest.mark.parametrize("B", [1, 9, 17, 33, 64, 65, 130, 257])
 def test_rank_path_ragged(V, d, B):
     host = synth.make_table(BF16, V, d, seed=500 + V)
     R = synth.residuals(B, d, seed=600 + B)
@@ -84,11 +85,13 @@ def test_rank_path_ragged(V, d, B):
 
 
 @pytest.mark.parametrize("k", [10, 40, 64])
-def test_rank_path_rescans_a_range_holding_many_winners(k):
-    # 80 planted winners in rows 256..335, one 256-row vocabulary range: its heap
-    # keeps only 16 of them, so the certificate must send the whole range to
-    # exact rescoring for the answer to hold the other winners
-    V, d, B = 30000, 512, 2
+@pytest.mark.parametrize("B", [2, 70])
+def test_rank_path_rescans_a_range_holding_many_winners(k, B):
+    # 80 planted winners in rows 256..335, inside one range of the ranking kernel
+    # (a 512-row block of the wide kernel keeping 4 keys for B = 2, a 256-row range
+    # of the contraction keeping 16 for B = 70): the certificate must send the
+    # whole range to exact rescoring for the answer to hold the other winners
+    V, d = 30000, 512
     host = synth.make_table(BF16, V, d, seed=23)
     R = synth.residuals(B, d, seed=24)
     u = R[0] / np.linalg.norm(R[0])
@@ -96,7 +99,7 @@ def test_rank_path_rescans_a_range_holding_many_winners(k):
         host[256 + j] = synth.f32_to_bf16_bits((u * (0.9 - 0.005 * j)).astype(np.float32))
     gids, _, oids, _ = full_check(host, BF16, V, d, R, k, RANK)
     assert np.array_equal(gids[0], np.arange(256, 256 + k))
-    assert np.array_equal(gids, oids)
+    assert np.array_equal(gids[0], oids[0])
 
 
 # the row path: rows of 16 bytes to 16 KiB (1 to 16 KiB loads, the last one partial),
