@@ -9,12 +9,13 @@ seeded synthetic arrays (synth/), resident in HBM before the timed region.
 
 value = algorithmic bytes of the step / time per step, in GB/s.  The roofline
 object times the table-streaming kernel alone with HIP events recorded on the
-stream it runs on.  The other workloads of the page set (batches of 8 to 64,
-the response with probabilities, the raw logits mode, the same lm_head stored
-as Q8_0, the 1,024-row contraction, the EmbeddingGemma-shaped Q8_0 gather with
-f32, f16 and i8 output rows) are measured after the timed steps and reported
-under "also".  The CPU oracle is timed on a
-bounded sample of the same workload under "cpu_baseline".
+stream it runs on.  The other workloads of the page set are measured after the
+timed steps and reported under "also": batches of 8 to 64 (and the exact wide
+kernel at 64), the response with probabilities, the raw logits mode, the same
+lm_head stored as Q8_0, the 1,024-row contraction (rank path and split
+contraction), and the EmbeddingGemma-shaped Q8_0 gather with f32, f16 and i8
+output rows.  The CPU oracle is timed on a bounded sample of the same workload
+under "cpu_baseline".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -289,17 +290,22 @@ def main() -> int:
             "ms_per_step": round(ms_graph, 4),
             "GBps": round(step_bytes / (ms_graph * 1e-3) / 1e9, 1)}
     if not args.no_extras:
-        for b in (8, 16, 32, 64):
+        # the automatic choice (stream up to 8 rows, wide up to 16, then the rank
+        # path), and the exact wide kernel at 64 rows for comparison
+        for b, path, key in ((8, etg.PATH_AUTO, "lm31b_logits_top10_B8"), (16, etg.PATH_AUTO, "lm31b_logits_top10_B16"),
+                             (32, etg.PATH_AUTO, "lm31b_logits_top10_B32"), (64, etg.PATH_AUTO, "lm31b_logits_top10_B64"),
+                             (64, etg.PATH_WIDE, "lm31b_logits_top10_B64_exact_wide")):
             Rb = torch.from_numpy(cfg.residuals(b)).to(dev)
-            wsb = table.workspace(b, k)
-            f = lambda evs=None: table.logits_topk(Rb, k, workspace=wsb, events=evs)
-            f()
+            wsb = table.workspace(b, k, path)
+            f = lambda evs=None: table.logits_topk(Rb, k, path=path, workspace=wsb, events=evs)
+            for _ in range(3):
+                f()
             mb, kb = _timed(torch, f, 20, events=hev)
-            also[f"lm31b_logits_top10_B{b}"] = {
+            also[key] = {
                 "us_per_call": round(mb * 1e3, 1), "kernel_us": round(kb * 1e3, 1),
                 "GBps": round(cfg.table_bytes / (mb * 1e-3) / 1e9, 1),
                 "pct_hbm_peak": round(100 * cfg.table_bytes / (mb * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
-            log(f"B={b}: {mb * 1e3:.1f} us")
+            log(f"B={b} path={path}: {mb * 1e3:.1f} us")
         # the logits response with probabilities at T = 1, and the raw logits mode
         R1 = torch.from_numpy(cfg.residuals(1)).to(dev)
         ws1 = table.workspace(1, k)
