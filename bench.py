@@ -14,8 +14,9 @@ timed steps and reported under "also": batches of 8 to 64 (and the exact wide
 kernel at 64), the response with probabilities, the raw logits mode, the same
 lm_head stored as Q8_0, the 1,024-row contraction (rank path and split
 contraction), and the EmbeddingGemma-shaped Q8_0 gather with f32, f16 and i8
-output rows.  The CPU oracle is timed on a bounded sample of the same workload
-under "cpu_baseline".
+output rows, and the Qwen2.5-0.5B-shaped prompt gather and one-row logits.  The
+CPU oracle is timed on a bounded sample of the same workload under
+"cpu_baseline".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -329,6 +330,35 @@ def main() -> int:
     torch.cuda.empty_cache()
 
     if not args.no_extras:
+        # Qwen2.5-0.5B-shaped tied table (bf16 151,936 x 896, 272 MB): the prompt's
+        # gather of 628 Zipf ids over 109 distinct rows, and logits + top-10 for 1 row
+        qc = synth.CONFIGS["qwen05b"]
+        qw = qc.table()
+        qwt = etg.Table(torch.from_numpy(qw.view(np.int16)).to(dev), qc.dtype, qc.V, qc.d)
+        del qw
+        qids_host = qc.ids()
+        qids = torch.from_numpy(qids_host).to(dev)
+        qx = torch.empty((qids.numel(), qc.d), dtype=torch.float32, device=dev)
+        f = lambda: qwt.embed_gather(qids, out=qx, check=False)
+        f()
+        mqg, _ = _timed(torch, f, 100)
+        also["qwen05b_gather_628_zipf_ids"] = {
+            "rows": int(qids.numel()), "distinct_rows": int(np.unique(qids_host).size),
+            "us_per_call": round(mqg * 1e3, 2), "rows_per_s": round(qids.numel() / (mqg * 1e-3))}
+        Rq1 = torch.from_numpy(qc.residuals(1)).to(dev)
+        wsq1 = qwt.workspace(1, qc.k)
+        f = lambda evs=None: qwt.logits_topk(Rq1, qc.k, workspace=wsq1, events=evs)
+        for _ in range(3):
+            f()
+        mql, kql = _timed(torch, f, 50, events=hev)
+        also["qwen05b_logits_top10_B1"] = {
+            "us_per_call": round(mql * 1e3, 1), "kernel_us": round(kql * 1e3, 1),
+            "GBps": round(qc.table_bytes / (mql * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * qc.table_bytes / (mql * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
+        log(f"qwen05b gather {mqg * 1e3:.1f} us, logits B=1 {mql * 1e3:.1f} us")
+        del qwt
+        torch.cuda.empty_cache()
+
         g = synth.CONFIGS["gemma_embed"]
         gh = g.table()
         gt = etg.Table(torch.from_numpy(gh).to(dev), g.dtype, g.V, g.d)
