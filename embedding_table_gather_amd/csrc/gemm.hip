@@ -567,12 +567,14 @@ __global__ void __launch_bounds__(256) rank_norm_kernel(const float* __restrict_
 // smallest kept key), so r . e_v < thr + slack = T1 - 2 eps <= T - 2 eps, below
 // the exact logit of every selected row (each >= T - eps).
 // ---------------------------------------------------------------------------
-// Waves per residual row: 4 for large batches (with the LDS below, four or more
-// rows share a CU, so a 1,024-row batch is rescored in one round, bound by HBM),
-// 16 for batches of up to kRescoreWideBatch rows (few workgroups: each row's
-// rescoring is latency-bound and the extra waves shorten it).
+// Waves per residual row, rows per wave and 1 KiB chunk loads per row in flight:
+// 4 waves x 2 rows x 6 chunks for large batches (with the LDS below, four or more
+// residual rows share a CU, so a 1,024-row batch is rescored in one round, bound
+// by HBM); 16 waves x 2 rows x 6 chunks for batches of up to kRescoreWideBatch
+// rows (few workgroups, each latency-bound: 32 rows are rescored in one round of
+// rows; more chunks or rows per wave in flight measured no faster, as the time
+// goes to first touches of randomly placed table rows).
 static constexpr int kRescoreWideBatch = 256;
-static constexpr int kRescoreChunks = 6;  // 1 KiB loads per row in flight per wave
 static constexpr int kRankMaxHidden = 16384;  // the residual row is kept in LDS
 static constexpr int kRankMaxKeys = 4096;     // heap keys per residual row (nvr kb)
 // Keys per vocabulary-range heap in ranking mode.  A range keeps its 16 best
@@ -697,7 +699,7 @@ __device__ __forceinline__ float f32_round_down(double x) {
 //  kpad    terms the ranking kernel accumulated per logit
 //  sorted  each range's keys are in descending order (the wide kernel's lists)
 //  ids, scores  [B][k] the answer, best first
-template <int NW>
+template <int NW, int ROWS, int CH>
 __global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden, int kpad,
     const void* __restrict__ R, int wire, const uint64_t* __restrict__ cand, int nvr, int kb, int64_t range_rows,
@@ -791,59 +793,63 @@ __global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
 
   // One wave per row: f32 FMAs over values 8 lane + 512 j + e (j ascending), then
   // a butterfly; every lane holds the same key, and the wave checks its heap for
-  // it.  A wave takes two rows at a time and issues kRescoreChunks 1 KiB loads of
-  // each together (the last block's loads past hidden read the row's last chunk
-  // and are not used), so each row's sum has the same order either way.
+  // it.  A wave takes ROWS rows at a time and issues CH 1 KiB loads of each
+  // together (the last block's loads past hidden read the row's last chunk and are
+  // not used), so each row's sum has the same order whatever ROWS and CH are.
   uint64_t* hp = heaps + wv * k;
   auto insert = [&](float acc, int64_t v) {
     const uint64_t key = make_key(acc, (uint32_t)v);
     if (key > hp[0] && __ballot(lane < k && hp[lane] == key) == 0 && lane == 0) heap_replace_root(hp, k, key);
   };
-  auto rescore2 = [&](int64_t va, int64_t vb) {  // vb < 0: one row
-    const uint8_t* rowa = table + (uint64_t)va * (uint64_t)row_bytes;
-    const uint8_t* rowb = table + (uint64_t)(vb >= 0 ? vb : va) * (uint64_t)row_bytes;
-    float acca = 0.f, accb = 0.f;
-    for (int c0 = 8 * lane; c0 < hidden; c0 += 512 * kRescoreChunks) {
-      u32x4 wa[kRescoreChunks], wb[kRescoreChunks];
+  auto rescore_rows = [&](const int64_t (&v)[ROWS]) {  // v[j] < 0: no row (v[0] is a row)
+    const uint8_t* row[ROWS];
+    float acc[ROWS];
 #pragma unroll
-      for (int j = 0; j < kRescoreChunks; j++) {
-        const int c = min(c0 + 512 * j, hidden - 8);
-        wa[j] = *(const u32x4*)(rowa + 2 * c);
-        wb[j] = *(const u32x4*)(rowb + 2 * c);
+    for (int j = 0; j < ROWS; j++) {
+      row[j] = table + (uint64_t)(v[j] >= 0 ? v[j] : v[0]) * (uint64_t)row_bytes;
+      acc[j] = 0.f;
+    }
+    for (int c0 = 8 * lane; c0 < hidden; c0 += 512 * CH) {
+      u32x4 w[ROWS][CH];
+#pragma unroll
+      for (int q = 0; q < CH; q++) {
+        const int c = min(c0 + 512 * q, hidden - 8);
+#pragma unroll
+        for (int j = 0; j < ROWS; j++) w[j][q] = *(const u32x4*)(row[j] + 2 * c);
       }
 #pragma unroll
-      for (int j = 0; j < kRescoreChunks; j++) {
-        const int c = c0 + 512 * j;
+      for (int q = 0; q < CH; q++) {
+        const int c = c0 + 512 * q;
         if (c < hidden) {
           const f32x4 x0 = *(const f32x4*)(r + c), x1 = *(const f32x4*)(r + c + 4);
-          acca = __builtin_fmaf(bf16_lo(wa[j].x), x0.x, acca);
-          acca = __builtin_fmaf(bf16_hi(wa[j].x), x0.y, acca);
-          acca = __builtin_fmaf(bf16_lo(wa[j].y), x0.z, acca);
-          acca = __builtin_fmaf(bf16_hi(wa[j].y), x0.w, acca);
-          acca = __builtin_fmaf(bf16_lo(wa[j].z), x1.x, acca);
-          acca = __builtin_fmaf(bf16_hi(wa[j].z), x1.y, acca);
-          acca = __builtin_fmaf(bf16_lo(wa[j].w), x1.z, acca);
-          acca = __builtin_fmaf(bf16_hi(wa[j].w), x1.w, acca);
-          accb = __builtin_fmaf(bf16_lo(wb[j].x), x0.x, accb);
-          accb = __builtin_fmaf(bf16_hi(wb[j].x), x0.y, accb);
-          accb = __builtin_fmaf(bf16_lo(wb[j].y), x0.z, accb);
-          accb = __builtin_fmaf(bf16_hi(wb[j].y), x0.w, accb);
-          accb = __builtin_fmaf(bf16_lo(wb[j].z), x1.x, accb);
-          accb = __builtin_fmaf(bf16_hi(wb[j].z), x1.y, accb);
-          accb = __builtin_fmaf(bf16_lo(wb[j].w), x1.z, accb);
-          accb = __builtin_fmaf(bf16_hi(wb[j].w), x1.w, accb);
+#pragma unroll
+          for (int j = 0; j < ROWS; j++) {
+            acc[j] = __builtin_fmaf(bf16_lo(w[j][q].x), x0.x, acc[j]);
+            acc[j] = __builtin_fmaf(bf16_hi(w[j][q].x), x0.y, acc[j]);
+            acc[j] = __builtin_fmaf(bf16_lo(w[j][q].y), x0.z, acc[j]);
+            acc[j] = __builtin_fmaf(bf16_hi(w[j][q].y), x0.w, acc[j]);
+            acc[j] = __builtin_fmaf(bf16_lo(w[j][q].z), x1.x, acc[j]);
+            acc[j] = __builtin_fmaf(bf16_hi(w[j][q].z), x1.y, acc[j]);
+            acc[j] = __builtin_fmaf(bf16_lo(w[j][q].w), x1.z, acc[j]);
+            acc[j] = __builtin_fmaf(bf16_hi(w[j][q].w), x1.w, acc[j]);
+          }
         }
       }
     }
-    acca = wave_sum(acca);
-    accb = wave_sum(accb);
-    insert(acca, va);
-    if (vb >= 0) insert(accb, vb);
+#pragma unroll
+    for (int j = 0; j < ROWS; j++) acc[j] = wave_sum(acc[j]);
+#pragma unroll
+    for (int j = 0; j < ROWS; j++)
+      if (v[j] >= 0) insert(acc[j], v[j]);
   };
-  // rows S[i0], S[i0 + W], ... of a list, two at a time
+  // rows S[i], S[i + NW], ... of a list, ROWS at a time per wave
   auto rescore_list = [&](int cnt) {
-    for (int i = wv; i < cnt; i += 2 * NW)
-      rescore2(S[i], i + NW < cnt ? (int64_t)S[i + NW] : -1);
+    for (int i = wv; i < cnt; i += ROWS * NW) {
+      int64_t v[ROWS];
+#pragma unroll
+      for (int j = 0; j < ROWS; j++) v[j] = i + j * NW < cnt ? (int64_t)S[i + j * NW] : -1;
+      rescore_rows(v);
+    }
   };
 
   // phase 1: the keys of U at or above lo1
@@ -882,8 +888,12 @@ __global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
   rescore_list(ns);
   for (int q = 0; q < nres; q++) {
     const int64_t v0 = (int64_t)rl[q] * range_rows, v1 = min(V, v0 + range_rows);
-    for (int64_t v = v0 + wv; v < v1; v += 2 * NW)
-      rescore2(v, v + NW < v1 ? v + NW : -1);
+    for (int64_t v = v0 + wv; v < v1; v += ROWS * NW) {
+      int64_t vs[ROWS];
+#pragma unroll
+      for (int j = 0; j < ROWS; j++) vs[j] = v + j * NW < v1 ? v + j * NW : -1;
+      rescore_rows(vs);
+    }
   }
   __syncthreads();
   if (wv == 0) {
@@ -907,15 +917,15 @@ hipError_t launch_rescore(const TableDesc& t, const LogitsPlan& p, const void* R
                           int nranges, int64_t range_rows, const float* nrm2, int nnrm, int kpad, int32_t* ids,
                           float* scores, hipStream_t stream, int sorted) {
   const int nw = rescore_waves(p.batch);
-  const void* fn = nw == 16 ? (const void*)rank_rescore_kernel<16> : (const void*)rank_rescore_kernel<4>;
+  const void* fn = nw == 16 ? (const void*)rank_rescore_kernel<16, 2, 6> : (const void*)rank_rescore_kernel<4, 2, 6>;
   hipError_t e = set_dynamic_lds(fn, p.rescore_lds);
   if (e != hipSuccess) return e;
   if (nw == 16) {
-    hipLaunchKernelGGL(rank_rescore_kernel<16>, dim3((unsigned)p.batch), dim3(64 * 16), p.rescore_lds, stream, t.rows,
+    hipLaunchKernelGGL((rank_rescore_kernel<16, 2, 6>), dim3((unsigned)p.batch), dim3(64 * 16), p.rescore_lds, stream, t.rows,
                        t.V, t.row_bytes, (int)t.hidden, kpad, R, wire, cand, nranges, p.kb, range_rows, nrm2, nnrm, p.k,
                        ids, scores, sorted);
   } else {
-    hipLaunchKernelGGL(rank_rescore_kernel<4>, dim3((unsigned)p.batch), dim3(64 * 4), p.rescore_lds, stream, t.rows,
+    hipLaunchKernelGGL((rank_rescore_kernel<4, 2, 6>), dim3((unsigned)p.batch), dim3(64 * 4), p.rescore_lds, stream, t.rows,
                        t.V, t.row_bytes, (int)t.hidden, kpad, R, wire, cand, nranges, p.kb, range_rows, nrm2, nnrm, p.k,
                        ids, scores, sorted);
   }
