@@ -52,6 +52,7 @@ SIGNATURES = {
     "etg_wire_row_bytes": (_I64, [_I32, _I64]),
     "etg_embed_gather_wire": (_I32, [_VP, _VP, _I64, _F, _I32, _VP, _VP, _VP]),
     "etg_logits_topk_wire": (_I32, [_VP, _VP, _I32, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP]),
+    "etg_hbm_read_probe": (_I32, [_VP, _I64, _VP, _VP]),
     "etg_last_error": (ctypes.c_char_p, []),
 }
 
@@ -301,6 +302,17 @@ class Table:
             _check(lib().etg_logits_raw(self._h, _ptr(R), B, _ptr(out), _ptr(workspace), workspace.numel(),
                                         int(path), _stream_ptr(self.device)))
         return out
+
+
+def hbm_read_probe(t: torch.Tensor, sink: torch.Tensor | None = None) -> None:
+    """Enqueue a plain read stream of the bytes of a contiguous device tensor (a
+    multiple of 16 bytes) on the current stream: the measured HBM read reference."""
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("a contiguous device tensor is required")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=t.device)
+    _check(lib().etg_hbm_read_probe(t.data_ptr(), t.numel() * t.element_size(), sink.data_ptr(),
+                                    torch.cuda.current_stream(t.device).cuda_stream))
 
 
 def wire_row_bytes(wire: int, hidden: int) -> int:

@@ -262,6 +262,17 @@ int32_t etg_logits_topk_ex(const etg_table* t, const float* d_residual, int64_t 
                                   workspace_bytes, path, nullptr, nullptr, stream);
 }
 
+int32_t etg_hbm_read_probe(const void* d_src, int64_t bytes, uint32_t* d_sink, void* stream) {
+  if (d_src == nullptr || d_sink == nullptr) return fail(ETG_EINVAL, "source or sink pointer is NULL");
+  if (!aligned(d_src, 16)) return fail(ETG_EALIGN, "source pointer is not 16-byte aligned");
+  if (!aligned(d_sink, 4)) return fail(ETG_EALIGN, "sink pointer is not 4-byte aligned");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(ETG_ESHAPE, "bytes %lld is not a positive multiple of 16",
+                                                 (long long)bytes);
+  hipError_t e = etg::launch_read_probe(d_src, bytes, d_sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ETG_EHIP, "read probe launch failed: %s", hipGetErrorString(e));
+  return ETG_OK;
+}
+
 int32_t etg_logits_topk(const etg_table* t, const float* d_residual, int64_t batch, int32_t k, int32_t* d_topk_ids,
                         float* d_topk_scores, void* d_workspace, size_t workspace_bytes, void* stream) {
   return etg_logits_topk_ex(t, d_residual, batch, k, d_topk_ids, d_topk_scores, d_workspace, workspace_bytes,

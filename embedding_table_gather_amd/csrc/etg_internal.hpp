@@ -153,6 +153,9 @@ hipError_t launch_rescore(const TableDesc& t, const LogitsPlan& p, const void* R
                           int nranges, int64_t range_rows, const float* nrm2, int nnrm, int kpad, int32_t* ids,
                           float* scores, hipStream_t stream, int sorted);
 int32_t rescore_waves(int64_t batch);
+// Plain read stream of bytes (a multiple of 16) at src (16-byte aligned); sink
+// (4 bytes) is written only if the XOR of the data equals a fixed word (probe.hip).
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 size_t rescore_lds(int64_t hidden, int n, int nvr, int k, int64_t batch);
 hipError_t launch_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs, uint64_t* cand,
                        const LogitsExtras& x, int32_t* ids, float* scores, hipStream_t stream, hipEvent_t ev0,

@@ -268,6 +268,19 @@ int32_t etg_logits_topk_wire(const etg_table* lm_head, const void* d_residual, i
                              int64_t batch, int32_t k, int32_t* d_topk_ids, float* d_topk_scores,
                              void* d_workspace, size_t workspace_bytes, int32_t path, void* stream);
 
+/*
+ * Measurement: a plain read stream of a device buffer (16-byte non-temporal loads,
+ * one contiguous range per wave read 8 KiB at a time, 16 waves per compute unit),
+ * the measured HBM
+ * read bandwidth the table-streaming kernels are compared with beside the nominal
+ * peak.  Reads `bytes` at d_src; writes d_sink[0] only if the XOR of all 32-bit
+ * words of the buffer equals 0x9e3779b9 (so that the loads are not removed).
+ *   d_src    device pointer, 16-byte aligned (ETG_EALIGN otherwise)
+ *   bytes    a positive multiple of 16 (ETG_ESHAPE otherwise)
+ *   d_sink   4 bytes of device memory, 4-byte aligned
+ */
+int32_t etg_hbm_read_probe(const void* d_src, int64_t bytes, uint32_t* d_sink, void* stream);
+
 /* Message of the calling thread's last failed call ("" if none). */
 const char* etg_last_error(void);
 

@@ -199,6 +199,16 @@ def test_rank_path_planning(L, table):
     L.etg_table_destroy(h)
 
 
+def test_read_probe_errors_without_launch(L):
+    p, s = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64)
+    f = L.etg_hbm_read_probe
+    assert f(None, 1024, s, None) == -1
+    assert f(p, 1024, None, None) == -1
+    assert f(ctypes.c_void_p(FAKE + 8), 1024, s, None) == -4
+    assert f(p, 1024, ctypes.c_void_p(FAKE + 2), None) == -4
+    assert f(p, 0, s, None) == -3 and f(p, 1000, s, None) == -3
+
+
 def test_f16_tables_take_the_valu_path(L):
     st, h = _create(L, FAKE, etg.F16, 1000, 64)
     assert st == 0
