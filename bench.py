@@ -287,6 +287,20 @@ def main() -> int:
 
     also = {}
     if not args.no_extras:
+        # single-call latency of the decode step: each step alone between two
+        # synchronisations (median, p10, p90 of 20), beside the back-to-back average
+        lat = []
+        for _ in range(20):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s0.record()
+            step()
+            s1.record()
+            torch.cuda.synchronize()
+            lat.append(s0.elapsed_time(s1) * 1e3)
+        also["decode_step_single_call_us"] = {
+            "median": round(float(np.median(lat)), 1), "p10": round(float(np.percentile(lat, 10)), 1),
+            "p90": round(float(np.percentile(lat, 90)), 1)}
         # a plain read stream of the same 2.82 GB on the same box (the library's
         # etg_hbm_read_probe), as a measured reference beside the 8 TB/s nominal
         sink = torch.empty(1, dtype=torch.int32, device=dev)
