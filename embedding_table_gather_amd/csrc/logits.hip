@@ -232,8 +232,81 @@ __global__ void __launch_bounds__(1024) topk_merge_wide_kernel(const uint64_t* _
   }
 }
 
+// Per residual row, the k largest of nl lists of k keys each, every list in
+// descending order with its empty (0) slots at the end (the lists of the stream,
+// wide, VALU, q8 and row kernels): k rounds of taking the largest list head.
+// The workgroup stages the row's nl k keys in LDS (a few loads per thread, all in
+// flight); then wave 0 keeps the heads of lists l + 64 j (j < PL) in lane l.
+static constexpr int kSortedMergeMaxKeys = 8192;  // 64 KiB of LDS
+template <int PL>
+__global__ void __launch_bounds__(kMergeThreads) topk_merge_sorted_kernel(const uint64_t* __restrict__ cand, int nl,
+                                                                          int k, int32_t* __restrict__ ids,
+                                                                          float* __restrict__ scores) {
+  extern __shared__ uint64_t sk[];  // [nl * k]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t b = blockIdx.x;
+  const int n = nl * k;
+  const uint64_t* c = cand + b * (int64_t)n;
+  constexpr int LPT = kSortedMergeMaxKeys / kMergeThreads;  // keys per thread at most
+  uint64_t v[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; j++) {
+    const int i = tid + kMergeThreads * j;
+    v[j] = i < n ? c[i] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < LPT; j++) {
+    const int i = tid + kMergeThreads * j;
+    if (i < n) sk[i] = v[j];
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  uint64_t head[PL];
+  int pos[PL];
+#pragma unroll
+  for (int j = 0; j < PL; j++) {
+    const int l = lane + 64 * j;
+    pos[j] = 0;
+    head[j] = l < nl ? sk[l * k] : 0;
+  }
+  for (int t = 0; t < k; t++) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int j = 0; j < PL; j++) m = head[j] > m ? head[j] : m;
+    const uint64_t best = wave_max_u64(m);
+    if (lane == 0) {
+      ids[b * k + t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
+      scores[b * k + t] = ord_score((uint32_t)(best >> 32));
+    }
+#pragma unroll
+    for (int j = 0; j < PL; j++) {
+      if (best != 0 && head[j] == best) {  // keys are unique: one list owns it
+        pos[j]++;
+        head[j] = pos[j] < k ? sk[(lane + 64 * j) * k + pos[j]] : 0;
+      }
+    }
+  }
+}
+
 static hipError_t launch_merge(const uint64_t* cand, int64_t batch, int n, int k, int32_t* ids, float* scores,
-                               const float2* lse, int nparts, float c, float* probs, hipStream_t stream) {
+                               const float2* lse, int nparts, float c, float* probs, hipStream_t stream,
+                               bool sorted) {
+  const int nl = n / k;
+  if (sorted && probs == nullptr && nl <= 1024 && n <= kSortedMergeMaxKeys) {
+    const size_t lds = (size_t)n * 8;
+#define ETG_SMERGE_CASE(PLV)                                                                                      \
+  if (nl <= 64 * PLV) {                                                                                           \
+    hipLaunchKernelGGL((topk_merge_sorted_kernel<PLV>), dim3((unsigned)batch), dim3(kMergeThreads), lds, stream,    \
+                       cand, nl, k, ids, scores);                                                                 \
+    return hipGetLastError();                                                                                     \
+  }
+    ETG_SMERGE_CASE(1)
+    ETG_SMERGE_CASE(2)
+    ETG_SMERGE_CASE(4)
+    ETG_SMERGE_CASE(8)
+    ETG_SMERGE_CASE(16)
+#undef ETG_SMERGE_CASE
+  }
   const dim3 grid((unsigned)batch), block(kMergeThreads);
   const int kpt = (n + kMergeThreads - 1) / kMergeThreads;
 #define ETG_MERGE_CASE(KV)                                                                                     \
@@ -312,7 +385,9 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const voi
     }
   }
   if (e != hipSuccess || ids == nullptr) return e;
-  return launch_merge(cand, p.batch, p.ncand, p.k, ids, scores, x.lse, p.nparts, lse_scale, probs, stream);
+  // every path but the split contraction (heaps) emits each block's keys best first
+  return launch_merge(cand, p.batch, p.ncand, p.k, ids, scores, x.lse, p.nparts, lse_scale, probs, stream,
+                      p.path != 3);
 }
 
 // ---------------------------------------------------------------------------
