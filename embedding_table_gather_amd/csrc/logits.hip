@@ -235,16 +235,21 @@ __global__ void __launch_bounds__(1024) topk_merge_wide_kernel(const uint64_t* _
 // Per residual row, the k largest of nl lists of k keys each, every list in
 // descending order with its empty (0) slots at the end (the lists of the stream,
 // wide, VALU, q8 and row kernels): k rounds of taking the largest list head.
-// The workgroup stages the row's nl k keys in LDS (a few loads per thread, all in
+// The workgroup combines the row's log-partition partials when probabilities are
+// asked for and stages the row's nl k keys in LDS (a few loads per thread, all in
 // flight); then wave 0 keeps the heads of lists l + 64 j (j < PL) in lane l.
 static constexpr int kSortedMergeMaxKeys = 8192;  // 64 KiB of LDS
 template <int PL>
 __global__ void __launch_bounds__(kMergeThreads) topk_merge_sorted_kernel(const uint64_t* __restrict__ cand, int nl,
                                                                           int k, int32_t* __restrict__ ids,
-                                                                          float* __restrict__ scores) {
+                                                                          float* __restrict__ scores,
+                                                                          const float2* __restrict__ lse, int nparts,
+                                                                          float lc, float* __restrict__ probs) {
   extern __shared__ uint64_t sk[];  // [nl * k]
+  __shared__ float2 red[kMergeWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t b = blockIdx.x;
+  const float2 ml = probs != nullptr ? block_log_partition(lse + b * nparts, nparts, lc, red) : float2{};
   const int n = nl * k;
   const uint64_t* c = cand + b * (int64_t)n;
   constexpr int LPT = kSortedMergeMaxKeys / kMergeThreads;  // keys per thread at most
@@ -275,8 +280,10 @@ __global__ void __launch_bounds__(kMergeThreads) topk_merge_sorted_kernel(const 
     for (int j = 0; j < PL; j++) m = head[j] > m ? head[j] : m;
     const uint64_t best = wave_max_u64(m);
     if (lane == 0) {
+      const float sc = ord_score((uint32_t)(best >> 32));
       ids[b * k + t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
-      scores[b * k + t] = ord_score((uint32_t)(best >> 32));
+      scores[b * k + t] = sc;
+      if (probs != nullptr) probs[b * k + t] = prob_of(sc, ml, lc);
     }
 #pragma unroll
     for (int j = 0; j < PL; j++) {
@@ -292,12 +299,12 @@ static hipError_t launch_merge(const uint64_t* cand, int64_t batch, int n, int k
                                const float2* lse, int nparts, float c, float* probs, hipStream_t stream,
                                bool sorted) {
   const int nl = n / k;
-  if (sorted && probs == nullptr && nl <= 1024 && n <= kSortedMergeMaxKeys) {
+  if (sorted && nl <= 1024 && n <= kSortedMergeMaxKeys) {
     const size_t lds = (size_t)n * 8;
 #define ETG_SMERGE_CASE(PLV)                                                                                      \
   if (nl <= 64 * PLV) {                                                                                           \
     hipLaunchKernelGGL((topk_merge_sorted_kernel<PLV>), dim3((unsigned)batch), dim3(kMergeThreads), lds, stream,    \
-                       cand, nl, k, ids, scores);                                                                 \
+                       cand, nl, k, ids, scores, lse, nparts, c, probs);                                          \
     return hipGetLastError();                                                                                     \
   }
     ETG_SMERGE_CASE(1)
