@@ -10,8 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libetg.so")
-SOURCES = ["etg_api.cpp", "gather.hip", "logits.hip", "stream.hip", "wide.hip", "gemm.hip", "q8.hip", "row.hip",
-           "probe.hip"]
+SOURCES = ["etg_api.cpp", "gather.hip", "logits.hip", "stream.hip", "wide.hip", "gemm.hip", "rank.hip", "q8.hip",
+           "row.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -114,6 +114,28 @@ __device__ __forceinline__ uint64_t wave_pop_max(uint64_t (&key)[N]) {
   return best;
 }
 
+// Min-heap of k keys in LDS (root = smallest kept key = admission threshold).
+// Replacing the root and sifting down costs at most log2(k) levels.
+__device__ __forceinline__ void heap_replace_root(uint64_t* h, int k, uint64_t key) {
+  int i = 0;
+  while (true) {
+    int c = 2 * i + 1;
+    if (c >= k) break;
+    uint64_t cv = h[c];
+    if (c + 1 < k) {
+      const uint64_t c2 = h[c + 1];
+      if (c2 < cv) {
+        cv = c2;
+        c = c + 1;
+      }
+    }
+    if (cv >= key) break;
+    h[i] = cv;
+    i = c;
+  }
+  h[i] = key;
+}
+
 // Butterfly sum: every lane ends with the same (bitwise) value because each
 // pairwise add is commutative.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -123,7 +123,8 @@ inline hipError_t record_event(hipEvent_t ev, hipStream_t stream) {
 
 // Per-path geometry (fill the path's fields and nblk, npass, lds_bytes,
 // img_bytes, aux_bytes, ncand) and launchers of the table-streaming kernel
-// (recording ev0 / ev1 around it).  stream.hip, wide.hip, gemm.hip (gemm and rank), q8.hip, row.hip.
+// (recording ev0 / ev1 around it).  stream.hip, wide.hip, gemm.hip (gemm and the ranking contraction), q8.hip,
+// row.hip; the rank path's rescoring is in rank.hip.
 int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why, bool rank = false);
 int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
@@ -145,7 +146,7 @@ hipError_t launch_row(const TableDesc& t, const LogitsPlan& p, const void* R, ui
 hipError_t launch_wide_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
                             const LogitsExtras& x, int32_t* ids, float* scores, hipStream_t stream, hipEvent_t ev0,
                             hipEvent_t ev1);
-// Rescoring and certificate of the rank path (gemm.hip): candidate keys [batch][nranges][p.kb]
+// Rescoring and certificate of the rank path (rank.hip): candidate keys [batch][nranges][p.kb]
 // of ranges of range_rows table rows, nrm2 [nnrm] upper bounds of the squared row norms,
 // kpad the terms the ranking kernel accumulated per logit; sorted: each range's keys
 // are in descending order.
@@ -153,6 +154,13 @@ hipError_t launch_rescore(const TableDesc& t, const LogitsPlan& p, const void* R
                           int nranges, int64_t range_rows, const float* nrm2, int nnrm, int kpad, int32_t* ids,
                           float* scores, hipStream_t stream, int sorted);
 int32_t rescore_waves(int64_t batch);
+// Rank path constants (rank.hip): the residual row is kept in LDS by the rescoring;
+// rank_norm_kernel reduces the row norm parts per block of kRankNormRows rows.
+constexpr int kRankMaxHidden = 16384;
+constexpr int kRankNormRows = 1024;
+// Squared row norms from parts npart [ngrp][V]: nrm2[x] = the largest norm of rows
+// [x kRankNormRows, (x + 1) kRankNormRows) (rank.hip).
+hipError_t launch_rank_norm(const float* npart, int ngrp, int64_t V, float* nrm2, hipStream_t stream);
 // Plain read stream of bytes (a multiple of 16) at src (16-byte aligned); sink
 // (4 bytes) is written only if the XOR of the data equals a fixed word (probe.hip).
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
