@@ -614,7 +614,7 @@ int32_t plan_rank(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
   p->ngrp = (int32_t)std::min<int64_t>(p->nct, 8);
   p->aux_bytes = (align_up((size_t)p->ngrp * t.V, 64) + (size_t)cdiv(t.V, kRankNormRows)) * 4;
   p->rescore_lds = rescore_lds(t.hidden, p->ncand, p->nvr, k, batch);
-  if (p->rescore_lds > kMaxLds - 2048) {  // static LDS besides
+  if (p->rescore_lds > kMaxLds - 4096) {  // static LDS besides
     *why = "the rank path's rescoring does not fit in LDS";
     return -5;
   }

@@ -171,6 +171,116 @@ __device__ uint32_t wave_kth_sorted(const uint64_t* U, int nl, int kb, int k) {
   return (uint32_t)(best >> 32);
 }
 
+// The k largest keys of src[0, c) (k rounds of wave maxima; a key present twice
+// counts once), written to top[0, k) in descending order with 0 past the last
+// one (top may be null); returns the order value of the k-th, or 0 with fewer
+// than k keys.  One wave; lane l takes keys l + 64 j, j < PL (c <= 64 PL).  With
+// idx, key i is src[idx[i]].
+template <int PL>
+__device__ uint32_t wave_top_keys(const uint64_t* src, const uint32_t* idx, int c, int k, uint64_t* top) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[PL];
+#pragma unroll
+  for (int j = 0; j < PL; j++) {
+    const int i = lane + 64 * j;
+    key[j] = i < c ? src[idx != nullptr ? idx[i] : i] : 0;
+  }
+  uint64_t best = 0;
+  for (int t = 0; t < k; t++) {
+    best = wave_pop_max(key);
+    if (top != nullptr && lane == 0) top[t] = best;
+  }
+  return (uint32_t)(best >> 32);
+}
+
+// wave_top_keys with the register count chosen for c keys (c <= 1024).
+__device__ __forceinline__ uint32_t wave_top_keys_any(const uint64_t* src, const uint32_t* idx, int c, int k,
+                                                      uint64_t* top) {
+  if (c <= 64) return wave_top_keys<1>(src, idx, c, k, top);
+  if (c <= 128) return wave_top_keys<2>(src, idx, c, k, top);
+  if (c <= 256) return wave_top_keys<4>(src, idx, c, k, top);
+  if (c <= 512) return wave_top_keys<8>(src, idx, c, k, top);
+  return wave_top_keys<16>(src, idx, c, k, top);
+}
+
+// Most candidate keys the selections below rank at once, and the largest k for
+// which the rescoring selects that way (else by radix selection).
+static constexpr int kSelMaxCand = 512;
+static constexpr int kSelSmallK = 16;
+
+// The k largest of the c distinct keys src[idx[i]] (0 = no key), c <= kSelMaxCand,
+// into fin[0, k) in descending order with 0 past the last; returns the order
+// value of the k-th, or 0 with fewer than k.  Each key's rank is the number of
+// larger keys, counted by NT / c threads per key over a share of the others
+// (no serial rounds).  rk [c] is LDS scratch; every thread of the block calls it.
+template <int NT>
+__device__ uint32_t block_top_distinct(const uint64_t* src, const uint32_t* idx, int c, int k, uint32_t* rk,
+                                       uint64_t* fin) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < c; i += NT) rk[i] = 0;
+  for (int t = tid; t < k; t += NT) fin[t] = 0;
+  __syncthreads();
+  if (c > 0) {
+    const int parts = c <= NT ? NT / c : 1;
+    for (int p = tid; p < c * parts; p += NT) {
+      const int i = p % c, part = p / c;
+      const uint64_t ki = src[idx[i]];
+      uint32_t n = 0;
+      for (int j = part; j < c; j += parts) n += src[idx[j]] > ki ? 1u : 0u;
+      if (n != 0) atomicAdd(&rk[i], n);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < c; i += NT) {
+    const uint64_t key = src[idx[i]];
+    if (key != 0 && rk[i] < (uint32_t)k) fin[rk[i]] = key;
+  }
+  __syncthreads();
+  return (uint32_t)(fin[k - 1] >> 32);
+}
+
+// Order value of the k-th largest nonzero key of U[0, n) (ranges of kb keys; keys
+// unique), or 0 with fewer than k, without serial rounds over U:
+//  * thread t takes the largest key of ranges t, t + NT, ...; 16-lane rows reduce
+//    theirs by DPP, and row x joins group x % k;
+//  * L = the smallest of the k group maxima.  They are k distinct keys, all >= L,
+//    so the k-th largest key is >= L too (an empty group gives L = 0: every key
+//    qualifies);
+//  * C = the keys >= L, listed by index in idx (for random scores about 3 k);
+//  * the k largest of C are ranked as above (fin receives them).
+// Returns false, with nothing selected, when C holds more than kSelMaxCand keys.
+// gmax [k], idx [n], rk [kSelMaxCand], fin [k] are LDS scratch; every thread of
+// the block calls it.
+template <int NT>
+__device__ bool block_kth_small(const uint64_t* U, int n, int kb, int k, uint64_t* gmax, uint32_t* idx,
+                                uint32_t* cnt, uint32_t* rk, uint64_t* fin, uint32_t* ord) {
+  const int tid = threadIdx.x;
+  for (int g = tid; g < k; g += NT) gmax[g] = 0;
+  if (tid == 0) cnt[0] = 0;
+  __syncthreads();
+  uint64_t m = 0;
+  for (int i = tid * kb; i < n; i += NT * kb)
+    for (int j = 0; j < kb; j++) m = max(m, U[i + j]);
+  m = dpp_max_u64<0x111, 0xf>(m);  // row_shr:1, 2, 4, 8: lane 15 of the row holds its maximum
+  m = dpp_max_u64<0x112, 0xf>(m);
+  m = dpp_max_u64<0x114, 0xf>(m);
+  m = dpp_max_u64<0x118, 0xf>(m);
+  if ((tid & 15) == 15 && m != 0) atomicMax((unsigned long long*)&gmax[(tid >> 4) % k], (unsigned long long)m);
+  __syncthreads();
+  uint64_t L = ~0ull;
+  for (int g = 0; g < k; g++) L = min(L, gmax[g]);
+  for (int i = tid; i < n; i += NT) {
+    const uint64_t key = U[i];
+    if (key != 0 && key >= L) idx[atomicAdd(&cnt[0], 1u)] = (uint32_t)i;
+  }
+  __syncthreads();
+  const int c = (int)cnt[0];
+  __syncthreads();  // every thread has read the count
+  if (c > kSelMaxCand) return false;
+  *ord = block_top_distinct<NT>(U, idx, c, k, rk, fin);
+  return true;
+}
+
 // f32 value rounded toward -inf from a finite double.
 __device__ __forceinline__ float f32_round_down(double x) {
   float f = (float)x;
@@ -198,9 +308,11 @@ __global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
     int sorted) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ float red[NW][4];
-  __shared__ uint32_t hist[256];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];  // also gmax [k] and fin [k] keys below
   __shared__ uint32_t sel[2];
   __shared__ uint32_t cnt[2];  // rows in S, ranges to rescan
+  __shared__ uint32_t scnt[1];
+  __shared__ uint32_t rk[kSelMaxCand];
   const int n = nvr * kb;
   uint64_t* U = (uint64_t*)smem;
   uint64_t* heaps = U + n;                                     // [waves][k]
@@ -265,8 +377,14 @@ __global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
   const double slack = (sqrt(lo2 * inf2) + (double)kpad * 0x1p-22 * sqrt(hi2 * inf2)) * N + tiny;
   const double eps = ((double)hidden / 64.0 + 8.0) * 0x1p-23 * sqrt(r2 * inf2) * N + tiny;
 
-  uint32_t a_ord;
-  if (sorted && nvr <= 512) {
+  // k <= kSelSmallK: the selections take k rounds of wave maxima over a few
+  // registers per lane; the k best rescored keys of phase 1 are kept in fin.
+  const bool small = k <= kSelSmallK;
+  uint64_t* gmax = (uint64_t*)hist;
+  uint64_t* fin = (uint64_t*)(hist + 128);
+  uint32_t a_ord = 0;
+  if (small && block_kth_small<64 * NW>(U, n, kb, k, gmax, S, scnt, rk, fin, &a_ord)) {
+  } else if (sorted && nvr <= 512) {
     if (wv == 0) {
       const uint32_t o = nvr <= 64    ? wave_kth_sorted<1>(U, nvr, kb, k)
                          : nvr <= 128 ? wave_kth_sorted<2>(U, nvr, kb, k)
@@ -354,7 +472,18 @@ __global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
   rescore_list(ns1);
   __syncthreads();
   if (tid == 0) cnt[0] = 0;
-  const uint32_t t_ord = block_kth_ord<64 * NW>(heaps, NW * k, k, hist, sel);
+  uint32_t t_ord;
+  if (small) {
+    // the rescored keys of phase 1 (distinct rows, at most ns1 <= n of them), listed in S
+    if (tid == 0) scnt[0] = 0;
+    __syncthreads();
+    for (int i = tid; i < NW * k; i += (64 * NW))
+      if (heaps[i] != 0) S[atomicAdd(&scnt[0], 1u)] = (uint32_t)i;
+    __syncthreads();
+    t_ord = block_top_distinct<64 * NW>(heaps, S, (int)scnt[0], k, rk, fin);
+  } else {
+    t_ord = block_kth_ord<64 * NW>(heaps, NW * k, k, hist, sel);
+  }
   const float thr =
       t_ord == 0u ? -__builtin_inff() : f32_round_down((double)ord_score(t_ord) - slack - 2.0 * eps);
 
@@ -387,20 +516,15 @@ __global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
     }
   }
   __syncthreads();
-  if (wv == 0) {
-    uint64_t key[NW];  // the waves' heaps, NW keys per lane (k <= 64)
-#pragma unroll
-    for (int j = 0; j < NW; j++) {
-      const int i = lane + 64 * j;
-      key[j] = i < NW * k ? heaps[i] : 0;
-    }
-    for (int t = 0; t < k; t++) {
-      const uint64_t best = wave_pop_max(key);
-      if (lane == 0) {
-        ids[b * k + t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
-        scores[b * k + t] = ord_score((uint32_t)(best >> 32));
-      }
-    }
+  // the answer: fin still holds it when phase 2 rescored nothing
+  if (!(small && ns == 0 && nres == 0)) {
+    if (wv == 0) wave_top_keys_any(heaps, nullptr, NW * k, k, fin);
+    __syncthreads();
+  }
+  for (int t = tid; t < k; t += (64 * NW)) {
+    const uint64_t best = fin[t];
+    ids[b * k + t] = (int32_t)(~(uint32_t)(best & 0xffffffffu));
+    scores[b * k + t] = ord_score((uint32_t)(best >> 32));
   }
 }
 

@@ -470,7 +470,7 @@ int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
     p->ncand = p->nblk * p->kb;
     p->aux_bytes = (size_t)p->nblk * 4;  // largest squared row norm per block
     p->rescore_lds = rescore_lds(t.hidden, p->ncand, p->nblk, k, batch);
-    if (p->rescore_lds > kMaxLds - 2048) {
+    if (p->rescore_lds > kMaxLds - 4096) {
       *why = "too many vocabulary blocks for the rank path's rescoring";
       return -5;
     }
