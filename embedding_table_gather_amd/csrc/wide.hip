@@ -44,6 +44,9 @@ static constexpr int kWideMaxTiles = 4;                      // 16-column N-tile
 // rows are spread over 512 blocks; a block holding more of the candidates than
 // this is rescanned by the rescoring kernel.
 static constexpr int kWideRankKeys = 4;
+// Ranking mode: most candidate logits per block and residual row the fast
+// selection keys (more, from ties, take the general selection).
+static constexpr int kWideRankCap = 16;
 
 // Barrier that orders LDS accesses only: outstanding global loads are not waited for.
 __device__ __forceinline__ void lds_barrier() {
@@ -284,6 +287,93 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
       float mm = nred[0];
       for (int w = 1; w < kWideWaves; w++) mm = fmaxf(mm, nred[w]);
       nrm2[blockIdx.x] = mm;
+    }
+  }
+
+  if constexpr (RANK) {
+    // Ranking mode: the block's kb best keys per residual row, without passing the
+    // logits through LDS.  Lane l holds 16 rows of column 16 nt + l % 16 in each
+    // N-tile (rows 64 wv + 16 mt + 4 (l / 16) + i), one of the column's 32 groups
+    // of rows.  G = the kb-th largest group maximum bounds the column's kb-th
+    // largest logit from below (kb groups reach G, each with a row of its own), so
+    // only logits >= G are keyed, and the kb best keys of those are taken.  A
+    // column with more than kWideRankCap of them (ties) sends the block to the
+    // general selection below.
+    __shared__ float gmx[NC][kWideWaves * 4 + 1];  // group maxima (odd stride)
+    __shared__ float glim[NC];
+    __shared__ uint32_t gcnt[NC];
+    __shared__ uint64_t gkey[NC][kWideRankCap];
+    __shared__ uint32_t govf;
+    const bool tail = row0 + kWideRows > V;  // the block has rows past the table
+    const int rbase = wv * (kWideMT * 16) + 4 * (lane >> 4);
+#pragma unroll
+    for (int nt = 0; nt < NTILE; nt++) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int mt = 0; mt < kWideMT; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          m = (!tail || row0 + rbase + 16 * mt + i < V) ? fmaxf(m, acc[mt][nt][i]) : m;
+      gmx[16 * nt + (lane & 15)][wv * 4 + (lane >> 4)] = m;
+    }
+    if (tid < NC) gcnt[tid] = 0;
+    if (tid == 0) govf = 0;
+    lds_barrier();
+    if (tid < NC) {
+      float t[kWideRankKeys];  // the largest group maxima, descending
+#pragma unroll
+      for (int j = 0; j < kWideRankKeys; j++) t[j] = -__builtin_inff();
+      for (int g = 0; g < kWideWaves * 4; g++) {
+        float x = gmx[tid][g];
+#pragma unroll
+        for (int j = 0; j < kWideRankKeys; j++) {
+          const float hi = fmaxf(t[j], x);
+          x = fminf(t[j], x);
+          t[j] = hi;
+        }
+      }
+      float lim = t[0];
+#pragma unroll
+      for (int j = 1; j < kWideRankKeys; j++) lim = j == k - 1 ? t[j] : lim;
+      glim[tid] = lim;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int nt = 0; nt < NTILE; nt++) {
+      const int col = 16 * nt + (lane & 15);
+      const float lim = glim[col];
+#pragma unroll
+      for (int mt = 0; mt < kWideMT; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int rl = rbase + 16 * mt + i;
+          const float x = acc[mt][nt][i];
+          if (x >= lim && (!tail || row0 + rl < V)) {
+            const uint32_t slot = atomicAdd(&gcnt[col], 1u);
+            if (slot < (uint32_t)kWideRankCap) gkey[col][slot] = make_key(x, (uint32_t)(row0 + rl));
+          }
+        }
+    }
+    lds_barrier();
+    if (tid < NC && gcnt[tid] > (uint32_t)kWideRankCap) atomicOr(&govf, 1u);
+    lds_barrier();
+    if (govf == 0u) {
+      const int64_t b = (int64_t)blockIdx.y * NC + tid;
+      if (tid < NC && b < B) {
+        const int c = (int)gcnt[tid];
+        uint64_t* out = cand + (b * gridDim.x + blockIdx.x) * (int64_t)k;
+        uint64_t prev = ~0ull;
+        for (int t = 0; t < k; t++) {  // keys are unique (one per row)
+          uint64_t best = 0;
+          for (int j = 0; j < c; j++) {
+            const uint64_t y = gkey[tid][j];
+            best = (y < prev && y > best) ? y : best;
+          }
+          out[t] = best;  // 0: no key left
+          prev = best;
+        }
+      }
+      return;
     }
   }
 
