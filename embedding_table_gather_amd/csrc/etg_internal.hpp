@@ -49,6 +49,7 @@ struct LogitsPlan {
   int32_t lpr_log2;      // log2 of the lanes that split one row's blocks
   int32_t q8_t;          // blocks per lane per row
   int32_t q8_chunks;     // 16-byte chunks per lane per step when rows are staged through LDS (0: not)
+  int32_t q8_mfma;       // 1: the matrix-core kernel (stream.hip; nbc, steps, chunk, ngroups, max_groups)
   // valu and q8 paths
   int32_t rb;            // residual rows per pass (valu: 1, 2, 4 or 8; q8: 1 or 2)
   int64_t rows_per_blk;  // most table rows one block handles
@@ -131,6 +132,11 @@ int32_t plan_gemm(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
 int32_t plan_q8(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_row(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
 int32_t plan_rank(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
+// Q8_0 tables with hidden a multiple of 256 through the matrix cores (stream.hip);
+// plan_q8 and launch_q8 use it when it applies.
+int32_t plan_stream_q8(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why);
+hipError_t launch_stream_q8(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
+                            const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
                          const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,

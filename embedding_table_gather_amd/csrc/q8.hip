@@ -277,11 +277,18 @@ static hipError_t launch_q8_rb(const TableDesc& t, const LogitsPlan& p, const vo
 
 hipError_t launch_q8(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand, const LogitsExtras& x,
                      hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (p.q8_mfma) return launch_stream_q8(t, p, R, cand, x, stream, ev0, ev1);
   return p.rb == 2 ? launch_q8_rb<2>(t, p, R, cand, x, stream, ev0, ev1)
                    : launch_q8_rb<1>(t, p, R, cand, x, stream, ev0, ev1);
 }
 
 int32_t plan_q8(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
+  // hidden a multiple of 256 and two or more residual rows: the matrix-core kernel
+  // (8 residual rows per table pass); one row streams faster through this one
+  if (t.hidden % 256 == 0 && batch >= 2) {
+    const char* w = "";
+    if (plan_stream_q8(t, batch, k, p, &w) == 0) return 0;
+  }
   const int64_t nb = t.hidden / 32;
   int lg = 0;
   while ((1 << lg) < nb && lg < 6) lg++;

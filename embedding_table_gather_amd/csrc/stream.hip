@@ -116,6 +116,46 @@ __device__ void stream_block_topk(const float* slog, const int64_t* sg0, const i
   }
 }
 
+// After the K loop: the block's logits are in slog ([wave][row][NBC], the wave's
+// rows from group sg0[wave], sng[wave] groups; written and synchronised).  Raw
+// logits, the per-block top-k candidates of each residual column and the
+// log-partition partials.
+template <int NBC>
+__device__ __forceinline__ void stream_epilogue(const float* slog, const int64_t* sg0, const int* sng, const float* mylog,
+                                                int64_t g_begin, int ng, int max_groups, int64_t V, int64_t B,
+                                                int64_t b0, int k, uint64_t* __restrict__ cand,
+                                                float* __restrict__ logits, float2* __restrict__ lse, float lse_c) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // raw logits: each wave writes the rows it computed (64 consecutive per store)
+  if (logits != nullptr) {
+    for (int i = lane; i < ng * 8; i += 64) {
+      const int64_t row = g_begin * 8 + i;
+      if (row < V) {
+#pragma unroll
+        for (int b = 0; b < NBC; b++)
+          if (b0 + b < B) logits[(b0 + b) * V + row] = mylog[i * NBC + b];
+      }
+    }
+  }
+  if (wv < NBC && b0 + wv < B) {
+    uint64_t* out = cand + ((b0 + wv) * gridDim.x + blockIdx.x) * (int64_t)k;
+    stream_block_topk<NBC>(slog, sg0, sng, wv, lane, max_groups, V, k, out);
+  } else if (lse != nullptr && wv >= NBC && wv < 2 * NBC && b0 + (wv - NBC) < B) {
+    // waves NBC .. 2 NBC - 1: log-partition partial of column wv - NBC over the
+    // block's rows (lane holds row lane of every wave's run, as in the top-k)
+    const int b = wv - NBC, per_wave = max_groups * 8;
+    float x[kStreamWaves];
+    bool ok[kStreamWaves];
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; w++) {
+      ok[w] = lane < sng[w] * 8 && sg0[w] * 8 + lane < V;
+      x[w] = ok[w] ? slog[(w * per_wave + lane) * NBC + b] : 0.f;
+    }
+    const float2 part = wave_lse_part(x, ok, lse_c);
+    if (lane == 0) lse[(b0 + b) * gridDim.x + blockIdx.x] = part;
+  }
+}
+
 // One pass over the table for NBC residual rows (pass = blockIdx.y).
 //  table      bf16 [V][hidden], row_bytes = 2 * hidden
 //  R          residual rows [B][hidden] in wire format `wire` (0 = fp32)
@@ -228,34 +268,7 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
   }
   __syncthreads();
 
-  // raw logits: each wave writes the rows it computed (64 consecutive per store)
-  if (logits != nullptr) {
-    for (int i = lane; i < ng * 8; i += 64) {
-      const int64_t row = g_begin * 8 + i;
-      if (row < V) {
-#pragma unroll
-        for (int b = 0; b < NBC; b++)
-          if (b0 + b < B) logits[(b0 + b) * V + row] = mylog[i * NBC + b];
-      }
-    }
-  }
-  if (wv < NBC && b0 + wv < B) {
-    uint64_t* out = cand + ((b0 + wv) * gridDim.x + blockIdx.x) * (int64_t)k;
-    stream_block_topk<NBC>(slog, sg0, sng, wv, lane, max_groups, V, k, out);
-  } else if (lse != nullptr && wv >= NBC && wv < 2 * NBC && b0 + (wv - NBC) < B) {
-    // waves NBC .. 2 NBC - 1: log-partition partial of column wv - NBC over the
-    // block's rows (lane holds row lane of every wave's run, as in the top-k)
-    const int b = wv - NBC, per_wave = max_groups * 8;
-    float x[kStreamWaves];
-    bool ok[kStreamWaves];
-#pragma unroll
-    for (int w = 0; w < kStreamWaves; w++) {
-      ok[w] = lane < sng[w] * 8 && sg0[w] * 8 + lane < V;
-      x[w] = ok[w] ? slog[(w * per_wave + lane) * NBC + b] : 0.f;
-    }
-    const float2 part = wave_lse_part(x, ok, lse_c);
-    if (lane == 0) lse[(b0 + b) * gridDim.x + blockIdx.x] = part;
-  }
+  stream_epilogue<NBC>(slog, sg0, sng, mylog, g_begin, ng, max_groups, V, B, b0, k, cand, logits, lse, lse_c);
 }
 
 
@@ -276,6 +289,250 @@ hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const void* R,
                          const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   return p.nimg == 1 ? launch_stream_nimg<1>(t, p, R, cand, x, stream, ev0, ev1)
                      : launch_stream_nimg<2>(t, p, R, cand, x, stream, ev0, ev1);
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0 tables through the matrix cores (rows of a multiple of 16 bytes: hidden a
+// multiple of 256), one table pass per 8 residual rows.
+//
+// A Q8_0 block (a binary16 scale, then 32 int8 values; the embeddinggemma.c port
+// specification, "Tensor inventory") is exactly the K extent of one
+// v_mfma_f32_16x16x32_bf16, and int8 values are exact in bf16.  One MFMA per block
+// and 16-row table tile gives, exactly multiplied and summed in f32,
+//   D[slot][row] = sum_p q[row][p] x[slot][p],
+// and the block's scale enters once per result: acc += scale[row] D.  The
+// residual image is the A operand (slot m = lane % 16, values 8 (lane / 16) + e
+// of the block) and the table the B operand (table row n = lane % 16, the same
+// values), so lane L's four results D[4 (L / 16) + i][L % 16] all belong to table
+// row L % 16 and take one scale.  Slot b + 8 part carries residual row b as its
+// bf16 hi (part 0) or lo (part 1) value; lanes L and L + 32 hold the hi and lo
+// sums of residual rows 4 (L / 16) + i.
+//
+// Table bytes reach the lanes through a per-wave LDS buffer.  A step is 8 blocks
+// (272 bytes, 17 16-byte chunks) of each row of a 16-row tile; lane l loads
+// chunks l + 64 u of the step, one step ahead of their use.  The row pieces are
+// not aligned to 128-byte lines, and this load pattern is what bounds the kernel
+// (about 4.6 TB/s with the arithmetic removed), so one residual row keeps the
+// lane-split kernel of q8.hip.  The residual image
+// is staged per block of the table in chunks of whole steps, as in the bf16 path.
+// ---------------------------------------------------------------------------
+static constexpr int kQ8mBlocks = 8;                       // Q8_0 blocks per step
+static constexpr int kQ8mRowStep = 34 * kQ8mBlocks;        // bytes of a row per step (272)
+static constexpr int kQ8mTileChunks = 16 * kQ8mRowStep / 16;  // 16-byte chunks per tile step (272)
+static constexpr int kQ8mLoads = (kQ8mTileChunks + 63) / 64;  // per lane (5; the last for 16 lanes)
+static constexpr int kQ8mWaveBuf = 16 * kQ8mRowStep;       // bytes of a wave's step buffer
+static constexpr int kQ8mMaxPairs = 4;                     // 16-row tiles per wave (accumulator registers)
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// Eight int8 values (two dwords) as eight bf16 values (exact).
+__device__ __forceinline__ bf16x8 q8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const u32x4 v = {bf16_pair((float)(int8_t)(w0 & 0xffu), (float)(int8_t)((w0 >> 8) & 0xffu)),
+                   bf16_pair((float)(int8_t)((w0 >> 16) & 0xffu), (float)(int8_t)(w0 >> 24)),
+                   bf16_pair((float)(int8_t)(w1 & 0xffu), (float)(int8_t)((w1 >> 8) & 0xffu)),
+                   bf16_pair((float)(int8_t)((w1 >> 16) & 0xffu), (float)(int8_t)(w1 >> 24))};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Image slots of table blocks [j0, j0 + n): slot (j, lane) holds the 8 values
+// 32 (j0 + j) + 8 (lane / 16) + e of slot lane % 16 (residual row b0 + slot % 8,
+// part slot / 8) as bf16.
+__device__ __forceinline__ void stream_q8_stage_image(u32x4* simg, const void* __restrict__ R, int wire, int64_t B,
+                                                      int hidden, int64_t b0, int j0, int n) {
+  // f32 rows, 16-byte aligned (hidden is a multiple of 256): two 16-byte loads per slot
+  const bool vec = wire == WIRE_F32 && ((uintptr_t)R & 15) == 0;
+  for (int i = threadIdx.x; i < n * 64; i += blockDim.x) {
+    const int lane = i & 63, j = j0 + (i >> 6);
+    const int m = lane & 15, g = lane >> 4;
+    const int64_t b = b0 + (m & 7);
+    const int cbase = 32 * j + 8 * g;
+    float x[8];
+    if (b >= B) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = 0.f;
+    } else if (vec) {
+      const f32x4* src = (const f32x4*)((const float*)R + b * hidden + cbase);
+      const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; e++) x[e] = x0[e], x[4 + e] = x1[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = residual_value(R, wire, b, hidden, cbase + e);
+    }
+    uint32_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const uint32_t hi = bf16_rne(x[e]);
+      v[e] = (m >> 3) ? bf16_rne(x[e] - __uint_as_float(hi << 16)) : hi;  // x - hi is exact in f32
+    }
+    simg[i] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+  }
+}
+
+//  table     Q8_0 [V][hidden / 32 blocks], row_bytes = 34 hidden / 32, a multiple of 16
+//  steps     8-block steps per row (hidden / 256)
+//  chunk     steps of the residual image staged in LDS at a time
+//  wbuf_off  byte offset of the waves' step buffers in dynamic LDS
+// The rest as for stream_logits_kernel (8 residual rows per pass).
+__global__ void __launch_bounds__(1024) stream_q8_kernel(
+    const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden, const void* __restrict__ R,
+    int wire, int64_t B, int steps, int chunk, int wbuf_off, int k, uint64_t* __restrict__ cand, int64_t ngroups,
+    int max_groups, float* __restrict__ logits, float2* __restrict__ lse, float lse_c) {
+  constexpr int NBC = 8;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  u32x4* simg = (u32x4*)smem;
+  float* slog = (float*)smem;  // after the K loop
+  __shared__ int64_t sg0[kStreamWaves];
+  __shared__ int sng[kStreamWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t b0 = (int64_t)blockIdx.y * NBC;
+  unsigned char* wb = smem + wbuf_off + wv * kQ8mWaveBuf;
+
+  // waves own contiguous runs of 16-row tiles (pairs of 8-row groups), as in the bf16 path
+  const int64_t nw = (int64_t)gridDim.x * kStreamWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kStreamWaves + wv;
+  const int64_t npairs_all = (ngroups + 1) >> 1;
+  const int64_t pb = gw * npairs_all / nw;
+  const int npairs = (int)((gw + 1) * npairs_all / nw - pb);
+  const int64_t g_begin = 2 * pb;
+  const int ng = (int)min((int64_t)(2 * npairs), ngroups - g_begin);
+  if (lane == 0) {
+    sg0[wv] = g_begin;
+    sng[wv] = ng;
+  }
+  const int n = lane & 15, g = lane >> 4;
+
+  f32x4 acc[kQ8mMaxPairs];
+#pragma unroll
+  for (int p = 0; p < kQ8mMaxPairs; p++) acc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < steps; c0 += chunk) {
+    const int c1 = min(steps, c0 + chunk), ns = c1 - c0;
+    if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
+    stream_q8_stage_image(simg, R, wire, B, hidden, b0, kQ8mBlocks * c0, kQ8mBlocks * ns);
+    __syncthreads();
+    // iterations (tile p, step c0 + s), tile-major; the loads of iteration it + 1
+    // are issued once those of iteration it are in the wave's buffer, before its
+    // blocks (a second register set for two steps ahead measured slower)
+    const int nit = npairs * ns;
+    u32x4 nx[kQ8mLoads];
+    auto issue = [&](int it) {
+      const int p = it / ns, st = c0 + it % ns;
+      const int64_t rbase = (g_begin + 2 * p) * 8;
+#pragma unroll
+      for (int u = 0; u < kQ8mLoads; u++) {
+        // chunk c = lane + 64 u of the step: row c / 17, 16-byte piece c % 17
+        const int c = min(lane + 64 * u, kQ8mTileChunks - 1), cr = c / 17;
+        const int64_t row = min(rbase + cr, V - 1);  // rows past V: never ranked
+        nx[u] = __builtin_nontemporal_load((const u32x4*)(table + (uint64_t)row * (uint64_t)row_bytes +
+                                                          kQ8mRowStep * st + 16 * (c - 17 * cr)));
+      }
+    };
+    if (nit > 0) issue(0);
+    for (int it = 0; it < nit; it++) {
+#pragma unroll
+      for (int u = 0; u < kQ8mLoads; u++)
+        if (lane + 64 * u < kQ8mTileChunks) *(u32x4*)(wb + 16 * (lane + 64 * u)) = nx[u];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (it + 1 < nit) issue(it + 1);
+      const int p = it / ns, s = it % ns;
+      const u32x4* bl = simg + (size_t)s * kQ8mBlocks * 64 + lane;
+      const unsigned char* rowb = wb + n * kQ8mRowStep;
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kQ8mBlocks; j++) {
+        // values 8 g .. 8 g + 7 of block j: bytes 34 j + 2 + 8 g ..; the scale: bytes 34 j, 34 j + 1
+        uint32_t w0, w1;
+        if ((34 * j + 2) % 4 == 0) {
+          const uint32_t* q = (const uint32_t*)(rowb + 34 * j + 2 + 8 * g);
+          w0 = q[0];
+          w1 = q[1];
+        } else {
+          const uint32_t* q = (const uint32_t*)(rowb + 34 * j + 8 * g);
+          const uint32_t a = q[0], b = q[1], c = q[2];
+          w0 = __builtin_amdgcn_alignbit(b, a, 16);
+          w1 = __builtin_amdgcn_alignbit(c, b, 16);
+        }
+        const float sc = f16_bits_to_f32(*(const uint16_t*)(rowb + 34 * j));
+        const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bl[j * 64]),
+                                                                q8_to_bf16x8(w0, w1), f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; i++) sacc[i] = __builtin_fmaf(sc, d[i], sacc[i]);
+      }
+#pragma unroll
+      for (int q = 0; q < kQ8mMaxPairs; q++)
+        if (q == p) acc[q] += sacc;  // p is the same for the whole wave
+      // the buffer is rewritten by the next iteration
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  __syncthreads();  // the image area becomes the logit area
+
+  // lanes L < 32: residual rows 4 (L / 16) + i, table row L % 16 of each tile (hi + lo)
+  float* mylog = slog + (size_t)wv * max_groups * 8 * NBC;
+#pragma unroll
+  for (int p = 0; p < kQ8mMaxPairs; p++) {
+    f32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; i++) y[i] = acc[p][i] + __shfl(acc[p][i], (lane + 32) & 63, 64);
+    if (p < npairs && lane < 32) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) mylog[(16 * p + n) * NBC + 4 * g + i] = y[i];
+    }
+  }
+  __syncthreads();
+
+  stream_epilogue<NBC>(slog, sg0, sng, mylog, g_begin, ng, max_groups, V, B, b0, k, cand, logits, lse, lse_c);
+}
+
+hipError_t launch_stream_q8(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
+                            const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  hipError_t e = set_dynamic_lds((const void*)stream_q8_kernel, p.lds_bytes);
+  if (e != hipSuccess) return e;
+  if ((e = record_event(ev0, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL(stream_q8_kernel, dim3((unsigned)p.nblk, (unsigned)p.npass), dim3(64 * kStreamWaves),
+                     p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (int)t.hidden, R, (int)x.wire, p.batch, p.steps,
+                     p.chunk, (int)(p.lds_bytes - (size_t)kStreamWaves * kQ8mWaveBuf), p.k, cand, p.ngroups,
+                     p.max_groups, x.logits, x.lse, x.lse_scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return record_event(ev1, stream);
+}
+
+int32_t plan_stream_q8(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {
+  if (t.dtype != DT_Q8_0 || t.hidden % (32 * kQ8mBlocks) != 0) {
+    *why = "the Q8_0 matrix-core kernel needs hidden a multiple of 256";
+    return -5;
+  }
+  p->nbc = 8;
+  p->steps = (int32_t)(t.hidden / (32 * kQ8mBlocks));
+  p->ngroups = cdiv(t.V, 8);
+  p->npass = (int32_t)cdiv(batch, 8);
+  const int64_t npairs_all = cdiv(p->ngroups, 2);
+  p->nblk = (int32_t)std::max<int64_t>(cdiv(npairs_all, (int64_t)kStreamWaves * kQ8mMaxPairs),
+                                       std::min<int64_t>(kTargetBlocks, cdiv(npairs_all, kStreamWaves)));
+  p->max_groups = (int32_t)(2 * cdiv(npairs_all, (int64_t)p->nblk * kStreamWaves));
+  const size_t log_bytes = (size_t)kStreamWaves * p->max_groups * 8 * p->nbc * 4;
+  const size_t wbuf = (size_t)kStreamWaves * kQ8mWaveBuf;
+  const size_t step_img = (size_t)kQ8mBlocks * 1024;  // image bytes per step
+  const int64_t max_chunk = (int64_t)((kMaxLds - 1024 - wbuf) / step_img);
+  const int64_t nchunks = cdiv(p->steps, max_chunk);
+  p->chunk = (int32_t)cdiv(p->steps, nchunks);
+  p->lds_bytes = std::max((size_t)p->chunk * step_img, log_bytes) + wbuf;
+  if (p->lds_bytes > kMaxLds - 1024) {
+    *why = "the Q8_0 matrix-core kernel's LDS";
+    return -5;
+  }
+  p->q8_mfma = 1;
+  p->img_bytes = 0;
+  p->ncand = p->nblk * k;
+  return 0;
 }
 
 int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why) {

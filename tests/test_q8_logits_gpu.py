@@ -1,8 +1,12 @@
 """The Q8_0 stream path of logits_topk on the GPU against the CPU oracle.
 
-Shapes cover every lane layout of the kernel: hidden / 32 blocks per row from 1
-(64 rows per wave) to 256 (4 blocks per lane), ragged vocabularies and 1 to 5
-residual rows (passes of 2).  Special cases pin exact ids and scores.
+Two kernels serve the path.  Hidden a multiple of 256 (768, 5376, 8192 below)
+takes the matrix-core kernel: one MFMA per 32-value block and 16-row tile,
+passes of 8 residual rows (1 to 17 rows: one pass, ragged passes, three passes).
+Other widths take the lane-split kernel; its shapes cover every lane layout,
+from 1 block per row (64 rows per wave) to 100 (2 blocks per lane), with passes
+of 2 residual rows.  Ragged vocabularies throughout.  Special cases pin exact ids
+and scores.
 """
 import numpy as np
 import pytest
@@ -38,7 +42,7 @@ def full_check(host, V, d, R, k, path=Q8):
 # blocks per row: 1, 3, 9, 24, 100, 168, 256 -> lanes per row 1, 4, 16, 32, 64, 64, 64
 @pytest.mark.parametrize("V,d", [(1001, 32), (3001, 96), (777, 288), (2000, 768), (4099, 3200), (4099, 5376),
                                  (1500, 8192), (37, 64)])
-@pytest.mark.parametrize("B", [1, 2, 3, 5])
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 9, 17])
 def test_q8_path_ragged(V, d, B):
     host = synth.make_table(Q8_0, V, d, seed=2000 + V + d)
     R = synth.residuals(B, d, seed=2100 + B)
