@@ -227,4 +227,20 @@ __device__ __forceinline__ float residual_value(const void* R, int wire, int64_t
   return (float)(int8_t)row[8 + c] * *(const float*)row;
 }
 
+// Values c0 .. c0 + 7 of residual row b (0 past hidden or for b >= B).  f32 rows
+// starting 16-byte aligned (R aligned, hidden a multiple of 4) with c0 a multiple
+// of 4 and all eight inside the row are read as two 16-byte loads.
+__device__ __forceinline__ void residual_values8(const void* R, int wire, int64_t B, int64_t b, int hidden, int c0,
+                                                 float (&x)[8]) {
+  if (b < B && wire == WIRE_F32 && ((uintptr_t)R & 15) == 0 && hidden % 4 == 0 && c0 % 4 == 0 && c0 + 8 <= hidden) {
+    const f32x4* src = (const f32x4*)((const float*)R + b * hidden + c0);
+    const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+    for (int e = 0; e < 4; e++) x[e] = x0[e], x[4 + e] = x1[e];
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e++) x[e] = (b < B && c0 + e < hidden) ? residual_value(R, wire, b, hidden, c0 + e) : 0.0f;
+}
+
 }  // namespace etg

@@ -219,8 +219,9 @@ __global__ void __launch_bounds__(256) gather_q8_aligned_kernel(const uint8_t* _
 //                 f32, clamped to [-127, 127]; a row with scale 0 is all zeros.
 // A bad id gives an all-zero record.  One wave per row, four consecutive values
 // per lane (hidden is a multiple of 4): one load of the four stored values and
-// one 8-byte (f16) or 4-byte (i8) store.  The i8 codes take a second pass over
-// the source row (L1/L2 hits) once the row maximum is known.
+// one 8-byte (f16) or 4-byte (i8) store.  The i8 codes need the row maximum
+// first: rows of up to 2,048 values keep theirs in registers, longer rows are
+// read a second time (L1/L2 hits).
 template <int DT>
 __device__ __forceinline__ f32x4 deq4(const uint8_t* row, int c) {  // values c .. c + 3, c % 4 == 0
   if constexpr (DT == DT_F32) {
@@ -240,6 +241,10 @@ __device__ __forceinline__ f32x4 deq4(const uint8_t* row, int c) {  // values c 
                  (float)(int8_t)((q >> 16) & 0xffu) * sc, (float)(int8_t)(q >> 24) * sc};
   }
 }
+
+// Rows of up to 256 kWireRegs values are read once for the i8 codes (the values
+// wait in registers for the row maximum); longer rows are read twice.
+static constexpr int kWireRegs = 8;
 
 template <int DT, bool SCALE>
 __global__ void __launch_bounds__(256) gather_wire_kernel(const uint8_t* __restrict__ table, uint32_t V,
@@ -272,19 +277,7 @@ __global__ void __launch_bounds__(256) gather_wire_kernel(const uint8_t* __restr
     }
     return;
   }
-  float m = 0.f;
-  for (int c = 4 * lane; c < hidden; c += 256) {
-    const f32x4 x = value4(c);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
-  }
-  m = wave_max_f32(m);
-  const float sc = m / 127.0f;  // correctly rounded f32 division
-  if (lane == 0) {
-    ((float*)o)[0] = sc;
-    ((float*)o)[1] = 0.f;
-  }
-  for (int c = 4 * lane; c < hidden; c += 256) {
-    const f32x4 x = value4(c);
+  auto codes = [&](int c, const f32x4& x, float sc) {
     uint32_t w = 0;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
@@ -292,7 +285,40 @@ __global__ void __launch_bounds__(256) gather_wire_kernel(const uint8_t* __restr
       w |= ((uint32_t)(int32_t)v & 0xffu) << (8 * e);
     }
     *(uint32_t*)(o + 8 + c) = w;
+  };
+  auto store_scale = [&](float sc) {
+    if (lane == 0) {
+      ((float*)o)[0] = sc;
+      ((float*)o)[1] = 0.f;
+    }
+  };
+  auto amax = [](const f32x4& x) { return fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))); };
+  if (hidden <= 256 * kWireRegs) {
+    // one read of the row: its values stay in registers until the maximum is known
+    f32x4 xs[kWireRegs];
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < kWireRegs; r++) {
+      const int c = 4 * lane + 256 * r;
+      xs[r] = c < hidden ? value4(c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      m = fmaxf(m, amax(xs[r]));
+    }
+    m = wave_max_f32(m);
+    const float sc = m / 127.0f;  // correctly rounded f32 division
+    store_scale(sc);
+#pragma unroll
+    for (int r = 0; r < kWireRegs; r++) {
+      const int c = 4 * lane + 256 * r;
+      if (c < hidden) codes(c, xs[r], sc);
+    }
+    return;
   }
+  float m = 0.f;
+  for (int c = 4 * lane; c < hidden; c += 256) m = fmaxf(m, amax(value4(c)));
+  m = wave_max_f32(m);
+  const float sc = m / 127.0f;  // correctly rounded f32 division
+  store_scale(sc);
+  for (int c = 4 * lane; c < hidden; c += 256) codes(c, value4(c), sc);
 }
 
 template <int DT>

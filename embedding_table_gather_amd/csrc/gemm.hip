@@ -105,13 +105,13 @@ __global__ void __launch_bounds__(256) gemm_prep_kernel(const void* __restrict__
   const int nw = j / wc, tt = (j % wc) / 32;
   const int part = tt >= nt / 2;
   const int64_t b = ct * kGemmCols + nw * (wc / 2) + (tt % (nt / 2)) * 32 + j % 32;
+  float x[8];
+  residual_values8(R, wire, B, b, hidden, c0, x);
   uint32_t v[8];
 #pragma unroll
   for (int e = 0; e < 8; e++) {
-    const int c = c0 + e;
-    const float x = (b < B && c < hidden) ? residual_value(R, wire, b, hidden, c) : 0.0f;
-    const uint32_t hi = bf16_rne(x);
-    v[e] = part == 1 ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;  // x - hi is exact in f32
+    const uint32_t hi = bf16_rne(x[e]);
+    v[e] = part == 1 ? bf16_rne(x[e] - __uint_as_float(hi << 16)) : hi;  // x - hi is exact in f32
   }
   Rs[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
 }
@@ -127,12 +127,11 @@ __global__ void __launch_bounds__(256) gemm_prep_hi_kernel(const void* __restric
   if (t >= nrows * kc) return;
   const int64_t b = t / kc;
   const int c0 = (int)(t % kc) * 8;
+  float x[8];
+  residual_values8(R, wire, B, b, hidden, c0, x);
   uint32_t v[8];
 #pragma unroll
-  for (int e = 0; e < 8; e++) {
-    const int c = c0 + e;
-    v[e] = (b < B && c < hidden) ? bf16_rne(residual_value(R, wire, b, hidden, c)) : 0u;
-  }
+  for (int e = 0; e < 8; e++) v[e] = bf16_rne(x[e]);
   Rs[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
 }
 

@@ -62,14 +62,22 @@ __device__ __forceinline__ void stream_stage_image(u32x4* simg, const void* __re
     const int part = NIMG == 1 ? j8 / NBC : im;
     const int64_t b = b0 + j8 % NBC;
     const int cbase = 64 * s + 16 * g + 8 * h;
+    float x[8];
+    if constexpr (NIMG == 2) {
+      residual_values8(R, wire, B, b, hidden, cbase, x);
+    } else {  // value by value: the vector loads cost the one-image kernel a register spill
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const int c = cbase + e;
+        x[e] = (b < B && c < hidden) ? residual_value(R, wire, b, hidden, c) : 0.0f;
+      }
+    }
     uint32_t v[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      const int c = cbase + e;
-      const float x = (b < B && c < hidden) ? residual_value(R, wire, b, hidden, c) : 0.0f;
-      const uint32_t hi = bf16_rne(x);
+      const uint32_t hi = bf16_rne(x[e]);
       // part 1 carries the remainder x - hi (exact in f32), rounded to bf16
-      v[e] = part == 1 ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;
+      v[e] = part == 1 ? bf16_rne(x[e] - __uint_as_float(hi << 16)) : hi;
     }
     simg[i] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
   }
@@ -341,26 +349,13 @@ __device__ __forceinline__ bf16x8 q8_to_bf16x8(uint32_t w0, uint32_t w1) {
 // part slot / 8) as bf16.
 __device__ __forceinline__ void stream_q8_stage_image(u32x4* simg, const void* __restrict__ R, int wire, int64_t B,
                                                       int hidden, int64_t b0, int j0, int n) {
-  // f32 rows, 16-byte aligned (hidden is a multiple of 256): two 16-byte loads per slot
-  const bool vec = wire == WIRE_F32 && ((uintptr_t)R & 15) == 0;
   for (int i = threadIdx.x; i < n * 64; i += blockDim.x) {
     const int lane = i & 63, j = j0 + (i >> 6);
     const int m = lane & 15, g = lane >> 4;
     const int64_t b = b0 + (m & 7);
     const int cbase = 32 * j + 8 * g;
     float x[8];
-    if (b >= B) {
-#pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = 0.f;
-    } else if (vec) {
-      const f32x4* src = (const f32x4*)((const float*)R + b * hidden + cbase);
-      const f32x4 x0 = src[0], x1 = src[1];
-#pragma unroll
-      for (int e = 0; e < 4; e++) x[e] = x0[e], x[4 + e] = x1[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = residual_value(R, wire, b, hidden, cbase + e);
-    }
+    residual_values8(R, wire, B, b, hidden, cbase, x);
     uint32_t v[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) {
@@ -426,8 +421,9 @@ __global__ void __launch_bounds__(1024) stream_q8_kernel(
         // chunk c = lane + 64 u of the step: row c / 17, 16-byte piece c % 17
         const int c = min(lane + 64 * u, kQ8mTileChunks - 1), cr = c / 17;
         const int64_t row = min(rbase + cr, V - 1);  // rows past V: never ranked
-        nx[u] = __builtin_nontemporal_load((const u32x4*)(table + (uint64_t)row * (uint64_t)row_bytes +
-                                                          kQ8mRowStep * st + 16 * (c - 17 * cr)));
+        // a plain load: the 128-byte lines at the piece's ends are touched again by
+        // the neighbouring step, which should find them in L2
+        nx[u] = *(const u32x4*)(table + (uint64_t)row * (uint64_t)row_bytes + kQ8mRowStep * st + 16 * (c - 17 * cr));
       }
     };
     if (nit > 0) issue(0);

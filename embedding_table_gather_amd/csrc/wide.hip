@@ -91,13 +91,13 @@ __global__ void __launch_bounds__(256) wide_prep_kernel(const void* __restrict__
   const int64_t b = (pass * ntile + nt) * 16 + (lane & 15);
   const int c0 = 64 * s + 16 * (lane >> 4) + 8 * (f >> 1);
   const bool lo = (f & 1) != 0;
+  float x[8];
+  residual_values8(R, wire, B, b, hidden, c0, x);
   uint32_t v[8];
 #pragma unroll
   for (int e = 0; e < 8; e++) {
-    const int c = c0 + e;
-    const float x = (b < B && c < hidden) ? residual_value(R, wire, b, hidden, c) : 0.0f;
-    const uint32_t hi = bf16_rne(x);
-    v[e] = lo ? bf16_rne(x - __uint_as_float(hi << 16)) : hi;  // x - hi is exact in f32
+    const uint32_t hi = bf16_rne(x[e]);
+    v[e] = lo ? bf16_rne(x[e] - __uint_as_float(hi << 16)) : hi;  // x - hi is exact in f32
   }
   img[i] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
 }

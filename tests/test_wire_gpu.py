@@ -23,7 +23,7 @@ F32, BF16, Q8_0, F16 = etg.F32, etg.BF16, etg.Q8_0, etg.F16
 WIRES = [etg.WIRE_F16, etg.WIRE_I8]
 
 
-@pytest.mark.parametrize("dtype,d", [(F32, 100), (BF16, 896), (F16, 2560), (Q8_0, 768), (Q8_0, 96)])
+@pytest.mark.parametrize("dtype,d", [(F32, 100), (BF16, 896), (BF16, 2048), (F16, 2560), (Q8_0, 768), (Q8_0, 96)])
 @pytest.mark.parametrize("wire", WIRES)
 @pytest.mark.parametrize("scaled", [False, True])
 def test_gather_wire_bit_exact(dtype, d, wire, scaled):
