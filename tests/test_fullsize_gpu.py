@@ -67,6 +67,13 @@ def test_lm31b_logits(B, sample):
     _check("lm31b", B, 10, sample)
 
 
+# the 31B-shaped lm_head stored as Q8_0 (1.50 GB): one residual row takes the
+# lane-split kernel, two or more the matrix-core kernel (8 rows per table pass)
+@pytest.mark.parametrize("B,sample", [(1, [0]), (2, [1]), (8, [0, 7])])
+def test_lm31b_q8_logits(B, sample):
+    _check("lm31b_q8", B, 10, sample)
+
+
 @pytest.mark.parametrize("path", [etg.PATH_STREAM, etg.PATH_ROW])
 def test_lm31b_logits_b1_paths(path):
     _check("lm31b", 1, 10, [0], path)
