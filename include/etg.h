@@ -160,8 +160,12 @@ typedef enum {
   ETG_PATH_GEMM = 3,   /* bf16 tables: tiled bf16 MFMA contraction for large batches     */
   ETG_PATH_WIDE = 4,   /* bf16 tables: one HBM pass per 64 residuals, bf16 MFMA dot engine,
                           hi+lo bf16 split of the residual                                */
-  ETG_PATH_Q8 = 5,     /* Q8_0 tables with hidden <= 8192: one HBM pass per 2 residuals,
-                          lanes split each row's blocks, f32 FMAs                         */
+  ETG_PATH_Q8 = 5,     /* Q8_0 tables.  Two or more residuals and hidden a multiple of
+                          256: one HBM pass per 8 residuals, one bf16 MFMA per 32-value
+                          block (int8 values are exact in bf16; residual as a hi+lo bf16
+                          split), the block's scale applied to the f32 result.  Otherwise
+                          hidden <= 8192: one HBM pass per 2 residuals, lanes split each
+                          row's blocks, f32 FMAs                                          */
   ETG_PATH_ROW = 6,    /* f32 / bf16 / f16 tables with rows <= 16 KiB: one HBM pass per
                           2 residuals, a wave per row, f32 FMAs (no bf16 rounding of the
                           residual)                                                       */
