@@ -41,7 +41,7 @@ def full_check(host, V, d, R, k, path=Q8):
 
 # blocks per row: 1, 3, 9, 24, 100, 168, 256 -> lanes per row 1, 4, 16, 32, 64, 64, 64
 @pytest.mark.parametrize("V,d", [(1001, 32), (3001, 96), (777, 288), (2000, 768), (4099, 3200), (4099, 5376),
-                                 (1500, 8192), (37, 64)])
+                                 (1500, 8192), (37, 64), (37, 256), (13, 512)])
 @pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 9, 17])
 def test_q8_path_ragged(V, d, B):
     host = synth.make_table(Q8_0, V, d, seed=2000 + V + d)
