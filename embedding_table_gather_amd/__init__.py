@@ -52,6 +52,8 @@ SIGNATURES = {
     "etg_wire_row_bytes": (_I64, [_I32, _I64]),
     "etg_embed_gather_wire": (_I32, [_VP, _VP, _I64, _F, _I32, _VP, _VP, _VP]),
     "etg_logits_topk_wire": (_I32, [_VP, _VP, _I32, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP]),
+    "etg_logits_topk_to_host": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP, _VP, _VP,
+                                       _VP]),
     "etg_hbm_read_probe": (_I32, [_VP, _I64, _VP, _VP]),
     "etg_last_error": (ctypes.c_char_p, []),
 }
@@ -241,6 +243,35 @@ class Table:
                                                   _ptr(workspace), workspace.numel(), int(path), ev0, ev1,
                                                   _stream_ptr(self.device)))
         return out_ids, out_scores
+
+    def logits_topk_to_host(self, residual: torch.Tensor, k: int, path: int = PATH_AUTO,
+                            workspace: torch.Tensor | None = None, host_out=None):
+        """logits_topk whose answer is also copied, without a synchronisation, into
+        page-locked host tensors (host_out: a reusable (int32, float32) pair of
+        [B, k] pinned CPU tensors, else new ones).  Returns (host ids, host scores,
+        event): the host tensors hold the answer once event.synchronize() (or a true
+        event.query())."""
+        R = self._residual(residual)
+        B = R.shape[0]
+        if workspace is None:
+            workspace = self.workspace(B, k, path)
+        ids = torch.empty((B, k), dtype=torch.int32, device=self.device)
+        sc = torch.empty((B, k), dtype=torch.float32, device=self.device)
+        if host_out is None:
+            host_out = (torch.empty((B, k), dtype=torch.int32, pin_memory=True),
+                        torch.empty((B, k), dtype=torch.float32, pin_memory=True))
+        h_ids, h_sc = host_out
+        if (h_ids.dtype != torch.int32 or h_sc.dtype != torch.float32 or h_ids.device.type != "cpu"
+                or h_sc.device.type != "cpu" or h_ids.numel() < B * k or h_sc.numel() < B * k
+                or not h_ids.is_contiguous() or not h_sc.is_contiguous()):
+            raise ValueError("host_out must be contiguous CPU int32 / float32 tensors of at least B * k entries")
+        ev = torch.cuda.Event()
+        with torch.cuda.device(self.device):
+            evh = ctypes.c_void_p(_event_handle(ev, self.device))
+            _check(lib().etg_logits_topk_to_host(self._h, _ptr(R), B, int(k), _ptr(ids), _ptr(sc), _ptr(workspace),
+                                                 workspace.numel(), int(path), _ptr(h_ids), _ptr(h_sc), evh,
+                                                 _stream_ptr(self.device)))
+        return h_ids, h_sc, ev
 
     def _residual(self, residual: torch.Tensor) -> torch.Tensor:
         if residual.dtype != torch.float32 or residual.device != self.device:

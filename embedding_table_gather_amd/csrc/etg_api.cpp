@@ -262,6 +262,25 @@ int32_t etg_logits_topk_ex(const etg_table* t, const float* d_residual, int64_t 
                                   workspace_bytes, path, nullptr, nullptr, stream);
 }
 
+int32_t etg_logits_topk_to_host(const etg_table* t, const float* d_residual, int64_t batch, int32_t k,
+                                int32_t* d_topk_ids, float* d_topk_scores, void* d_workspace, size_t workspace_bytes,
+                                int32_t path, int32_t* h_topk_ids, float* h_topk_scores, void* event,
+                                void* stream) {
+  if (h_topk_ids == nullptr || h_topk_scores == nullptr) return fail(ETG_EINVAL, "host result pointer is NULL");
+  if (d_topk_scores == nullptr) return fail(ETG_EINVAL, "scores pointer is NULL");
+  if (event == nullptr) return fail(ETG_EINVAL, "event is NULL");
+  const int32_t st = etg_logits_topk_ex(t, d_residual, batch, k, d_topk_ids, d_topk_scores, d_workspace,
+                                        workspace_bytes, path, stream);
+  if (st != ETG_OK) return st;
+  const size_t n = (size_t)batch * (size_t)k;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(h_topk_ids, d_topk_ids, n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(h_topk_scores, d_topk_scores, n * sizeof(float), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipEventRecord((hipEvent_t)event, s);
+  if (e != hipSuccess) return fail(ETG_EHIP, "result copy to host failed: %s", hipGetErrorString(e));
+  return ETG_OK;
+}
+
 int32_t etg_hbm_read_probe(const void* d_src, int64_t bytes, uint32_t* d_sink, void* stream) {
   if (d_src == nullptr || d_sink == nullptr) return fail(ETG_EINVAL, "source or sink pointer is NULL");
   if (!aligned(d_src, 16)) return fail(ETG_EALIGN, "source pointer is not 16-byte aligned");

@@ -213,6 +213,25 @@ int32_t etg_logits_topk_ex(const etg_table* lm_head, const float* d_residual, in
                            void* d_workspace, size_t workspace_bytes, int32_t path,
                            void* stream);
 
+/* As etg_logits_topk_ex, then the answer is also copied to host memory without a
+ * synchronisation, the pinned-buffer, copy and event pattern of the Perplexity blog
+ * "Fast embeddings on GPUs" (its serving runtime's lazy result tensors): after the
+ * kernels, d_topk_ids / d_topk_scores are copied asynchronously on `stream` into
+ * h_topk_ids / h_topk_scores (host memory of batch * k entries each, owned by the
+ * caller; page-locked memory from hipHostMalloc keeps the copy asynchronous,
+ * pageable memory works but the copy then blocks the calling thread), and `event`
+ * (a hipEvent_t the caller created, passed as void*) is recorded after the copy.
+ * The host buffers hold the answer once the event has completed
+ * (hipEventSynchronize / hipEventQuery); the caller meanwhile prepares its next
+ * step.  ETG_EINVAL if a host pointer, the scores or the event is NULL; the other
+ * errors as etg_logits_topk_ex (nothing is copied or recorded then); ETG_EHIP if
+ * the copy or the record fails to enqueue. */
+int32_t etg_logits_topk_to_host(const etg_table* lm_head, const float* d_residual, int64_t batch,
+                                int32_t k, int32_t* d_topk_ids, float* d_topk_scores,
+                                void* d_workspace, size_t workspace_bytes, int32_t path,
+                                int32_t* h_topk_ids, float* h_topk_scores, void* event,
+                                void* stream);
+
 /* As etg_logits_topk_ex, and records two caller-created hipEvent_t (passed as void*,
  * either may be NULL) on `stream` immediately before and after the kernel that
  * streams the table, so a caller can time that kernel alone with

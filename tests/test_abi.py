@@ -154,6 +154,19 @@ def test_logits_errors_without_launch(L, table):
     assert L.etg_logits_topk_ex(table, p, 2, 10, p, p, p, ws_n, 9, None) == -5
 
 
+def test_to_host_errors_without_launch(L, table):
+    p = ctypes.c_void_p(FAKE)
+    ws_n = L.etg_logits_topk_workspace(table, 2, 10)
+    f = L.etg_logits_topk_to_host
+    assert f(table, p, 2, 10, p, p, p, ws_n, 0, None, p, p, None) == -1 and "host" in _err(L)
+    assert f(table, p, 2, 10, p, p, p, ws_n, 0, p, None, p, None) == -1
+    assert f(table, p, 2, 10, p, None, p, ws_n, 0, p, p, p, None) == -1 and "scores" in _err(L)
+    assert f(table, p, 2, 10, p, p, p, ws_n, 0, p, p, None, None) == -1 and "event" in _err(L)
+    # the logits call's own checks come first: nothing is copied or recorded then
+    assert f(table, p, 0, 10, p, p, p, ws_n, 0, p, p, p, None) == -3
+    assert f(table, p, 2, 10, p, p, p, ws_n - 1, 0, p, p, p, None) == -6
+
+
 def test_probs_and_raw_errors_without_launch(L, table):
     p = ctypes.c_void_p(FAKE)
     ws_n = L.etg_logits_topk_workspace(table, 2, 10)

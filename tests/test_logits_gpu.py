@@ -260,3 +260,49 @@ def test_untied_lm_head_is_a_second_handle():
     oids, _ = oracle.topk(L, 10)
     fails = accept.check_full(gids.cpu().numpy(), gsc.cpu().numpy(), L, A, oids, accept.tol_coeff(BF16))
     assert not fails, fails[:3]
+
+
+@pytest.mark.parametrize("B", [1, 8, 33])
+def test_logits_to_host_matches_the_device_answer(B):
+    # the answer copied to page-locked host memory behind an event equals the
+    # device answer of the same call, bit for bit
+    V, d = 20011, 896
+    host = synth.make_table(BF16, V, d, seed=31)
+    R = to_dev(synth.residuals(B, d, seed=32))
+    t = table(host, BF16, V, d)
+    note(f"logits to host B={B}")
+    di, ds = t.logits_topk(R, 10)
+    hi, hs, ev = t.logits_topk_to_host(R, 10)
+    assert hi.is_pinned() and hs.is_pinned()
+    ev.synchronize()
+    assert torch.equal(hi, di.cpu()) and torch.equal(hs.view(torch.int32), ds.cpu().view(torch.int32))
+    # reused host buffers, a second call in a row
+    hi.fill_(-1)
+    hi2, hs2, ev2 = t.logits_topk_to_host(R, 10, host_out=(hi, hs))
+    ev2.synchronize()
+    assert hi2.data_ptr() == hi.data_ptr() and torch.equal(hi2, di.cpu())
+
+
+def test_logits_to_host_with_pageable_buffers():
+    # pageable host memory: the copy is still correct (it blocks instead)
+    import ctypes
+    V, d, B, k = 5003, 256, 3, 7
+    host = synth.make_table(BF16, V, d, seed=33)
+    R = to_dev(synth.residuals(B, d, seed=34))
+    t = table(host, BF16, V, d)
+    ws = t.workspace(B, k)
+    ids = torch.empty((B, k), dtype=torch.int32, device=R.device)
+    sc = torch.empty((B, k), dtype=torch.float32, device=R.device)
+    h_ids = np.full((B, k), -7, np.int32)
+    h_sc = np.zeros((B, k), np.float32)
+    ev = torch.cuda.Event()
+    ev.record()
+    note("logits to pageable host buffers")
+    st = etg.lib().etg_logits_topk_to_host(t._h, ctypes.c_void_p(R.data_ptr()), B, k, ctypes.c_void_p(ids.data_ptr()),
+                                           ctypes.c_void_p(sc.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                           etg.PATH_AUTO, h_ids.ctypes.data_as(ctypes.c_void_p),
+                                           h_sc.ctypes.data_as(ctypes.c_void_p), ctypes.c_void_p(ev.cuda_event),
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    ev.synchronize()
+    assert np.array_equal(h_ids, ids.cpu().numpy()) and np.array_equal(h_sc.view(np.int32), sc.cpu().numpy().view(np.int32))
