@@ -210,7 +210,12 @@ class Table:
         return n
 
     def workspace(self, batch: int, k: int, path: int = PATH_AUTO) -> torch.Tensor:
-        key = (int(batch), int(k), int(path))
+        """A device workspace for this shape, cached per (shape, path, current stream).
+
+        Calls on one stream run in order, so they can share a workspace; calls on
+        different streams get different ones.  Threads that enqueue on the same
+        stream concurrently must pass their own ``workspace``."""
+        key = (int(batch), int(k), int(path), torch.cuda.current_stream(self.device).cuda_stream)
         ws = self._ws.get(key)
         if ws is None:
             ws = torch.empty(max(self.workspace_bytes(batch, k, path), 256), dtype=torch.uint8, device=self.device)

@@ -20,6 +20,8 @@
 // Bit-exactness: dequant is exact in f32 (copy; bf16 and f16 widening; int8 * f16 has at
 // most 19 significant bits) and the scale is one f32 multiply, so there is one
 // rounding at most.  FP contraction is off in this file.
+#include <algorithm>
+
 #include "etg_device.hpp"
 #include "etg_internal.hpp"
 
@@ -29,6 +31,11 @@ namespace etg {
 
 static constexpr int kGatherWaves = 4;
 static constexpr int kGatherUnroll = 4;
+// Q8_0 blocks staged per piece by the general gather (2,176 bytes + 4 per wave).
+static constexpr int kGatherPieceBlocks = 64;
+// Rows per launch: a launch covers at most 2^24 rows (2^30 work-items), longer
+// gathers are split into several launches on the same stream.
+static constexpr int64_t kGatherLaunchRows = (int64_t)1 << 24;
 
 template <int DT, bool SCALE>
 __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__ table, uint32_t V,
@@ -103,38 +110,49 @@ __global__ void __launch_bounds__(256) gather_kernel(const uint8_t* __restrict__
       }
     }
   } else {
-    // Q8_0: stage [src & ~3, src + row_bytes) as aligned dwords.  row_bytes is even
-    // and the table base is 16-byte aligned, so src % 4 is 0 or 2: the first dword
-    // may start 2 bytes before the row (inside the previous row, never before the
-    // table), and a last dword that would run 2 bytes past the row is read as u16.
+    // Q8_0: the row is staged in pieces of up to kGatherPieceBlocks blocks.  A
+    // piece [p, p + 34 nblk) is read as the aligned dwords covering it: block
+    // offsets are even and the table base is 16-byte aligned, so p % 4 is 0 or 2;
+    // the first dword may start 2 bytes before the piece (inside the row or the
+    // previous row, never before the table), and a last dword that would run 2
+    // bytes past the piece is read as u16 (past the row's end it would leave the
+    // table).
     uint32_t* w = lds_words_buf + wv * lds_words;
-    const uintptr_t a = (uintptr_t)src;
-    const uintptr_t a0 = a & ~(uintptr_t)3;
-    const int head = (int)(a - a0);
-    const int nbytes = head + (int)row_bytes;
-    const int ndw = (nbytes + 3) >> 2;
-    const uint32_t* s = (const uint32_t*)a0;
-    for (int i = lane; i < ndw; i += 64) {
-      uint32_t v;
-      if (i == ndw - 1 && (nbytes & 3)) v = *(const uint16_t*)(s + i);
-      else v = s[i];
-      w[i] = v;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const uint8_t* wb = (const uint8_t*)w;
-    for (int c4 = lane; c4 < n4; c4 += 64) {
-      const int c = 4 * c4;
-      const int off = head + 34 * (c >> 5);  // even
-      const float sc = f16_bits_to_f32(*(const uint16_t*)(wb + off));
-      const int qo = off + 2 + (c & 31);     // even
-      const uint32_t q01 = *(const uint16_t*)(wb + qo);
-      const uint32_t q23 = *(const uint16_t*)(wb + qo + 2);
-      f32x4 v = {(float)(int8_t)(q01 & 0xffu) * sc, (float)(int8_t)(q01 >> 8) * sc,
-                 (float)(int8_t)(q23 & 0xffu) * sc, (float)(int8_t)(q23 >> 8) * sc};
-      if (SCALE) v = v * scale;
-      __builtin_nontemporal_store(v, o + c4);
+    const int nb = hidden >> 5;
+    for (int b0 = 0; b0 < nb; b0 += kGatherPieceBlocks) {
+      const int pb = min(kGatherPieceBlocks, nb - b0);
+      const uintptr_t a = (uintptr_t)(src + 34 * b0);
+      const uintptr_t a0 = a & ~(uintptr_t)3;
+      const int head = (int)(a - a0);
+      const int nbytes = head + 34 * pb;
+      const int ndw = (nbytes + 3) >> 2;
+      const uint32_t* s = (const uint32_t*)a0;
+      // the previous piece's reads of w are done before it is overwritten
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int i = lane; i < ndw; i += 64) {
+        uint32_t v;
+        if (i == ndw - 1 && (nbytes & 3)) v = *(const uint16_t*)(s + i);
+        else v = s[i];
+        w[i] = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int c4 = 8 * b0 + lane; c4 < 8 * (b0 + pb); c4 += 64) {
+        const int c = 4 * c4;
+        const int off = head + 34 * ((c >> 5) - b0);  // even
+        const float sc = f16_bits_to_f32(*(const uint16_t*)(wb + off));
+        const int qo = off + 2 + (c & 31);            // even
+        const uint32_t q01 = *(const uint16_t*)(wb + qo);
+        const uint32_t q23 = *(const uint16_t*)(wb + qo + 2);
+        f32x4 v = {(float)(int8_t)(q01 & 0xffu) * sc, (float)(int8_t)(q01 >> 8) * sc,
+                   (float)(int8_t)(q23 & 0xffu) * sc, (float)(int8_t)(q23 >> 8) * sc};
+        if (SCALE) v = v * scale;
+        __builtin_nontemporal_store(v, o + c4);
+      }
     }
   }
 }
@@ -336,12 +354,20 @@ static hipError_t launch_wire_dt(const TableDesc& t, const int32_t* ids, int64_t
 
 hipError_t launch_gather_wire(const TableDesc& t, const int32_t* ids, int64_t n, float scale, int32_t wire,
                               uint8_t* out, int32_t* bad, hipStream_t stream) {
-  switch (t.dtype) {
-    case DT_F32: return launch_wire_dt<DT_F32>(t, ids, n, scale, wire, out, bad, stream);
-    case DT_BF16: return launch_wire_dt<DT_BF16>(t, ids, n, scale, wire, out, bad, stream);
-    case DT_F16: return launch_wire_dt<DT_F16>(t, ids, n, scale, wire, out, bad, stream);
-    default: return launch_wire_dt<DT_Q8_0>(t, ids, n, scale, wire, out, bad, stream);
+  const int64_t rb = wire == WIRE_F16 ? 2 * t.hidden : t.hidden + 8;
+  for (int64_t r0 = 0; r0 < n; r0 += kGatherLaunchRows) {
+    const int64_t m = std::min(kGatherLaunchRows, n - r0);
+    uint8_t* o = out + r0 * rb;
+    hipError_t e;
+    switch (t.dtype) {
+      case DT_F32: e = launch_wire_dt<DT_F32>(t, ids + r0, m, scale, wire, o, bad, stream); break;
+      case DT_BF16: e = launch_wire_dt<DT_BF16>(t, ids + r0, m, scale, wire, o, bad, stream); break;
+      case DT_F16: e = launch_wire_dt<DT_F16>(t, ids + r0, m, scale, wire, o, bad, stream); break;
+      default: e = launch_wire_dt<DT_Q8_0>(t, ids + r0, m, scale, wire, o, bad, stream); break;
+    }
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 template <int DT>
@@ -363,7 +389,7 @@ static hipError_t launch_dt(const TableDesc& t, const int32_t* ids, int64_t n, f
                            (int)t.hidden, t.row_bytes, ids, n, scale, out, bad);
       return hipGetLastError();
     }
-    lds_words = (int)((t.row_bytes + 8 + 3) / 4);
+    lds_words = (34 * kGatherPieceBlocks + 4) / 4;
     lds = (size_t)kGatherWaves * lds_words * 4;
   }
   if (sc)
@@ -377,12 +403,19 @@ static hipError_t launch_dt(const TableDesc& t, const int32_t* ids, int64_t n, f
 
 hipError_t launch_gather(const TableDesc& t, const int32_t* ids, int64_t n, float scale, float* out,
                          int32_t* bad, hipStream_t stream) {
-  switch (t.dtype) {
-    case DT_F32: return launch_dt<DT_F32>(t, ids, n, scale, out, bad, stream);
-    case DT_BF16: return launch_dt<DT_BF16>(t, ids, n, scale, out, bad, stream);
-    case DT_F16: return launch_dt<DT_F16>(t, ids, n, scale, out, bad, stream);
-    default: return launch_dt<DT_Q8_0>(t, ids, n, scale, out, bad, stream);
+  for (int64_t r0 = 0; r0 < n; r0 += kGatherLaunchRows) {
+    const int64_t m = std::min(kGatherLaunchRows, n - r0);
+    float* o = out + r0 * t.hidden;
+    hipError_t e;
+    switch (t.dtype) {
+      case DT_F32: e = launch_dt<DT_F32>(t, ids + r0, m, scale, o, bad, stream); break;
+      case DT_BF16: e = launch_dt<DT_BF16>(t, ids + r0, m, scale, o, bad, stream); break;
+      case DT_F16: e = launch_dt<DT_F16>(t, ids + r0, m, scale, o, bad, stream); break;
+      default: e = launch_dt<DT_Q8_0>(t, ids + r0, m, scale, o, bad, stream); break;
+    }
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 }  // namespace etg

@@ -36,7 +36,14 @@ namespace etg {
 // VALU path: any dtype.  Block = 4 waves over a contiguous slice of rows; a wave
 // takes one row at a time, each lane accumulates RB residual rows over values
 // lane, lane + 64, ... with f32 FMAs, then a butterfly sum per residual row.
+// A lane sums its products in chunks of kValuChunk values (64 kValuChunk apart in
+// the row) and adds each chunk's sum to its total, so a logit carries at most
+// kValuChunk + hidden / (64 kValuChunk) + 6 roundings of 2^-24 relative to
+// sum_i |r_i e_i|: 70 for the widest rows (65,536 values), 4.2e-6 in all, inside
+// the f32 tables' 1e-5 bound at every supported width.
 // ---------------------------------------------------------------------------
+static constexpr int kValuChunk = 32;
+
 // logits (nullable [B][V]) receives the raw logits, lse (nullable [B][nblk]) the
 // log-partition partial of the block's rows at lse_c = log2(e) / temperature.
 template <int DT, int RB>
@@ -57,21 +64,29 @@ __global__ void __launch_bounds__(256) valu_logits_kernel(const uint8_t* __restr
     float acc[RB];
 #pragma unroll
     for (int b = 0; b < RB; b++) acc[b] = 0.f;
-    if (wire == WIRE_F32) {
-      const float* Rf = (const float*)R;
-      for (int c = lane; c < hidden; c += 64) {
-        const float x = deq_value<DT>(row, c);
+    for (int c0 = lane; c0 < hidden; c0 += 64 * kValuChunk) {
+      const int c1 = min(hidden, c0 + 64 * kValuChunk);
+      float part[RB];
 #pragma unroll
-        for (int b = 0; b < RB; b++)
-          if (b < nb) acc[b] = __builtin_fmaf(x, Rf[(b0 + b) * hidden + c], acc[b]);
-      }
-    } else {
-      for (int c = lane; c < hidden; c += 64) {
-        const float x = deq_value<DT>(row, c);
+      for (int b = 0; b < RB; b++) part[b] = 0.f;
+      if (wire == WIRE_F32) {
+        const float* Rf = (const float*)R;
+        for (int c = c0; c < c1; c += 64) {
+          const float x = deq_value<DT>(row, c);
 #pragma unroll
-        for (int b = 0; b < RB; b++)
-          if (b < nb) acc[b] = __builtin_fmaf(x, residual_value(R, wire, b0 + b, hidden, c), acc[b]);
+          for (int b = 0; b < RB; b++)
+            if (b < nb) part[b] = __builtin_fmaf(x, Rf[(b0 + b) * hidden + c], part[b]);
+        }
+      } else {
+        for (int c = c0; c < c1; c += 64) {
+          const float x = deq_value<DT>(row, c);
+#pragma unroll
+          for (int b = 0; b < RB; b++)
+            if (b < nb) part[b] = __builtin_fmaf(x, residual_value(R, wire, b0 + b, hidden, c), part[b]);
+        }
       }
+#pragma unroll
+      for (int b = 0; b < RB; b++) acc[b] += part[b];
     }
 #pragma unroll
     for (int b = 0; b < RB; b++) {

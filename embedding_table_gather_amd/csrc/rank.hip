@@ -74,10 +74,13 @@ hipError_t launch_rank_norm(const float* npart, int ngrp, int64_t V, float* nrm2
 // goes to first touches of randomly placed table rows).
 static constexpr int kRescoreWideBatch = 256;
 
-// LDS of rank_rescore_kernel: U [n] keys, heaps [waves][k] keys, the residual
-// [hidden rounded up to 8] f32, S [n] rows, flags [nvr], rescan list [nvr].
+// LDS of rank_rescore_kernel: U [n rounded up to even] keys, heaps [waves][k]
+// keys, the residual [hidden rounded up to 8] f32, S [n] rows, flags [nvr],
+// rescan list [nvr].  Rounding n up keeps the residual 16-byte aligned (the
+// rescoring reads it as f32x4; the wave counts are even).
 static size_t rescore_lds_bytes(int64_t hidden, int n, int nvr, int k, int nw) {
-  return (size_t)n * 8 + (size_t)nw * k * 8 + (size_t)((hidden + 7) & ~7) * 4 + (size_t)n * 4 + (size_t)nvr * 8;
+  return (size_t)((n + 1) & ~1) * 8 + (size_t)nw * k * 8 + (size_t)((hidden + 7) & ~7) * 4 + (size_t)n * 4 +
+         (size_t)nvr * 8;
 }
 
 int32_t rescore_waves(int64_t batch) { return batch <= kRescoreWideBatch ? 16 : 4; }
@@ -306,6 +309,7 @@ __global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
     const void* __restrict__ R, int wire, const uint64_t* __restrict__ cand, int nvr, int kb, int64_t range_rows,
     const float* __restrict__ nrm2, int nnrm, int k, int32_t* __restrict__ ids, float* __restrict__ scores,
     int sorted) {
+  static_assert(NW % 2 == 0, "the residual's LDS offset must stay 16-byte aligned");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ float red[NW][4];
   __shared__ __attribute__((aligned(16))) uint32_t hist[256];  // also gmax [k] and fin [k] keys below
@@ -315,8 +319,8 @@ __global__ void __launch_bounds__(64 * NW) rank_rescore_kernel(
   __shared__ uint32_t rk[kSelMaxCand];
   const int n = nvr * kb;
   uint64_t* U = (uint64_t*)smem;
-  uint64_t* heaps = U + n;                                     // [waves][k]
-  float* r = (float*)(heaps + NW * k);              // [hidden]
+  uint64_t* heaps = U + ((n + 1) & ~1);                       // [waves][k], 16-byte aligned
+  float* r = (float*)(heaps + NW * k);                         // [hidden], 16-byte aligned (NW is even)
   uint32_t* S = (uint32_t*)(r + ((hidden + 7) & ~7));          // [n]
   uint32_t* flag = S + n;                                      // [nvr] 1: rescanned
   uint32_t* rl = flag + nvr;                                   // [nvr]

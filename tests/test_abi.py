@@ -222,13 +222,23 @@ def test_read_probe_errors_without_launch(L):
     assert f(p, 0, s, None) == -3 and f(p, 1000, s, None) == -3
 
 
-def test_f16_tables_take_the_valu_path(L):
+def test_f16_tables_take_the_row_path_then_valu(L):
+    # rows of up to 16 KiB (8,192 binary16 values) take the row path, wider ones VALU
     st, h = _create(L, FAKE, etg.F16, 1000, 64)
     assert st == 0
     assert L.etg_logits_topk_workspace_ex(h, 1, 5, etg.PATH_STREAM) == -5
     assert L.etg_logits_topk_workspace_ex(h, 4, 5, etg.PATH_AUTO) == L.etg_logits_topk_workspace_ex(
-        h, 4, 5, etg.PATH_VALU) > 0
+        h, 4, 5, etg.PATH_ROW) > 0
     L.etg_table_destroy(h)
+    for d in (8192, 8200):
+        st, h = _create(L, FAKE, etg.F16, 1000, d)
+        assert st == 0
+        want = etg.PATH_ROW if d == 8192 else etg.PATH_VALU
+        assert L.etg_logits_topk_workspace_ex(h, 4, 5, etg.PATH_AUTO) == L.etg_logits_topk_workspace_ex(
+            h, 4, 5, want) > 0
+        if d == 8200:
+            assert L.etg_logits_topk_workspace_ex(h, 4, 5, etg.PATH_ROW) == -5
+        L.etg_table_destroy(h)
 
 
 def test_python_binding_rejects_host_tensors():

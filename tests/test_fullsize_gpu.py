@@ -47,14 +47,16 @@ def _check(name, B, k, sample_rows, path=0):
     fails = []
     for b in range(B):
         fails += [f"row {b}: {s}" for s in accept.check_row(gids[b], gsc[b], cfg.V, c, Lg[b], Ag[b])]
-    # sampled rows: the oracle's own top-k from a full pass
-    for b in sample_rows:
-        L, A = oracle.logits(host, cfg.dtype, cfg.V, cfg.d, R[b:b + 1])
-        oids, _ = oracle.topk(L, k)
-        fails += [f"row {b}: {s}" for s in accept.check_full(gids[b:b + 1], gsc[b:b + 1], L, A, oids, c)]
+    # sampled rows: the oracle's own top-k, all of them from one full pass over the table
+    rows = sorted(set(sample_rows))
+    L, A = oracle.logits(host, cfg.dtype, cfg.V, cfg.d, R[rows])
+    oids, _ = oracle.topk(L, k)
+    for i, b in enumerate(rows):
+        fails += [f"row {b}: {s}" for s in accept.check_full(gids[b:b + 1], gsc[b:b + 1], L[i:i + 1], A[i:i + 1],
+                                                             oids[i:i + 1], c)]
         # every returned logit is at least the oracle's k-th best minus the tolerance
-        kth = L[0, oids[0, -1]]
-        assert np.all(Lg[b] >= kth - c * (Ag[b] + A[0, oids[0, -1]]))
+        kth = L[i, oids[i, -1]]
+        assert np.all(Lg[b] >= kth - c * (Ag[b] + A[i, oids[i, -1]]))
     assert not fails, fails[:5]
 
 
@@ -62,14 +64,24 @@ def test_qwen05b_logits_b1():
     _check("qwen05b", 1, 10, [0])
 
 
-@pytest.mark.parametrize("B,sample", [(1, [0]), (8, [0, 7]), (64, [5, 63])])
+# B = 20 takes the rank path (the wide kernel ranking, then exact rescoring); the
+# Qwen-shaped table has 297 blocks of 512 rows, an odd count, and k = 1 or 3 keeps
+# 1 or 3 keys per block, so the rescoring's key list has an odd length
+@pytest.mark.parametrize("k", [1, 3])
+def test_qwen05b_logits_b20_rank_odd_block_count(k):
+    _check("qwen05b", 20, k, range(20))
+
+
+# B = 8: every row against the oracle's own top-k; B = 64: rows from each of the
+# four 16-row N-tiles of the wide kernel
+@pytest.mark.parametrize("B,sample", [(1, [0]), (8, range(8)), (64, [0, 9, 17, 31, 32, 47, 55, 63])])
 def test_lm31b_logits(B, sample):
     _check("lm31b", B, 10, sample)
 
 
 # the 31B-shaped lm_head stored as Q8_0 (1.50 GB): one residual row takes the
 # lane-split kernel, two or more the matrix-core kernel (8 rows per table pass)
-@pytest.mark.parametrize("B,sample", [(1, [0]), (2, [1]), (8, [0, 7])])
+@pytest.mark.parametrize("B,sample", [(1, [0]), (2, [0, 1]), (8, range(8))])
 def test_lm31b_q8_logits(B, sample):
     _check("lm31b_q8", B, 10, sample)
 
@@ -81,16 +93,21 @@ def test_lm31b_logits_b1_paths(path):
 
 @pytest.mark.parametrize("path", [etg.PATH_GEMM, etg.PATH_WIDE, etg.PATH_RANK])
 def test_lm31b_logits_b64_mfma_paths(path):
-    _check("lm31b", 64, 10, [31], path)
+    _check("lm31b", 64, 10, [0, 9, 17, 31, 32, 47, 55, 63], path)
+
+
+# rows from each 256-row column tile of the ranking contraction (and of the
+# 128-row column tiles of the split one): both ends of every tile
+_PREFILL_ROWS = [0, 255, 256, 300, 511, 512, 600, 767, 768, 1023]
 
 
 def test_prefill_logits_b1024():
     # the automatic choice here is the rank path
-    _check("prefill", 1024, 40, [0, 1023])
+    _check("prefill", 1024, 40, _PREFILL_ROWS)
 
 
 def test_prefill_logits_b1024_split_gemm():
-    _check("prefill", 1024, 40, [511], etg.PATH_GEMM)
+    _check("prefill", 1024, 40, _PREFILL_ROWS + [127, 128, 895, 896], etg.PATH_GEMM)
 
 
 def test_lm31b_tied_gather_then_logits():

@@ -56,6 +56,42 @@ def test_gather_shapes_bit_exact(dtype, d, n):
         assert np.array_equal(bits(out), bits(ref))
 
 
+# Q8_0 rows that are not whole 16-byte chunks are staged through LDS in pieces of
+# 64 blocks: a row of 257 blocks (the last piece has one block), 513 and 2,047
+# blocks (the widest row, 69,598 bytes); odd block counts put every other row
+# start 2 bytes past a dword boundary
+@pytest.mark.parametrize("d", [8224, 16416, 65504])
+def test_gather_long_q8_rows_bit_exact(d):
+    V = 67
+    host = synth.make_table(Q8_0, V, d, seed=70 + d)
+    ids = np.array([0, 66, 1, 65, 33, 2, 3, 34, 66, -1, 5], np.int32)
+    for scaled in (False, True):
+        out, ref, nbad = _gather_both(host, Q8_0, V, d, ids, scaled)
+        assert nbad == 1
+        assert np.array_equal(bits(out), bits(ref))
+
+
+def test_gather_more_rows_than_one_launch():
+    # 2^24 + 5 ids: the gather is split into two launches (at most 2^24 rows each);
+    # rows on both sides of the split, and the bad-id count over both
+    V, d = 1000, 4
+    n = (1 << 24) + 5
+    host = synth.make_table(F32, V, d, seed=71)
+    ids = synth.uniform_ids(n, V, seed=72)
+    ids[(1 << 24) - 1] = -7
+    ids[1 << 24] = V
+    t = table(host, F32, V, d)
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    note(f"gather n={n} in two launches")
+    out = t.embed_gather(ids_dev(ids), scale="sqrt_d", bad_count=cnt, check=False)
+    torch.cuda.synchronize()
+    ref, nbad = oracle.embed_gather(host, F32, V, d, ids, scale=oracle.sqrt_d(d))
+    assert int(cnt.item()) == nbad == 2
+    assert np.array_equal(bits(out), bits(ref))
+    del out
+    torch.cuda.empty_cache()
+
+
 def test_gather_special_values_bit_exact():
     # subnormal, huge and signed-zero inputs through every dtype
     V, d = 8, 64

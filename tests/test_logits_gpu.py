@@ -84,6 +84,29 @@ def test_rank_path_ragged(V, d, B):
     full_check(host, BF16, V, d, R, min(10, V), RANK)
 
 
+# batches past three 256-row column tiles of the ranking contraction (and past
+# six 128-row tiles of the split one): every row of tiles 2 and 3 against the
+# oracle's own top-k
+@pytest.mark.parametrize("path", [RANK, GEMM])
+@pytest.mark.parametrize("V,d,B", [(70000, 512, 769), (5003, 200, 1000)])
+def test_mfma_paths_past_three_column_tiles(path, V, d, B):
+    host = synth.make_table(BF16, V, d, seed=510 + V)
+    R = synth.residuals(B, d, seed=610 + B)
+    full_check(host, BF16, V, d, R, 10, path)
+
+
+# an odd number of 512-row blocks (9) with k = 1 or 3 keys per block: the
+# rescoring's list of block keys has an odd length, and its residual row must
+# still sit 16-byte aligned in LDS after that list
+@pytest.mark.parametrize("k", [1, 3])
+@pytest.mark.parametrize("path", [RANK, etg.PATH_AUTO])
+def test_rank_path_odd_block_count(k, path):
+    V, d, B = 4099, 512, 20
+    host = synth.make_table(BF16, V, d, seed=520 + k)
+    R = synth.residuals(B, d, seed=620 + k)
+    full_check(host, BF16, V, d, R, k, path)
+
+
 @pytest.mark.parametrize("k", [10, 40, 64])
 @pytest.mark.parametrize("B", [2, 70])
 def test_rank_path_rescans_a_range_holding_many_winners(k, B):
@@ -112,6 +135,21 @@ def test_row_path_ragged(dtype, V, d, B):
     host = synth.make_table(dtype, V, d, seed=700 + V + d)
     R = synth.residuals(B, d, seed=800 + B)
     full_check(host, dtype, V, d, R, min(10, V), ROW)
+
+
+# f32 and f16 rows too wide for the row path (over 16 KiB) take the VALU path;
+# the f32 tables' bound of 1e-5 sum|r e| holds there up to 65,536 values.  The
+# residual of row 0 is aligned with table row 3 (every product positive), so its
+# rounding errors do not cancel.
+@pytest.mark.parametrize("dtype,d", [(F32, 16384), (F16, 16384), (F32, 65536), (F16, 65536)])
+@pytest.mark.parametrize("path", [etg.PATH_AUTO, VALU])
+def test_wide_f32_f16_rows_within_1e5(dtype, d, path):
+    V, B = 1001, 3
+    host = synth.make_table(dtype, V, d, seed=900 + d + dtype)
+    R = synth.residuals(B, d, seed=901)
+    E3 = oracle.f16_to_f64(host[3]) if dtype == F16 else host[3].astype(np.float64)
+    R[0] = (np.sign(E3) * (1.0 + np.abs(R[0]) / 8)).astype(np.float32)
+    full_check(host, dtype, V, d, R, 10, path)
 
 
 # the wide path: 512-row blocks (ragged last block), 4-step K chunks (ragged last
