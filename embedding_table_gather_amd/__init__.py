@@ -55,6 +55,7 @@ SIGNATURES = {
     "etg_logits_topk_to_host": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP, _VP, _VP,
                                        _VP]),
     "etg_hbm_read_probe": (_I32, [_VP, _I64, _VP, _VP]),
+    "etg_logits_topk_noalloc": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP]),
     "etg_last_error": (ctypes.c_char_p, []),
 }
 
@@ -247,6 +248,21 @@ class Table:
             _check(lib().etg_logits_topk_profiled(self._h, _ptr(R), B, int(k), _ptr(out_ids), _ptr(out_scores),
                                                   _ptr(workspace), workspace.numel(), int(path), ev0, ev1,
                                                   _stream_ptr(self.device)))
+        return out_ids, out_scores
+
+    def logits_topk_noalloc(self, residual: torch.Tensor, k: int, out_ids: torch.Tensor,
+                            out_scores: torch.Tensor):
+        """logits_topk with the library's own device scratch as the workspace (for
+        callers that cannot allocate): writes into the given int32 / float32 [B, k]
+        device tensors and allocates nothing.  Calls that overlap on one GPU race."""
+        R = self._residual(residual)
+        B = R.shape[0]
+        for o, dt in ((out_ids, torch.int32), (out_scores, torch.float32)):
+            if o.dtype != dt or o.device != self.device or not o.is_contiguous() or o.numel() != B * k:
+                raise ValueError("out_ids / out_scores must be contiguous int32 / float32 [B, k] device tensors")
+        with torch.cuda.device(self.device):
+            _check(lib().etg_logits_topk_noalloc(self._h, _ptr(R), B, int(k), _ptr(out_ids), _ptr(out_scores),
+                                                 _stream_ptr(self.device)))
         return out_ids, out_scores
 
     def logits_topk_to_host(self, residual: torch.Tensor, k: int, path: int = PATH_AUTO,

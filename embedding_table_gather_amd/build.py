@@ -11,7 +11,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libetg.so")
 SOURCES = ["etg_api.cpp", "gather.hip", "logits.hip", "stream.hip", "wide.hip", "gemm.hip", "rank.hip", "q8.hip",
-           "row.hip", "probe.hip"]
+           "row.hip", "probe.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -55,6 +55,14 @@ int32_t check_logits_args(const etg_table* t, int64_t batch, int32_t k) {
 
 }  // namespace
 
+int32_t etg::set_error(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
 extern "C" {
 
 int32_t etg_version(void) { return 100; }

@@ -106,6 +106,9 @@ hipError_t launch_logits_topk(const TableDesc& t, const LogitsPlan& p, const voi
                               float* logits = nullptr, float* probs = nullptr, float lse_scale = 0.f,
                               int32_t wire = 0);
 
+// Set the calling thread's etg_last_error() message and return `code` (etg_api.cpp).
+int32_t set_error(int32_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kTargetBlocks = 256;  // one workgroup per MI355X compute unit
 

@@ -21,8 +21,9 @@
  * Conventions for every function below:
  *  - Pointers named d_* are DEVICE pointers (HBM of the current HIP device); the
  *    caller owns all of them.  The library keeps no device allocations and no
- *    hidden state: a table handle is immutable host metadata and may be shared
- *    by threads.
+ *    hidden state (the one exception is the scratch array behind
+ *    etg_logits_topk_noalloc): a table handle is immutable host metadata and may
+ *    be shared by threads.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Work
  *    is enqueued on it and the call returns without waiting.
  *  - Every function returns an etg_status; 0 is success.  A negative status
@@ -303,6 +304,31 @@ int32_t etg_logits_topk_wire(const etg_table* lm_head, const void* d_residual, i
  *   d_sink   4 bytes of device memory, 4-byte aligned
  */
 int32_t etg_hbm_read_probe(const void* d_src, int64_t bytes, uint32_t* d_sink, void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  As etg_logits_topk
+ * (ETG_PATH_AUTO), with the workspace taken from a library-owned device array of
+ * ETG_NOALLOC_SCRATCH_BYTES bytes instead of a caller's buffer.  The call
+ * allocates nothing; the array is a file-scope device variable, one copy per GPU
+ * the library runs on, held until the process ends (its address is looked up
+ * once per device, on the first call with that device current).
+ *   Limit: shapes whose etg_logits_topk_workspace() exceeds
+ *   ETG_NOALLOC_SCRATCH_BYTES are rejected with ETG_EWORKSPACE before any device
+ *   work (32 MiB covers batches up to 1,024 rows at k = 40 on a 262,144-row
+ *   table; the 31B-shaped decode step needs 22 KiB).
+ *   Sharing: every call on a GPU uses that GPU's one array and overwrites it
+ *   (the kernels write everything they read, so nothing depends on earlier
+ *   calls).  Calls whose kernels can overlap on one GPU -- on different
+ *   streams, or from threads enqueueing at the same time -- race on the array
+ *   and give wrong answers; such callers pass their own workspaces to
+ *   etg_logits_topk instead.  `stream` must belong to the current device.
+ * Errors: those of etg_logits_topk; ETG_EWORKSPACE beyond the limit; ETG_EHIP if
+ * the array's device address cannot be looked up.
+ */
+#define ETG_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int32_t etg_logits_topk_noalloc(const etg_table* lm_head, const float* d_residual, int64_t batch,
+                                int32_t k, int32_t* d_topk_ids, float* d_topk_scores, void* stream);
 
 /* Message of the calling thread's last failed call ("" if none). */
 const char* etg_last_error(void);

@@ -264,3 +264,17 @@ def test_wire_formats(L, table):
     assert f(table, ctypes.c_void_p(FAKE + 1), etg.WIRE_F16, 2, 10, p, p, p, ws_n, 0, None) == -4
     assert f(table, ctypes.c_void_p(FAKE + 2), etg.WIRE_I8, 2, 10, p, p, p, ws_n, 0, None) == -4
     assert f(table, p, etg.WIRE_I8, 2, 10, None, p, p, ws_n, 0, None) == -1
+
+
+def test_noalloc_host_errors_without_launch(L, table):
+    # host-detectable errors return before the scratch is looked up or anything runs
+    p = ctypes.c_void_p(FAKE)
+    f = L.etg_logits_topk_noalloc
+    assert f(None, p, 1, 10, p, p, None) == -1
+    assert f(table, p, 0, 10, p, p, None) == -3
+    assert f(table, p, 1, 0, p, p, None) == -5
+    # a shape whose workspace exceeds the 32 MiB scratch
+    big = 4096
+    assert L.etg_logits_topk_workspace(table, big, 64) > 32 << 20
+    assert f(table, p, big, 64, p, p, None) == -6
+    assert "scratch" in _err(L)
