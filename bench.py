@@ -77,7 +77,7 @@ def _counter_means(csv_path: str, counter: str):
     return out
 
 
-def write_traffic(fetch_csv: str, write_csv: str, kernel: str = "stream_logits_kernel<1>") -> dict:
+def write_traffic(fetch_csv: str, write_csv: str, kernel: str = "stream_logits_kernel<1, 0>") -> dict:
     """Turn a FETCH_SIZE run and a WRITE_SIZE run of `bench.py --no-extras --calib-copy`
     (rocprofv3 --pmc ..., csv output) into profiles/traffic.json.
 
@@ -150,6 +150,10 @@ class _HipEvents:
             evs.append(h.value)
         return tuple(evs)
 
+    def record(self, ev, torch) -> None:
+        if self.hip.hipEventRecord(self.ct.c_void_p(ev), self.ct.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def ms(self, a, b) -> float:
         out = self.ct.c_float()
         if self.hip.hipEventElapsedTime(self.ct.byref(out), self.ct.c_void_p(a), self.ct.c_void_p(b)) != 0:
@@ -179,6 +183,78 @@ def _timed(torch, fn, iters: int, events: _HipEvents = None):
     if events:
         events.close()
     return ms, kms
+
+
+def _dist(torch, fn, iters: int, events: _HipEvents, kernel: bool = False) -> dict:
+    """Per-call time of fn over `iters` repeats: median, p10 and p90 in us.  A
+    repeat is a batch of back-to-back calls between two events (batches of about
+    200 us, so that the events' own cost, a few us, stays out of the per-call
+    time of short calls), its time divided by the calls in it.  With kernel=True
+    fn takes (ev_before, ev_after), recorded by the library around its table
+    kernel on one call of each batch, and the kernel's median is added."""
+    import numpy as np
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    est_us = (time.perf_counter() - t1) / 3 * 1e6
+    per_batch = int(min(64, max(1, 200.0 // max(est_us, 1.0))))
+    bounds = [events.pair() for _ in range(iters)]
+    kev = [events.pair() for _ in range(iters)] if kernel else None
+    torch.cuda.synchronize()
+    for i in range(iters):
+        events.record(bounds[i][0], torch)
+        for j in range(per_batch):
+            fn(kev[i]) if kernel and j == per_batch - 1 else fn()
+        events.record(bounds[i][1], torch)
+    torch.cuda.synchronize()
+    per = np.array([events.ms(a, b) for a, b in bounds]) * 1e3 / per_batch
+    out = {"median_us": round(float(np.median(per)), 2), "p10_us": round(float(np.percentile(per, 10)), 2),
+           "p90_us": round(float(np.percentile(per, 90)), 2), "repeats": iters, "calls_per_repeat": per_batch}
+    if kernel:
+        kk = np.array([events.ms(a, b) for a, b in kev]) * 1e3
+        out["kernel_median_us"] = round(float(np.median(kk)), 2)
+    events.close()
+    return out
+
+
+def _single(torch, fn, iters: int = 30) -> float:
+    """Median wall time (us) of one call between two synchronisations."""
+    import numpy as np
+    lat = []
+    for _ in range(iters):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - t1) * 1e6)
+    return round(float(np.median(lat)), 1)
+
+
+def _graph(torch, fn):
+    """fn captured in a HIP graph (after one run on a side stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main() -> int:
@@ -260,7 +336,7 @@ def main() -> int:
     logits_bytes = cfg.table_bytes + B * cfg.d * 4 + B * k * 8
     step_bytes = gather_bytes + logits_bytes
     value = step_bytes / (ms * 1e-3) / 1e9
-    kernel_name = "stream_logits_kernel<1>"
+    kernel_name = "stream_logits_kernel<1, 0>"
     achieved = cfg.table_bytes / (kms * 1e-3) / 1e9
     traffic = _traffic(kernel_name)
     out = {
@@ -298,77 +374,135 @@ def main() -> int:
 
     also = {}
     if not args.no_extras:
-        # single-call latency of the decode step: each step alone between two
-        # synchronisations (median, p10, p90 of 20), beside the back-to-back average
-        lat = []
-        for _ in range(20):
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            s0.record()
-            step()
-            s1.record()
-            torch.cuda.synchronize()
-            lat.append(s0.elapsed_time(s1) * 1e3)
-        also["decode_step_single_call_us"] = {
-            "median": round(float(np.median(lat)), 1), "p10": round(float(np.percentile(lat, 10)), 1),
-            "p90": round(float(np.percentile(lat, 90)), 1)}
-        # a plain read stream of the same 2.82 GB on the same box (the library's
-        # etg_hbm_read_probe), as a measured reference beside the 8 TB/s nominal
+        also["decode_step"] = _dist(torch, step, 50, hev)
+        also["decode_step"]["single_call_us"] = _single(torch, step)
+        if ms_graph is not None:
+            also["decode_step"]["hipgraph_replay_us"] = round(ms_graph * 1e3, 1)
+        # plain read and write streams on the same box (the library's probes), as
+        # measured references beside the 8 TB/s nominal
         sink = torch.empty(1, dtype=torch.int32, device=dev)
-        f = lambda: etg.hbm_read_probe(rows, sink)
-        for _ in range(3):
-            f()
-        mrs, _ = _timed(torch, f, 20)
-        rs_gbps = cfg.table_bytes / (mrs * 1e-3) / 1e9
+        rd = _dist(torch, lambda: etg.hbm_read_probe(rows, sink), 20, hev)
+        rs_gbps = cfg.table_bytes / (rd["median_us"] * 1e-6) / 1e9
         also["read_stream_reference"] = {
-            "what": "etg_hbm_read_probe over the 2.82 GB table", "us_per_call": round(mrs * 1e3, 1),
+            "what": "etg_hbm_read_probe over the 2.82 GB table", "us_per_call": rd["median_us"],
             "GBps": round(rs_gbps, 1), "pct_hbm_peak": round(100 * rs_gbps / HBM_PEAK_GBPS, 1),
             "roofline_kernel_pct_of_it": round(100 * achieved / rs_gbps, 1)}
         log(f"read stream reference: {rs_gbps:.0f} GB/s")
-    if ms_graph is not None:
-        also["decode_step_hipgraph_replay"] = {
-            "ms_per_step": round(ms_graph, 4),
-            "GBps": round(step_bytes / (ms_graph * 1e-3) / 1e9, 1)}
-    if not args.no_extras:
-        # the automatic choice (stream up to 8 rows, wide up to 16, then the rank
-        # path), and the exact wide kernel at 64 rows for comparison
-        for b, path, key in ((8, etg.PATH_AUTO, "lm31b_logits_top10_B8"), (16, etg.PATH_AUTO, "lm31b_logits_top10_B16"),
-                             (32, etg.PATH_AUTO, "lm31b_logits_top10_B32"), (64, etg.PATH_AUTO, "lm31b_logits_top10_B64"),
-                             (64, etg.PATH_WIDE, "lm31b_logits_top10_B64_exact_wide")):
-            Rb = torch.from_numpy(cfg.residuals(b)).to(dev)
-            wsb = table.workspace(b, k, path)
-            f = lambda evs=None: table.logits_topk(Rb, k, path=path, workspace=wsb, events=evs)
+        wref = {}
+        for name, nbytes in (("50MB", 50331648), ("1GB", 1 << 30)):
+            wb = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+            wd = _dist(torch, lambda: etg.hbm_write_probe(wb, 0), 50, hev)
+            wref[name] = {"bytes": nbytes, "us_per_call": wd["median_us"],
+                          "GBps": round(nbytes / (wd["median_us"] * 1e-6) / 1e9, 1)}
+            del wb
+        also["write_stream_reference"] = {"what": "etg_hbm_write_probe (non-temporal 16-byte stores)", **wref}
+        log(f"write stream reference: {wref}")
+
+        def logits_entry(tbl, Rb, kk, path, nbytes, iters=50):
+            wsb = tbl.workspace(Rb.shape[0], kk, path)
+            f = lambda evs=None: tbl.logits_topk(Rb, kk, path=path, workspace=wsb, events=evs)
             for _ in range(3):
                 f()
-            mb, kb = _timed(torch, f, 20, events=hev)
-            also[key] = {
-                "us_per_call": round(mb * 1e3, 1), "kernel_us": round(kb * 1e3, 1),
-                "GBps": round(cfg.table_bytes / (mb * 1e-3) / 1e9, 1),
-                "pct_hbm_peak": round(100 * cfg.table_bytes / (mb * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
-            log(f"B={b} path={path}: {mb * 1e3:.1f} us")
+            d = _dist(torch, f, iters, hev, kernel=True)
+            d["GBps"] = round(nbytes / (d["median_us"] * 1e-6) / 1e9, 1)
+            d["pct_hbm_peak"] = round(100 * d["GBps"] / HBM_PEAK_GBPS, 1)
+            return d
+
+        # the automatic choice (stream up to 8 rows, wide up to 16, then the rank
+        # path), the exact wide kernel at 64 rows, and past 64 rows the rank path
+        # beside the split contraction
+        for b, path, key in ((8, etg.PATH_AUTO, "lm31b_logits_top10_B8"), (16, etg.PATH_AUTO, "lm31b_logits_top10_B16"),
+                             (32, etg.PATH_AUTO, "lm31b_logits_top10_B32"), (64, etg.PATH_AUTO, "lm31b_logits_top10_B64"),
+                             (64, etg.PATH_WIDE, "lm31b_logits_top10_B64_exact_wide"),
+                             (96, etg.PATH_AUTO, "lm31b_logits_top10_B96"), (128, etg.PATH_AUTO, "lm31b_logits_top10_B128"),
+                             (128, etg.PATH_GEMM, "lm31b_logits_top10_B128_split_gemm"),
+                             (192, etg.PATH_AUTO, "lm31b_logits_top10_B192"), (256, etg.PATH_AUTO, "lm31b_logits_top10_B256"),
+                             (256, etg.PATH_GEMM, "lm31b_logits_top10_B256_split_gemm")):
+            Rb = torch.from_numpy(cfg.residuals(b)).to(dev)
+            also[key] = logits_entry(table, Rb, k, path, cfg.table_bytes, iters=50 if b <= 64 else 20)
+            log(f"B={b} path={path}: {also[key]['median_us']:.1f} us")
+            del Rb
         # the logits response with probabilities at T = 1, and the raw logits mode
         R1 = torch.from_numpy(cfg.residuals(1)).to(dev)
         ws1 = table.workspace(1, k)
-        f = lambda: table.logits_topk_probs(R1, k, temperature=1.0, workspace=ws1)
-        f()
-        mq, _ = _timed(torch, f, 20)
-        also["lm31b_logits_top10_probs_B1"] = {
-            "us_per_call": round(mq * 1e3, 1), "GBps": round(cfg.table_bytes / (mq * 1e-3) / 1e9, 1),
-            "pct_hbm_peak": round(100 * cfg.table_bytes / (mq * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
+        d = _dist(torch, lambda: table.logits_topk_probs(R1, k, temperature=1.0, workspace=ws1), 50, hev)
+        d["GBps"] = round(cfg.table_bytes / (d["median_us"] * 1e-6) / 1e9, 1)
+        d["pct_hbm_peak"] = round(100 * d["GBps"] / HBM_PEAK_GBPS, 1)
+        also["lm31b_logits_top10_probs_B1"] = d
         raw = torch.empty((1, cfg.V), dtype=torch.float32, device=dev)
         wsr = torch.empty(max(table.workspace_bytes(1, 1), 256), dtype=torch.uint8, device=dev)
-        f = lambda: table.logits_raw(R1, out=raw, workspace=wsr)
-        f()
-        mr, _ = _timed(torch, f, 20)
+        d = _dist(torch, lambda: table.logits_raw(R1, out=raw, workspace=wsr), 50, hev)
         rbytes = cfg.table_bytes + cfg.V * 4
-        also["lm31b_logits_raw_B1"] = {
-            "us_per_call": round(mr * 1e3, 1), "GBps": round(rbytes / (mr * 1e-3) / 1e9, 1),
-            "pct_hbm_peak": round(100 * rbytes / (mr * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
-        log(f"probs B=1: {mq * 1e3:.1f} us, raw B=1: {mr * 1e3:.1f} us")
+        d["GBps"] = round(rbytes / (d["median_us"] * 1e-6) / 1e9, 1)
+        d["pct_hbm_peak"] = round(100 * d["GBps"] / HBM_PEAK_GBPS, 1)
+        also["lm31b_logits_raw_B1"] = d
+        log(f"probs B=1: {also['lm31b_logits_top10_probs_B1']['median_us']} us, raw B=1: {d['median_us']} us")
     del table, rows
     torch.cuda.empty_cache()
 
     if not args.no_extras:
+        # tiny f32 table (4,096 x 256): gather of 64 ids, logits + top-5 for 4 rows,
+        # and the two as one step; eager calls beside the same calls replayed from a
+        # captured HIP graph
+        c1 = synth.CONFIGS["tiny"]
+        t1 = etg.Table(torch.from_numpy(c1.table()).to(dev), c1.dtype, c1.V, c1.d)
+        ids1 = torch.from_numpy(c1.ids()).to(dev)
+        x1 = torch.empty((ids1.numel(), c1.d), dtype=torch.float32, device=dev)
+        R4 = torch.from_numpy(c1.residuals(4)).to(dev)
+        ws4 = t1.workspace(4, c1.k)
+        oi4 = torch.empty((4, c1.k), dtype=torch.int32, device=dev)
+        os4 = torch.empty((4, c1.k), dtype=torch.float32, device=dev)
+        g1 = lambda: t1.embed_gather(ids1, out=x1, check=False)
+        l1 = lambda evs=None: t1.logits_topk(R4, c1.k, workspace=ws4, out_ids=oi4, out_scores=os4, events=evs)
+        s1 = lambda: (g1(), l1())
+        for key, fn, kern in (("tiny_gather_64", g1, False), ("tiny_logits_top5_B4", l1, True),
+                              ("tiny_gather_then_logits", s1, False)):
+            for _ in range(5):
+                fn()
+            d = _dist(torch, fn, 50, hev, kernel=kern)
+            d["single_call_us"] = _single(torch, fn)
+            gr = _graph(torch, fn if not kern else (lambda: l1()))
+            d["hipgraph_replay"] = _dist(torch, gr.replay, 50, hev)
+            d["hipgraph_replay"]["single_call_us"] = _single(torch, gr.replay)
+            del gr
+            also[key] = d
+        also["tiny_gather_64"]["rows_per_s"] = round(ids1.numel() / (also["tiny_gather_64"]["median_us"] * 1e-6))
+        log(f"tiny: {also['tiny_gather_then_logits']}")
+        # the service step from host ids to a host answer: host ids -> device, gather,
+        # logits + top-5 of 4 rows -> page-locked host memory behind an event; eager
+        # calls of the plain entry points beside the graph-cached step calls (one
+        # graph per configuration, captured on the second hit)
+        ss = torch.cuda.Stream()
+        with torch.cuda.stream(ss):
+            ids1_h = torch.from_numpy(c1.ids()).pin_memory()
+            ids1_d = torch.empty_like(ids1_h, device=dev)
+            ho = (torch.empty((4, c1.k), dtype=torch.int32, pin_memory=True),
+                  torch.empty((4, c1.k), dtype=torch.float32, pin_memory=True))
+
+            def eager_step():
+                ids1_d.copy_(ids1_h, non_blocking=True)
+                t1.embed_gather(ids1_d, out=x1, check=False)
+                return t1.logits_topk_to_host(R4, c1.k, workspace=ws4, host_out=ho)
+
+            ids1_np = ids1_h.numpy()
+            d = {"plain_calls_with_copies": _dist(torch, eager_step, 50, hev)}
+            d["plain_calls_with_copies"]["single_call_us"] = _single(torch, lambda: eager_step()[2].synchronize())
+            # the step cache: kernels read the ids from and write the answer to mapped
+            # page-locked memory; run eagerly, then with graphs
+            for name, use_graphs in (("step_eager", False), ("step_graph_cached", True)):
+                sc1 = etg.StepCache(t1, max_ids=ids1_h.numel(), max_batch=4, k=c1.k, use_graphs=use_graphs)
+                sc1.residual.copy_(R4)
+
+                def graph_step():
+                    sc1.gather(ids1_np)
+                    return sc1.logits(4)
+                d[name] = _dist(torch, graph_step, 50, hev)
+                d[name]["single_call_us"] = _single(torch, lambda: graph_step().synchronize())
+                d[name]["graphs_captured"], d[name]["graph_launches"] = sc1.stats()
+                del sc1
+            also["tiny_step_host_ids_to_host_top5"] = d
+            log(f"tiny step: {d}")
+        del t1
         # Qwen2.5-0.5B-shaped tied table (bf16 151,936 x 896, 272 MB): the prompt's
         # gather of 628 Zipf ids over 109 distinct rows, and logits + top-10 for 1 row
         qc = synth.CONFIGS["qwen05b"]
@@ -382,11 +516,16 @@ def main() -> int:
         qids = torch.from_numpy(qids_host).to(dev)
         qx = torch.empty((qids.numel(), qc.d), dtype=torch.float32, device=dev)
         f = lambda: qwt.embed_gather(qids, out=qx, check=False)
-        f()
-        mqg, _ = _timed(torch, f, 100)
-        also["qwen05b_gather_628_zipf_ids"] = {
-            "rows": int(qids.numel()), "distinct_rows": int(np.unique(qids_host).size),
-            "us_per_call": round(mqg * 1e3, 2), "rows_per_s": round(qids.numel() / (mqg * 1e-3))}
+        for _ in range(5):
+            f()
+        d = _dist(torch, f, 50, hev)
+        d["single_call_us"] = _single(torch, f)
+        gr = _graph(torch, f)
+        d["hipgraph_replay"] = _dist(torch, gr.replay, 50, hev)
+        del gr
+        d.update({"rows": int(qids.numel()), "distinct_rows": int(np.unique(qids_host).size),
+                  "rows_per_s": round(qids.numel() / (d["median_us"] * 1e-6))})
+        also["qwen05b_gather_628_zipf_ids"] = d
         Rq1 = torch.from_numpy(qc.residuals(1)).to(dev)
         wsq1 = qwt.workspace(1, qc.k)
         turn = [0]
@@ -396,13 +535,51 @@ def main() -> int:
             return qwts[turn[0] % 4].logits_topk(Rq1, qc.k, workspace=wsq1, events=evs)
         for _ in range(4):
             fq()
-        mql, kql = _timed(torch, fq, 52, events=hev)
-        also["qwen05b_logits_top10_B1"] = {
-            "us_per_call": round(mql * 1e3, 1), "kernel_us": round(kql * 1e3, 1),
-            "GBps": round(qc.table_bytes / (mql * 1e-3) / 1e9, 1),
-            "pct_hbm_peak": round(100 * qc.table_bytes / (mql * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
-            "tables": "4 copies, cycled"}
-        log(f"qwen05b gather {mqg * 1e3:.1f} us, logits B=1 {mql * 1e3:.1f} us")
+        d = _dist(torch, fq, 52, hev, kernel=True)
+        d["GBps"] = round(qc.table_bytes / (d["median_us"] * 1e-6) / 1e9, 1)
+        d["pct_hbm_peak"] = round(100 * d["GBps"] / HBM_PEAK_GBPS, 1)
+        d["kernel_pct_hbm_peak"] = round(100 * qc.table_bytes / (d["kernel_median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)
+        d["single_call_us"] = _single(torch, fq)
+        d["tables"] = "4 copies, cycled"
+        also["qwen05b_logits_top10_B1"] = d
+        log(f"qwen05b gather {also['qwen05b_gather_628_zipf_ids']['median_us']} us, logits B=1 {d['median_us']} us")
+        # the same calls from host ids / to a host answer, eager beside graph-cached
+        ss = torch.cuda.Stream()
+        with torch.cuda.stream(ss):
+            qids_h = torch.from_numpy(qids_host).pin_memory()
+            qids_d = torch.empty_like(qids_h, device=dev)
+
+            def eager_gather():
+                qids_d.copy_(qids_h, non_blocking=True)
+                return qwt.embed_gather(qids_d, out=qx, check=False)
+            qids_np = qids_h.numpy()
+            hoq = (torch.empty((1, qc.k), dtype=torch.int32, pin_memory=True),
+                   torch.empty((1, qc.k), dtype=torch.float32, pin_memory=True))
+
+            def eager_logits():
+                turn[0] += 1
+                return qwts[turn[0] % 4].logits_topk_to_host(Rq1, qc.k, workspace=wsq1, host_out=hoq)
+            dq = {"plain_calls_with_copies": _dist(torch, eager_gather, 50, hev)}
+            dl = {"plain_calls_with_copies": _dist(torch, eager_logits, 52, hev)}
+            dl["plain_calls_with_copies"]["single_call_us"] = _single(torch, lambda: eager_logits()[2].synchronize())
+            for name, use_graphs in (("step_eager", False), ("step_graph_cached", True)):
+                scq = [etg.StepCache(tq, max_ids=qids_h.numel(), max_batch=1, k=qc.k, use_graphs=use_graphs)
+                       for tq in qwts]
+                for sq in scq:
+                    sq.residual.copy_(Rq1)
+                dq[name] = _dist(torch, lambda: scq[0].gather(qids_np), 50, hev)
+
+                def step_logits():
+                    turn[0] += 1
+                    return scq[turn[0] % 4].logits(1)
+                dl[name] = _dist(torch, step_logits, 52, hev)
+                dl[name]["single_call_us"] = _single(torch, lambda: step_logits().synchronize())
+                del scq
+            dq["graph_bucket_rows"] = 640
+            dl["tables"] = "4 copies, cycled"
+            also["qwen05b_step_gather_628_host_ids"] = dq
+            also["qwen05b_step_logits_top10_B1_to_host"] = dl
+            log(f"qwen05b step gather {dq}, logits {dl}")
         del qwt, qwts
         torch.cuda.empty_cache()
 
@@ -413,45 +590,44 @@ def main() -> int:
         gids = torch.from_numpy(gids_host).to(dev)
         gx = torch.empty((gids.numel(), g.d), dtype=torch.float32, device=dev)
         f = lambda: gt.embed_gather(gids, scale="sqrt_d", out=gx, check=False)
-        f()
-        mg, _ = _timed(torch, f, 100)
+        for _ in range(5):
+            f()
+        d = _dist(torch, f, 100, hev)
         U = int(np.unique(gids_host).size)
         alg = U * g.row_bytes + gids.numel() * g.d * 4 + gids.numel() * 4
-        also["gemma_embed_gather_q8_0_x_sqrt_d"] = {
-            "rows": int(gids.numel()), "distinct_rows": U, "us_per_call": round(mg * 1e3, 2),
-            "rows_per_s": round(gids.numel() / (mg * 1e-3)), "alg_GBps": round(alg / (mg * 1e-3) / 1e9, 1)}
-        out["gather_rows_per_s"] = also["gemma_embed_gather_q8_0_x_sqrt_d"]["rows_per_s"]
-        log(f"gather: {mg * 1e3:.1f} us")
+        wref50 = also.get("write_stream_reference", {}).get("50MB", {}).get("us_per_call")
+        d.update({"rows": int(gids.numel()), "distinct_rows": U, "us_per_call": d["median_us"],
+                  "rows_per_s": round(gids.numel() / (d["median_us"] * 1e-6)),
+                  "alg_GBps": round(alg / (d["median_us"] * 1e-6) / 1e9, 1),
+                  "pct_of_write_stream_50MB": round(100 * wref50 / d["median_us"], 1) if wref50 else None})
+        also["gemma_embed_gather_q8_0_x_sqrt_d"] = d
+        out["gather_rows_per_s"] = d["rows_per_s"]
+        log(f"gather: {d['median_us']} us")
         # the same gather with its output in the f16 and i8 residual wire formats
         for wname, wire in (("f16", etg.WIRE_F16), ("i8", etg.WIRE_I8)):
             wb = torch.empty((gids.numel(), etg.wire_row_bytes(wire, g.d)), dtype=torch.uint8, device=dev)
             f = lambda: gt.embed_gather_wire(gids, wire, scale="sqrt_d", out=wb)
             f()
-            mw, _ = _timed(torch, f, 100)
+            d = _dist(torch, f, 100, hev)
             algw = U * g.row_bytes + gids.numel() * wb.shape[1] + gids.numel() * 4
-            also[f"gemma_embed_gather_q8_0_x_sqrt_d_{wname}_wire"] = {
-                "us_per_call": round(mw * 1e3, 2), "rows_per_s": round(gids.numel() / (mw * 1e-3)),
-                "bytes_per_row_out": int(wb.shape[1]), "alg_GBps": round(algw / (mw * 1e-3) / 1e9, 1)}
+            d.update({"rows_per_s": round(gids.numel() / (d["median_us"] * 1e-6)), "bytes_per_row_out": int(wb.shape[1]),
+                      "alg_GBps": round(algw / (d["median_us"] * 1e-6) / 1e9, 1)})
+            also[f"gemma_embed_gather_q8_0_x_sqrt_d_{wname}_wire"] = d
             del wb
         del gt
         torch.cuda.empty_cache()
 
-        # the Q8_0 lm_head (31B-shaped, 1.50 GB): the q8 stream path
+        # the Q8_0 lm_head (31B-shaped, 1.50 GB)
         q = synth.CONFIGS["lm31b_q8"]
         qh = q.table()
         qt = etg.Table(torch.from_numpy(qh).to(dev), q.dtype, q.V, q.d)
         del qh
         for b in q.batches:
             Rq = torch.from_numpy(q.residuals(b)).to(dev)
-            wsq = qt.workspace(b, q.k)
-            f = lambda evs=None: qt.logits_topk(Rq, q.k, workspace=wsq, events=evs)
-            f()
-            mq8, kq8 = _timed(torch, f, 20, events=hev)
-            also[f"lm31b_q8_0_logits_top10_B{b}"] = {
-                "us_per_call": round(mq8 * 1e3, 1), "kernel_us": round(kq8 * 1e3, 1),
-                "GBps": round(q.table_bytes / (mq8 * 1e-3) / 1e9, 1),
-                "pct_hbm_peak": round(100 * q.table_bytes / (mq8 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
-            log(f"q8_0 B={b}: {mq8 * 1e3:.1f} us")
+            d = logits_entry(qt, Rq, q.k, etg.PATH_AUTO, q.table_bytes)
+            d["kernel_pct_hbm_peak"] = round(100 * q.table_bytes / (d["kernel_median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)
+            also[f"lm31b_q8_0_logits_top10_B{b}"] = d
+            log(f"q8_0 B={b}: {d['median_us']} us")
         del qt
         torch.cuda.empty_cache()
 
@@ -470,12 +646,12 @@ def main() -> int:
             f = lambda evs=None: pt.logits_topk(Rp, p.k, path=path, workspace=wsp, events=evs)
             for _ in range(5):  # the clocks settle over the first calls of this contraction
                 f()
-            mp, kp = _timed(torch, f, 10, events=hev)
-            also[key] = {
-                "ms_per_call": round(mp, 3), "kernel_ms": round(kp, 3),
-                "TFLOPs": round(flops / (mp * 1e-3) / 1e12, 1),
-                "pct_bf16_mfma_peak": round(100 * flops / (mp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1)}
-            log(f"prefill B=1024 path={path}: {mp:.2f} ms")
+            d = _dist(torch, f, 20, hev, kernel=True)
+            d.update({"ms_per_call": round(d["median_us"] * 1e-3, 3), "kernel_ms": round(d["kernel_median_us"] * 1e-3, 3),
+                      "TFLOPs": round(flops / (d["median_us"] * 1e-6) / 1e12, 1),
+                      "pct_bf16_mfma_peak": round(100 * flops / (d["median_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 1)})
+            also[key] = d
+            log(f"prefill B=1024 path={path}: {d['ms_per_call']} ms")
         del pt
         torch.cuda.empty_cache()
     if also:
@@ -504,6 +680,7 @@ def main() -> int:
             "value": round(cfg.table_bytes * reps / t_cpu / 1e9, 3),
             "unit": "GB/s",
             "cores": oracle.max_threads(),
+            "cpu_model": _cpu_model(),
             "kind": "oracle",
             "sample": f"{reps} full pass(es) of logits+top-10 for 1 residual over the "
                       f"262,144 x 5,376 bf16 table (f64 accumulation), {t_cpu:.1f} s",

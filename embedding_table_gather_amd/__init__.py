@@ -55,7 +55,16 @@ SIGNATURES = {
     "etg_logits_topk_to_host": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP, ctypes.c_size_t, _I32, _VP, _VP, _VP,
                                        _VP]),
     "etg_hbm_read_probe": (_I32, [_VP, _I64, _VP, _VP]),
+    "etg_hbm_write_probe": (_I32, [_VP, _I64, ctypes.c_uint32, _VP]),
     "etg_logits_topk_noalloc": (_I32, [_VP, _VP, _I64, _I32, _VP, _VP, _VP]),
+    "etg_step_cache_ids_capacity": (_I64, [_I64]),
+    "etg_step_cache_workspace": (_I64, [_VP, _I64, _I32]),
+    "etg_step_cache_create": (_I32, [_VP, _I64, _I64, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP,
+                                     _VP, _VP, ctypes.POINTER(_VP)]),
+    "etg_step_cache_destroy": (_I32, [_VP]),
+    "etg_step_cache_stats": (_I32, [_VP, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "etg_step_gather": (_I32, [_VP, _VP, _I64, _F, _VP]),
+    "etg_step_logits": (_I32, [_VP, _I64, _VP, _VP]),
     "etg_last_error": (ctypes.c_char_p, []),
 }
 
@@ -356,6 +365,82 @@ class Table:
         return out
 
 
+class StepCache:
+    """Embed and logits calls for small repeated shapes from host ids to a host
+    answer: the kernels read the ids from, and write the top-k answer to, mapped
+    page-locked memory (no copy operations), the answer tracked by an event.  With
+    use_graphs=True each configuration (token counts bucketed to multiples of 64 or
+    256) is captured into a HIP graph on its second hit and replayed after; on this
+    platform a graph launch measured slower than the two to four kernel launches it
+    replaces, so calls run eagerly by default.
+
+    Owns its buffers as tensors and lends them to the library:
+      rows      device f32 [ids capacity, hidden]: the gathered rows
+      residual  device f32 [max_batch, hidden]: write the residual rows here
+      ids, scores  page-locked CPU [max_batch, k]: the answer after event.synchronize()
+    """
+
+    STEP_ID_SLOTS = 4  # ETG_STEP_ID_SLOTS
+
+    def __init__(self, table: Table, max_ids: int, max_batch: int, k: int, use_graphs: bool = False):
+        L = lib()
+        self.table, self.k, self.max_ids, self.max_batch = table, int(k), int(max_ids), int(max_batch)
+        dev = table.device
+        cap = int(L.etg_step_cache_ids_capacity(int(max_ids)))
+        if cap < 0:
+            raise ValueError(f"max_ids {max_ids} out of range")
+        ws = int(L.etg_step_cache_workspace(table.handle, int(max_batch), int(k)))
+        if ws < 0:
+            _check(ws)
+        self.d_ids = torch.zeros(cap, dtype=torch.int32, device=dev)
+        self.rows = torch.empty((cap, table.hidden), dtype=torch.float32, device=dev)
+        self.residual = torch.zeros((int(max_batch), table.hidden), dtype=torch.float32, device=dev)
+        self.d_topk_ids = torch.empty((int(max_batch), int(k)), dtype=torch.int32, device=dev)
+        self.d_topk_scores = torch.empty((int(max_batch), int(k)), dtype=torch.float32, device=dev)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.h_ids = torch.zeros((self.STEP_ID_SLOTS, cap), dtype=torch.int32, pin_memory=True)
+        self.ids = torch.zeros((int(max_batch), int(k)), dtype=torch.int32, pin_memory=True)
+        self.scores = torch.zeros((int(max_batch), int(k)), dtype=torch.float32, pin_memory=True)
+        h = ctypes.c_void_p()
+        _check(L.etg_step_cache_create(table.handle, int(max_ids), int(max_batch), int(k), int(bool(use_graphs)),
+                                       _ptr(self.d_ids),
+                                       _ptr(self.rows), _ptr(self.residual), _ptr(self.d_topk_ids),
+                                       _ptr(self.d_topk_scores), _ptr(self.workspace), self.workspace.numel(),
+                                       _ptr(self.h_ids), _ptr(self.ids), _ptr(self.scores), ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.etg_step_cache_destroy(h)
+            self._h = None
+
+    def gather(self, ids, scale=None) -> torch.Tensor:
+        """Rows for host int32 ids (a CPU tensor or array of n ids): a view of the
+        first n rows of ``rows``, filled in stream order."""
+        import numpy as np
+        a = np.ascontiguousarray(ids.numpy() if isinstance(ids, torch.Tensor) else ids, dtype=np.int32).reshape(-1)
+        sc = 1.0 if scale is None else (sqrt_d(self.table.hidden) if scale == "sqrt_d" else float(scale))
+        with torch.cuda.device(self.table.device):
+            _check(lib().etg_step_gather(self._h, a.ctypes.data_as(ctypes.c_void_p), a.size, sc,
+                                         _stream_ptr(self.table.device)))
+        return self.rows[:a.size]
+
+    def logits(self, batch: int, event=None):
+        """Top-k of residual rows [0, batch) into the page-locked ``ids`` / ``scores``;
+        returns the event recorded after the copy (wait on it before reading)."""
+        ev = event if event is not None else torch.cuda.Event()
+        with torch.cuda.device(self.table.device):
+            evh = ctypes.c_void_p(_event_handle(ev, self.table.device))
+            _check(lib().etg_step_logits(self._h, int(batch), evh, _stream_ptr(self.table.device)))
+        return ev
+
+    def stats(self):
+        g, r = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().etg_step_cache_stats(self._h, ctypes.byref(g), ctypes.byref(r)))
+        return g.value, r.value
+
+
 def hbm_read_probe(t: torch.Tensor, sink: torch.Tensor | None = None) -> None:
     """Enqueue a plain read stream of the bytes of a contiguous device tensor (a
     multiple of 16 bytes) on the current stream: the measured HBM read reference."""
@@ -365,6 +450,16 @@ def hbm_read_probe(t: torch.Tensor, sink: torch.Tensor | None = None) -> None:
         sink = torch.empty(1, dtype=torch.int32, device=t.device)
     _check(lib().etg_hbm_read_probe(t.data_ptr(), t.numel() * t.element_size(), sink.data_ptr(),
                                     torch.cuda.current_stream(t.device).cuda_stream))
+
+
+def hbm_write_probe(t: torch.Tensor, value: int = 0) -> None:
+    """Enqueue a plain write stream over the bytes of a contiguous device tensor (a
+    multiple of 16 bytes), every 32-bit word set to `value`, on the current stream:
+    the measured HBM write reference."""
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("a contiguous device tensor is required")
+    _check(lib().etg_hbm_write_probe(t.data_ptr(), t.numel() * t.element_size(), int(value) & 0xFFFFFFFF,
+                                     torch.cuda.current_stream(t.device).cuda_stream))
 
 
 def wire_row_bytes(wire: int, hidden: int) -> int:

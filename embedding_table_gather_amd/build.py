@@ -12,7 +12,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libetg.so")
 SOURCES = ["etg_api.cpp", "gather.hip", "logits.hip", "stream.hip", "wide.hip", "gemm.hip", "rank.hip", "q8.hip",
            "row.hip", "probe.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "step.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

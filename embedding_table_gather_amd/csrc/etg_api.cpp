@@ -11,9 +11,6 @@
 
 #include "etg_internal.hpp"
 
-struct etg_table {
-  etg::TableDesc d;
-};
 
 namespace {
 
@@ -297,6 +294,16 @@ int32_t etg_hbm_read_probe(const void* d_src, int64_t bytes, uint32_t* d_sink, v
                                                  (long long)bytes);
   hipError_t e = etg::launch_read_probe(d_src, bytes, d_sink, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ETG_EHIP, "read probe launch failed: %s", hipGetErrorString(e));
+  return ETG_OK;
+}
+
+int32_t etg_hbm_write_probe(void* d_dst, int64_t bytes, uint32_t value, void* stream) {
+  if (d_dst == nullptr) return fail(ETG_EINVAL, "destination pointer is NULL");
+  if (!aligned(d_dst, 16)) return fail(ETG_EALIGN, "destination pointer is not 16-byte aligned");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(ETG_ESHAPE, "bytes %lld is not a positive multiple of 16",
+                                                 (long long)bytes);
+  hipError_t e = etg::launch_write_probe(d_dst, bytes, value, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ETG_EHIP, "write probe launch failed: %s", hipGetErrorString(e));
   return ETG_OK;
 }
 

@@ -173,9 +173,17 @@ hipError_t launch_rank_norm(const float* npart, int ngrp, int64_t V, float* nrm2
 // Plain read stream of bytes (a multiple of 16) at src (16-byte aligned); sink
 // (4 bytes) is written only if the XOR of the data equals a fixed word (probe.hip).
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+// Plain write stream: every 32-bit word of bytes (a multiple of 16) at dst
+// (16-byte aligned) is set to value (probe.hip).
+hipError_t launch_write_probe(void* dst, int64_t bytes, uint32_t value, hipStream_t stream);
 size_t rescore_lds(int64_t hidden, int n, int nvr, int k, int64_t batch);
 hipError_t launch_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* rs, uint64_t* cand,
                        const LogitsExtras& x, int32_t* ids, float* scores, hipStream_t stream, hipEvent_t ev0,
                        hipEvent_t ev1);
 
 }  // namespace etg
+
+// The opaque handle of etg.h: host metadata of a table in device memory.
+struct etg_table {
+  etg::TableDesc d;
+};

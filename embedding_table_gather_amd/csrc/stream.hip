@@ -48,38 +48,55 @@ static constexpr int kStreamMaxPairs = 4;  // a wave handles at most 8 groups (6
 // Fill LDS with steps [c0, c0 + n) of the bf16 hi/lo operand image, converted from
 // the residual rows of this pass (f32, or decoded from their wire format).  Image slot (s, im, lane) holds the 8
 // values of B column n = lane % 16, K-group g = lane / 16 (layout above).
-template <int NIMG>
-__device__ __forceinline__ void stream_stage_image(u32x4* simg, const void* __restrict__ R, int wire, int64_t B,
-                                                   int hidden, int64_t b0, int c0, int n) {
+// WIRE is the residual rows' wire format, fixed per kernel instance so that no
+// value is read behind a branch on the format (such branches serialise the loads).
+template <int NIMG, int WIRE>
+__device__ __forceinline__ void stream_stage_image(u32x4* simg, const void* __restrict__ R, int64_t B, int hidden,
+                                                   int64_t b0, int c0, int n) {
   constexpr int NBC = NIMG == 1 ? 4 : 8;
-  for (int i = threadIdx.x; i < n * NIMG * 64; i += blockDim.x) {
-    const int lane = i & 63;
-    const int q = i >> 6;
-    const int im = q % NIMG;
-    const int s = c0 + q / NIMG;
-    const int nn = lane & 15, g = lane >> 4;
-    const int h = nn >> 3, j8 = nn & 7;
-    const int part = NIMG == 1 ? j8 / NBC : im;
-    const int64_t b = b0 + j8 % NBC;
-    const int cbase = 64 * s + 16 * g + 8 * h;
-    float x[8];
-    if constexpr (NIMG == 2) {
-      residual_values8(R, wire, B, b, hidden, cbase, x);
-    } else {  // value by value: the vector loads cost the one-image kernel a register spill
+  // slots per thread per round, their loads all issued before any conversion (fewer in
+  // the one-image kernel, whose K loop sits at the 128-register line of its workgroup)
+  constexpr int SU = NIMG == 1 ? 2 : 4;
+  const int total = n * NIMG * 64;
+  for (int i0 = threadIdx.x; i0 < total; i0 += SU * blockDim.x) {
+    float x[SU][8];
+    int part[SU];
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const int c = cbase + e;
-        x[e] = (b < B && c < hidden) ? residual_value(R, wire, b, hidden, c) : 0.0f;
+    for (int u = 0; u < SU; u++) {
+      const int i = i0 + u * blockDim.x;
+      const int lane = i & 63;
+      const int q = i >> 6;
+      const int im = q % NIMG;
+      const int s = c0 + q / NIMG;
+      const int nn = lane & 15, g = lane >> 4;
+      const int h = nn >> 3, j8 = nn & 7;
+      part[u] = NIMG == 1 ? j8 / NBC : im;
+      const int64_t b = b0 + j8 % NBC;
+      const int cbase = 64 * s + 16 * g + 8 * h;
+      const bool live = i < total && b < B;
+      if constexpr (NIMG == 2) {
+        residual_values8(R, WIRE, live ? B : 0, b, hidden, cbase, x[u]);
+      } else {  // value by value: vector loads cost the one-image kernel a register spill
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int c = cbase + e;
+          x[u][e] = (live && c < hidden) ? residual_value(R, WIRE, b, hidden, c) : 0.0f;
+        }
       }
     }
-    uint32_t v[8];
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      const uint32_t hi = bf16_rne(x[e]);
-      // part 1 carries the remainder x - hi (exact in f32), rounded to bf16
-      v[e] = part == 1 ? bf16_rne(x[e] - __uint_as_float(hi << 16)) : hi;
+    for (int u = 0; u < SU; u++) {
+      const int i = i0 + u * blockDim.x;
+      if (i >= total) break;
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const uint32_t hi = bf16_rne(x[u][e]);
+        // part 1 carries the remainder x - hi (exact in f32), rounded to bf16
+        v[e] = part[u] == 1 ? bf16_rne(x[u][e] - __uint_as_float(hi << 16)) : hi;
+      }
+      simg[i] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
     }
-    simg[i] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
   }
 }
 
@@ -124,6 +141,87 @@ __device__ void stream_block_topk(const float* slog, const int64_t* sg0, const i
   }
 }
 
+// The k best keys of this block for each of its nb residual columns, for k up to
+// kStreamWaves, by threshold: each wave takes the largest logit of its rows per
+// column; T, the k-th largest of those wave maxima, is a lower bound on the
+// column's k-th largest logit (the k waves reaching T each hold a row of their
+// own at or above it).  Only the logits >= T (k to a few k of them) are keyed into
+// an LDS list, and each listed key is written to the slot of its rank among them
+// (keys are unique).  Returns false, having written nothing, when a list would
+// hold more than kStreamThrCap keys (ties, or blocks with fewer than k waves of
+// rows); the caller then selects by rounds.  Called by every thread of the block.
+static constexpr int kStreamThrCap = 32;
+
+template <int NBC>
+__device__ bool stream_block_topk_thr(const float* slog, const int64_t* sg0, const int* sng, int nb, int max_groups,
+                                      int64_t V, int k, int64_t b0, uint64_t* __restrict__ cand) {
+  __shared__ uint32_t smax[NBC][kStreamWaves];
+  __shared__ uint32_t sthr[NBC];
+  __shared__ uint32_t scnt[NBC];
+  __shared__ uint64_t slist[NBC][kStreamThrCap];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per_wave = max_groups * 8;
+  const int64_t row = sg0[wv] * 8 + lane;
+  const bool ok = lane < sng[wv] * 8 && row < V;
+  uint32_t o[NBC], m[NBC];
+#pragma unroll
+  for (int b = 0; b < NBC; b++) {
+    o[b] = (ok && b < nb) ? score_ord(slog[(wv * per_wave + lane) * NBC + b]) : 0u;
+    m[b] = o[b];
+  }
+  wave_minmax_u32_multi<true>(m);
+  if (lane == 0) {
+#pragma unroll
+    for (int b = 0; b < NBC; b++) smax[b][wv] = m[b];
+  }
+  if (tid < NBC) scnt[tid] = 0;
+  __syncthreads();
+  if (tid < nb) {
+    // the k-th largest of the wave maxima: insertion into a descending list
+    uint32_t t[kStreamWaves];
+#pragma unroll
+    for (int j = 0; j < kStreamWaves; j++) t[j] = 0u;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; w++) {
+      uint32_t x = smax[tid][w];
+#pragma unroll
+      for (int j = 0; j < kStreamWaves; j++) {
+        const uint32_t hi = max(t[j], x);
+        x = min(t[j], x);
+        t[j] = hi;
+      }
+    }
+    uint32_t thr = t[0];
+#pragma unroll
+    for (int j = 1; j < kStreamWaves; j++) thr = j == k - 1 ? t[j] : thr;
+    sthr[tid] = thr;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NBC; b++) {
+    if (b < nb && ok && o[b] >= sthr[b]) {
+      const uint32_t slot = atomicAdd(&scnt[b], 1u);
+      if (slot < (uint32_t)kStreamThrCap) slist[b][slot] = ((uint64_t)o[b] << 32) | (uint64_t)(~(uint32_t)row);
+    }
+  }
+  __syncthreads();
+  bool over = false;
+  for (int b = 0; b < nb; b++) over |= scnt[b] > (uint32_t)kStreamThrCap;
+  if (over) return false;
+  if (wv < nb) {
+    const int c = (int)scnt[wv];
+    uint64_t* out = cand + ((b0 + wv) * gridDim.x + blockIdx.x) * (int64_t)k;
+    if (lane < c) {
+      const uint64_t key = slist[wv][lane];
+      int rank = 0;
+      for (int j = 0; j < c; j++) rank += slist[wv][j] > key ? 1 : 0;
+      if (rank < k) out[rank] = key;
+    }
+    for (int t = c + lane; t < k; t += 64) out[t] = 0;  // fewer than k rows in the block
+  }
+  return true;
+}
+
 // After the K loop: the block's logits are in slog ([wave][row][NBC], the wave's
 // rows from group sg0[wave], sng[wave] groups; written and synchronised).  Raw
 // logits, the per-block top-k candidates of each residual column and the
@@ -145,10 +243,13 @@ __device__ __forceinline__ void stream_epilogue(const float* slog, const int64_t
       }
     }
   }
-  if (wv < NBC && b0 + wv < B) {
+  const int nb = (int)min((int64_t)NBC, B - b0);
+  const bool done = k <= kStreamWaves && stream_block_topk_thr<NBC>(slog, sg0, sng, nb, max_groups, V, k, b0, cand);
+  if (!done && wv < nb) {
     uint64_t* out = cand + ((b0 + wv) * gridDim.x + blockIdx.x) * (int64_t)k;
     stream_block_topk<NBC>(slog, sg0, sng, wv, lane, max_groups, V, k, out);
-  } else if (lse != nullptr && wv >= NBC && wv < 2 * NBC && b0 + (wv - NBC) < B) {
+  }
+  if (lse != nullptr && wv >= NBC && wv < 2 * NBC && b0 + (wv - NBC) < B) {
     // waves NBC .. 2 NBC - 1: log-partition partial of column wv - NBC over the
     // block's rows (lane holds row lane of every wave's run, as in the top-k)
     const int b = wv - NBC, per_wave = max_groups * 8;
@@ -175,10 +276,10 @@ __device__ __forceinline__ void stream_epilogue(const float* slog, const int64_t
 // Out-of-range rows and K positions are read from clamped in-range addresses and
 // meet zero residual values or are never ranked, so no load is predicated (table
 // entries are assumed finite).
-template <int NIMG>
+template <int NIMG, int WIRE>
 __global__ void __launch_bounds__(1024) stream_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, int hidden,
-    const void* __restrict__ R, int wire, int64_t B, int steps, int chunk, int k, uint64_t* __restrict__ cand,
+    const void* __restrict__ R, int64_t B, int steps, int chunk, int k, uint64_t* __restrict__ cand,
     int64_t ngroups, int max_groups, float* __restrict__ logits, float2* __restrict__ lse, float lse_c) {
   constexpr int NBC = NIMG == 1 ? 4 : 8;
   constexpr int U = NIMG == 1 ? kStreamUnroll : kStreamUnroll / 2;
@@ -191,15 +292,16 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t b0 = (int64_t)blockIdx.y * NBC;
 
-  // Waves own contiguous runs of group pairs (16 rows); only the last pair of the
-  // table can be half empty.
+  // Waves own contiguous runs of 8-row groups, as even as the group count allows
+  // (on a table of 151,936 rows: 4 or 5 groups per wave; runs of whole 16-row
+  // pairs would leave some waves 3 pairs against an average of 2.3).  A run is
+  // taken in pairs; an odd run ends with a half pair whose second group reloads
+  // the first group's rows (cache hits) and is never stored.
   const int64_t nw = (int64_t)gridDim.x * kStreamWaves;
   const int64_t gw = (int64_t)blockIdx.x * kStreamWaves + wv;
-  const int64_t npairs_all = (ngroups + 1) >> 1;
-  const int64_t pb = gw * npairs_all / nw;
-  const int npairs = (int)((gw + 1) * npairs_all / nw - pb);
-  const int64_t g_begin = 2 * pb;
-  const int ng = (int)min((int64_t)(2 * npairs), ngroups - g_begin);
+  const int64_t g_begin = gw * ngroups / nw;
+  const int ng = (int)((gw + 1) * ngroups / nw - g_begin);
+  const int npairs = (ng + 1) >> 1;
   if (lane == 0) {
     sg0[wv] = g_begin;
     sng[wv] = ng;
@@ -214,13 +316,13 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
   for (int c0 = 0; c0 < steps; c0 += chunk) {
     const int c1 = min(steps, c0 + chunk);
     if (c0 > 0) __syncthreads();  // every wave is done with the previous chunk
-    stream_stage_image<NIMG>(simg, R, wire, B, hidden, b0, c0, c1 - c0);
+    stream_stage_image<NIMG, WIRE>(simg, R, B, hidden, b0, c0, c1 - c0);
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kStreamMaxPairs; p++) {
       if (p < npairs) {
         const int64_t row0 = min((g_begin + 2 * p) * 8 + r, V - 1);
-        const int64_t row1 = min((g_begin + 2 * p) * 8 + 8 + r, V - 1);
+        const int64_t row1 = 2 * p + 1 < ng ? min((g_begin + 2 * p) * 8 + 8 + r, V - 1) : row0;
         const uint8_t* p0 = table + (uint64_t)row0 * (uint64_t)row_bytes;
         const uint8_t* p1 = table + (uint64_t)row1 * (uint64_t)row_bytes;
         const u32x4* q0 = (const u32x4*)(p0 + 16 * ck);
@@ -280,23 +382,33 @@ __global__ void __launch_bounds__(1024) stream_logits_kernel(
 }
 
 
-template <int NIMG>
+template <int NIMG, int WIRE>
 static hipError_t launch_stream_nimg(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
                                      const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  hipError_t e = set_dynamic_lds((const void*)stream_logits_kernel<NIMG>, p.lds_bytes);
+  hipError_t e = set_dynamic_lds((const void*)stream_logits_kernel<NIMG, WIRE>, p.lds_bytes);
   if (e != hipSuccess) return e;
   if ((e = record_event(ev0, stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL((stream_logits_kernel<NIMG>), dim3((unsigned)p.nblk, (unsigned)p.npass),
+  hipLaunchKernelGGL((stream_logits_kernel<NIMG, WIRE>), dim3((unsigned)p.nblk, (unsigned)p.npass),
                      dim3(64 * kStreamWaves), p.lds_bytes, stream, t.rows, t.V, t.row_bytes, (int)t.hidden, R,
-                     (int)x.wire, p.batch, p.steps, p.chunk, p.k, cand, p.ngroups, p.max_groups, x.logits, x.lse, x.lse_scale);
+                     p.batch, p.steps, p.chunk, p.k, cand, p.ngroups, p.max_groups, x.logits, x.lse, x.lse_scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(ev1, stream);
 }
 
+template <int NIMG>
+static hipError_t launch_stream_wire(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
+                                     const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  switch (x.wire) {
+    case WIRE_F16: return launch_stream_nimg<NIMG, WIRE_F16>(t, p, R, cand, x, stream, ev0, ev1);
+    case WIRE_I8: return launch_stream_nimg<NIMG, WIRE_I8>(t, p, R, cand, x, stream, ev0, ev1);
+    default: return launch_stream_nimg<NIMG, WIRE_F32>(t, p, R, cand, x, stream, ev0, ev1);
+  }
+}
+
 hipError_t launch_stream(const TableDesc& t, const LogitsPlan& p, const void* R, uint64_t* cand,
                          const LogitsExtras& x, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  return p.nimg == 1 ? launch_stream_nimg<1>(t, p, R, cand, x, stream, ev0, ev1)
-                     : launch_stream_nimg<2>(t, p, R, cand, x, stream, ev0, ev1);
+  return p.nimg == 1 ? launch_stream_wire<1>(t, p, R, cand, x, stream, ev0, ev1)
+                     : launch_stream_wire<2>(t, p, R, cand, x, stream, ev0, ev1);
 }
 
 // ---------------------------------------------------------------------------
@@ -538,13 +650,13 @@ int32_t plan_stream(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p,
     p->steps = (int32_t)cdiv(t.hidden, 64);
     p->ngroups = cdiv(t.V, 8);
     p->npass = (int32_t)cdiv(batch, p->nbc);
-    // one block per CU, unless a wave would then own more than kStreamMaxPairs pairs
-    const int64_t npairs_all = cdiv(p->ngroups, 2);
-    p->nblk = (int32_t)std::max<int64_t>(cdiv(npairs_all, (int64_t)kStreamWaves * kStreamMaxPairs),
-                                         std::min<int64_t>(kTargetBlocks, cdiv(npairs_all, kStreamWaves)));
-    p->max_groups = (int32_t)(2 * cdiv(npairs_all, (int64_t)p->nblk * kStreamWaves));
+    // one block per CU, unless a wave would then own more than 2 kStreamMaxPairs
+    // groups; fewer blocks for tables of under a pair per wave
+    p->nblk = (int32_t)std::max<int64_t>(cdiv(p->ngroups, (int64_t)kStreamWaves * 2 * kStreamMaxPairs),
+                                         std::min<int64_t>(kTargetBlocks, cdiv(p->ngroups, 2 * kStreamWaves)));
+    p->max_groups = (int32_t)cdiv(p->ngroups, (int64_t)p->nblk * kStreamWaves);
     const size_t log_bytes = (size_t)kStreamWaves * p->max_groups * 8 * p->nbc * 4;
-    const size_t img_room = kMaxLds - 1024 - log_bytes;
+    const size_t img_room = kMaxLds - 4096 - log_bytes;  // static LDS: wave runs and the threshold selection
     const int64_t max_chunk = (int64_t)(img_room / ((size_t)p->nimg * 1024)) / kStreamUnroll * kStreamUnroll;
     // equal chunks (multiples of the unroll), as few as fit
     const int64_t nchunks = cdiv(p->steps, max_chunk);

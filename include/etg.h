@@ -306,6 +306,82 @@ int32_t etg_logits_topk_wire(const etg_table* lm_head, const void* d_residual, i
 int32_t etg_hbm_read_probe(const void* d_src, int64_t bytes, uint32_t* d_sink, void* stream);
 
 /*
+ * Graph-cached endpoint calls for small, repeated shapes (the serving pattern of
+ * the Perplexity blog "Fast embeddings on GPUs", section "Tulip": one GPU graph per
+ * shape configuration, token counts padded to buckets that are multiples of 64 or
+ * 256, captured lazily -- the first hit of a configuration runs eagerly, the
+ * second is captured and replayed, later hits replay -- and the answer tracked as
+ * a page-locked host buffer behind an event, its lazy result tensors).
+ *
+ * A step cache binds one table to caller-owned buffers at fixed addresses, which
+ * the captured graphs read and write:
+ *   d_ids         int32 [etg_step_cache_ids_capacity(max_ids)], device
+ *   d_rows        f32 [ids capacity][hidden], device, 16-byte aligned: gathered rows
+ *   d_residual    f32 [max_batch][hidden], device: the residual rows the caller
+ *                 writes before etg_step_logits (rows 0 .. batch - 1 are read)
+ *   d_topk_ids, d_topk_scores  [max_batch][k], device
+ *   d_workspace   etg_step_cache_workspace(table, max_batch, k) bytes, 256-aligned
+ *   h_ids         int32 [ETG_STEP_ID_SLOTS][ids capacity], page-locked host memory
+ *                 (hipHostMalloc): a ring of id staging slots, one per call in turn;
+ *                 a slot is rewritten only after the gather that last read it has
+ *                 run (the call waits on the host for that if needed)
+ *   h_topk_ids, h_topk_scores  [max_batch][k], page-locked host memory: the answer
+ * All are borrowed and must outlive the cache, as must the table rows (the cache
+ * copies the table handle's metadata).  Page-locked buffers mapped into the
+ * device's address space (hipHostGetDevicePointer succeeds, as for hipHostMalloc
+ * memory on this platform) are read and written by the kernels directly, so a call
+ * is kernels only; otherwise the ids and the answer are copied with async memcpys
+ * (d_ids, d_topk_ids, d_topk_scores are those copies' device ends).
+ * use_graphs = 0 runs every call eagerly (the same work, for comparison).  A cache is not thread-safe across streams:
+ * its calls are serialised by a lock, and calls in flight on different streams
+ * share its buffers.  Work is enqueued on `stream`; a NULL stream cannot be
+ * captured, so every call on it runs eagerly.
+ *
+ * Bucketing: n token ids take a graph of round_up(n, 64) rows for n <= 1024, else
+ * round_up(n, 256); the padding ids are 0 and their rows (past row n of d_rows)
+ * are not part of the answer.  Logits graphs are keyed by the exact batch.
+ */
+typedef struct etg_step_cache etg_step_cache;
+#define ETG_STEP_ID_SLOTS 4
+
+/* Padded id capacity for max_ids ids (the bucket of max_ids); -1 if max_ids < 1. */
+int64_t etg_step_cache_ids_capacity(int64_t max_ids);
+/* Workspace bytes for every batch up to max_batch at this k (negative status on error). */
+int64_t etg_step_cache_workspace(const etg_table* table, int64_t max_batch, int32_t k);
+/* Errors: EINVAL (null), ESHAPE (max_ids, max_batch), ERANGE (k), EALIGN, EWORKSPACE. */
+int32_t etg_step_cache_create(const etg_table* table, int64_t max_ids, int64_t max_batch, int32_t k,
+                              int32_t use_graphs, int32_t* d_ids, float* d_rows, const float* d_residual, int32_t* d_topk_ids,
+                              float* d_topk_scores, void* d_workspace, size_t workspace_bytes, int32_t* h_ids,
+                              int32_t* h_topk_ids, float* h_topk_scores, etg_step_cache** out);
+/* Destroys the captured graphs and the handle (not the buffers).  NULL is accepted. */
+int32_t etg_step_cache_destroy(etg_step_cache* cache);
+/* Graphs captured so far and graph launches made (for tests and measurement). */
+int32_t etg_step_cache_stats(etg_step_cache* cache, int64_t* graphs, int64_t* replays);
+/* ADR-0008 "POST /v1/embed" on host ids: copies ids[0 .. n) into h_ids (padding
+ * ids 0 up to the bucket) in the next slot of h_ids, then, in the captured
+ * sequence, the gather of the bucket's rows into d_rows (scale as
+ * etg_embed_gather).  Bad token ids (>= vocab as uint32) are refused on the host
+ * with ETG_ERANGE, nothing enqueued.  1 <= n <= max_ids (ETG_ESHAPE). */
+int32_t etg_step_gather(etg_step_cache* cache, const int32_t* h_ids, int64_t n, float scale, void* stream);
+/* ADR-0008 "POST /v1/logits" on d_residual rows 0 .. batch - 1: top-k (as
+ * etg_logits_topk, ETG_PATH_AUTO) into h_topk_ids / h_topk_scores; `event` (a
+ * hipEvent_t the caller created, passed as void*, nullable) is recorded after it:
+ * the host buffers hold the answer once the event has completed, until the next
+ * etg_step_logits call.  1 <= batch <= max_batch. */
+int32_t etg_step_logits(etg_step_cache* cache, int64_t batch, void* event, void* stream);
+
+/*
+ * Measurement: a plain write stream of a device buffer (16-byte non-temporal
+ * stores, one contiguous range per wave written 8 KiB at a time, 16 waves per
+ * compute unit), the measured HBM write bandwidth that the gathers (whose HBM
+ * traffic is mostly their output rows) are compared with beside the nominal
+ * peak.  Sets every 32-bit word of the `bytes` at d_dst to `value`.
+ *   d_dst    device pointer, 16-byte aligned (ETG_EALIGN otherwise)
+ *   bytes    a positive multiple of 16 (ETG_ESHAPE otherwise)
+ */
+int32_t etg_hbm_write_probe(void* d_dst, int64_t bytes, uint32_t value, void* stream);
+
+/*
  * For callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  As etg_logits_topk
  * (ETG_PATH_AUTO), with the workspace taken from a library-owned device array of

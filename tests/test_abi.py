@@ -278,3 +278,40 @@ def test_noalloc_host_errors_without_launch(L, table):
     assert L.etg_logits_topk_workspace(table, big, 64) > 32 << 20
     assert f(table, p, big, 64, p, p, None) == -6
     assert "scratch" in _err(L)
+
+
+def test_write_probe_errors_without_launch(L):
+    p = ctypes.c_void_p(FAKE)
+    f = L.etg_hbm_write_probe
+    assert f(None, 1024, 0, None) == -1
+    assert f(ctypes.c_void_p(FAKE + 8), 1024, 0, None) == -4
+    assert f(p, 0, 0, None) == -3 and f(p, 1000, 0, None) == -3
+
+
+def test_step_cache_host_errors(L, table):
+    assert L.etg_step_cache_ids_capacity(1) == 64 and L.etg_step_cache_ids_capacity(64) == 64
+    assert L.etg_step_cache_ids_capacity(65) == 128 and L.etg_step_cache_ids_capacity(1024) == 1024
+    assert L.etg_step_cache_ids_capacity(1025) == 1280 and L.etg_step_cache_ids_capacity(0) == -1
+    assert L.etg_step_cache_workspace(table, 8, 10) == max(L.etg_logits_topk_workspace(table, b, 10)
+                                                            for b in range(1, 9))
+    assert L.etg_step_cache_workspace(table, 8, 0) == -5
+    p = ctypes.c_void_p(FAKE)
+    out = ctypes.c_void_p()
+    f = L.etg_step_cache_create
+    ws = L.etg_step_cache_workspace(table, 4, 5)
+    assert f(table, 10, 4, 5, 1, p, p, p, p, p, p, ws, p, p, p, None) == -1
+    assert f(table, 10, 4, 5, 1, None, p, p, p, p, p, ws, p, p, p, ctypes.byref(out)) == -1
+    assert f(table, 0, 4, 5, 1, p, p, p, p, p, p, ws, p, p, p, ctypes.byref(out)) == -3
+    assert f(table, 10, 4, 5, 1, p, p, p, p, p, p, ws - 1, p, p, p, ctypes.byref(out)) == -6
+    assert f(table, 10, 4, 5, 1, p, ctypes.c_void_p(FAKE + 4), p, p, p, p, ws, p, p, p, ctypes.byref(out)) == -4
+    assert f(table, 10, 4, 5, 1, p, p, p, p, p, p, ws, p, p, p, ctypes.byref(out)) == 0
+    c = out.value
+    import numpy as np
+    ids = np.array([1, 262144], np.int32)  # the second is past the vocabulary
+    assert L.etg_step_gather(ctypes.c_void_p(c), ids.ctypes.data_as(ctypes.c_void_p), 2, 1.0, None) == -5
+    assert "bad token id" in _err(L)
+    assert L.etg_step_gather(ctypes.c_void_p(c), ids.ctypes.data_as(ctypes.c_void_p), 11, 1.0, None) == -3
+    assert L.etg_step_logits(ctypes.c_void_p(c), 5, None, None) == -3
+    g, r = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    assert L.etg_step_cache_stats(ctypes.c_void_p(c), ctypes.byref(g), ctypes.byref(r)) == 0 and (g.value, r.value) == (0, 0)
+    assert L.etg_step_cache_destroy(ctypes.c_void_p(c)) == 0

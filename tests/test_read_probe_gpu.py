@@ -35,3 +35,16 @@ def test_probe_writes_nothing_for_other_data():
     etg.hbm_read_probe(x, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
+
+
+@pytest.mark.parametrize("nbytes", [16, 1008, 1024, 65536 + 48, 64 << 20])
+def test_write_probe_writes_every_word_and_nothing_else(nbytes):
+    # the buffer sits between two guard regions that must stay untouched
+    n = nbytes // 4
+    buf = torch.full((n + 2048,), -1, dtype=torch.int32, device="cuda")
+    x = buf[1024:1024 + n]
+    note(f"write probe {nbytes} B")
+    etg.hbm_write_probe(x, 0x12345678)
+    torch.cuda.synchronize()
+    assert torch.all(x == 0x12345678)
+    assert torch.all(buf[:1024] == -1) and torch.all(buf[1024 + n:] == -1)
