@@ -22,7 +22,7 @@ def test_step_gather_buckets_replay_bit_exact():
     V, d = 5003, 896
     host = synth.make_table(BF16, V, d, seed=301)
     t = table(host, BF16, V, d)
-    sc = etg.StepCache(t, max_ids=700, max_batch=4, k=10)
+    sc = etg.StepCache(t, max_ids=700, max_batch=4, k=10, use_graphs=True)
     assert sc.rows.shape[0] == 704  # 700 ids take the bucket of 704 (a multiple of 64)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
@@ -46,7 +46,7 @@ def test_step_gather_bucket_sharing_and_null_stream():
     V, d = 3001, 256
     host = synth.make_table(etg.F32, V, d, seed=302)
     t = table(host, etg.F32, V, d)
-    sc = etg.StepCache(t, max_ids=300, max_batch=1, k=1)
+    sc = etg.StepCache(t, max_ids=300, max_batch=1, k=1, use_graphs=True)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         for i, n in enumerate((3, 64, 10, 60) * 3):  # one bucket (64): 4 slots eager, captured, replayed
@@ -67,7 +67,7 @@ def test_step_gather_bucket_sharing_and_null_stream():
             assert np.array_equal(bits(rows), bits(ref))
     assert sc3.stats() == (0, 0)
     # the null stream cannot be captured: every call there runs eagerly
-    sc2 = etg.StepCache(t, max_ids=300, max_batch=1, k=1)
+    sc2 = etg.StepCache(t, max_ids=300, max_batch=1, k=1, use_graphs=True)
     for n in (7, 7, 7):
         ids = synth.uniform_ids(n, V, seed=99)
         rows = sc2.gather(ids)
@@ -82,7 +82,7 @@ def test_step_logits_replays_match_eager_and_oracle(dtype, V, d):
     host = synth.make_table(dtype, V, d, seed=303)
     t = table(host, dtype, V, d)
     k = 10
-    sc = etg.StepCache(t, max_ids=64, max_batch=24, k=k)
+    sc = etg.StepCache(t, max_ids=64, max_batch=24, k=k, use_graphs=True)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         for B in (1, 4, 8, 20):
@@ -111,7 +111,7 @@ def test_step_gather_back_to_back_calls_keep_their_ids():
     V, d = 4099, 128
     host = synth.make_table(BF16, V, d, seed=305)
     t = table(host, BF16, V, d)
-    sc = etg.StepCache(t, max_ids=64, max_batch=1, k=1)
+    sc = etg.StepCache(t, max_ids=64, max_batch=1, k=1, use_graphs=True)
     outs = [torch.empty((40, d), dtype=torch.float32, device="cuda") for _ in range(12)]
     s = torch.cuda.Stream()
     idss = [synth.uniform_ids(40, V, seed=500 + i) for i in range(12)]
