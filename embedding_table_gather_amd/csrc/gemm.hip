@@ -37,11 +37,12 @@ namespace etg {
 // 16-row group; the MFMA fragment reads (16 consecutive rows of one piece per
 // 16 lanes) are then free of bank conflicts.
 //
-// Top-k: one min-heap of k keys per residual row of the column tile, in LDS.
-// After a vocabulary tile each lane compares its logits (hi + lo, in registers)
-// with the heap root of their residual row and inserts only those above it
-// (rare after the first tiles).  At the end the heaps are written out,
-// unordered, as candidates [batch][vocabulary range][k].
+// Top-k: one descending list of k keys per residual row of the column tile, in
+// LDS.  After a vocabulary tile each lane offers its logits (hi + lo, in
+// registers) that reach its row's k-th key (on the first tile, a lower bound
+// from group maxima) to an append buffer, and one thread per row inserts them
+// (few after the first tiles).  At the end the lists are written out, best
+// first, as candidates [batch][vocabulary range][k].
 //
 // Workgroup ids are mapped so the column tiles of one vocabulary range sit on
 // the same XCD (ids go round-robin over the 8 XCDs): a table stage is fetched
@@ -53,6 +54,8 @@ static constexpr int kGemmBK = 32;                                    // K value
 static constexpr int kGemmStage = (kGemmBM + kGemmBN) * kGemmBK * 2;  // bytes per stage
 static constexpr int kGemmCols = kGemmBN / 2;                         // residual rows per column tile
 static constexpr int kXcds = 8;
+// List length merged in registers (the ranking contraction's usual heap size).
+static constexpr int kGemmRegList = 16;
 
 template <int WM, int WN>
 struct GemmCfg {
@@ -137,6 +140,7 @@ __global__ void __launch_bounds__(256) gemm_prep_hi_kernel(const void* __restric
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // s + the squares of 8 bf16 values: four v_dot2c_f32_bf16 (two exact products
@@ -176,7 +180,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
   static_assert(NA >= 2 && NB >= 2 && NA <= 5 && NB <= 5, "ring depths");
   static_assert(NT == 2 && MT == WN, "one hi and one lo N-tile (split) or two N-tiles; one M-tile per wave column");
   constexpr int SLICE = kGemmBM * 64;                     // one stage of 256 table or residual rows
-  uint64_t* heaps = (uint64_t*)(smem + (NA + NB) * SLICE);  // [COLS][k]
+  uint64_t* heaps = (uint64_t*)(smem + (NA + NB) * SLICE);  // [COLS][k] descending lists
   // logit of register i of tile a, N-tile t (hi + lo for split columns)
   auto val = [&](const f32x16 (&ac)[MT][NT], int a, int t, int i) -> float {
     if constexpr (SPLIT) return ac[a][0][i] + ac[a][1][i];
@@ -347,121 +351,170 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
         }
       }
     }
-    // Epilogue.  Register i of tile (a, t) holds row WR mw + 32 a + 8 (i / 4) +
-    // 4 (lane / 32) + i % 4 of operand column WC nw + 32 t + lane % 32.  Split
-    // columns: N-tile 0 is hi and 1 is lo, so a lane sees 64 rows of one residual
-    // row; ranking columns: each N-tile is its own residual row.  Each lane marks
-    // its logits whose order value reaches the heap root of that residual row
-    // (rare after the first tiles).  A wave with marks writes its logits to LDS
-    // and its lanes insert the marked entries that beat the root.  Each heap has
-    // one writer at a time: the wave rows mw take turns (barrier between), and
-    // within a wave the half-waves (lanes l and l + 32 share a column).
-    if (vt == 0) {
-      // First tile: the heaps are empty, so each residual row's heap is built by
-      // selection.  In groups of 64 residual rows (one wave column pair when split,
-      // one wave column otherwise) the logits pass through LDS as [256 rows][65];
-      // wave w then takes the k largest keys of columns w + 8 i (i < 8) in rounds
-      // (largest order value left, smallest row holding it) and stores them in
-      // ascending order, a valid min-heap; missing keys (rows past V) are 0 at the
-      // front.
-      static_assert(WN == 4 && WM == 2 && COLS % 64 == 0, "tile-0 selection layout");
-      float* Lt = (float*)smem;
-      constexpr int TS = 65;
-#pragma unroll 1
-      for (int grp = 0; grp < COLS / 64; grp++) {
-        if (SPLIT ? (nw >> 1) == grp : nw == grp) {
+    // Epilogue: every column (residual row) of the tile keeps its k best keys in
+    // LDS (0 = empty slot): a descending list for k <= 16, else a min-heap.  Register i of tile (a, t) holds
+    // row WR mw + 32 a + 8 (i / 4) + 4 (lane / 32) + i % 4 of operand column
+    // WC nw + 32 t + lane % 32 (split columns: N-tile 0 is hi and 1 is lo, so a lane
+    // sees 64 rows of one residual row; ranking columns: each N-tile is its own
+    // residual row), so a column's 256 rows are spread over 4 holders (two wave
+    // rows, two half-waves) of 64 values.
+    //  * T = the list's k-th key (0 while not full); on the first tile and for
+    //    k <= 16, at least the smallest of the column's 16 group maxima (groups of
+    //    16 rows, one per M-tile and holder), a lower bound on its 16th best since
+    //    every group holds a row reaching it.
+    //  * Each lane appends its keys at or above T to the column's append buffer (the
+    //    stage rings are idle between tiles: no load is in flight after a tile's
+    //    last stage and the next tile's first stages are issued after this).
+    //  * One thread per column inserts the appended keys: into the list held in
+    //    registers, or by replacing the heap root.
+    //  * A buffer that overflowed sends the tile into another round, in which only
+    //    the values not yet appended are offered against the raised T.
+    // Rows past the table are never ranked.
+    {
+      // the smaller stage ring holds counters, the wave staging areas and the
+      // append buffers
+      constexpr int ACAP = (6 * SLICE - 4096 - 8 * 4096) / (COLS * 8);  // keys per column and round
+      static_assert(ACAP >= 16 && C::THREADS == 512, "append buffers fit the smaller stage ring");
+      uint32_t* acnt = (uint32_t*)smem;                   // [COLS] appended keys this round
+      uint32_t* athr = acnt + COLS;                        // [COLS] first-tile order-value threshold
+      uint32_t* aovf = athr + COLS;                        // [2] overflow flags, by round parity
+      float* xs = (float*)(smem + 4096) + 1024 * wv;      // [8 waves][4][64 lanes][4] staging
+      uint64_t* app = (uint64_t*)(smem + 4096 + 8 * 4096);  // [COLS][ACAP]
+      // an opaque copy of the thread index keeps the per-lane rows and addresses
+      // below inside the tile loop (no free registers to hold them across K)
+      int xt = tid;
+      asm volatile("" : "+v"(xt));
+      const int xl = xt & 63;
+      // The lane's rows grow with the register-order bit 16 a + i, so its rows
+      // inside the table are a prefix of the bits: 16 per full M-tile, 4 per full
+      // group of 8 rows, and up to 4 more.
+      const int vl = max(0, (int)min((int64_t)kGemmBM, V - v0) - (WR * mw + 4 * (xl >> 5)));
+      const int nvalid = vl >= 128 ? 64 : 16 * (vl >> 5) + 4 * ((vl & 31) >> 3) + min(vl & 7, 4);
+      const uint64_t valid = nvalid >= 64 ? ~0ull : (1ull << nvalid) - 1;
+      if constexpr (SPLIT) {
+        // the column's logits, once (N-tile 1 is not read again this tile)
 #pragma unroll
-          for (int t = 0; t < NTR; t++)
-#pragma unroll
-            for (int a = 0; a < MT; a++)
-#pragma unroll
-              for (int i = 0; i < 16; i++)
-                Lt[(WR * mw + 32 * a + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * TS +
-                   (SPLIT ? (nw & 1) * 32 : 32 * t) + (lane & 31)] = val(acc, a, t, i);
-        }
-        gemm_stage_barrier<0>();
-        uint32_t v[8][4];
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const int r = lane + 64 * q;
-            v[i][q] = v0 + r < V ? score_ord(Lt[r * TS + wv + 8 * i]) : 0u;
-          }
-        for (int t = 0; t < k; t++) {
-          uint32_t M[8], Rw[8];
-#pragma unroll
-          for (int i = 0; i < 8; i++) M[i] = max(max(v[i][0], v[i][1]), max(v[i][2], v[i][3]));
-          wave_minmax_u32_multi<true>(M);
-#pragma unroll
-          for (int i = 0; i < 8; i++) {
-            uint32_t rq = 0xffffffffu;
-#pragma unroll
-            for (int q = 3; q >= 0; q--) rq = v[i][q] == M[i] ? (uint32_t)(lane + 64 * q) : rq;
-            Rw[i] = rq;
-          }
-          wave_minmax_u32_multi<false>(Rw);
-#pragma unroll
-          for (int i = 0; i < 8; i++) {
-#pragma unroll
-            for (int q = 0; q < 4; q++) v[i][q] = (M[i] != 0u && lane + 64 * q == (int)Rw[i]) ? 0u : v[i][q];
-          }
-          if (lane == 0) {
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-              heaps[(size_t)(64 * grp + wv + 8 * i) * k + (k - 1 - t)] =
-                  M[i] != 0u ? ((uint64_t)M[i] << 32) | (uint64_t)(~(uint32_t)(v0 + Rw[i])) : 0ull;
-          }
-        }
-        gemm_stage_barrier<0>();
+        for (int a = 0; a < MT; a++) acc[a][0] += acc[a][1];
       }
-      continue;
-    }
-    // per lane and N-tile t: its residual row's heap and the marks
-    float* xs = (float*)smem + (size_t)(nw * 64 + lane) * 64;  // [WN waves][64 lanes][64], 64 KiB
+      constexpr int TT = SPLIT ? 1 : NT;  // accumulator N-tile of column tile t
+      const bool regl = k <= kGemmRegList;  // sorted lists (else min-heaps, root = k-th key)
+      uint64_t taken[NTR];
 #pragma unroll
-    for (int p = 0; p < WM; p++) {
-      if (mw == p) {
+      for (int t = 0; t < NTR; t++) taken[t] = 0;
+      // the first tile's bound holds for k up to the column's 16 groups
+      const bool thr0 = vt == 0 && k <= 4 * MT;
+      if (tid < COLS) athr[tid] = ~0u;
+      if (tid < 2) aovf[tid] = 0;
+      if (thr0) {
+        gemm_stage_barrier<0>();
 #pragma unroll
         for (int t = 0; t < NTR; t++) {
-          const int col = nw * WCR + 32 * t + (lane & 31);
-          const bool col_ok = (int64_t)ct * COLS + col < B;
-          uint64_t* heap = heaps + (size_t)col * k;
-          const uint32_t tord = col_ok ? (uint32_t)(heap[0] >> 32) : 0xffffffffu;
-          uint64_t mask = 0;
+          uint32_t gmin = ~0u;
 #pragma unroll
-          for (int a = 0; a < MT; a++)
+          for (int a = 0; a < MT; a++) {
+            uint32_t gm = 0;
 #pragma unroll
-            for (int i = 0; i < 16; i++) mask |= (uint64_t)(score_ord(val(acc, a, t, i)) >= tord) << (16 * a + i);
-          if (__ballot(mask != 0) != 0) {
-            // a lane's own 64 logits of N-tile t; the lane reads them back itself
+            for (int i = 0; i < 16; i++)
+              gm = max(gm, score_ord(acc[a][t % TT][i]) & (0u - (uint32_t)((valid >> (16 * a + i)) & 1)));
+            gmin = min(gmin, gm);
+          }
+          atomicMin(&athr[nw * WCR + 32 * t + (xl & 31)], gmin);
+        }
+      }
+      for (int round = 0;; round++) {
+        if (tid < COLS) acnt[tid] = 0;
+        if (tid == 0) aovf[(round + 1) & 1] = 0;
+        gemm_stage_barrier<0>();
 #pragma unroll
-            for (int a = 0; a < MT; a++)
+        for (int t = 0; t < NTR; t++) {
+          const int col = nw * WCR + 32 * t + (xl & 31);
+          const uint64_t* list = heaps + (size_t)col * k;
+          uint32_t T = (uint32_t)(list[regl ? k - 1 : 0] >> 32);
+          if (thr0) T = max(T, athr[col]);
+          // the values at or above T (as floats: ord_score inverts score_ord, with
+          // -0 equal to +0) not offered yet, as a mask in register order
+          const bool all = T == 0u;
+          const float tf = ord_score(all ? 0x80000000u : T);
+          uint64_t m = 0;
 #pragma unroll
-              for (int i = 0; i < 16; i += 4)
-                *(f32x4*)(xs + 16 * a + i) =
-                    f32x4{val(acc, a, t, i), val(acc, a, t, i + 1), val(acc, a, t, i + 2), val(acc, a, t, i + 3)};
-            const int64_t r0 = v0 + WR * p + 4 * (lane >> 5);
-            for (int h = 0; h < 2; h++) {
-              if ((lane >> 5) == h && mask != 0) {
-                uint64_t thr = heap[0];
-                while (mask != 0) {
-                  const int j = __builtin_ctzll(mask);
-                  mask &= mask - 1;
-                  const int64_t row = r0 + 32 * (j >> 4) + 8 * ((j & 15) >> 2) + (j & 3);
-                  const uint64_t key = row < V ? make_key(xs[j], (uint32_t)row) : 0;
-                  if (key > thr) {
-                    heap_replace_root(heap, k, key);
-                    thr = heap[0];
-                  }
-                }
+          for (int a = 0; a < MT; a++) {
+            uint32_t ma = 0;
+#pragma unroll
+            for (int i = 0; i < 16; i++) ma |= (uint32_t)(acc[a][t % TT][i] >= tf) << i;
+            m |= (uint64_t)ma << (16 * a);
+          }
+          m = (int64_t)ct * COLS + col < B ? (all ? ~0ull : m) & valid & ~taken[t] : 0ull;
+          // one slot reservation per lane; the keys that fit go in register order
+          const uint32_t nm = (uint32_t)__builtin_popcountll(m);
+          const uint32_t base = nm != 0 ? atomicAdd(&acnt[col], nm) : 0u;
+          uint64_t st = m;
+          if (base + nm > (uint32_t)ACAP) {
+            uint64_t rest = m;  // drop the lowest set bits that still fit
+            for (uint32_t q = base; q < (uint32_t)ACAP; q++) rest &= rest - 1;
+            st = m ^ rest;
+          }
+          taken[t] |= st;
+          if (__ballot(st != 0) != 0) {
+            uint64_t* dst = app + (size_t)col * ACAP + base;
+            const uint32_t r0 = (uint32_t)(v0 + WR * mw + 4 * (xl >> 5));
+#pragma unroll
+            for (int a = 0; a < MT; a++) {
+              uint32_t ma = (uint32_t)(st >> (16 * a)) & 0xffffu;
+              if (__ballot(ma != 0) == 0) continue;
+              // the lane's 16 values of M-tile a, read back by index (value i at
+              // float 256 (i / 4) + 4 lane + i % 4 of the wave's area)
+#pragma unroll
+              for (int q = 0; q < 4; q++)
+                *(f32x4*)(xs + 256 * q + 4 * xl) = f32x4{acc[a][t % TT][4 * q], acc[a][t % TT][4 * q + 1],
+                                                         acc[a][t % TT][4 * q + 2], acc[a][t % TT][4 * q + 3]};
+              while (ma != 0) {
+                const int j = __builtin_ctz(ma);
+                ma &= ma - 1;
+                *dst++ = make_key(xs[256 * (j >> 2) + 4 * xl + (j & 3)], r0 + 32 * a + 8 * (j >> 2) + (j & 3));
               }
-              __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this half-wave's heap writes are done
             }
           }
         }
+        gemm_stage_barrier<0>();
+        if (tid < COLS) {
+          uint32_t n = acnt[tid];
+          if (n > (uint32_t)ACAP) {
+            aovf[round & 1] = 1;
+            n = ACAP;
+          }
+          if (n != 0) {
+            uint64_t* list = heaps + (size_t)tid * k;
+            const uint64_t* ap = app + (size_t)tid * ACAP;
+            if (regl) {
+              // the list in registers, padded with empty keys; each key enters by a
+              // branch-free insertion (position j takes max(L[j], min(L[j - 1], key)),
+              // high j first)
+              uint64_t L[kGemmRegList];
+#pragma unroll
+              for (int j = 0; j < kGemmRegList; j++) L[j] = j < k ? list[j] : 0ull;
+              for (uint32_t q = 0; q < n; q++) {
+                const uint64_t key = ap[q];
+#pragma unroll
+                for (int j = kGemmRegList - 1; j > 0; j--) {
+                  const uint64_t lo = L[j - 1] < key ? L[j - 1] : key;
+                  L[j] = L[j] > lo ? L[j] : lo;
+                }
+                L[0] = L[0] > key ? L[0] : key;
+              }
+#pragma unroll
+              for (int j = 0; j < kGemmRegList; j++)
+                if (j < k) list[j] = L[j];
+            } else {
+              for (uint32_t q = 0; q < n; q++) {
+                const uint64_t key = ap[q];
+                if (key > list[0]) heap_replace_root(list, k, key);  // keys are unique: offered once
+              }
+            }
+          }
+        }
+        gemm_stage_barrier<0>();
+        if (aovf[round & 1] == 0) break;
       }
-      gemm_stage_barrier<0>();
     }
   }
   if (SPLIT && lse != nullptr) {
@@ -531,7 +584,7 @@ static hipError_t launch_gemm_cfg(const TableDesc& t, const LogitsPlan& p, const
     float* nrm2 = (float*)x.aux + align_up((size_t)p.ngrp * t.V, 64);
     if ((e = launch_rank_norm((const float*)x.aux, p.ngrp, t.V, nrm2, stream)) != hipSuccess) return e;
     if ((e = launch_rescore(t, p, R, (int)x.wire, cand, p.nvr, (int64_t)p.tiles_per_range * kGemmBM, nrm2, nnrm,
-                            p.kpad, ids, scores, stream, 0)) != hipSuccess)
+                            p.kpad, ids, scores, stream, 1)) != hipSuccess)
       return e;
   }
   return hipSuccess;

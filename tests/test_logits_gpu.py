@@ -125,6 +125,27 @@ def test_rank_path_rescans_a_range_holding_many_winners(k, B):
     assert np.array_equal(gids[0], oids[0])
 
 
+# 256 planted rows filling the tile of rows 256..511 of the split contraction,
+# ranked round-robin over the 16 row groups its register layout splits a column's
+# tile into (wave row, M-tile, half-wave; 16 rows each): the group maxima are then
+# the 16 best, so a group bound would drop every winner past the 16th when k > 16
+@pytest.mark.parametrize("k", [16, 17, 40, 64])
+@pytest.mark.parametrize("B", [2, 70])
+def test_split_path_keeps_many_winners_of_one_tile(k, B):
+    V, d = 30000, 512
+    host = synth.make_table(BF16, V, d, seed=25)
+    R = synth.residuals(B, d, seed=26)
+    u = R[0] / np.linalg.norm(R[0])
+    rows = np.arange(256)
+    group = (rows // 128) * 8 + (rows % 128) // 32 * 2 + (rows % 8) // 4
+    rank = (4 * ((rows % 32) // 8) + rows % 4) * 16 + group
+    for r in rows:
+        host[256 + r] = synth.f32_to_bf16_bits((u * (0.9 - 0.002 * rank[r])).astype(np.float32))
+    gids, _, oids, _ = full_check(host, BF16, V, d, R, k, GEMM)
+    assert np.array_equal(gids[0], 256 + np.argsort(rank)[:k])
+    assert np.array_equal(gids[0], oids[0])
+
+
 # the row path: rows of 16 bytes to 16 KiB (1 to 16 KiB loads, the last one partial),
 # f32 / bf16 / f16 tables, one table pass per residual row
 @pytest.mark.parametrize("dtype,V,d", [(BF16, 5003, 200), (BF16, 4099, 896), (BF16, 37, 8), (BF16, 20000, 5376),
