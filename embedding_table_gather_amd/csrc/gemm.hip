@@ -653,7 +653,7 @@ int32_t plan_rank(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
     *why = "hidden too large for the rank path (the residual row is kept in LDS)";
     return -5;
   }
-  if (batch <= 64) {  // one pass of the wide kernel in ranking mode
+  if (batch <= kRankWideBatch) {  // the wide kernel in ranking mode
     p->rank_wide = 1;
     return plan_wide(t, batch, k, p, why, true);
   }

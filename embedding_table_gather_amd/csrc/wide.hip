@@ -1,5 +1,5 @@
 // Wide stream path of the tied lm_head projection (bf16 tables, up to 64 residual
-// rows per table pass): ADR-0008 "POST /v1/logits", logits = residual @ lm_head.T
+// rows per table pass, 128 when ranking): ADR-0008 "POST /v1/logits", logits = residual @ lm_head.T
 // over every vocabulary row, fused with a per-block top-k.
 #include <algorithm>
 
@@ -11,8 +11,9 @@ namespace etg {
 // ---------------------------------------------------------------------------
 // Wide stream path: bf16 tables, batches beyond the stream path's 8 rows.
 //
-// Still one HBM pass over the table per pass of up to 64 residual rows, with
-// the table read straight into VGPRs; the residual operand comes from LDS.
+// Still one HBM pass over the table per pass of up to 64 residual rows (128 in
+// ranking mode), with the table read straight into VGPRs; the residual operand
+// comes from LDS.
 // A block owns 512 table rows (8 waves x 4 M-tiles of 16 rows).
 //
 // Loads: per 16-row M-tile and 64-value K step, two load instructions X (rows
@@ -31,15 +32,19 @@ namespace etg {
 // and 16-column N-tile there are four B fragments (P/Q x hi/lo), all four
 // accumulating into the same 16x16 tile: logit = D after the K loop.
 // The operand image [pass][step][nt][pq][hl][lane] x 16 bytes is built once per
-// call by wide_prep_kernel; blocks stage it through LDS kWideCK steps at a time
+// call by wide_prep_kernel; blocks stage it through LDS wide_ck steps at a time
 // in two buffers, the next chunk's image being copied in while the current one is
 // used, with one LDS-only barrier per chunk (table loads stay in flight across it).
+// Past 4 N-tiles the accumulators leave room for a chunk (and table-load ring)
+// of 2 steps only.
 // ---------------------------------------------------------------------------
 static constexpr int kWideWaves = 8;
 static constexpr int kWideMT = 4;                            // 16-row M-tiles per wave
 static constexpr int kWideRows = kWideWaves * kWideMT * 16;  // table rows per block
-static constexpr int kWideCK = 3;  // K steps per staged chunk = depth of the table-load ring
-static constexpr int kWideMaxTiles = 4;                      // 16-column N-tiles: 64 residual rows
+static constexpr int kWideMaxTiles = 4;      // 16-column N-tiles per pass: 64 residual rows
+static constexpr int kWideRankMaxTiles = 8;  // ranking mode: 128 residual rows
+// K steps per staged chunk = depth of the table-load ring
+__host__ __device__ constexpr int wide_ck(int ntile) { return ntile > 4 ? 2 : 3; }
 // Ranking mode: keys kept per 512-row block and residual row.  The answer's k
 // rows are spread over 512 blocks; a block holding more of the candidates than
 // this is rescanned by the rescoring kernel.
@@ -105,7 +110,7 @@ __global__ void __launch_bounds__(256) wide_prep_kernel(const void* __restrict__
 // One pass (blockIdx.y) over the table for 16 NTILE residual rows.
 //  table      bf16 [V][hidden], row_bytes = 2 hidden, a multiple of 16
 //  img        operand image (wide_prep_kernel), steps_pad K steps per pass
-//  steps_pad  ceil(hidden / 64) rounded up to kWideCK
+//  steps_pad  ceil(hidden / 64) rounded up to wide_ck(NTILE)
 //  logits     nullable [B][V]: the block's raw logits
 //  lse        nullable [B][gridDim.x]: log-partition partial of the block's rows
 //             at lse_c = log2(e) / temperature
@@ -122,9 +127,11 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
     const uint8_t* __restrict__ table, int64_t V, int64_t row_bytes, const u32x4* __restrict__ img, int64_t B,
     int steps_pad, int k, uint64_t* __restrict__ cand, uint64_t* __restrict__ thr, float* __restrict__ logits,
     float2* __restrict__ lse, float lse_c, float* __restrict__ nrm2) {
+  static_assert(NTILE <= (RANK ? kWideRankMaxTiles : kWideMaxTiles), "N-tiles per pass");
+  constexpr int CK = wide_ck(NTILE);
   constexpr int NF = RANK ? 2 : 4;          // image fragments per N-tile and step
   constexpr int STEP_U4 = NTILE * NF * 64;  // image slots per K step
-  constexpr int CHUNK_U4 = kWideCK * STEP_U4;
+  constexpr int CHUNK_U4 = CK * STEP_U4;
   constexpr int NTHR = 64 * kWideWaves;
   constexpr int NPER = (STEP_U4 + NTHR - 1) / NTHR;
   constexpr int NC = NTILE * 16;
@@ -172,10 +179,10 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
   for (int q = 0; q < NPRE; q++) pre[q] = pimg[min(tid + q * NTHR, CHUNK_U4 - 1)];
 
   // ring of table loads: the j-th step of a chunk lives in slot j and is loaded
-  // kWideCK - 1 steps ahead of its use
-  u32x4 ax[kWideCK][kWideMT], ay[kWideCK][kWideMT];
+  // CK - 1 steps ahead of its use
+  u32x4 ax[CK][kWideMT], ay[CK][kWideMT];
 #pragma unroll
-  for (int r = 0; r < kWideCK - 1; r++) {
+  for (int r = 0; r < CK - 1; r++) {
     const uint32_t ko = koff(r);
 #pragma unroll
     for (int mt = 0; mt < kWideMT; mt++) {
@@ -187,7 +194,7 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
   for (int q = 0; q < NPRE; q++) sbuf[min(tid + q * NTHR, CHUNK_U4 - 1)] = pre[q];
   lds_barrier();
 
-  const int nchunks = steps_pad / kWideCK;
+  const int nchunks = steps_pad / CK;
   for (int c = 0; c < nchunks; c++) {
     const u32x4* cur = sbuf + (c & 1) * CHUNK_U4;
     u32x4* nxt = sbuf + ((c + 1) & 1) * CHUNK_U4;
@@ -196,16 +203,16 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
     const int pn = min(c + 1, nchunks - 1);
     const int pc = c;
 #pragma unroll
-    for (int j = 0; j < kWideCK; j++) {
-      const int cb = j, nb = (j + kWideCK - 1) % kWideCK;
+    for (int j = 0; j < CK; j++) {
+      const int cb = j, nb = (j + CK - 1) % CK;
       // image piece j of the next chunk
       u32x4 st[NPER];
-      const u32x4* ps = pimg + ((size_t)pn * kWideCK + j) * STEP_U4;
+      const u32x4* ps = pimg + ((size_t)pn * CK + j) * STEP_U4;
 #pragma unroll
       for (int q = 0; q < NPER; q++) st[q] = ps[min(tid + q * NTHR, STEP_U4 - 1)];
-      // table loads of the step kWideCK - 1 ahead: the last step of this chunk for
+      // table loads of the step CK - 1 ahead: the last step of this chunk for
       // j = 0, else step j - 1 of the next chunk (clamped to the row end)
-      const uint32_t ko = koff(j == 0 ? pc * kWideCK + kWideCK - 1 : pn * kWideCK + j - 1);
+      const uint32_t ko = koff(j == 0 ? pc * CK + CK - 1 : pn * CK + j - 1);
 #pragma unroll
       for (int mt = 0; mt < kWideMT; mt++) {
         ax[nb][mt] = __builtin_nontemporal_load((const u32x4*)(tbase + (xoff[mt] + ko)));
@@ -375,6 +382,44 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
       }
       return;
     }
+    // Ties: k rounds over the accumulators, each taking per column the largest
+    // key below the previous round's (wave maxima through LDS, then the block's)
+    uint64_t* wbest = (uint64_t*)smem;          // [kWideWaves][NC] (the image buffers are free)
+    uint64_t* rsel = wbest + kWideWaves * NC;  // [NC] this round's key per column
+    for (int t = 0; t < k; t++) {
+#pragma unroll
+      for (int nt = 0; nt < NTILE; nt++) {
+        // the previous round's key of the column (read before this round's barrier)
+        const uint64_t prev = t == 0 ? ~0ull : rsel[16 * nt + (lane & 15)];
+        uint64_t best = 0;
+#pragma unroll
+        for (int mt = 0; mt < kWideMT; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int rl = rbase + 16 * mt + i;
+            const uint64_t key = (!tail || row0 + rl < V) ? make_key(acc[mt][nt][i], (uint32_t)(row0 + rl)) : 0ull;
+            best = (key < prev && key > best) ? key : best;
+          }
+#pragma unroll
+        for (int m = 16; m <= 32; m *= 2) {
+          const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), m, 64) << 32) |
+                             (uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)best, m, 64);
+          best = o > best ? o : best;
+        }
+        if (lane < 16) wbest[wv * NC + 16 * nt + lane] = best;
+      }
+      lds_barrier();
+      if (tid < NC) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int w = 0; w < kWideWaves; w++) m = max(m, wbest[w * NC + tid]);
+        rsel[tid] = m;
+        const int64_t b = (int64_t)blockIdx.y * NC + tid;
+        if (b < B) cand[(b * gridDim.x + blockIdx.x) * (int64_t)k + t] = m;  // 0: no key left
+      }
+      lds_barrier();
+    }
+    return;
   }
 
   // logits of the block's rows through LDS (the image buffers are free now)
@@ -514,8 +559,18 @@ static hipError_t launch_wide_mode(const TableDesc& t, const LogitsPlan& p, cons
     case 2: return launch_wide_nt<2, RANK>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
     case 3: return launch_wide_nt<3, RANK>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
     case 4: return launch_wide_nt<4, RANK>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
-    default: return hipErrorInvalidValue;
+    default: break;
   }
+  if constexpr (RANK) {
+    switch (p.ntile) {
+      case 5: return launch_wide_nt<5, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 6: return launch_wide_nt<6, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 7: return launch_wide_nt<7, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 8: return launch_wide_nt<8, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
@@ -523,7 +578,7 @@ hipError_t launch_wide(const TableDesc& t, const LogitsPlan& p, const void* R, u
   return launch_wide_mode<false>(t, p, R, img, cand, thr, x, stream, ev0, ev1);
 }
 
-// Ranking mode for batches of up to 64 rows: the wide kernel ranks with bf16
+// Ranking mode for batches of up to 128 rows a pass: the wide kernel ranks with bf16
 // residual rows and keeps kb keys per 512-row block; the rescoring kernel
 // certifies and completes the answer (aux holds the blocks' squared row norms).
 hipError_t launch_wide_rank(const TableDesc& t, const LogitsPlan& p, const void* R, uint8_t* img, uint64_t* cand,
@@ -537,18 +592,23 @@ hipError_t launch_wide_rank(const TableDesc& t, const LogitsPlan& p, const void*
 }
 
 int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why, bool rank) {
-    // passes of at most 64 residual rows, split evenly into 16-row N-tiles
+    // passes of at most 64 residual rows (128 ranking), split evenly into 16-row
+    // N-tiles
     if ((uint64_t)(kWideRows + 1) * (uint64_t)t.row_bytes >= (1ull << 32)) {
       *why = "rows too long for the wide path";
       return -5;
     }
     const int nf = rank ? 2 : 4;  // image fragments per N-tile and step
-    p->npass = (int32_t)cdiv(batch, kWideMaxTiles * 16);
+    p->npass = (int32_t)cdiv(batch, (rank ? kWideRankMaxTiles : kWideMaxTiles) * 16);
     p->ntile = (int32_t)cdiv(cdiv(batch, p->npass), 16);
-    p->steps = (int32_t)(cdiv(cdiv(t.hidden, 64), kWideCK) * kWideCK);
+    const int ck = wide_ck(p->ntile);
+    p->steps = (int32_t)(cdiv(cdiv(t.hidden, 64), ck) * ck);
     p->nblk = (int32_t)cdiv(t.V, kWideRows);
-    const size_t img_lds = (size_t)2 * kWideCK * p->ntile * nf * 1024;
-    const size_t log_lds = (size_t)kWideRows * (16 * p->ntile + 1) * 4;
+    const size_t img_lds = (size_t)2 * ck * p->ntile * nf * 1024;
+    // the logits pass through LDS after the K loop (ranking mode: the selection
+    // rounds' [waves + 1][columns] keys)
+    const size_t log_lds = rank ? (size_t)(kWideWaves + 1) * 16 * p->ntile * 8
+                                : (size_t)kWideRows * (16 * p->ntile + 1) * 4;
     p->lds_bytes = std::max(img_lds, log_lds);
     p->img_bytes = (size_t)p->npass * p->steps * p->ntile * nf * 1024;
     if (!rank) {

@@ -96,6 +96,13 @@ def test_lm31b_logits_b64_mfma_paths(path):
     _check("lm31b", 64, 10, [0, 9, 17, 31, 32, 47, 55, 63], path)
 
 
+# past 64 rows: the automatic choice ranks with the wide kernel in one table pass
+# of 5 to 8 N-tiles (up to 128 rows), then with two passes
+@pytest.mark.parametrize("B", [96, 128, 200])
+def test_lm31b_logits_wide_rank_past_64_rows(B):
+    _check("lm31b", B, 10, [0, 15, 16, 63, 64, B // 2 + 1, B - 1])
+
+
 # rows from each 256-row column tile of the ranking contraction (and of the
 # 128-row column tiles of the split one): both ends of every tile
 _PREFILL_ROWS = [0, 255, 256, 300, 511, 512, 600, 767, 768, 1023]

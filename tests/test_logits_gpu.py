@@ -73,11 +73,12 @@ def test_gemm_path_ragged(V, d, B):
     full_check(host, BF16, V, d, R, min(10, V), GEMM)
 
 
-# the rank path: up to 64 rows the wide kernel ranks (1 to 4 N-tiles, 512-row
-# blocks keeping 4 keys each), beyond that the contraction (256-row column tiles,
-# ragged last one, one or many vocabulary ranges, heaps of fewer keys than k)
+# the rank path: up to 128 rows a pass the wide kernel ranks (1 to 8 N-tiles,
+# 512-row blocks keeping 4 keys each; 65 and 100 rows are one pass of 5 and 7
+# N-tiles, 130 rows two passes of 5), past 128 the contraction (256-row column
+# tiles, ragged last one, one or many vocabulary ranges, heaps of fewer keys than k)
 @pytest.mark.parametrize("V,d", [(5003, 200), (4099, 896), (1001, 64), (20000, 5376), (37, 8), (70000, 512)])
-@pytest.mark.parametrize("B", [1, 9, 17, 33, 64, 65, 130, 257])
+@pytest.mark.parametrize("B", [1, 9, 17, 33, 64, 65, 100, 128, 130, 257])
 def test_rank_path_ragged(V, d, B):
     host = synth.make_table(BF16, V, d, seed=500 + V)
     R = synth.residuals(B, d, seed=600 + B)
@@ -108,12 +109,13 @@ def test_rank_path_odd_block_count(k, path):
 
 
 @pytest.mark.parametrize("k", [10, 40, 64])
-@pytest.mark.parametrize("B", [2, 70])
+@pytest.mark.parametrize("B", [2, 70, 140])
 def test_rank_path_rescans_a_range_holding_many_winners(k, B):
     # 80 planted winners in rows 256..335, inside one range of the ranking kernel
-    # (a 512-row block of the wide kernel keeping 4 keys for B = 2, a 256-row range
-    # of the contraction keeping 16 for B = 70): the certificate must send the
-    # whole range to exact rescoring for the answer to hold the other winners
+    # (a 512-row block of the wide kernel keeping 4 keys for B = 2 and 70, a
+    # 256-row range of the contraction keeping 16 for B = 140): the certificate
+    # must send the whole range to exact rescoring for the answer to hold the
+    # other winners
     V, d = 30000, 512
     host = synth.make_table(BF16, V, d, seed=23)
     R = synth.residuals(B, d, seed=24)
@@ -200,6 +202,22 @@ def test_zero_residual_gives_ids_in_order(path):
     ids, sc = run(table(host, BF16, V, d), np.zeros((2, d), np.float32), 64, path)
     assert np.array_equal(ids, np.tile(np.arange(64), (2, 1)))
     assert np.all(sc == 0)
+
+
+# all-tie blocks of the wide ranking kernel (every logit 0) take its selection
+# rounds over the accumulators, at 1 to 8 N-tiles; rows 16..31 are nonzero so
+# that tied and untied columns share a block
+@pytest.mark.parametrize("B", [3, 40, 72, 128])
+def test_rank_path_all_tie_blocks(B):
+    V, d = 3000, 128
+    host = synth.make_table(BF16, V, d, seed=5)
+    R = np.zeros((B, d), np.float32)
+    if B > 16:
+        n = min(B, 32) - 16
+        R[16:16 + n] = synth.residuals(n, d, seed=7)
+    gids, gsc, oids, osc = full_check(host, BF16, V, d, R, 20, RANK)
+    assert np.array_equal(gids[0], np.arange(20))
+    assert np.all(gsc[0] == 0)
 
 
 @pytest.mark.parametrize("path", ALL)
