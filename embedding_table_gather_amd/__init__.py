@@ -24,7 +24,9 @@ F32, BF16, Q8_0, F16 = 0, 1, 2, 3
 WIRE_F32, WIRE_F16, WIRE_I8 = 0, 1, 2
 PATH_AUTO, PATH_VALU, PATH_STREAM, PATH_GEMM, PATH_WIDE, PATH_Q8, PATH_ROW, PATH_RANK = 0, 1, 2, 3, 4, 5, 6, 7
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libetg.so")
+# ETG_LIBRARY names another build of the same library (e.g. one whose host code
+# carries sanitizers); by default the in-tree libetg.so
+LIB_PATH = os.environ.get("ETG_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libetg.so")
 
 _STATUS = {
     0: "ETG_OK", -1: "ETG_EINVAL", -2: "ETG_EDTYPE", -3: "ETG_ESHAPE", -4: "ETG_EALIGN",

@@ -181,11 +181,6 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
   static_assert(NT == 2 && MT == WN, "one hi and one lo N-tile (split) or two N-tiles; one M-tile per wave column");
   constexpr int SLICE = kGemmBM * 64;                     // one stage of 256 table or residual rows
   uint64_t* heaps = (uint64_t*)(smem + (NA + NB) * SLICE);  // [COLS][k] descending lists
-  // logit of register i of tile a, N-tile t (hi + lo for split columns)
-  auto val = [&](const f32x16 (&ac)[MT][NT], int a, int t, int i) -> float {
-    if constexpr (SPLIT) return ac[a][0][i] + ac[a][1][i];
-    else return ac[a][t][i];
-  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps wave choices scalar
   const int mw = wv / WN, nw = wv % WN;

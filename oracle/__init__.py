@@ -19,6 +19,8 @@ WIRE_F32, WIRE_F16, WIRE_I8 = 0, 1, 2
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "etg_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# ETG_ORACLE_LIBRARY loads another build of the same source (e.g. with sanitizers)
+_LOAD = os.environ.get("ETG_ORACLE_LIBRARY") or _LIB
 _lib = None
 
 
@@ -37,9 +39,9 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    if _LOAD == _LIB and not os.path.exists(_LIB):
         build(force=True)
-    L = ctypes.CDLL(_LIB)
+    L = ctypes.CDLL(_LOAD)
     i64, i32, f32p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     vp = ctypes.c_void_p
     L.orc_row_bytes.restype = i64
