@@ -354,9 +354,10 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
     // residual row), so a column's 256 rows are spread over 4 holders (two wave
     // rows, two half-waves) of 64 values.
     //  * T = the list's k-th key (0 while not full); on the first tile and for
-    //    k <= 16, at least the smallest of the column's 16 group maxima (groups of
-    //    16 rows, one per M-tile and holder), a lower bound on its 16th best since
-    //    every group holds a row reaching it.
+    //    k <= 64, at least the smallest over the 4 holders of each one's
+    //    ceil(k / 4)-th largest maximum of its 16 groups of 4 rows: at least k
+    //    groups, each with a row of its own, reach it, so it bounds the k-th best
+    //    from below.
     //  * Each lane appends its keys at or above T to the column's append buffer (the
     //    stage rings are idle between tiles: no load is in flight after a tile's
     //    last stage and the next tile's first stages are issued after this).
@@ -396,24 +397,44 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
       uint64_t taken[NTR];
 #pragma unroll
       for (int t = 0; t < NTR; t++) taken[t] = 0;
-      // the first tile's bound holds for k up to the column's 16 groups
-      const bool thr0 = vt == 0 && k <= 4 * MT;
+      // the first tile's bound holds for k up to the column's 64 groups
+      const bool thr0 = vt == 0 && k <= 16 * MT;
       if (tid < COLS) athr[tid] = ~0u;
       if (tid < 2) aovf[tid] = 0;
       if (thr0) {
         gemm_stage_barrier<0>();
+        // groups each holder vouches for (opaque: its compares below stay here
+        // instead of holding scalar registers across the tile loop)
+        int q = (k + 3) >> 2;
+        asm volatile("" : "+s"(q));
 #pragma unroll
         for (int t = 0; t < NTR; t++) {
-          uint32_t gmin = ~0u;
+          // the holder's 16 group maxima (groups of 4 rows: M-tile a, register
+          // quad i / 4), sorted descending by insertion
+          uint32_t srt[16];
 #pragma unroll
-          for (int a = 0; a < MT; a++) {
-            uint32_t gm = 0;
+          for (int g = 0; g < 16; g++) srt[g] = 0;
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-              gm = max(gm, score_ord(acc[a][t % TT][i]) & (0u - (uint32_t)((valid >> (16 * a + i)) & 1)));
-            gmin = min(gmin, gm);
-          }
-          atomicMin(&athr[nw * WCR + 32 * t + (xl & 31)], gmin);
+          for (int a = 0; a < MT; a++)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; g4++) {
+              uint32_t x = 0;
+#pragma unroll
+              for (int e = 0; e < 4; e++) {
+                const int i = 4 * g4 + e;
+                x = max(x, score_ord(acc[a][t % TT][i]) & (0u - (uint32_t)((valid >> (16 * a + i)) & 1)));
+              }
+#pragma unroll
+              for (int g = 0; g < 16; g++) {
+                const uint32_t hi = max(srt[g], x);
+                x = min(srt[g], x);
+                srt[g] = hi;
+              }
+            }
+          uint32_t gq = srt[0];
+#pragma unroll
+          for (int g = 1; g < 16; g++) gq = g == q - 1 ? srt[g] : gq;
+          atomicMin(&athr[nw * WCR + 32 * t + (xl & 31)], gq);
         }
       }
       for (int round = 0;; round++) {

@@ -128,9 +128,10 @@ def test_rank_path_rescans_a_range_holding_many_winners(k, B):
 
 
 # 256 planted rows filling the tile of rows 256..511 of the split contraction,
-# ranked round-robin over the 16 row groups its register layout splits a column's
-# tile into (wave row, M-tile, half-wave; 16 rows each): the group maxima are then
-# the 16 best, so a group bound would drop every winner past the 16th when k > 16
+# ranked round-robin over 16 row groups of its register layout (wave row, M-tile,
+# half-wave; 16 rows each): the first tile's lower bound on the k-th best must
+# vouch for k groups (k = 17 fails a bound taking floor(k / 4) of each holder's
+# 4-row groups, k > 16 one taking the 16-row groups)
 @pytest.mark.parametrize("k", [16, 17, 40, 64])
 @pytest.mark.parametrize("B", [2, 70])
 def test_split_path_keeps_many_winners_of_one_tile(k, B):
