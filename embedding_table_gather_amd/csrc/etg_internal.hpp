@@ -38,7 +38,7 @@ struct LogitsPlan {
   int32_t tiles_per_range;
   // rank path (the gemm kernel in ranking mode, then exact rescoring)
   int32_t kb;            // keys per vocabulary-range heap (or per wide-kernel block)
-  int32_t rank_wide;     // 1: the wide kernel ranks (passes of up to 128 rows), 0: the gemm kernel
+  int32_t rank_wide;     // 1: the wide kernel ranks (one pass of up to 256 rows), 0: the gemm kernel
   int32_t ngrp;          // column tiles that measure table row norms (a share of K each)
   size_t rescore_lds;    // dynamic LDS of the rescoring kernel
   // wide path
@@ -166,8 +166,8 @@ int32_t rescore_waves(int64_t batch);
 // Rank path constants (rank.hip): the residual row is kept in LDS by the rescoring;
 // rank_norm_kernel reduces the row norm parts per block of kRankNormRows rows.
 constexpr int kRankMaxHidden = 16384;
-// Largest batch the rank path gives to the wide kernel (in passes of 128 rows).
-constexpr int64_t kRankWideBatch = 128;
+// Largest batch the rank path gives to the wide kernel (one pass of up to 256 rows).
+constexpr int64_t kRankWideBatch = 256;
 constexpr int kRankNormRows = 1024;
 // Squared row norms from parts npart [ngrp][V]: nrm2[x] = the largest norm of rows
 // [x kRankNormRows, (x + 1) kRankNormRows) (rank.hip).

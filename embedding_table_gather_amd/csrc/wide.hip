@@ -14,7 +14,9 @@ namespace etg {
 // Still one HBM pass over the table per pass of up to 64 residual rows (128 in
 // ranking mode), with the table read straight into VGPRs; the residual operand
 // comes from LDS.
-// A block owns 512 table rows (8 waves x 4 M-tiles of 16 rows).
+// A block owns 512 table rows (8 waves x 4 M-tiles of 16 rows); past 8 N-tiles
+// (ranking mode only), 256 (2 M-tiles per wave), since the accumulators of
+// 4 M-tiles would fill a wave's registers.
 //
 // Loads: per 16-row M-tile and 64-value K step, two load instructions X (rows
 // 0-7) and Y (rows 8-15); lane l reads row l % 8 of its half, 16-byte chunk
@@ -39,15 +41,16 @@ namespace etg {
 // of 2 steps only.
 // ---------------------------------------------------------------------------
 static constexpr int kWideWaves = 8;
-static constexpr int kWideMT = 4;                            // 16-row M-tiles per wave
-static constexpr int kWideRows = kWideWaves * kWideMT * 16;  // table rows per block
+// 16-row M-tiles per wave, and table rows per block
+__host__ __device__ constexpr int wide_mt(int ntile) { return ntile > 8 ? 2 : 4; }
+__host__ __device__ constexpr int wide_rows(int ntile) { return kWideWaves * wide_mt(ntile) * 16; }
 static constexpr int kWideMaxTiles = 4;      // 16-column N-tiles per pass: 64 residual rows
-static constexpr int kWideRankMaxTiles = 8;  // ranking mode: 128 residual rows
+static constexpr int kWideRankMaxTiles = 16;  // ranking mode: 256 residual rows
 // K steps per staged chunk = depth of the table-load ring
 __host__ __device__ constexpr int wide_ck(int ntile) { return ntile > 4 ? 2 : 3; }
-// Ranking mode: keys kept per 512-row block and residual row.  The answer's k
-// rows are spread over 512 blocks; a block holding more of the candidates than
-// this is rescanned by the rescoring kernel.
+// Ranking mode: keys kept per block and residual row.  The answer's k rows are
+// spread over the blocks; a block holding more of the candidates than this is
+// rescanned by the rescoring kernel.
 static constexpr int kWideRankKeys = 4;
 // Ranking mode: most candidate logits per block and residual row the fast
 // selection keys (more, from ties, take the general selection).
@@ -129,6 +132,8 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
     float2* __restrict__ lse, float lse_c, float* __restrict__ nrm2) {
   static_assert(NTILE <= (RANK ? kWideRankMaxTiles : kWideMaxTiles), "N-tiles per pass");
   constexpr int CK = wide_ck(NTILE);
+  constexpr int MT = wide_mt(NTILE);
+  constexpr int ROWS = wide_rows(NTILE);
   constexpr int NF = RANK ? 2 : 4;          // image fragments per N-tile and step
   constexpr int STEP_U4 = NTILE * NF * 64;  // image slots per K step
   constexpr int CHUNK_U4 = CK * STEP_U4;
@@ -138,37 +143,37 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
   constexpr int LS = NC + 1;  // logit row stride in LDS (odd: conflict-free column reads)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   u32x4* sbuf = (u32x4*)smem;  // two chunk buffers
-  float* slog = (float*)smem;  // after the K loop: [kWideRows][LS]
+  float* slog = (float*)smem;  // after the K loop: [ROWS][LS]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t row0 = (int64_t)blockIdx.x * kWideRows;
+  const int64_t row0 = (int64_t)blockIdx.x * ROWS;
   const u32x4* pimg = img + (size_t)blockIdx.y * steps_pad * STEP_U4;
   const uint8_t* tbase = table + (uint64_t)row0 * (uint64_t)row_bytes;
   const int r8 = lane & 7, ck = lane >> 3;
   const uint32_t last_off = (uint32_t)(row_bytes - 16);
 
   // byte offsets of this lane's X and Y rows from the block's first row (32-bit:
-  // the planner bounds kWideRows * row_bytes)
-  uint32_t xoff[kWideMT], yoff[kWideMT];
+  // the planner bounds ROWS * row_bytes)
+  uint32_t xoff[MT], yoff[MT];
 #pragma unroll
-  for (int mt = 0; mt < kWideMT; mt++) {
-    const int64_t rx = min(row0 + wv * (kWideMT * 16) + 16 * mt + r8, V - 1) - row0;
-    const int64_t ry = min(row0 + wv * (kWideMT * 16) + 16 * mt + 8 + r8, V - 1) - row0;
+  for (int mt = 0; mt < MT; mt++) {
+    const int64_t rx = min(row0 + wv * (MT * 16) + 16 * mt + r8, V - 1) - row0;
+    const int64_t ry = min(row0 + wv * (MT * 16) + 16 * mt + 8 + r8, V - 1) - row0;
     xoff[mt] = (uint32_t)(rx * row_bytes);
     yoff[mt] = (uint32_t)(ry * row_bytes);
   }
   // offset of this lane's 16-byte chunk of K step s within a row
   auto koff = [&](int s) { return min(128u * (uint32_t)s + 16u * (uint32_t)ck, last_off); };
 
-  f32x4 acc[kWideMT][NTILE];
+  f32x4 acc[MT][NTILE];
 #pragma unroll
-  for (int mt = 0; mt < kWideMT; mt++)
+  for (int mt = 0; mt < MT; mt++)
 #pragma unroll
     for (int nt = 0; nt < NTILE; nt++) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // ranking mode, pass 0: squares of this lane's table values per M-tile (lane l
   // holds row l % 16 of each M-tile, 16 of every 64 values)
-  float nsq[kWideMT];
+  float nsq[MT];
 #pragma unroll
-  for (int mt = 0; mt < kWideMT; mt++) nsq[mt] = 0.f;
+  for (int mt = 0; mt < MT; mt++) nsq[mt] = 0.f;
   const bool do_nrm = RANK && blockIdx.y == 0;
 
   // first chunk of the image: loads issued before the table loads, so the LDS
@@ -180,12 +185,12 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
 
   // ring of table loads: the j-th step of a chunk lives in slot j and is loaded
   // CK - 1 steps ahead of its use
-  u32x4 ax[CK][kWideMT], ay[CK][kWideMT];
+  u32x4 ax[CK][MT], ay[CK][MT];
 #pragma unroll
   for (int r = 0; r < CK - 1; r++) {
     const uint32_t ko = koff(r);
 #pragma unroll
-    for (int mt = 0; mt < kWideMT; mt++) {
+    for (int mt = 0; mt < MT; mt++) {
       ax[r][mt] = __builtin_nontemporal_load((const u32x4*)(tbase + (xoff[mt] + ko)));
       ay[r][mt] = __builtin_nontemporal_load((const u32x4*)(tbase + (yoff[mt] + ko)));
     }
@@ -214,14 +219,14 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
       // j = 0, else step j - 1 of the next chunk (clamped to the row end)
       const uint32_t ko = koff(j == 0 ? pc * CK + CK - 1 : pn * CK + j - 1);
 #pragma unroll
-      for (int mt = 0; mt < kWideMT; mt++) {
+      for (int mt = 0; mt < MT; mt++) {
         ax[nb][mt] = __builtin_nontemporal_load((const u32x4*)(tbase + (xoff[mt] + ko)));
         ay[nb][mt] = __builtin_nontemporal_load((const u32x4*)(tbase + (yoff[mt] + ko)));
       }
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 P[kWideMT], Q[kWideMT];
+      bf16x8 P[MT], Q[MT];
 #pragma unroll
-      for (int mt = 0; mt < kWideMT; mt++) {
+      for (int mt = 0; mt < MT; mt++) {
         const u32x4 x = ax[cb][mt], y = ay[cb][mt];
         u32x4 p, qv;
 #pragma unroll
@@ -241,14 +246,14 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
         for (int f = 0; f < NF; f++) {
           const bf16x8 bop = __builtin_bit_cast(bf16x8, bl[(NF * nt + f) * 64]);
 #pragma unroll
-          for (int mt = 0; mt < kWideMT; mt++)
+          for (int mt = 0; mt < MT; mt++)
             acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f < NF / 2 ? P[mt] : Q[mt], bop, acc[mt][nt], 0,
                                                                    0, 0);
         }
       }
       if (do_nrm) {
 #pragma unroll
-        for (int mt = 0; mt < kWideMT; mt++) nsq[mt] = wide_sumsq(P[mt], wide_sumsq(Q[mt], nsq[mt]));
+        for (int mt = 0; mt < MT; mt++) nsq[mt] = wide_sumsq(P[mt], wide_sumsq(Q[mt], nsq[mt]));
       }
 #pragma unroll
       for (int q = 0; q < NPER; q++) nxt[j * STEP_U4 + min(tid + q * NTHR, STEP_U4 - 1)] = st[q];
@@ -264,7 +269,7 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
   // top k is still emitted, so the merged result does not depend on timing.
   // Only the order value (the upper 32 bits) of each bound is used; the bounds
   // of this wave's rows are loaded together, before the logits pass through LDS.
-  constexpr int PER_LANE = kWideRows / 64;
+  constexpr int PER_LANE = ROWS / 64;
   constexpr int MAXC = (NC + kWideWaves - 1) / kWideWaves;
   const int64_t bcol0 = (int64_t)blockIdx.y * NC + wv;
   uint32_t tords[MAXC];
@@ -282,7 +287,7 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
     __shared__ float nred[kWideWaves];
     float m = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < kWideMT; mt++) {
+    for (int mt = 0; mt < MT; mt++) {
       float x = nsq[mt] + __shfl_xor(nsq[mt], 16, 64);
       x += __shfl_xor(x, 32, 64);
       m = fmaxf(m, x);
@@ -299,29 +304,31 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
 
   if constexpr (RANK) {
     // Ranking mode: the block's kb best keys per residual row, without passing the
-    // logits through LDS.  Lane l holds 16 rows of column 16 nt + l % 16 in each
-    // N-tile (rows 64 wv + 16 mt + 4 (l / 16) + i), one of the column's 32 groups
-    // of rows.  G = the kb-th largest group maximum bounds the column's kb-th
+    // logits through LDS.  Lane l holds 4 MT rows of column 16 nt + l % 16 in each
+    // N-tile (rows 16 MT wv + 16 mt + 4 (l / 16) + i), one of the column's 32
+    // groups of rows.  G = the kb-th largest group maximum bounds the column's kb-th
     // largest logit from below (kb groups reach G, each with a row of its own), so
     // only logits >= G are keyed, and the kb best keys of those are taken.  A
     // column with more than kWideRankCap of them (ties) sends the block to the
     // general selection below.
-    __shared__ float gmx[NC][kWideWaves * 4 + 1];  // group maxima (odd stride)
-    __shared__ float glim[NC];
-    __shared__ uint32_t gcnt[NC];
-    __shared__ uint64_t gkey[NC][kWideRankCap];
+    // in the image buffers, free after the K loop (wide_rank_lds bytes)
+    constexpr int GS = kWideWaves * 4 + 1;                  // group maxima stride (odd)
+    uint64_t* gkey = (uint64_t*)smem;                        // [NC][kWideRankCap]
+    float* gmx = (float*)(gkey + NC * kWideRankCap);         // [NC][GS] group maxima
+    float* glim = gmx + NC * GS;                             // [NC]
+    uint32_t* gcnt = (uint32_t*)(glim + NC);                 // [NC]
     __shared__ uint32_t govf;
-    const bool tail = row0 + kWideRows > V;  // the block has rows past the table
-    const int rbase = wv * (kWideMT * 16) + 4 * (lane >> 4);
+    const bool tail = row0 + ROWS > V;  // the block has rows past the table
+    const int rbase = wv * (MT * 16) + 4 * (lane >> 4);
 #pragma unroll
     for (int nt = 0; nt < NTILE; nt++) {
       float m = -__builtin_inff();
 #pragma unroll
-      for (int mt = 0; mt < kWideMT; mt++)
+      for (int mt = 0; mt < MT; mt++)
 #pragma unroll
         for (int i = 0; i < 4; i++)
           m = (!tail || row0 + rbase + 16 * mt + i < V) ? fmaxf(m, acc[mt][nt][i]) : m;
-      gmx[16 * nt + (lane & 15)][wv * 4 + (lane >> 4)] = m;
+      gmx[(16 * nt + (lane & 15)) * GS + wv * 4 + (lane >> 4)] = m;
     }
     if (tid < NC) gcnt[tid] = 0;
     if (tid == 0) govf = 0;
@@ -331,7 +338,7 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
 #pragma unroll
       for (int j = 0; j < kWideRankKeys; j++) t[j] = -__builtin_inff();
       for (int g = 0; g < kWideWaves * 4; g++) {
-        float x = gmx[tid][g];
+        float x = gmx[tid * GS + g];
 #pragma unroll
         for (int j = 0; j < kWideRankKeys; j++) {
           const float hi = fmaxf(t[j], x);
@@ -350,14 +357,14 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
       const int col = 16 * nt + (lane & 15);
       const float lim = glim[col];
 #pragma unroll
-      for (int mt = 0; mt < kWideMT; mt++)
+      for (int mt = 0; mt < MT; mt++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int rl = rbase + 16 * mt + i;
           const float x = acc[mt][nt][i];
           if (x >= lim && (!tail || row0 + rl < V)) {
             const uint32_t slot = atomicAdd(&gcnt[col], 1u);
-            if (slot < (uint32_t)kWideRankCap) gkey[col][slot] = make_key(x, (uint32_t)(row0 + rl));
+            if (slot < (uint32_t)kWideRankCap) gkey[col * kWideRankCap + slot] = make_key(x, (uint32_t)(row0 + rl));
           }
         }
     }
@@ -373,7 +380,7 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
         for (int t = 0; t < k; t++) {  // keys are unique (one per row)
           uint64_t best = 0;
           for (int j = 0; j < c; j++) {
-            const uint64_t y = gkey[tid][j];
+            const uint64_t y = gkey[tid * kWideRankCap + j];
             best = (y < prev && y > best) ? y : best;
           }
           out[t] = best;  // 0: no key left
@@ -393,7 +400,7 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
         const uint64_t prev = t == 0 ? ~0ull : rsel[16 * nt + (lane & 15)];
         uint64_t best = 0;
 #pragma unroll
-        for (int mt = 0; mt < kWideMT; mt++)
+        for (int mt = 0; mt < MT; mt++)
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const int rl = rbase + 16 * mt + i;
@@ -424,12 +431,12 @@ __global__ void __launch_bounds__(64 * kWideWaves) wide_logits_kernel(
 
   // logits of the block's rows through LDS (the image buffers are free now)
 #pragma unroll
-  for (int mt = 0; mt < kWideMT; mt++)
+  for (int mt = 0; mt < MT; mt++)
 #pragma unroll
     for (int nt = 0; nt < NTILE; nt++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int rl = wv * (kWideMT * 16) + 16 * mt + 4 * (lane >> 4) + i;
+        const int rl = wv * (MT * 16) + 16 * mt + 4 * (lane >> 4) + i;
         slog[rl * LS + 16 * nt + (lane & 15)] = acc[mt][nt][i];
       }
   lds_barrier();
@@ -567,6 +574,14 @@ static hipError_t launch_wide_mode(const TableDesc& t, const LogitsPlan& p, cons
       case 6: return launch_wide_nt<6, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
       case 7: return launch_wide_nt<7, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
       case 8: return launch_wide_nt<8, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 9: return launch_wide_nt<9, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 10: return launch_wide_nt<10, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 11: return launch_wide_nt<11, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 12: return launch_wide_nt<12, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 13: return launch_wide_nt<13, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 14: return launch_wide_nt<14, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 15: return launch_wide_nt<15, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
+      case 16: return launch_wide_nt<16, true>(t, p, (const u32x4*)img, cand, thr, x, stream, ev0, ev1);
       default: break;
     }
   }
@@ -587,14 +602,14 @@ hipError_t launch_wide_rank(const TableDesc& t, const LogitsPlan& p, const void*
   hipError_t e = launch_wide_mode<true>(t, p, R, img, cand, nullptr, x, stream, ev0, ev1);
   if (e != hipSuccess) return e;
   // the kernel emits each block's keys best first
-  return launch_rescore(t, p, R, (int)x.wire, cand, p.nblk, kWideRows, (const float*)x.aux, p.nblk, p.steps * 64, ids,
+  return launch_rescore(t, p, R, (int)x.wire, cand, p.nblk, wide_rows(p.ntile), (const float*)x.aux, p.nblk, p.steps * 64, ids,
                         scores, stream, 1);
 }
 
 int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, const char** why, bool rank) {
     // passes of at most 64 residual rows (128 ranking), split evenly into 16-row
     // N-tiles
-    if ((uint64_t)(kWideRows + 1) * (uint64_t)t.row_bytes >= (1ull << 32)) {
+    if ((uint64_t)(wide_rows(1) + 1) * (uint64_t)t.row_bytes >= (1ull << 32)) {
       *why = "rows too long for the wide path";
       return -5;
     }
@@ -603,12 +618,16 @@ int32_t plan_wide(const TableDesc& t, int64_t batch, int32_t k, LogitsPlan* p, c
     p->ntile = (int32_t)cdiv(cdiv(batch, p->npass), 16);
     const int ck = wide_ck(p->ntile);
     p->steps = (int32_t)(cdiv(cdiv(t.hidden, 64), ck) * ck);
-    p->nblk = (int32_t)cdiv(t.V, kWideRows);
+    const int rows = wide_rows(p->ntile);
+    p->nblk = (int32_t)cdiv(t.V, rows);
     const size_t img_lds = (size_t)2 * ck * p->ntile * nf * 1024;
-    // the logits pass through LDS after the K loop (ranking mode: the selection
-    // rounds' [waves + 1][columns] keys)
-    const size_t log_lds = rank ? (size_t)(kWideWaves + 1) * 16 * p->ntile * 8
-                                : (size_t)kWideRows * (16 * p->ntile + 1) * 4;
+    // after the K loop, in the same buffer: the logits (exact mode); ranking mode:
+    // the candidate lists, group maxima, bounds and counts per column, or the
+    // selection rounds' [waves + 1][columns] keys
+    const size_t nc = (size_t)16 * p->ntile;
+    const size_t log_lds = rank ? std::max(nc * (kWideRankCap * 8 + (kWideWaves * 4 + 1) * 4 + 8),
+                                           (size_t)(kWideWaves + 1) * nc * 8)
+                                : (size_t)rows * (nc + 1) * 4;
     p->lds_bytes = std::max(img_lds, log_lds);
     p->img_bytes = (size_t)p->npass * p->steps * p->ntile * nf * 1024;
     if (!rank) {

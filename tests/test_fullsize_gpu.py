@@ -97,8 +97,9 @@ def test_lm31b_logits_b64_mfma_paths(path):
 
 
 # past 64 rows: the automatic choice ranks with the wide kernel in one table pass
-# of 5 to 8 N-tiles (up to 128 rows), then with two passes
-@pytest.mark.parametrize("B", [96, 128, 200])
+# of 5 to 8 N-tiles over 512-row blocks (up to 128 rows), then of 9 to 16 over
+# 256-row blocks (up to 256 rows)
+@pytest.mark.parametrize("B", [96, 128, 200, 256])
 def test_lm31b_logits_wide_rank_past_64_rows(B):
     _check("lm31b", B, 10, [0, 15, 16, 63, 64, B // 2 + 1, B - 1])
 

@@ -73,12 +73,13 @@ def test_gemm_path_ragged(V, d, B):
     full_check(host, BF16, V, d, R, min(10, V), GEMM)
 
 
-# the rank path: up to 128 rows a pass the wide kernel ranks (1 to 8 N-tiles,
-# 512-row blocks keeping 4 keys each; 65 and 100 rows are one pass of 5 and 7
-# N-tiles, 130 rows two passes of 5), past 128 the contraction (256-row column
-# tiles, ragged last one, one or many vocabulary ranges, heaps of fewer keys than k)
+# the rank path: up to 256 rows the wide kernel ranks in one pass (1 to 8 N-tiles
+# over 512-row blocks, 9 to 16 over 256-row blocks, 4 keys per block; 65, 100,
+# 130, 200 and 256 rows are 5, 7, 9, 13 and 16 N-tiles), past 256 the contraction
+# (256-row column tiles, ragged last one, one or many vocabulary ranges, lists of
+# fewer keys than k)
 @pytest.mark.parametrize("V,d", [(5003, 200), (4099, 896), (1001, 64), (20000, 5376), (37, 8), (70000, 512)])
-@pytest.mark.parametrize("B", [1, 9, 17, 33, 64, 65, 100, 128, 130, 257])
+@pytest.mark.parametrize("B", [1, 9, 17, 33, 64, 65, 100, 128, 130, 200, 256, 257])
 def test_rank_path_ragged(V, d, B):
     host = synth.make_table(BF16, V, d, seed=500 + V)
     R = synth.residuals(B, d, seed=600 + B)
@@ -109,13 +110,13 @@ def test_rank_path_odd_block_count(k, path):
 
 
 @pytest.mark.parametrize("k", [10, 40, 64])
-@pytest.mark.parametrize("B", [2, 70, 140])
+@pytest.mark.parametrize("B", [2, 70, 140, 300])
 def test_rank_path_rescans_a_range_holding_many_winners(k, B):
     # 80 planted winners in rows 256..335, inside one range of the ranking kernel
     # (a 512-row block of the wide kernel keeping 4 keys for B = 2 and 70, a
-    # 256-row range of the contraction keeping 16 for B = 140): the certificate
-    # must send the whole range to exact rescoring for the answer to hold the
-    # other winners
+    # 256-row block keeping 4 for B = 140, a 256-row range of the contraction
+    # keeping 16 for B = 300): the certificate must send the whole range to exact
+    # rescoring for the answer to hold the other winners
     V, d = 30000, 512
     host = synth.make_table(BF16, V, d, seed=23)
     R = synth.residuals(B, d, seed=24)
@@ -206,9 +207,9 @@ def test_zero_residual_gives_ids_in_order(path):
 
 
 # all-tie blocks of the wide ranking kernel (every logit 0) take its selection
-# rounds over the accumulators, at 1 to 8 N-tiles; rows 16..31 are nonzero so
+# rounds over the accumulators, at 1 to 16 N-tiles; rows 16..31 are nonzero so
 # that tied and untied columns share a block
-@pytest.mark.parametrize("B", [3, 40, 72, 128])
+@pytest.mark.parametrize("B", [3, 40, 72, 128, 200, 256])
 def test_rank_path_all_tie_blocks(B):
     V, d = 3000, 128
     host = synth.make_table(BF16, V, d, seed=5)
