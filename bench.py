@@ -541,6 +541,21 @@ def main() -> int:
         d["kernel_pct_hbm_peak"] = round(100 * qc.table_bytes / (d["kernel_median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)
         d["single_call_us"] = _single(torch, fq)
         d["tables"] = "4 copies, cycled"
+        # a plain read stream over the same copies, cycled alike: what a pass over
+        # 272 MB costs on its own (launch, ramp and tail included)
+        sink = torch.empty(1, dtype=torch.int32, device=dev)
+        pturn = [0]
+
+        def fprobe():
+            pturn[0] += 1
+            etg.hbm_read_probe(qwts[pturn[0] % 4].rows, sink)
+        for _ in range(4):
+            fprobe()
+        dp = _dist(torch, fprobe, 52, hev)
+        dp["GBps"] = round(qc.table_bytes / (dp["median_us"] * 1e-6) / 1e9, 1)
+        dp["pct_hbm_peak"] = round(100 * dp["GBps"] / HBM_PEAK_GBPS, 1)
+        d["read_stream_reference_272MB"] = dp
+        d["pct_of_read_stream_272MB"] = round(100 * dp["median_us"] / d["median_us"], 1)
         also["qwen05b_logits_top10_B1"] = d
         log(f"qwen05b gather {also['qwen05b_gather_628_zipf_ids']['median_us']} us, logits B=1 {d['median_us']} us")
         # the same calls from host ids / to a host answer, eager beside graph-cached
