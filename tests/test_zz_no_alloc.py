@@ -44,8 +44,9 @@ def _both(t, R, k):
 
 
 # (first batch, second smaller batch): the rank path's contraction then its wide
-# kernel, the wide kernel then the stream kernel, the stream kernel with 8 then 1 row
-@pytest.mark.parametrize("B1,B2", [(300, 40), (64, 5), (8, 1)])
+# kernel over 256-row blocks (16 N-tiles), the wide kernel at 8 then 3 N-tiles, the
+# wide kernel then the stream kernel, the stream kernel with 8 then 1 row
+@pytest.mark.parametrize("B1,B2", [(300, 256), (128, 40), (64, 5), (8, 1)])
 def test_noalloc_matches_the_workspace_entry_point(B1, B2):
     V, d, k = 20011, 896, 10
     host = synth.make_table(synth.BF16, V, d, seed=41)
