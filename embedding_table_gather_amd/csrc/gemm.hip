@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
   static_assert(NA >= 2 && NB >= 2 && NA <= 5 && NB <= 5, "ring depths");
   static_assert(NT == 2 && MT == WN, "one hi and one lo N-tile (split) or two N-tiles; one M-tile per wave column");
   constexpr int SLICE = kGemmBM * 64;                     // one stage of 256 table or residual rows
-  uint64_t* heaps = (uint64_t*)(smem + (NA + NB) * SLICE);  // [COLS][k] descending lists
+  uint64_t* heaps = (uint64_t*)(smem + (NA + NB) * SLICE);  // [COLS][k] lists or heaps
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps wave choices scalar
   const int mw = wv / WN, nw = wv % WN;
@@ -347,12 +347,12 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
       }
     }
     // Epilogue: every column (residual row) of the tile keeps its k best keys in
-    // LDS (0 = empty slot): a descending list for k <= 16, else a min-heap.  Register i of tile (a, t) holds
-    // row WR mw + 32 a + 8 (i / 4) + 4 (lane / 32) + i % 4 of operand column
-    // WC nw + 32 t + lane % 32 (split columns: N-tile 0 is hi and 1 is lo, so a lane
-    // sees 64 rows of one residual row; ranking columns: each N-tile is its own
-    // residual row), so a column's 256 rows are spread over 4 holders (two wave
-    // rows, two half-waves) of 64 values.
+    // LDS (0 = empty slot): a descending list for k <= 16, else a min-heap.
+    // Register i of tile (a, t) holds row WR mw + 32 a + 8 (i / 4) + 4 (lane / 32)
+    // + i % 4 of operand column WC nw + 32 t + lane % 32 (split columns: N-tile 0
+    // is hi and 1 is lo, so a lane sees 64 rows of one residual row; ranking
+    // columns: each N-tile is its own residual row), so a column's 256 rows are
+    // spread over 4 holders (two wave rows, two half-waves) of 64 values.
     //  * T = the list's k-th key (0 while not full); on the first tile and for
     //    k <= 64, at least the smallest over the 4 holders of each one's
     //    ceil(k / 4)-th largest maximum of its 16 groups of 4 rows: at least k
@@ -529,7 +529,11 @@ __global__ void __launch_bounds__(64 * WM * WN) gemm_logits_kernel(
           }
         }
         gemm_stage_barrier<0>();
-        if (aovf[round & 1] == 0) break;
+        if (aovf[round & 1] == 0) {
+          // every wave has read the flag before the next tile's copies refill the rings
+          gemm_stage_barrier<0>();
+          break;
+        }
       }
     }
   }
