@@ -55,7 +55,7 @@ def test_gather_wire_bit_exact(dtype, d, wire, scaled):
     (etg.PATH_STREAM, BF16, 5003, 896, 1), (etg.PATH_STREAM, BF16, 5003, 200, 8),
     (etg.PATH_WIDE, BF16, 5003, 896, 33), (etg.PATH_GEMM, BF16, 4099, 512, 70),
     (etg.PATH_Q8, Q8_0, 3001, 768, 3), (etg.PATH_ROW, BF16, 5003, 896, 1), (etg.PATH_ROW, F32, 2049, 100, 2),
-    (etg.PATH_RANK, BF16, 4099, 512, 70),
+    (etg.PATH_RANK, BF16, 4099, 512, 70), (etg.PATH_RANK, BF16, 4099, 512, 200), (etg.PATH_RANK, BF16, 4099, 512, 300),
 ])
 @pytest.mark.parametrize("wire", WIRES)
 def test_logits_wire_equals_logits_of_decoded_rows(path, dtype, V, d, B, wire):
