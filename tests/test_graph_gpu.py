@@ -90,7 +90,7 @@ def test_captured_step_replays_match_eager(dtype, V, d, B, path):
                 assert np.array_equal(bits(a), bits(b)), (rep, j)
 
 
-@pytest.mark.parametrize("B", [70, 300])
+@pytest.mark.parametrize("B", [70, 200, 300])
 def test_captured_rank_path_replays_match_eager(B):
     # the rank path answers the top-k alone (no probabilities or raw logits):
     # gather + top-k captured, replayed with new inputs, against eager calls
