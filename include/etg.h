@@ -171,7 +171,7 @@ typedef enum {
                           2 residuals, a wave per row, f32 FMAs (no bf16 rounding of the
                           residual)                                                       */
   ETG_PATH_RANK = 7    /* bf16 tables with hidden <= 16384, top-k only: the WIDE kernel
-                          (up to 64 rows) or the GEMM tiles rank with the residual
+                          (one pass of up to 256 rows) or the GEMM tiles rank with the residual
                           rounded once to bf16, then every row that a rigorous error
                           bound cannot rule out is rescored with f32 FMAs from the f32
                           residual (half the MFMA work of the hi + lo split)               */
