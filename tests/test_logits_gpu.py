@@ -150,6 +150,30 @@ def test_split_path_keeps_many_winners_of_one_tile(k, B):
     assert np.array_equal(gids[0], oids[0])
 
 
+# 256 planted rows filling the tile of rows 256..511, ranked round-robin over the 4
+# holders of a column's tile rows (wave row, half-wave) first and then over each
+# holder's 16 groups of 4 rows: the top k are spread as evenly as possible, so a
+# first-tile bound vouching for fewer than ceil(k / 4) groups per holder drops a
+# winner whenever 4 does not divide k (split contraction, and the rank path's
+# contraction, whose certificate relies on each range's list being its top keys)
+@pytest.mark.parametrize("k", [1, 5, 6, 13, 40, 63])
+@pytest.mark.parametrize("path,B", [(GEMM, 2), (GEMM, 70), (RANK, 300)])
+def test_first_tile_bound_keeps_winners_spread_over_holders(path, B, k):
+    V, d = 30000, 512
+    host = synth.make_table(BF16, V, d, seed=27)
+    R = synth.residuals(B, d, seed=28)
+    u = R[0] / np.linalg.norm(R[0])
+    rows = np.arange(256)
+    holder = (rows // 128) * 2 + (rows % 8) // 4
+    group = (rows % 128) // 32 * 4 + (rows % 32) // 8
+    rank = 4 * ((rows % 4) * 16 + group) + holder
+    for r in rows:
+        host[256 + r] = synth.f32_to_bf16_bits((u * (0.9 - 0.002 * rank[r])).astype(np.float32))
+    gids, _, oids, _ = full_check(host, BF16, V, d, R, k, path)
+    assert np.array_equal(gids[0], 256 + np.argsort(rank)[:k])
+    assert np.array_equal(gids[0], oids[0])
+
+
 # the row path: rows of 16 bytes to 16 KiB (1 to 16 KiB loads, the last one partial),
 # f32 / bf16 / f16 tables, one table pass per residual row
 @pytest.mark.parametrize("dtype,V,d", [(BF16, 5003, 200), (BF16, 4099, 896), (BF16, 37, 8), (BF16, 20000, 5376),
