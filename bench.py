@@ -185,6 +185,21 @@ def _timed(torch, fn, iters: int, events: _HipEvents = None):
     return ms, kms
 
 
+def _settle(torch, fn, seconds: float = 0.1):
+    """Run fn back to back for about `seconds` before it is timed.  The GPU's clocks
+    drop while the host generates a table and take tens of milliseconds of load to
+    come back (measured after a 1.5 s idle: the Q8_0 one-row call ran 284, 273, 269
+    and 266 us in its first four windows of 30 calls and 263-265 us from then on; the
+    Qwen-shaped one-row call 58.2, then 55.4, then 54.5-54.8 us per call in windows
+    of 120 calls), so every distribution below is taken in that settled state."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def _dist(torch, fn, iters: int, events: _HipEvents, kernel: bool = False) -> dict:
     """Per-call time of fn over `iters` repeats: median, p10 and p90 in us.  A
     repeat is a batch of back-to-back calls between two events (batches of about
@@ -193,7 +208,7 @@ def _dist(torch, fn, iters: int, events: _HipEvents, kernel: bool = False) -> di
     fn takes (ev_before, ev_after), recorded by the library around its table
     kernel on one call of each batch, and the kernel's median is added."""
     import numpy as np
-    torch.cuda.synchronize()
+    _settle(torch, fn)
     t1 = time.perf_counter()
     for _ in range(3):
         fn()
@@ -306,11 +321,18 @@ def main() -> int:
         table.embed_gather(ids, out=x, check=False)
         table.logits_topk(R, k, workspace=ws, out_ids=oid, out_scores=osc, events=evs)
 
+    hev = _HipEvents()
+    rd = None
+    if not args.no_extras:
+        # the plain read stream over the same table (the library's probe), as a measured
+        # reference beside the 8 TB/s nominal; taken first, it also brings the GPU's
+        # clocks out of the idle state the host-side table generation leaves
+        sink = torch.empty(1, dtype=torch.int32, device=dev)
+        rd = _dist(torch, lambda: etg.hbm_read_probe(rows, sink), 20, hev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    hev = _HipEvents()
     # eager steps, with the table kernel timed alone by events around it
     ms, kms = _timed(torch, step, args.steps, events=hev)
     ms_graph = None
@@ -378,10 +400,7 @@ def main() -> int:
         also["decode_step"]["single_call_us"] = _single(torch, step)
         if ms_graph is not None:
             also["decode_step"]["hipgraph_replay_us"] = round(ms_graph * 1e3, 1)
-        # plain read and write streams on the same box (the library's probes), as
-        # measured references beside the 8 TB/s nominal
-        sink = torch.empty(1, dtype=torch.int32, device=dev)
-        rd = _dist(torch, lambda: etg.hbm_read_probe(rows, sink), 20, hev)
+        # plain read (taken before the steps) and write streams on the same box
         rs_gbps = cfg.table_bytes / (rd["median_us"] * 1e-6) / 1e9
         also["read_stream_reference"] = {
             "what": "etg_hbm_read_probe over the 2.82 GB table", "us_per_call": rd["median_us"],
