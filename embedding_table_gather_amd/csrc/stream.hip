@@ -100,14 +100,28 @@ __device__ __forceinline__ void stream_stage_image(u32x4* simg, const void* __re
   }
 }
 
+// Lanes 0..31 receive lane L + 32's value (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float lane_plus32(float v) {
+  return __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
+}
+
+// Lane L receives lane L + N's value within its row of 16 lanes (DPP row_shl:N; 0 past
+// the row's end).
+template <int N>
+__device__ __forceinline__ float row_shl(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x100 + N, 0xf, 0xf, false));
+}
+
 template <int NBC>
 __device__ __forceinline__ void stream_store_group(f32x4 acc, float* dst, int lane) {
+  // y = D[r][b] + D[r + 8][8 + b] (lanes L and L + 40), then + the lo columns' sum
+  // from lane L + 4 when packed; cross-lane moves by permlane and DPP, not LDS
   f32x4 y;
 #pragma unroll
-  for (int i = 0; i < 4; i++) y[i] = acc[i] + __shfl(acc[i], (lane + 40) & 63, 64);
+  for (int i = 0; i < 4; i++) y[i] = acc[i] + row_shl<8>(lane_plus32(acc[i]));
   if (NBC == 4) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) y[i] = y[i] + __shfl(y[i], (lane + 4) & 63, 64);
+    for (int i = 0; i < 4; i++) y[i] = y[i] + row_shl<4>(y[i]);
   }
   if (lane < 32 && (lane & 15) < NBC) {
     const int b = lane & 15, r0 = 4 * (lane >> 4);
@@ -589,7 +603,7 @@ __global__ void __launch_bounds__(1024) stream_q8_kernel(
   for (int p = 0; p < kQ8mMaxPairs; p++) {
     f32x4 y;
 #pragma unroll
-    for (int i = 0; i < 4; i++) y[i] = acc[p][i] + __shfl(acc[p][i], (lane + 32) & 63, 64);
+    for (int i = 0; i < 4; i++) y[i] = acc[p][i] + lane_plus32(acc[p][i]);
     if (p < npairs && lane < 32) {
 #pragma unroll
       for (int i = 0; i < 4; i++) mylog[(16 * p + n) * NBC + 4 * g + i] = y[i];
