@@ -1,12 +1,13 @@
 """The Q8_0 stream path of logits_topk on the GPU against the CPU oracle.
 
-Two kernels serve the path.  Hidden a multiple of 256 (768, 5376, 8192 below)
-takes the matrix-core kernel: one MFMA per 32-value block and 16-row tile,
-passes of 8 residual rows (1 to 17 rows: one pass, ragged passes, three passes).
-Other widths take the lane-split kernel; its shapes cover every lane layout,
-from 1 block per row (64 rows per wave) to 100 (2 blocks per lane), with passes
-of 2 residual rows.  Ragged vocabularies throughout.  Special cases pin exact ids
-and scores.
+Two kernels serve the path.  Hidden a multiple of 256 (768, 4096, 4608, 5376,
+8192 below) takes the matrix-core kernel for two or more residual rows: one MFMA
+per 32-value block and 16-row tile, passes of 8 residual rows (2 to 17 rows: one
+pass, ragged passes, three passes).  One residual row, and other widths, take the
+lane-split kernel; its shapes cover every lane layout, from 1 block per row (64
+rows per wave) to 256 (4 blocks per lane; 128, 144 and 168 blocks leave the last
+of a lane's blocks to some lanes only), with passes of 2 residual rows.  Ragged
+vocabularies throughout.  Special cases pin exact ids and scores.
 """
 import numpy as np
 import pytest
@@ -39,9 +40,10 @@ def full_check(host, V, d, R, k, path=Q8):
     return gids, gsc, oids, osc
 
 
-# blocks per row: 1, 3, 9, 24, 100, 168, 256 -> lanes per row 1, 4, 16, 32, 64, 64, 64
+# blocks per row: 1, 3, 9, 24, 100, 168, 256, 128, 144 -> lanes per row 1, 4, 16, 32, 64, 64, 64, 64, 64
 @pytest.mark.parametrize("V,d", [(1001, 32), (3001, 96), (777, 288), (2000, 768), (4099, 3200), (4099, 5376),
-                                 (1500, 8192), (37, 64), (37, 256), (13, 512)])
+                                 (1500, 8192), (2049, 4096), (5000, 4608), (37, 64), (37, 256), (13, 512),
+                                 (61, 5376)])
 @pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 9, 17])
 def test_q8_path_ragged(V, d, B):
     host = synth.make_table(Q8_0, V, d, seed=2000 + V + d)
@@ -71,6 +73,27 @@ def test_q8_one_hot_residual_selects_column_exactly(d):
     oids, osc = oracle.topk(L, 20)
     assert np.array_equal(gids, oids)
     assert np.array_equal(bits(gsc), bits(osc))
+
+
+@pytest.mark.parametrize("d", [4096, 4608, 5376, 8192])
+def test_q8_one_row_one_hot_in_every_block_round(d):
+    # one residual row (the lane-split kernel, 64 lanes per row, lane l taking blocks
+    # l, l + 64, ...): a single 1 at the first and last value of each round of 64
+    # blocks and in an odd block (both byte alignments of a block) gives the logit
+    # int8 * scale exactly
+    V = 3001
+    host = synth.make_table(Q8_0, V, d, seed=2350 + d)
+    t = table(host, Q8_0, V, d)
+    nb = d // 32
+    cols = sorted({c for s0 in range(0, nb, 64) for c in (32 * s0, 32 * min(s0 + 64, nb) - 1, 32 * s0 + 33)})
+    for c in cols:
+        R = np.zeros((1, d), np.float32)
+        R[0, c] = 1.0
+        gids, gsc = run(t, R, 12)
+        L, _ = oracle.logits(host, Q8_0, V, d, R)
+        oids, osc = oracle.topk(L, 12)
+        assert np.array_equal(gids, oids), c
+        assert np.array_equal(bits(gsc), bits(osc)), c
 
 
 def test_q8_duplicate_rows_rank_by_id_and_planted_winners():
