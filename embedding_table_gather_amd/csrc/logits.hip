@@ -253,7 +253,18 @@ __global__ void __launch_bounds__(1024) topk_merge_wide_kernel(const uint64_t* _
 // The workgroup combines the row's log-partition partials when probabilities are
 // asked for and stages the row's nl k keys in LDS (a few loads per thread, all in
 // flight); then wave 0 keeps the heads of lists l + 64 j (j < PL) in lane l.
+//
+// For k <= 16 and at least 16 k lists, a threshold pass first, which usually
+// replaces those rounds: thread l holds list l (nl <= 1,024) in registers; the
+// lists form groups of 16 (a row of 16 lanes), and the k-th largest of the groups'
+// largest heads is a lower bound T on the row's k-th largest key (the k groups
+// reaching it hold a key each at or above it), so the answer is among the keys
+// >= T, a prefix of each list.  Those keys (k to a few k) are gathered in LDS and
+// each is written to the slot of its rank among them (keys are unique).  More than
+// kMergeThrCap of them falls back to the rounds.
 static constexpr int kSortedMergeMaxKeys = 8192;  // 64 KiB of LDS
+static constexpr int kMergeThrKeys = 16;          // keys per list held by a thread
+static constexpr int kMergeThrCap = 256;
 template <int PL>
 __global__ void __launch_bounds__(kMergeThreads) topk_merge_sorted_kernel(const uint64_t* __restrict__ cand, int nl,
                                                                           int k, int32_t* __restrict__ ids,
@@ -262,11 +273,70 @@ __global__ void __launch_bounds__(kMergeThreads) topk_merge_sorted_kernel(const 
                                                                           float lc, float* __restrict__ probs) {
   extern __shared__ uint64_t sk[];  // [nl * k]
   __shared__ float2 red[kMergeWaves];
-  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ uint64_t gmax[kMergeThreads / 16];
+  __shared__ uint64_t tbuf[kMergeThrCap];
+  __shared__ uint64_t sthr;
+  __shared__ uint32_t scnt;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t b = blockIdx.x;
   const float2 ml = probs != nullptr ? block_log_partition(lse + b * nparts, nparts, lc, red) : float2{};
   const int n = nl * k;
   const uint64_t* c = cand + b * (int64_t)n;
+  const int ngr = (nl + 15) >> 4;
+  if (k <= kMergeThrKeys && nl <= kMergeThreads && ngr >= k) {
+    uint64_t key[kMergeThrKeys];
+#pragma unroll
+    for (int j = 0; j < kMergeThrKeys; j++) key[j] = (tid < nl && j < k) ? c[(int64_t)tid * k + j] : 0;
+    // the largest head of each group of 16 lists, left in the row's lane 15
+    uint64_t m = key[0];
+    m = dpp_max_u64<0x111, 0xf>(m);  // row_shr:1
+    m = dpp_max_u64<0x112, 0xf>(m);  // row_shr:2
+    m = dpp_max_u64<0x114, 0xf>(m);  // row_shr:4
+    m = dpp_max_u64<0x118, 0xf>(m);  // row_shr:8
+    if ((lane & 15) == 15 && (tid >> 4) < ngr) gmax[tid >> 4] = m;
+    if (tid == 0) scnt = 0;
+    __syncthreads();
+    if (wv == 0) {
+      // T: the smallest group maximum with fewer than k group maxima above it
+      const uint64_t x = lane < ngr ? gmax[lane] : ~0ull;
+      int above = 0;
+      for (int g = 0; g < ngr; g++) above += gmax[g] > x ? 1 : 0;
+      const uint64_t t = (lane < ngr && above < k) ? x : ~0ull;
+      const uint64_t tmin = ~wave_max_u64(~t);
+      if (lane == 0) sthr = tmin;
+    }
+    __syncthreads();
+    const uint64_t T = sthr;
+    int nk = 0;
+#pragma unroll
+    for (int j = 0; j < kMergeThrKeys; j++) nk += (key[j] != 0 && key[j] >= T) ? 1 : 0;
+    const uint32_t slot = nk > 0 ? atomicAdd(&scnt, (uint32_t)nk) : 0u;
+    if (nk > 0 && slot + nk <= (uint32_t)kMergeThrCap) {
+#pragma unroll
+      for (int j = 0; j < kMergeThrKeys; j++)
+        if (j < nk) tbuf[slot + j] = key[j];  // the list's prefix at or above T
+    }
+    __syncthreads();
+    const int total = (int)scnt;
+    if (total <= kMergeThrCap) {
+      if (tid < total) {
+        const uint64_t x = tbuf[tid];
+        int rank = 0;
+        for (int j = 0; j < total; j++) rank += tbuf[j] > x ? 1 : 0;
+        if (rank < k) {
+          const float sc = ord_score((uint32_t)(x >> 32));
+          ids[b * k + rank] = (int32_t)(~(uint32_t)(x & 0xffffffffu));
+          scores[b * k + rank] = sc;
+          if (probs != nullptr) probs[b * k + rank] = prob_of(sc, ml, lc);
+        }
+      } else if (tid < k) {  // fewer than k keys in all: the empty key, as the rounds give
+        ids[b * k + tid] = (int32_t)~0u;
+        scores[b * k + tid] = ord_score(0u);
+        if (probs != nullptr) probs[b * k + tid] = prob_of(ord_score(0u), ml, lc);
+      }
+      return;
+    }
+  }
   constexpr int LPT = kSortedMergeMaxKeys / kMergeThreads;  // keys per thread at most
   uint64_t v[LPT];
 #pragma unroll

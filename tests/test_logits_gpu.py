@@ -290,6 +290,26 @@ def test_planted_winners_exact_order(path):
     assert np.array_equal(gids, oids)
 
 
+@pytest.mark.parametrize("k", [1, 10, 16])
+def test_merge_threshold_pass_and_its_fallback(k):
+    # 70,001 rows on the stream path: 256 per-block lists, so the merge takes its
+    # threshold pass (16-list group maxima); rows: a random residual, winners that
+    # all sit in one block's list (a whole list prefix at or above the bound), a
+    # zero residual (every logit ties: the pass overflows and the rounds answer)
+    V, d = 70001, 64
+    host = synth.make_table(BF16, V, d, seed=15)
+    R = synth.residuals(3, d, seed=16)
+    u = R[1] / np.linalg.norm(R[1])
+    planted = list(range(40000, 40000 + 16))  # one 273-row block holds them all
+    for j, v in enumerate(planted):
+        host[v] = synth.f32_to_bf16_bits((u * (2.0 - 0.05 * j)).astype(np.float32))
+    R[2] = 0
+    gids, gsc, oids, _ = full_check(host, BF16, V, d, R, k, STREAM)
+    assert gids[1].tolist() == planted[:k]
+    assert gids[2].tolist() == list(range(k)) and np.all(gsc[2] == 0)
+    assert np.array_equal(gids[:2], oids[:2])
+
+
 @pytest.mark.parametrize("path", ALL)
 def test_repeatable_bitwise(path):
     V, d = 50000, 896
