@@ -315,3 +315,30 @@ def test_step_cache_host_errors(L, table):
     g, r = ctypes.c_int64(-1), ctypes.c_int64(-1)
     assert L.etg_step_cache_stats(ctypes.c_void_p(c), ctypes.byref(g), ctypes.byref(r)) == 0 and (g.value, r.value) == (0, 0)
     assert L.etg_step_cache_destroy(ctypes.c_void_p(c)) == 0
+
+
+def test_every_valid_shape_has_an_automatic_plan(L):
+    # seeded random shapes over the whole accepted range: the automatic path always
+    # plans (a positive, 256-byte multiple workspace), and forced paths either plan or
+    # return ETG_ERANGE / ETG_ESHAPE with a message
+    import numpy as np
+    rng = np.random.default_rng(7)
+    step = {etg.F32: 4, etg.BF16: 8, etg.F16: 8, etg.Q8_0: 32}
+    paths = [etg.PATH_VALU, etg.PATH_STREAM, etg.PATH_GEMM, etg.PATH_WIDE, etg.PATH_Q8, etg.PATH_ROW, etg.PATH_RANK]
+    for _ in range(300):
+        dt = [etg.F32, etg.BF16, etg.F16, etg.Q8_0][int(rng.integers(4))]
+        d = int(rng.choice([step[dt], 64, 256, 768, 896, 2048, 4096, 5120, 5376, 8192, 16384, 65536]))
+        d = max(step[dt], d // step[dt] * step[dt])
+        V = int(rng.choice([1, 7, 63, 64, 65, 4099, 151936, 262144, 1 << 21]))
+        st, h = _create(L, FAKE, dt, V, d)
+        assert st == 0, (dt, V, d)
+        try:
+            k = int(rng.integers(1, min(V, 64) + 1))
+            for B in sorted({1, 2, 8, 9, 17, 64, 65, 256, 257, 65536, int(rng.integers(1, 4097))}):
+                n = L.etg_logits_topk_workspace(h, B, k)
+                assert n > 0 and n % 256 == 0, (dt, V, d, B, k, n, _err(L))
+                for p in paths:
+                    m = L.etg_logits_topk_workspace_ex(h, B, k, p)
+                    assert m > 0 or (m in (-3, -5) and _err(L)), (dt, V, d, B, k, p, m)
+        finally:
+            L.etg_table_destroy(h)
