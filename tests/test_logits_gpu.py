@@ -429,3 +429,40 @@ def test_logits_to_host_with_pageable_buffers():
     assert st == 0
     ev.synchronize()
     assert np.array_equal(h_ids, ids.cpu().numpy()) and np.array_equal(h_sc.view(np.int32), sc.cpu().numpy().view(np.int32))
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    step = {F32: 4, BF16: 8, F16: 8, Q8_0: 32}
+    out = []
+    for i in range(n):
+        dt = [F32, BF16, F16, Q8_0][int(rng.integers(4))]
+        d = int(rng.integers(1, 768 // step[dt] + 1)) * step[dt]
+        V = int(rng.choice([1, 5, 63, 64, 65, 257, int(rng.integers(2, 6000))]))
+        B = int(rng.choice([1, 2, 3, 8, 9, 16, 17, 33, int(rng.integers(1, 41))]))
+        k = int(rng.integers(1, min(V, 64) + 1))
+        out.append((i, dt, V, d, B, k))
+    return out
+
+
+@pytest.mark.parametrize("i,dtype,V,d,B,k", _random_shapes(40, 31))
+def test_random_shapes_every_path(i, dtype, V, d, B, k):
+    # seeded random shapes (dtype, vocabulary from 1 row up, hidden, batch, k): the
+    # automatic choice and every path that plans the shape against the oracle
+    host = synth.make_table(dtype, V, d, seed=3000 + i)
+    R = synth.residuals(B, d, seed=3100 + i)
+    t = table(host, dtype, V, d)
+    L, A = oracle.logits(host, dtype, V, d, R)
+    oids, _ = oracle.topk(L, k)
+    for path in [etg.PATH_AUTO] + ALL + [etg.PATH_Q8]:
+        if _plans(t, B, k, path):
+            gids, gsc = run(t, R, k, path)
+            fails = accept.check_full(gids, gsc, L, A, oids, accept.tol_coeff(dtype))
+            assert not fails, (path, fails[:3])
+
+
+def _plans(t, B, k, path):
+    try:
+        return t.workspace_bytes(B, k, path) > 0
+    except etg.EtgError:
+        return False
