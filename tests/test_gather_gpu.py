@@ -176,3 +176,36 @@ def test_gather_repeatable():
     for _ in range(10):
         again = t.embed_gather(ids, scale="sqrt_d", check=False)
         assert torch.equal(first.view(torch.int32), again.view(torch.int32))
+
+
+def _random_gathers(n, seed):
+    rng = np.random.default_rng(seed)
+    step = {F32: 4, BF16: 8, F16: 8, Q8_0: 32}
+    out = []
+    for i in range(n):
+        dt = [F32, BF16, F16, Q8_0][int(rng.integers(4))]
+        d = int(rng.integers(1, 2048 // step[dt] + 1)) * step[dt]
+        V = int(rng.choice([1, 2, 17, int(rng.integers(3, 5000))]))
+        cnt = int(rng.choice([1, 63, 64, 65, int(rng.integers(2, 3000))]))
+        out.append((i, dt, V, d, cnt, int(rng.integers(3))))
+    return out
+
+
+@pytest.mark.parametrize("i,dtype,V,d,n,scale_kind", _random_gathers(30, 41))
+def test_gather_random_shapes_bit_exact(i, dtype, V, d, n, scale_kind):
+    # seeded random tables, widths and id lists with some ids out of range: rows and
+    # the bad-id count bit-exact against the oracle, with no scale, x sqrt(d), or an
+    # arbitrary f32 scale
+    rng = np.random.default_rng(4000 + i)
+    host = synth.make_table(dtype, V, d, seed=4100 + i)
+    ids = rng.integers(-2, V + 2, size=n).astype(np.int32)
+    scale = [None, "sqrt_d", float(np.float32(rng.uniform(-3, 3)))][scale_kind]
+    oscale = None if scale is None else oracle.sqrt_d(d) if scale == "sqrt_d" else np.float32(scale)
+    t = table(host, dtype, V, d)
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    note(f"gather random i={i} dtype={dtype} V={V} d={d} n={n} scale={scale}")
+    out = t.embed_gather(ids_dev(ids), scale=scale, bad_count=cnt, check=False)
+    torch.cuda.synchronize()
+    ref, nbad = oracle.embed_gather(host, dtype, V, d, ids, scale=oscale)
+    assert int(cnt.item()) == nbad
+    assert np.array_equal(bits(out), bits(ref))
